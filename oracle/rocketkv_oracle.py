@@ -1,0 +1,389 @@
+"""Plain CPU oracle for RocketKV's two-stage KV-cache compression hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test-suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+helper with the HIP library and imports nothing but numpy and the standard
+library.  It is written to be read against the pages, not to be fast.
+
+Sources (cited by key in every docstring below):
+
+[RKV]   papercache.org deep notes "RocketKV: Accelerating Long-Context LLM
+        Inference via Two-Stage KV Cache Compression" (arXiv 2502.14051,
+        ICML'25).  Sections used: quick read ("how it works"), method details
+        (SnapKV stage, GQA group-level selection, pooling kernel size, HSA
+        steps 1-3, Algorithm 1, RocketKV-MT, token budget, adaptive split
+        equation for r, split inside HSA and its worked c=64 example,
+        storage/traffic analysis and Table 1).
+[GUIDE] aifetchly blog "RocketKV Guide: Two-Stage KV Cache Compression for
+        LLMs", section "Stage 1: Coarse-Grain Permanent Eviction via SnapKV"
+        (observation window and softmax(Q K^T / sqrt(D)) scoring).
+
+Precision.  Every quantity that decides an index set (window scores, pooled
+scores, channel magnitudes, approximate block scores) is computed in float32,
+the precision both sides must take such decisions in; reductions whose order
+could change a float32 result that decides an index are written in an
+explicit order (stated per function).  The attention output, which decides
+nothing, is computed in float64.  bf16 inputs are up-cast exactly by the
+caller (every bf16 value is an exact float32).
+
+Readings where the pages are silent or ambiguous (each is listed again in
+the design doc):
+  R1  r is clamped to [0.2, 0.8] (the prose bound), c >= 1 is required.
+  R2  the stage-1 keep count is ceil(S / c^r), at least the window W and at
+      most S.
+  R3  k2 (in blocks) = ceil(t / block) with t = S / c the token budget.
+  R5  softmax scale 1/sqrt(d) for both window scoring and decode attention.
+  R6  window rows attend causally (row r at position S-W+r sees keys <= it).
+  R7  candidates for eviction are the prefix [0, S-W); the window is kept.
+  R8  group aggregation is a sum over the G heads and the W window rows.
+  R9  pooling is an average pool evaluated as a zero-padded windowed SUM of
+      width k (same ranking as the average); parity of this choice with the
+      pages is unpinned.
+  R11 ties in every top-k go to the lower index.
+  R12 kept tokens are stored in ascending original position.
+  R14 sign 0 selects Kmax (q_bar >= 0).
+  R15 the approximate block score is sum over i in i1 of q_bar_i * P_i[b].
+  R16 no block is forced into the selection.
+  R17 RocketKV-MT builds blocks over the sorted candidate list.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F32 = np.float32
+
+
+# --------------------------------------------------------------------------
+# Adaptive compression split
+# --------------------------------------------------------------------------
+def split(c: float, seq_len: int, window: int, block: int, head_dim: int) -> dict:
+    """Adaptive split of the total compression ratio c.
+
+    [RKV] method details, adaptive split equation: r = min(0.2 + 0.06*log2 c,
+    0.8), and the prose right after it restricting r to [0.2, 0.8]; stage 1
+    takes c^r, stage 2 takes c^(1-r).  [RKV] token budget paragraph: t = S/c
+    (KV pairs fetched per attention op, per GQA group).  [RKV] split inside
+    HSA: page = ceil(c^((1-r)/2)) on the sequence axis, the head-dim axis gets
+    c^(1-r)/page, hence k1 = d / (c^(1-r)/page).
+
+    Returns float64 scalars r, c1, c2, t and the integer sizes n_keep (stage-1
+    kept tokens, reading R2), k2_blocks (reading R3), paper_page and the
+    paper's (real-valued) k1.
+    """
+    if not (c >= 1.0):
+        raise ValueError("compression ratio must be >= 1")
+    if not (0 < window <= seq_len) or block < 1 or head_dim < 1:
+        raise ValueError("bad sizes")
+    r = min(max(0.2 + 0.06 * math.log2(c), 0.2), 0.8)
+    c1 = c ** r
+    c2 = c ** (1.0 - r)
+    t = seq_len / c
+    n_keep = min(seq_len, max(window, math.ceil(seq_len / c1)))
+    k2 = max(1, math.ceil(t / block))
+    page = math.ceil(c ** ((1.0 - r) / 2.0))
+    paper_k1 = head_dim / (c2 / page)
+    return dict(r=r, c1=c1, c2=c2, budget_t=t, n_keep=n_keep, k2_blocks=k2,
+                paper_page=page, paper_k1=paper_k1)
+
+
+def table1_storage_traffic(c: float) -> dict:
+    """Normalised KV storage (including aux data) and traffic at ratio c.
+
+    [RKV] storage/traffic analysis and Table 1: after stage 1 the relative KV
+    storage is 1/c^r; the element-wise max and min tensors each add
+    1/c^((1-r)/2) of that (one value per page of size c^((1-r)/2), rounding
+    ignored), giving 2/c^((1+r)/2).  RocketKV-MT keeps the full cache (1).
+    Traffic is 1/c for both.
+    """
+    r = split(c, 1 << 20, 1, 1, 1)["r"]
+    after_stage1 = 1.0 / c ** r
+    per_tensor = 1.0 / c ** ((1.0 - r) / 2.0)
+    aux = after_stage1 * per_tensor * 2.0
+    return dict(rocketkv_storage=after_stage1 + aux, mt_storage=1.0 + aux,
+                traffic=1.0 / c)
+
+
+# --------------------------------------------------------------------------
+# Top-k with the lower-index tie rule
+# --------------------------------------------------------------------------
+def topk_lower_index(values: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest values, ties to the lower index, ascending.
+
+    [RKV] Algorithm 1 (argtopk) and the stage-1 top-k; tie rule is reading
+    R11.  Defined by a stable sort on the negated values: among equal values
+    the original (ascending) index order survives, so the first k entries are
+    exactly {j : #{i : v_i > v_j or (v_i == v_j and i < j)} < k}.  -0.0 and
+    +0.0 compare equal here.  Returned sorted ascending (reading R12).
+    """
+    values = np.asarray(values)
+    n = values.shape[0]
+    if not (0 <= k <= n):
+        raise ValueError("k out of range")
+    order = np.argsort(-values, kind="stable")
+    return np.sort(order[:k]).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# Stage 1: SnapKV window scoring, pooling, selection, compaction
+# --------------------------------------------------------------------------
+def window_scores(q_win_group: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Group-aggregated observation-window attention over the prefix.
+
+    [RKV] method details, SnapKV paragraph (aggregate attention between the
+    input context and the observation window at the prompt tail) and the GQA
+    paragraph (selection on group-level aggregated scores, shared by the
+    group); [GUIDE] stage 1, softmax(Q_obs K^T / sqrt(D)) summed over the
+    window.
+
+    q_win_group: [G, W, d] float32, the window queries of the G query heads
+    that share this KV head (window row r sits at position S-W+r).
+    k: [S, d] float32.
+    Returns score[j] for j in [0, S-W), float32:
+        score[j] = sum_g sum_r softmax_row(L[g, r, :])[j],
+        L[g, r, j] = q[g, r] . k[j] / sqrt(d), masked to -inf for j > S-W+r.
+    Readings R5, R6, R7, R8.  Summation order is numpy's (no index decision
+    depends on it beyond the stated tolerance).
+    """
+    q = np.asarray(q_win_group, dtype=F32)
+    k = np.asarray(k, dtype=F32)
+    G, W, d = q.shape
+    S = k.shape[0]
+    if W > S:
+        raise ValueError("window longer than sequence")
+    logits = (np.matmul(q, k.T) / F32(math.sqrt(d))).astype(F32)   # [G, W, S]
+    pos = np.arange(S)[None, :]
+    row_pos = (S - W + np.arange(W))[:, None]
+    logits = np.where((pos > row_pos)[None, :, :], F32(-np.inf), logits)
+    m = logits.max(axis=2, keepdims=True)
+    e = np.exp(logits - m).astype(F32)
+    z = e.sum(axis=2, keepdims=True, dtype=F32)
+    p = (e / z).astype(F32)
+    return p[:, :, : S - W].sum(axis=(0, 1), dtype=F32)
+
+
+def pool_sum(scores: np.ndarray, kernel: int) -> np.ndarray:
+    """Sequence pooling of the window scores (reading R9).
+
+    [RKV] quick read ("how it works", stage 1) and method details, pooling
+    paragraph: SnapKV pools along the sequence so that a key token is kept
+    together with its neighbours; kernel 63 in all RocketKV experiments.
+
+    out[j] = sum_{i=j-h}^{j+h} scores[i], h = (kernel-1)/2, terms outside
+    [0, n) are zero.  Added strictly left to right (i ascending) in float32,
+    starting from the first term.  kernel must be odd.
+    """
+    s = np.asarray(scores, dtype=F32)
+    if kernel < 1 or kernel % 2 == 0:
+        raise ValueError("pool kernel must be odd and positive")
+    n = s.shape[0]
+    h = (kernel - 1) // 2
+    out = np.zeros(n, dtype=F32)
+    for off in range(-h, h + 1):
+        lo = max(0, -off)
+        hi = min(n, n - off)
+        if lo < hi:
+            out[lo:hi] = (out[lo:hi] + s[lo + off:hi + off]).astype(F32)
+    return out
+
+
+def snapkv_select(pooled: np.ndarray, seq_len: int, window: int, n_keep: int) -> np.ndarray:
+    """Kept token positions of one KV head (readings R7, R11, R12).
+
+    [RKV] method details, SnapKV paragraph (keep the most relevant prompt
+    tokens, permanently drop the rest) and quick read (stage 1).  The top
+    (n_keep - W) prefix positions by pooled score, ascending, followed by the
+    W window positions [S-W, S).
+    """
+    if not (window <= n_keep <= seq_len):
+        raise ValueError("n_keep outside [W, S]")
+    sel = topk_lower_index(pooled, n_keep - window)
+    return np.concatenate([sel, np.arange(seq_len - window, seq_len)]).astype(np.int64)
+
+
+def snapkv_evict(q_win: np.ndarray, k: np.ndarray, v: np.ndarray | None,
+                 window: int, pool_kernel: int, n_keep: int) -> dict:
+    """Stage 1 for a whole [B, H_kv] cache.
+
+    q_win: [B, H_q, W, d]; k, v: [B, H_kv, S, d] (v may be None for the
+    RocketKV-MT form, which returns indices only).  Query head j uses KV head
+    j // G (contiguous groups).  Returns kept [B, H_kv, n_keep] int64, pooled
+    [B, H_kv, S-W] float32, and compact k/v [B, H_kv, n_keep, d] (gathered
+    rows, [RKV] quick read: permanent eviction into a smaller cache).
+    """
+    q_win = np.asarray(q_win, dtype=F32)
+    k = np.asarray(k, dtype=F32)
+    B, Hq, W, d = q_win.shape
+    _, Hkv, S, _ = k.shape
+    if W != window or Hq % Hkv:
+        raise ValueError("shape mismatch")
+    G = Hq // Hkv
+    kept = np.zeros((B, Hkv, n_keep), np.int64)
+    pooled = np.zeros((B, Hkv, S - W), F32)
+    for b in range(B):
+        for h in range(Hkv):
+            sc = window_scores(q_win[b, h * G:(h + 1) * G], k[b, h])
+            pooled[b, h] = pool_sum(sc, pool_kernel)
+            kept[b, h] = snapkv_select(pooled[b, h], S, W, n_keep)
+    out = dict(kept=kept, pooled=pooled)
+    out["k"] = np.take_along_axis(k, kept[..., None], axis=2)
+    if v is not None:
+        out["v"] = np.take_along_axis(np.asarray(v, dtype=F32), kept[..., None], axis=2)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Stage 2: HSA
+# --------------------------------------------------------------------------
+def build_aux(kc: np.ndarray, n_tokens: int, block: int) -> tuple[np.ndarray, np.ndarray]:
+    """Per-page element-wise key max/min (HSA step 1).
+
+    [RKV] method details, HSA step 1: keys grouped into consecutive pages
+    along the sequence; the element-wise max (Kmax) and min (Kmin) of each
+    page are kept as auxiliary storage, laid out along the head dimension for
+    the step-2 gather.  kc: [N, d] (rows >= n_tokens ignored).  Returns
+    (kmax, kmin), each [d, nblk] with nblk = ceil(n_tokens / block); the last
+    page covers only its valid tokens.  Exact (no rounding).
+    """
+    kc = np.asarray(kc)
+    nblk = -(-n_tokens // block)
+    d = kc.shape[1]
+    kmax = np.empty((d, nblk), kc.dtype)
+    kmin = np.empty((d, nblk), kc.dtype)
+    for b in range(nblk):
+        rows = kc[b * block:min((b + 1) * block, n_tokens)]
+        kmax[:, b] = rows.max(axis=0)
+        kmin[:, b] = rows.min(axis=0)
+    return kmax, kmin
+
+
+def channel_select(q_group: np.ndarray, k1: int) -> tuple[np.ndarray, np.ndarray]:
+    """HSA step 2, channel part, for one GQA group.
+
+    [RKV] method details, HSA step 2 and the GQA paragraph of Algorithm 1:
+    i1 = argtopk(sum over the group of |q|, k1); the sign comes from the sum
+    over the group of q.  q_group: [G, d] float32.  Both group sums are taken
+    in float32 with g ascending.  Returns (i1 ascending, q_bar [d]).
+    """
+    q = np.asarray(q_group, dtype=F32)
+    G, d = q.shape
+    if not (1 <= k1 <= d):
+        raise ValueError("k1 outside [1, d]")
+    a = np.zeros(d, F32)
+    qbar = np.zeros(d, F32)
+    for g in range(G):
+        a = (a + np.abs(q[g])).astype(F32)
+        qbar = (qbar + q[g]).astype(F32)
+    return topk_lower_index(a, k1), qbar
+
+
+def block_scores(qbar: np.ndarray, i1: np.ndarray, kmax: np.ndarray, kmin: np.ndarray) -> np.ndarray:
+    """HSA step 2, approximate page scores.
+
+    [RKV] Algorithm 1: P takes row i of Kmax where the group-summed q is >= 0
+    and of Kmin otherwise (reading R14); s1 = score(q[i1], P).  [RKV] HSA
+    step 2: the element-wise max(q*Kmax, q*Kmin) over the k1 channels
+    approximates the best attention score inside the page; for each channel
+    that max is q_bar_i * P_i[b], so s1[b] = sum_{i in i1} q_bar_i * P_i[b]
+    (reading R15), accumulated in float32 over i1 in ascending channel order,
+    one multiply then one add per term.
+    """
+    qbar = np.asarray(qbar, F32)
+    kmax = np.asarray(kmax, F32)
+    kmin = np.asarray(kmin, F32)
+    s1 = np.zeros(kmax.shape[1], F32)
+    for i in np.sort(i1):
+        row = kmax[i] if qbar[i] >= 0 else kmin[i]
+        s1 = (s1 + (qbar[i] * row).astype(F32)).astype(F32)
+    return s1
+
+
+def block_select(s1: np.ndarray, k2: int) -> np.ndarray:
+    """HSA step 2, page choice: i2 = argtopk(s1, k2) ([RKV] Algorithm 1).
+
+    min(k2, nblk) pages, ties to the lower page, ascending (R11, R16).
+    """
+    return topk_lower_index(s1, min(k2, s1.shape[0]))
+
+
+def selected_tokens(sel_blocks: np.ndarray, n_tokens: int, block: int) -> np.ndarray:
+    """Token positions covered by the chosen pages (valid tokens only)."""
+    toks = (np.asarray(sel_blocks)[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    return toks[toks < n_tokens]
+
+
+def attention(q_group: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray) -> np.ndarray:
+    """Exact attention of the G group heads over the given rows (HSA step 3).
+
+    [RKV] method details, HSA step 3 and Algorithm 1 (y = attn(q, K[i2],
+    V[i2])): o_g = softmax(q_g K^T / sqrt(d)) V, reading R5.  Float64.
+    """
+    q = np.asarray(q_group, np.float64)
+    kr = np.asarray(k_rows, np.float64)
+    vr = np.asarray(v_rows, np.float64)
+    d = q.shape[1]
+    logits = q @ kr.T / math.sqrt(d)
+    logits -= logits.max(axis=1, keepdims=True)
+    p = np.exp(logits)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ vr
+
+
+def hsa_unit(q_group, kc, vc, kmax, kmin, n_tokens, block, k1, k2, sel_override=None) -> dict:
+    """Algorithm 1 of [RKV] for one GQA group over a compact cache.
+
+    q_group [G, d]; kc, vc [N, d] (rows >= n_tokens ignored); kmax/kmin
+    [d, nblk].  ``sel_override`` replaces the chosen pages when the caller
+    wants the attention over a given page set (used to compare outputs over
+    another implementation's selection).  Returns i1, qbar, s1, sel, out
+    [G, d] float64.
+    """
+    i1, qbar = channel_select(q_group, k1)
+    s1 = block_scores(qbar, i1, kmax, kmin)
+    sel = block_select(s1, k2)
+    use = sel if sel_override is None else np.sort(np.asarray(sel_override))
+    toks = selected_tokens(use, n_tokens, block)
+    out = attention(q_group, np.asarray(kc)[toks], np.asarray(vc)[toks])
+    return dict(i1=i1, qbar=qbar, s1=s1, sel=sel, out=out)
+
+
+def hsa_decode(q: np.ndarray, kc: np.ndarray, vc: np.ndarray, n_tokens: int,
+               block: int, k1: int, k2: int) -> dict:
+    """HSA decode for a whole [B, H_kv] compact cache (aux built here).
+
+    q: [B, H_q, d]; kc, vc: [B, H_kv, N, d].  Returns stacked i1, s1, sel
+    and out [B, H_q, d] float64.
+    """
+    q = np.asarray(q, F32)
+    B, Hq, d = q.shape
+    Hkv = kc.shape[1]
+    G = Hq // Hkv
+    res = dict(i1=[], s1=[], sel=[], out=np.zeros((B, Hq, d)))
+    for b in range(B):
+        for h in range(Hkv):
+            kmax, kmin = build_aux(kc[b, h], n_tokens, block)
+            u = hsa_unit(q[b, h * G:(h + 1) * G], kc[b, h], vc[b, h], kmax, kmin,
+                         n_tokens, block, k1, k2)
+            res["i1"].append(u["i1"])
+            res["s1"].append(u["s1"])
+            res["sel"].append(u["sel"])
+            res["out"][b, h * G:(h + 1) * G] = u["out"]
+    return res
+
+
+def hsa_decode_mt_unit(q_group, k_full, v_full, cand, block, k1, k2, sel_override=None) -> dict:
+    """RocketKV-MT decode for one group (reading R17).
+
+    [RKV] method details, RocketKV-MT: all M tokens stay in memory, but stage
+    2 chooses only among the N tokens stage 1 kept (plus newly generated
+    ones).  Pages are formed over the ascending candidate list, so this is
+    HSA over the candidate rows K[cand], V[cand].
+    """
+    cand = np.asarray(cand)
+    kc = np.asarray(k_full)[cand]
+    vc = np.asarray(v_full)[cand]
+    kmax, kmin = build_aux(kc, len(cand), block)
+    return hsa_unit(q_group, kc, vc, kmax, kmin, len(cand), block, k1, k2, sel_override)
