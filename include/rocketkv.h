@@ -1,0 +1,218 @@
+/*
+ * rocketkv.h -- C ABI of librocketkv.so, the MI355X (gfx950) hot path of
+ * RocketKV two-stage KV-cache compression: SnapKV-style permanent eviction
+ * (stage 1) and Hybrid Sparse Attention decode (stage 2).
+ *
+ * Sources cited below:
+ *   [RKV]   papercache.org deep notes "RocketKV: Accelerating Long-Context LLM
+ *           Inference via Two-Stage KV Cache Compression" (arXiv 2502.14051).
+ *   [GUIDE] aifetchly blog "RocketKV Guide: Two-Stage KV Cache Compression for
+ *           LLMs", section "Stage 1: Coarse-Grain Permanent Eviction via SnapKV".
+ *
+ * Conventions shared by every call:
+ *   - Pointers named q*, k*, v*, kmax, kmin, out, *_idx, *_opt and ws are
+ *     DEVICE pointers on the current HIP device; rk_shape and rk_split_out
+ *     are HOST pointers.
+ *   - Tensors are dense row-major.  B = batch, Hq = query heads, Hkv = KV
+ *     heads, G = Hq / Hkv (query head j belongs to KV head j / G), d = head
+ *     dim.  One (batch, KV head) pair is a "unit"; units are independent.
+ *   - Element type of q, q_win, k, v, kmax, kmin is shape->dtype: RK_F32 or
+ *     RK_BF16 (bf16 = the upper 16 bits of an IEEE float32).  Supported head
+ *     dims: 64 and 128.  Scores, outputs and internal accumulation are float32.
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     device memory and keeps no pointer after a call returns; scratch space
+ *     is the caller's workspace `ws` of at least *_workspace_bytes() bytes
+ *     (256-byte aligned).
+ *   - Calls that take a stream enqueue asynchronously on it (NULL = the null
+ *     stream).  Outputs are valid after the stream reaches that point; inputs
+ *     must stay alive until then.  Calls on one workspace must not overlap.
+ *   - Errors: every argument is checked on the host before any launch; on an
+ *     error nothing is enqueued and the code is returned.  A failed launch
+ *     returns RK_EDEVICE.  rk_last_error() gives a thread-local message about
+ *     the last failure.  Inputs must be finite; NaN/Inf give unspecified
+ *     results (never out-of-bounds accesses).
+ */
+#ifndef ROCKETKV_H_
+#define ROCKETKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RK_OK = 0,
+  RK_EINVAL = 1,        /* bad argument: null pointer, size out of range   */
+  RK_EUNSUPPORTED = 2,  /* valid but not built: dtype/head dim/group size  */
+  RK_EWORKSPACE = 3,    /* workspace smaller than *_workspace_bytes()      */
+  RK_EDEVICE = 4        /* a HIP launch or runtime call failed             */
+} rk_status;
+
+typedef enum { RK_F32 = 0, RK_BF16 = 1 } rk_dtype;
+
+/* A hipStream_t, passed as an opaque pointer. */
+typedef void* rk_stream;
+
+typedef struct {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  rk_dtype dtype;
+} rk_shape;
+
+typedef struct {
+  double r;          /* split factor, clamp(0.2 + 0.06 log2 c, 0.2, 0.8)      */
+  double c1;         /* stage-1 compression c^r                               */
+  double c2;         /* stage-2 compression c^(1-r)                           */
+  double budget_t;   /* token budget t = S / c (KV pairs per attention op)    */
+  int64_t n_keep;    /* stage-1 kept tokens: min(S, max(W, ceil(S / c^r)))    */
+  int32_t k2_blocks; /* stage-2 pages: ceil(t / block)                        */
+  int32_t paper_page;/* the notes' own page size ceil(c^((1-r)/2))            */
+  double paper_k1;   /* the notes' own head-dim share: d / (c^(1-r)/page)     */
+} rk_split_out;
+
+/*
+ * rk_split -- the adaptive compression split.
+ * [RKV] method details: adaptive split equation r = min(0.2 + 0.06 log2 c,
+ * 0.8) with r restricted to [0.2, 0.8]; stage 1 takes c^r, stage 2 c^(1-r);
+ * token budget paragraph: t = S / c per GQA group; split inside HSA: page =
+ * ceil(c^((1-r)/2)), the head-dim axis gets c^(1-r)/page.
+ * c >= 1, 1 <= window <= seq_len, block >= 1, head_dim >= 1.  Pure host math
+ * in double; touches no device.  RK_EINVAL on bad arguments or out == NULL.
+ */
+rk_status rk_split(double c, int64_t seq_len, int32_t window, int32_t block,
+                   int32_t head_dim, rk_split_out* out);
+
+/*
+ * rk_snapkv_workspace_bytes -- workspace needed by rk_snapkv_evict for this
+ * shape, prompt length and window (0 if the arguments are invalid).
+ */
+size_t rk_snapkv_workspace_bytes(const rk_shape* shape, int64_t seq_len, int32_t window);
+
+/*
+ * rk_snapkv_evict -- stage 1: SnapKV-style permanent eviction per unit.
+ * [RKV] quick read (stage 1) and method details (SnapKV paragraph, GQA
+ * group-level selection, pooling kernel 63); [GUIDE] stage 1 (observation
+ * window, softmax(Q K^T / sqrt(D)) summed over the window).
+ *
+ * For each unit: the G*W window queries of its group attend causally (window
+ * row r sits at position S-W+r) over the S prompt keys with scale 1/sqrt(d);
+ * each row is softmax-normalised; score[j] = sum over the G heads and W rows
+ * of the probability of key j, for the prefix j < S-W; pooled[j] = the sum of
+ * score over [j-h, j+h] (h = (pool_kernel-1)/2, zero outside the prefix,
+ * added left to right); the n_keep - W prefix positions with the largest
+ * pooled score (ties to the lower position) are kept, ascending, followed by
+ * the W window positions S-W .. S-1.
+ *
+ *   q_win    [B, Hq, W, d]          window queries (rows in position order)
+ *   k, v     [B, Hkv, kv_cap, d]    prompt keys/values, first seq_len valid;
+ *                                   v is read only when v_out != NULL
+ *   kept_idx [B, Hkv, n_keep]       out: kept positions (int32, ascending)
+ *   k_out, v_out [B, Hkv, out_cap, d]  out: compact cache rows 0..n_keep-1
+ *                                   (row n = k[kept_idx[n]]).  Both NULL for
+ *                                   the RocketKV-MT form (indices only).
+ *   pooled_opt [B, Hkv, seq_len-W]  out (optional, float32): pooled scores
+ * Requires 1 <= W <= seq_len <= kv_cap, W <= n_keep <= seq_len, odd
+ * pool_kernel >= 1, out_cap >= n_keep when k_out is given, seq_len < 2^31.
+ */
+rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* k,
+                          const void* v, int64_t kv_cap, int64_t seq_len, int32_t window,
+                          int32_t pool_kernel, int64_t n_keep, int32_t* kept_idx,
+                          void* k_out, void* v_out, int64_t out_cap, float* pooled_opt,
+                          void* ws, size_t ws_bytes, rk_stream stream);
+
+/*
+ * rk_hsa_build_aux -- HSA step 1: per-page element-wise Kmax / Kmin.
+ * [RKV] method details, HSA step 1: keys are grouped into consecutive pages
+ * of `block` tokens; the element-wise max and min of each page are stored
+ * aligned along the head dimension and refreshed whenever new keys arrive.
+ *
+ *   k        [B, Hkv, k_cap, d]     keys
+ *   idx_opt  [B, Hkv, idx_stride]   optional candidate rows (RocketKV-MT): page
+ *                                   token n is key row idx_opt[n]; NULL means
+ *                                   token n is row n
+ *   kmax, kmin [B, Hkv, d, nblk_cap]  out, channel-major (page index fastest)
+ * Pages first_token/block .. ceil(n_tokens/block)-1 are (re)computed from
+ * tokens [page*block, min((page+1)*block, n_tokens)); other pages are left
+ * untouched, so after appending tokens n_old..n_tokens-1 a call with
+ * first_token = n_old equals a full rebuild bit for bit.  Exact: max/min only.
+ * Requires 0 <= first_token < n_tokens, ceil(n_tokens/block) <= nblk_cap,
+ * n_tokens <= k_cap (identity map) or <= idx_stride (candidate map); every
+ * idx_opt entry must lie in [0, k_cap).
+ */
+rk_status rk_hsa_build_aux(const rk_shape* shape, const void* k, int64_t k_cap,
+                           const int32_t* idx_opt, int64_t idx_stride, int64_t n_tokens,
+                           int64_t first_token, int32_t block, void* kmax, void* kmin,
+                           int64_t nblk_cap, rk_stream stream);
+
+/*
+ * rk_hsa_workspace_bytes -- workspace needed by rk_hsa_decode / _mt for this
+ * shape, token count, page size and k1/k2 (0 if the arguments are invalid).
+ */
+size_t rk_hsa_workspace_bytes(const rk_shape* shape, int64_t n_tokens, int32_t block,
+                              int32_t k1, int32_t k2);
+
+/*
+ * rk_hsa_decode -- HSA steps 2 and 3 for one decode query per head.
+ * [RKV] method details, HSA steps 2-3, and Algorithm 1:
+ *   a_i   = sum_g |q_g,i|, q_bar_i = sum_g q_g,i     (float32, g ascending)
+ *   i1    = the k1 channels of largest a_i (ties to the lower channel)
+ *   P_i   = Kmax row i if q_bar_i >= 0, else Kmin row i
+ *   s1[b] = sum over i in i1, ascending, of q_bar_i * P_i[b]  (float32,
+ *           one rounded multiply and one rounded add per term)
+ *   i2    = the min(k2, nblk) pages of largest s1 (ties to the lower page)
+ *   out_g = softmax(q_g . K_T^T / sqrt(d)) V_T over the valid tokens T of
+ *           the pages i2, for each head g of the group (float32 accumulation)
+ *
+ *   q        [B, Hq, d]             decode queries
+ *   k, v     [B, Hkv, kv_cap, d]    compact cache, tokens 0..n_tokens-1 valid
+ *   kmax, kmin [B, Hkv, d, nblk_cap]  from rk_hsa_build_aux
+ *   out      [B, Hq, d] float32     out
+ *   sel_blocks_opt   [B, Hkv, min(k2, nblk)] int32  out (optional): i2 ascending
+ *   sel_channels_opt [B, Hkv, k1] int32             out (optional): i1 ascending
+ *   block_scores_opt [B, Hkv, nblk] float32         out (optional): s1
+ * nblk = ceil(n_tokens / block).  Requires 1 <= n_tokens <= kv_cap,
+ * nblk <= nblk_cap, nblk <= 16384, 1 <= k1 <= d, k2 >= 1, G in {1, 2, 4, 8}.
+ */
+rk_status rk_hsa_decode(const rk_shape* shape, const void* q, const void* k, const void* v,
+                        int64_t kv_cap, const void* kmax, const void* kmin, int64_t nblk_cap,
+                        int64_t n_tokens, int32_t block, int32_t k1, int32_t k2, float* out,
+                        int32_t* sel_blocks_opt, int32_t* sel_channels_opt,
+                        float* block_scores_opt, void* ws, size_t ws_bytes, rk_stream stream);
+
+/*
+ * rk_hsa_decode_mt -- RocketKV-MT decode: HSA over a candidate subset of a
+ * full, never-evicted cache.
+ * [RKV] method details, RocketKV-MT: every token stays in memory, but stage 2
+ * chooses only among the N tokens that stage 1 kept for this turn.  Pages are
+ * formed over the ascending candidate list: page token n is key/value row
+ * cand_idx[n] of the full cache, and kmax/kmin must have been built by
+ * rk_hsa_build_aux with idx_opt = cand_idx.  Otherwise identical to
+ * rk_hsa_decode with n_tokens = n_cand.
+ *
+ *   k, v     [B, Hkv, kv_cap, d]    full cache
+ *   cand_idx [B, Hkv, cand_stride]  candidate rows, entries 0..n_cand-1 used,
+ *                                   each in [0, kv_cap)
+ */
+rk_status rk_hsa_decode_mt(const rk_shape* shape, const void* q, const void* k, const void* v,
+                           int64_t kv_cap, const int32_t* cand_idx, int64_t cand_stride,
+                           int64_t n_cand, const void* kmax, const void* kmin, int64_t nblk_cap,
+                           int32_t block, int32_t k1, int32_t k2, float* out,
+                           int32_t* sel_blocks_opt, int32_t* sel_channels_opt,
+                           float* block_scores_opt, void* ws, size_t ws_bytes,
+                           rk_stream stream);
+
+/* Static name of a status code. */
+const char* rk_status_string(rk_status status);
+
+/* Thread-local description of the last error on this thread ("" if none). */
+const char* rk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROCKETKV_H_ */

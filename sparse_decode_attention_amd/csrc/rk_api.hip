@@ -1,0 +1,243 @@
+// rk_api.hip -- the C ABI of librocketkv.so: argument validation, workspace
+// sizing, the host-side split arithmetic and dispatch to the HIP launchers.
+// The contract of every entry point is documented in include/rocketkv.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/rocketkv.h"
+#include "rk_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rk_status fail(rk_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rk_status fail(rk_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+rk_status device_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return RK_OK;
+  return fail(RK_EDEVICE, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every device entry point.
+rk_status check_shape(const rk_shape* sh, rk::Dims* d) {
+  if (!sh) return fail(RK_EINVAL, "shape is NULL");
+  if (sh->batch < 1 || sh->n_q_heads < 1 || sh->n_kv_heads < 1 || sh->head_dim < 1)
+    return fail(RK_EINVAL, "batch, heads and head_dim must be positive");
+  if (sh->n_q_heads % sh->n_kv_heads)
+    return fail(RK_EINVAL, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                sh->n_q_heads, sh->n_kv_heads);
+  if (sh->dtype != RK_F32 && sh->dtype != RK_BF16) return fail(RK_EINVAL, "unknown dtype");
+  if (sh->head_dim != 64 && sh->head_dim != 128)
+    return fail(RK_EUNSUPPORTED, "head_dim %d not built (64, 128)", sh->head_dim);
+  if (int64_t(sh->batch) * sh->n_kv_heads > 65535)
+    return fail(RK_EUNSUPPORTED, "batch * n_kv_heads above 65535");
+  d->B = sh->batch;
+  d->Hq = sh->n_q_heads;
+  d->Hkv = sh->n_kv_heads;
+  d->G = sh->n_q_heads / sh->n_kv_heads;
+  d->D = sh->head_dim;
+  d->bf16 = sh->dtype == RK_BF16;
+  return RK_OK;
+}
+
+rk_status check_ws(void* ws, size_t have, size_t need) {
+  if (need && !ws) return fail(RK_EINVAL, "workspace is NULL");
+  if (have < need) return fail(RK_EWORKSPACE, "workspace %zu bytes, need %zu", have, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(RK_EINVAL, "workspace not 256-byte aligned");
+  return RK_OK;
+}
+
+rk_status decode_common(const rk_shape* shape, const void* q, const void* k, const void* v,
+                        int64_t kv_cap, const int32_t* cand, int64_t cand_stride,
+                        const void* kmax, const void* kmin, int64_t nblk_cap, int64_t n_tokens,
+                        int32_t block, int32_t k1, int32_t k2, float* out, int32_t* sel_opt,
+                        int32_t* chan_opt, float* s1_opt, void* ws, size_t ws_bytes,
+                        rk_stream stream, bool mt) {
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  if (!q || !k || !v || !kmax || !kmin || !out) return fail(RK_EINVAL, "null tensor argument");
+  if (mt && !cand) return fail(RK_EINVAL, "cand_idx is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(RK_EINVAL, "q, k and v must be 16-byte aligned");
+  if (d.G != 1 && d.G != 2 && d.G != 4 && d.G != 8)
+    return fail(RK_EUNSUPPORTED, "group size %d not built (1, 2, 4, 8)", d.G);
+  if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
+  if (n_tokens < 1) return fail(RK_EINVAL, "n_tokens must be >= 1");
+  if (n_tokens > (int64_t(1) << 31) - 1) return fail(RK_EINVAL, "n_tokens too large");
+  if (mt) {
+    if (n_tokens > cand_stride) return fail(RK_EINVAL, "n_cand exceeds cand_stride");
+    if (kv_cap < 1) return fail(RK_EINVAL, "kv_cap must be >= 1");
+  } else if (n_tokens > kv_cap) {
+    return fail(RK_EINVAL, "n_tokens (%lld) exceeds kv_cap (%lld)", (long long)n_tokens,
+                (long long)kv_cap);
+  }
+  const int64_t nblk = (n_tokens + block - 1) / block;
+  if (nblk > nblk_cap) return fail(RK_EINVAL, "pages (%lld) exceed nblk_cap", (long long)nblk);
+  if (nblk > rk::kMaxPages)
+    return fail(RK_EUNSUPPORTED, "pages (%lld) above %lld", (long long)nblk,
+                (long long)rk::kMaxPages);
+  if (k1 < 1 || k1 > d.D) return fail(RK_EINVAL, "k1 (%d) outside [1, head_dim]", k1);
+  if (k2 < 1) return fail(RK_EINVAL, "k2 must be >= 1");
+  const rk::DecodeWs lay = rk::decode_ws_layout(d, nblk, k2);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != RK_OK) return st;
+  return device_status(
+      rk::launch_hsa_decode(d, q, k, v, kv_cap, mt ? cand : nullptr, cand_stride, kmax, kmin,
+                            nblk_cap, n_tokens, block, k1, k2, out, sel_opt, chan_opt, s1_opt,
+                            ws, static_cast<hipStream_t>(stream)),
+      mt ? "rk_hsa_decode_mt launch" : "rk_hsa_decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rk_status_string(rk_status s) {
+  switch (s) {
+    case RK_OK: return "RK_OK";
+    case RK_EINVAL: return "RK_EINVAL";
+    case RK_EUNSUPPORTED: return "RK_EUNSUPPORTED";
+    case RK_EWORKSPACE: return "RK_EWORKSPACE";
+    case RK_EDEVICE: return "RK_EDEVICE";
+  }
+  return "RK_UNKNOWN";
+}
+
+const char* rk_last_error(void) { return g_last_error.c_str(); }
+
+rk_status rk_split(double c, int64_t seq_len, int32_t window, int32_t block, int32_t head_dim,
+                   rk_split_out* out) {
+  if (!out) return fail(RK_EINVAL, "out is NULL");
+  if (!(c >= 1.0) || !isfinite(c)) return fail(RK_EINVAL, "compression ratio must be >= 1");
+  if (window < 1 || window > seq_len) return fail(RK_EINVAL, "window outside [1, seq_len]");
+  if (block < 1 || head_dim < 1) return fail(RK_EINVAL, "block and head_dim must be >= 1");
+  double r = 0.2 + 0.06 * log2(c);
+  r = r < 0.2 ? 0.2 : (r > 0.8 ? 0.8 : r);
+  const double c1 = pow(c, r);
+  const double c2 = pow(c, 1.0 - r);
+  const double t = double(seq_len) / c;
+  int64_t keep = int64_t(ceil(double(seq_len) / c1));
+  keep = keep < window ? window : keep;
+  keep = keep > seq_len ? seq_len : keep;
+  int64_t k2 = int64_t(ceil(t / double(block)));
+  k2 = k2 < 1 ? 1 : k2;
+  const int32_t page = int32_t(ceil(pow(c, (1.0 - r) / 2.0)));
+  out->r = r;
+  out->c1 = c1;
+  out->c2 = c2;
+  out->budget_t = t;
+  out->n_keep = keep;
+  out->k2_blocks = int32_t(k2 > INT32_MAX ? INT32_MAX : k2);
+  out->paper_page = page;
+  out->paper_k1 = double(head_dim) / (c2 / double(page));
+  return RK_OK;
+}
+
+size_t rk_snapkv_workspace_bytes(const rk_shape* shape, int64_t seq_len, int32_t window) {
+  rk::Dims d;
+  if (check_shape(shape, &d) != RK_OK || window < 1 || window > seq_len) return 0;
+  return rk::evict_ws_layout(d, seq_len, window).total;
+}
+
+rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* k,
+                          const void* v, int64_t kv_cap, int64_t seq_len, int32_t window,
+                          int32_t pool_kernel, int64_t n_keep, int32_t* kept_idx, void* k_out,
+                          void* v_out, int64_t out_cap, float* pooled_opt, void* ws,
+                          size_t ws_bytes, rk_stream stream) {
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  if (!q_win || !k || !kept_idx) return fail(RK_EINVAL, "null tensor argument");
+  if ((k_out == nullptr) != (v_out == nullptr))
+    return fail(RK_EINVAL, "k_out and v_out must both be given or both be NULL");
+  if (k_out && !v) return fail(RK_EINVAL, "v is NULL but a compact cache is requested");
+  if (!aligned16(q_win) || !aligned16(k) || (v && !aligned16(v)) ||
+      (k_out && (!aligned16(k_out) || !aligned16(v_out))))
+    return fail(RK_EINVAL, "tensors must be 16-byte aligned");
+  if (window < 1 || window > seq_len) return fail(RK_EINVAL, "window outside [1, seq_len]");
+  if (seq_len > kv_cap) return fail(RK_EINVAL, "seq_len exceeds kv_cap");
+  if (seq_len > (int64_t(1) << 31) - 1) return fail(RK_EINVAL, "seq_len too large");
+  if (n_keep < window || n_keep > seq_len) return fail(RK_EINVAL, "n_keep outside [W, S]");
+  if (pool_kernel < 1 || (pool_kernel % 2) == 0 || pool_kernel > 4097)
+    return fail(RK_EINVAL, "pool_kernel must be odd, in [1, 4097]");
+  if (k_out && out_cap < n_keep) return fail(RK_EINVAL, "out_cap below n_keep");
+  if (int64_t(d.G) * window > 1024)
+    return fail(RK_EUNSUPPORTED, "group * window above 1024 rows");
+  const rk::EvictWs lay = rk::evict_ws_layout(d, seq_len, window);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != RK_OK) return st;
+  return device_status(
+      rk::launch_snapkv_evict(d, q_win, k, v, kv_cap, seq_len, window, pool_kernel, n_keep,
+                              kept_idx, k_out, v_out, out_cap, pooled_opt, ws,
+                              static_cast<hipStream_t>(stream)),
+      "rk_snapkv_evict launch");
+}
+
+rk_status rk_hsa_build_aux(const rk_shape* shape, const void* k, int64_t k_cap,
+                           const int32_t* idx_opt, int64_t idx_stride, int64_t n_tokens,
+                           int64_t first_token, int32_t block, void* kmax, void* kmin,
+                           int64_t nblk_cap, rk_stream stream) {
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  if (!k || !kmax || !kmin) return fail(RK_EINVAL, "null tensor argument");
+  if (!aligned16(k)) return fail(RK_EINVAL, "k must be 16-byte aligned");
+  if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
+  if (n_tokens < 1 || n_tokens > (int64_t(1) << 31) - 1)
+    return fail(RK_EINVAL, "n_tokens outside [1, 2^31)");
+  if (first_token < 0 || first_token >= n_tokens)
+    return fail(RK_EINVAL, "first_token outside [0, n_tokens)");
+  if (idx_opt ? n_tokens > idx_stride : n_tokens > k_cap)
+    return fail(RK_EINVAL, "n_tokens exceeds %s", idx_opt ? "idx_stride" : "k_cap");
+  const int64_t nblk = (n_tokens + block - 1) / block;
+  if (nblk > nblk_cap) return fail(RK_EINVAL, "pages (%lld) exceed nblk_cap", (long long)nblk);
+  return device_status(rk::launch_build_aux(d, k, k_cap, idx_opt, idx_stride, n_tokens,
+                                            first_token / block, block, kmax, kmin, nblk_cap,
+                                            static_cast<hipStream_t>(stream)),
+                       "rk_hsa_build_aux launch");
+}
+
+size_t rk_hsa_workspace_bytes(const rk_shape* shape, int64_t n_tokens, int32_t block, int32_t k1,
+                              int32_t k2) {
+  rk::Dims d;
+  if (check_shape(shape, &d) != RK_OK || n_tokens < 1 || block < 1 || k1 < 1 || k2 < 1) return 0;
+  return rk::decode_ws_layout(d, (n_tokens + block - 1) / block, k2).total;
+}
+
+rk_status rk_hsa_decode(const rk_shape* shape, const void* q, const void* k, const void* v,
+                        int64_t kv_cap, const void* kmax, const void* kmin, int64_t nblk_cap,
+                        int64_t n_tokens, int32_t block, int32_t k1, int32_t k2, float* out,
+                        int32_t* sel_blocks_opt, int32_t* sel_channels_opt,
+                        float* block_scores_opt, void* ws, size_t ws_bytes, rk_stream stream) {
+  return decode_common(shape, q, k, v, kv_cap, nullptr, 0, kmax, kmin, nblk_cap, n_tokens, block,
+                       k1, k2, out, sel_blocks_opt, sel_channels_opt, block_scores_opt, ws,
+                       ws_bytes, stream, false);
+}
+
+rk_status rk_hsa_decode_mt(const rk_shape* shape, const void* q, const void* k, const void* v,
+                           int64_t kv_cap, const int32_t* cand_idx, int64_t cand_stride,
+                           int64_t n_cand, const void* kmax, const void* kmin, int64_t nblk_cap,
+                           int32_t block, int32_t k1, int32_t k2, float* out,
+                           int32_t* sel_blocks_opt, int32_t* sel_channels_opt,
+                           float* block_scores_opt, void* ws, size_t ws_bytes,
+                           rk_stream stream) {
+  return decode_common(shape, q, k, v, kv_cap, cand_idx, cand_stride, kmax, kmin, nblk_cap,
+                       n_cand, block, k1, k2, out, sel_blocks_opt, sel_channels_opt,
+                       block_scores_opt, ws, ws_bytes, stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// rk_aux.hip -- HSA step 1: per-page element-wise Kmax / Kmin.
+//
+// Source: papercache notes "RocketKV: Accelerating Long-Context LLM Inference
+// via Two-Stage KV Cache Compression", method details, HSA step 1 (pages of
+// consecutive keys, element-wise max/min kept as auxiliary data laid out
+// along the head dimension, refreshed as new keys arrive) and RocketKV-MT
+// (pages over the stage-1 candidate list of the full cache).
+//
+// One workgroup covers kPagesPerWg consecutive pages of one unit.  Each thread
+// owns one 16-byte channel chunk of one page: it streams the page's rows
+// (coalesced 16-byte loads, a whole 256-byte row per 16 lanes), keeps the
+// running max/min in registers, then the tile is transposed through LDS so
+// the channel-major output is written in contiguous page runs.  Bandwidth
+// bound: bytes = rows read + 2 * d * pages * sizeof(T) written.
+#include "rk_device.hpp"
+#include "rk_internal.hpp"
+
+namespace rk {
+namespace {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void aux_build_kernel(
+    const T* __restrict__ k, int64_t k_cap, const int32_t* __restrict__ idx, int64_t idx_stride,
+    int n_tokens, int first_block, int nblk, int block, T* __restrict__ kmax,
+    T* __restrict__ kmin, int64_t nblk_cap) {
+  constexpr int EPL = Vec16<T>::N;   // elements per 16-byte chunk
+  constexpr int CPR = D / EPL;       // chunks per row
+  constexpr int PPW = 256 / CPR;     // pages per workgroup
+  static_assert(D % EPL == 0 && 256 % CPR == 0, "row must split into 16-byte chunks");
+  __shared__ T smax[D][PPW + 1];
+  __shared__ T smin[D][PPW + 1];
+
+  const int u = blockIdx.y;
+  const int t = threadIdx.x;
+  const int c = t % CPR;
+  const int j = t / CPR;
+  const int p0 = first_block + blockIdx.x * PPW;
+  const int p = p0 + j;
+  const T* ku = k + size_t(u) * size_t(k_cap) * D + c * EPL;
+  const int32_t* iu = idx ? idx + size_t(u) * size_t(idx_stride) : nullptr;
+
+  if (p < nblk) {
+    const int n0 = p * block;
+    const int n1 = min(n0 + block, n_tokens);
+    float mx[EPL], mn[EPL];
+    {
+      const int row = iu ? clamp_row(iu[n0], k_cap) : n0;
+      unpack16(load16(ku + size_t(row) * D), mx);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) mn[e] = mx[e];
+    }
+    for (int n = n0 + 1; n < n1; ++n) {
+      const int row = iu ? clamp_row(iu[n], k_cap) : n;
+      float x[EPL];
+      unpack16(load16(ku + size_t(row) * D), x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        mx[e] = x[e] > mx[e] ? x[e] : mx[e];
+        mn[e] = x[e] < mn[e] ? x[e] : mn[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      if constexpr (sizeof(T) == 2) {
+        // values came from bf16, so dropping the low half is exact
+        smax[c * EPL + e][j].bits = uint16_t(__float_as_uint(mx[e]) >> 16);
+        smin[c * EPL + e][j].bits = uint16_t(__float_as_uint(mn[e]) >> 16);
+      } else {
+        smax[c * EPL + e][j] = mx[e];
+        smin[c * EPL + e][j] = mn[e];
+      }
+    }
+  }
+  __syncthreads();
+  T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
+  T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
+  for (int e = t; e < D * PPW; e += 256) {
+    const int ch = e / PPW;
+    const int jj = e % PPW;
+    const int pp = p0 + jj;
+    if (pp < nblk) {
+      xu[size_t(ch) * nblk_cap + pp] = smax[ch][jj];
+      nu[size_t(ch) * nblk_cap + pp] = smin[ch][jj];
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_aux_t(const Dims& d, const void* k, int64_t k_cap, const int32_t* idx,
+                        int64_t idx_stride, int64_t n_tokens, int64_t first_block, int block,
+                        void* kmax, void* kmin, int64_t nblk_cap, hipStream_t s) {
+  constexpr int PPW = 256 / (D / Vec16<T>::N);
+  const int64_t nblk = (n_tokens + block - 1) / block;
+  const int64_t npages = nblk - first_block;
+  dim3 grid(unsigned((npages + PPW - 1) / PPW), unsigned(d.units()));
+  hipLaunchKernelGGL((aux_build_kernel<T, D>), grid, dim3(256), 0, s,
+                     static_cast<const T*>(k), k_cap, idx, idx_stride, int(n_tokens),
+                     int(first_block), int(nblk), block, static_cast<T*>(kmax),
+                     static_cast<T*>(kmin), nblk_cap);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_build_aux(const Dims& d, const void* k, int64_t k_cap, const int32_t* idx,
+                            int64_t idx_stride, int64_t n_tokens, int64_t first_block,
+                            int block, void* kmax, void* kmin, int64_t nblk_cap,
+                            hipStream_t s) {
+  if (d.bf16) {
+    if (d.D == 128)
+      return launch_aux_t<bf16_t, 128>(d, k, k_cap, idx, idx_stride, n_tokens, first_block,
+                                       block, kmax, kmin, nblk_cap, s);
+    return launch_aux_t<bf16_t, 64>(d, k, k_cap, idx, idx_stride, n_tokens, first_block, block,
+                                    kmax, kmin, nblk_cap, s);
+  }
+  if (d.D == 128)
+    return launch_aux_t<float, 128>(d, k, k_cap, idx, idx_stride, n_tokens, first_block, block,
+                                    kmax, kmin, nblk_cap, s);
+  return launch_aux_t<float, 64>(d, k, k_cap, idx, idx_stride, n_tokens, first_block, block,
+                                 kmax, kmin, nblk_cap, s);
+}
+
+}  // namespace rk

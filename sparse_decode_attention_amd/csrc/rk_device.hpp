@@ -1,0 +1,209 @@
+// rk_device.hpp -- device-side helpers shared by the RocketKV kernels (gfx950,
+// wave64): element loads, order-preserving float keys, workgroup scans and the
+// workgroup top-k selection used for tokens (stage 1), channels and pages
+// (HSA step 2).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rk {
+
+constexpr int kWave = 64;
+
+// bf16 is carried as raw uint16 bits (the upper half of an IEEE float32).
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x.bits) << 16); }
+
+// 16-byte vector of elements: 4 float or 8 bf16.
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  float4 raw;
+  __device__ __forceinline__ float get(int i) const {
+    return i == 0 ? raw.x : i == 1 ? raw.y : i == 2 ? raw.z : raw.w;
+  }
+};
+template <>
+struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  uint4 raw;
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t w = i < 2 ? raw.x : i < 4 ? raw.y : i < 6 ? raw.z : raw.w;
+    return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ Vec16<T> load16(const T* p) {
+  Vec16<T> v;
+  v.raw = *reinterpret_cast<const decltype(v.raw)*>(p);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const Vec16<T>& v, float* out) {
+#pragma unroll
+  for (int i = 0; i < Vec16<T>::N; ++i) out[i] = v.get(i);
+}
+
+// Order-preserving map float -> uint32: a > b  <=>  key(a) > key(b); -0 and +0
+// share one key (they compare equal as floats).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u << 1) == 0u) u = 0u;  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// A caller-supplied row index forced into [0, cap): out-of-range indices give
+// unspecified values, never out-of-bounds reads.
+__device__ __forceinline__ int clamp_row(int32_t row, int64_t cap) {
+  return uint64_t(uint32_t(row)) < uint64_t(cap) ? row : 0;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Exclusive prefix sum of v over the workgroup (NT threads, wave64).  `tmp`
+// must hold NT/64 + 1 ints of LDS.  Returns the exclusive prefix; *total gets
+// the workgroup sum.  Contains barriers: every thread must call it.
+template <int NT>
+__device__ __forceinline__ int wg_excl_scan(int v, int* tmp, int* total) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(x, off);
+    if (lane >= off) x += t;
+  }
+  if (lane == kWave - 1) tmp[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < NT / kWave; ++w) {
+      const int t = tmp[w];
+      tmp[w] = run;
+      run += t;
+    }
+    tmp[NT / kWave] = run;
+  }
+  __syncthreads();
+  const int res = tmp[wave] + x - v;
+  *total = tmp[NT / kWave];
+  __syncthreads();
+  return res;
+}
+
+// Exclusive prefix count of a predicate over the workgroup (ballot based).
+template <int NT>
+__device__ __forceinline__ int wg_excl_count(bool p, int* tmp, int* total) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const unsigned long long b = __ballot(p);
+  const int below = __popcll(b & ((1ull << lane) - 1ull));
+  if (lane == 0) tmp[wave] = __popcll(b);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < NT / kWave; ++w) {
+      const int t = tmp[w];
+      tmp[w] = run;
+      run += t;
+    }
+    tmp[NT / kWave] = run;
+  }
+  __syncthreads();
+  const int res = tmp[wave] + below;
+  *total = tmp[NT / kWave];
+  __syncthreads();
+  return res;
+}
+
+template <int NT>
+struct TopkSmem {
+  static constexpr int kBins = 2048;
+  uint32_t hist[kBins];
+  int tmp[NT / kWave + 1];
+  int found[2];
+};
+
+// Workgroup top-k: calls emit(rank, position) for the k largest keys among
+// key(0..n-1), ties broken toward the lower position; ranks 0..k-1 follow
+// ascending position order.  Selected <=> #{i : key_i > key_j or (key_i == key_j and
+// i < j)} < k.  Radix select over 11/11/10-bit digits finds the exact k-th
+// key T and how many keys equal to T are taken; an ordered scan then writes
+// the selection.  0 <= k <= n.  All threads of the workgroup must call it.
+template <int NT, typename KeyFn, typename EmitFn>
+__device__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit, TopkSmem<NT>& sm) {
+  const int t = threadIdx.x;
+  if (k <= 0) return;
+  if (k >= n) {
+    for (int i = t; i < n; i += NT) emit(i, i);
+    return;
+  }
+  uint32_t prefix = 0, mask = 0;
+  int need = k;  // keys still to take among those matching `prefix`
+  constexpr int kShift[3] = {21, 10, 0};
+  constexpr int kBits[3] = {11, 11, 10};
+  constexpr int kPer = TopkSmem<NT>::kBins / NT;  // bins owned by one thread
+  static_assert(kPer >= 1 && TopkSmem<NT>::kBins % NT == 0, "bins per thread");
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = kShift[pass];
+    const uint32_t dmask = (1u << kBits[pass]) - 1u;
+    for (int b = t; b < TopkSmem<NT>::kBins; b += NT) sm.hist[b] = 0u;
+    __syncthreads();
+    for (int i = t; i < n; i += NT) {
+      const uint32_t kk = key(i);
+      if ((kk & mask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // Thread t owns bins [top - (t+1)*kPer, top - t*kPer): thread 0 the highest.
+    const int hi = TopkSmem<NT>::kBins - t * kPer;
+    int own = 0;
+#pragma unroll
+    for (int j = 1; j <= kPer; ++j) own += int(sm.hist[hi - j]);
+    int total;
+    int above = wg_excl_scan<NT>(own, sm.tmp, &total);
+#pragma unroll
+    for (int j = 1; j <= kPer; ++j) {
+      const int c = int(sm.hist[hi - j]);
+      if (above < need && above + c >= need) {
+        sm.found[0] = hi - j;
+        sm.found[1] = need - above;
+      }
+      above += c;
+    }
+    __syncthreads();
+    prefix |= uint32_t(sm.found[0]) << shift;
+    mask |= dmask << shift;
+    need = sm.found[1];
+    __syncthreads();
+  }
+  // prefix == T (the k-th largest key); take `need` of the keys equal to T,
+  // lowest positions first, and every key above T.
+  const uint32_t T = prefix;
+  const int need_eq = need;
+  int base_sel = 0, base_eq = 0;
+  for (int c0 = 0; c0 < n && base_sel < k; c0 += NT) {
+    const int i = c0 + t;
+    const uint32_t kk = i < n ? key(i) : 0u;
+    const bool is_eq = i < n && kk == T;
+    const bool is_gt = i < n && kk > T;
+    int eq_tot, sel_tot;
+    const int eq_before = base_eq + wg_excl_count<NT>(is_eq, sm.tmp, &eq_tot);
+    const bool sel = is_gt || (is_eq && eq_before < need_eq);
+    const int pos = base_sel + wg_excl_count<NT>(sel, sm.tmp, &sel_tot);
+    if (sel) emit(pos, i);
+    base_eq += eq_tot;
+    base_sel += sel_tot;
+  }
+}
+
+}  // namespace rk

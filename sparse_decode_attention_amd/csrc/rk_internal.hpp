@@ -1,0 +1,80 @@
+// rk_internal.hpp -- host-side interface between the C ABI (rk_api.hip) and the
+// kernel launchers.  Arguments are validated by the caller; launchers only
+// pick a kernel instance and a grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rk {
+
+// Largest page count HSA step 2 keeps in LDS (keys of 4 bytes each).
+constexpr int64_t kMaxPages = 12288;
+// Stage-1 column tile of the window-score passes (partials are sized by it).
+constexpr int kWsTile = 64;
+// Pages handled by one attention workgroup at least (split-K granularity).
+constexpr int kMinPagesPerSplit = 4;
+
+struct Dims {
+  int B, Hq, Hkv, G, D;
+  bool bf16;
+  int units() const { return B * Hkv; }
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- workspace layouts (shared by *_workspace_bytes and the calls) ----
+struct EvictWs {
+  size_t partials, stats, scores, pooled, total;
+  int n_tiles, m_rows;
+};
+inline EvictWs evict_ws_layout(const Dims& d, int64_t S, int W) {
+  EvictWs w{};
+  w.m_rows = d.G * W;
+  w.n_tiles = int((S + kWsTile - 1) / kWsTile);
+  const size_t u = size_t(d.units());
+  size_t off = 0;
+  w.partials = off; off += align256(u * w.n_tiles * w.m_rows * 2 * sizeof(float));
+  w.stats = off;    off += align256(u * w.m_rows * 2 * sizeof(float));
+  w.scores = off;   off += align256(u * size_t(S - W) * sizeof(float));
+  w.pooled = off;   off += align256(u * size_t(S - W) * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+struct DecodeWs {
+  size_t sel, partials, total;
+  int n_split_max, nsel;
+};
+inline DecodeWs decode_ws_layout(const Dims& d, int64_t nblk, int k2) {
+  DecodeWs w{};
+  w.nsel = int(nblk < k2 ? nblk : k2);
+  w.n_split_max = (w.nsel + kMinPagesPerSplit - 1) / kMinPagesPerSplit;
+  const size_t u = size_t(d.units());
+  size_t off = 0;
+  w.sel = off;      off += align256(u * w.nsel * sizeof(int32_t));
+  w.partials = off; off += align256(u * w.n_split_max * d.G * (d.D + 2) * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+// ---- launchers ----
+hipError_t launch_build_aux(const Dims& d, const void* k, int64_t k_cap, const int32_t* idx,
+                            int64_t idx_stride, int64_t n_tokens, int64_t first_block,
+                            int block, void* kmax, void* kmin, int64_t nblk_cap,
+                            hipStream_t s);
+
+hipError_t launch_hsa_decode(const Dims& d, const void* q, const void* k, const void* v,
+                             int64_t kv_cap, const int32_t* cand, int64_t cand_stride,
+                             const void* kmax, const void* kmin, int64_t nblk_cap,
+                             int64_t n_tokens, int block, int k1, int k2, float* out,
+                             int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
+                             hipStream_t s);
+
+hipError_t launch_snapkv_evict(const Dims& d, const void* q_win, const void* k, const void* v,
+                               int64_t kv_cap, int64_t S, int W, int pool_kernel,
+                               int64_t n_keep, int32_t* kept, void* k_out, void* v_out,
+                               int64_t out_cap, float* pooled_opt, void* ws, hipStream_t s);
+
+}  // namespace rk

@@ -1,0 +1,190 @@
+"""Thin ctypes binding of librocketkv.so (declared in include/rocketkv.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP kernels
+of the library.  Tensors are torch tensors on the current GPU (torch is used
+for device memory and streams); sizes and strides are read from their shapes.
+Importing this module loads the library and raises ImportError if it has not
+been built -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librocketkv.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m sparse_decode_attention_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+RK_OK, RK_EINVAL, RK_EUNSUPPORTED, RK_EWORKSPACE, RK_EDEVICE = range(5)
+RK_F32, RK_BF16 = 0, 1
+
+
+class RkShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int)]
+
+
+class RkSplitOut(ctypes.Structure):
+    _fields_ = [("r", ctypes.c_double), ("c1", ctypes.c_double), ("c2", ctypes.c_double),
+                ("budget_t", ctypes.c_double), ("n_keep", ctypes.c_int64),
+                ("k2_blocks", ctypes.c_int32), ("paper_page", ctypes.c_int32),
+                ("paper_k1", ctypes.c_double)]
+
+
+_i32, _i64, _f64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t
+_SP = ctypes.POINTER(RkShape)
+
+_lib.rk_split.argtypes = [_f64, _i64, _i32, _i32, _i32, ctypes.POINTER(RkSplitOut)]
+_lib.rk_snapkv_workspace_bytes.argtypes = [_SP, _i64, _i32]
+_lib.rk_snapkv_workspace_bytes.restype = _sz
+_lib.rk_snapkv_evict.argtypes = [_SP, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i64, _vp, _vp, _vp,
+                                 _i64, _vp, _vp, _sz, _vp]
+_lib.rk_hsa_build_aux.argtypes = [_SP, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _i64, _vp]
+_lib.rk_hsa_workspace_bytes.argtypes = [_SP, _i64, _i32, _i32, _i32]
+_lib.rk_hsa_workspace_bytes.restype = _sz
+_lib.rk_hsa_decode.argtypes = [_SP, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32, _i32, _i32,
+                               _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.rk_hsa_decode_mt.argtypes = [_SP, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _i64, _i32,
+                                  _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.rk_status_string.argtypes = [ctypes.c_int]
+_lib.rk_status_string.restype = ctypes.c_char_p
+_lib.rk_last_error.argtypes = []
+_lib.rk_last_error.restype = ctypes.c_char_p
+for _f in ("rk_split", "rk_snapkv_evict", "rk_hsa_build_aux", "rk_hsa_decode", "rk_hsa_decode_mt"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+class RocketKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        name = _lib.rk_status_string(status).decode()
+        super().__init__(f"{what}: {name}: {_lib.rk_last_error().decode()}")
+
+
+def _check(status: int, what: str):
+    if status != RK_OK:
+        raise RocketKVError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RK_F32
+    if t.dtype == torch.bfloat16:
+        return RK_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def shape_of(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype) -> RkShape:
+    code = dtype if isinstance(dtype, int) else (RK_F32 if dtype == torch.float32 else RK_BF16)
+    return RkShape(batch, n_q_heads, n_kv_heads, head_dim, code)
+
+
+def _need_contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _ws(nbytes: int, like: torch.Tensor, ws):
+    if ws is not None:
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+
+
+# --------------------------------------------------------------------------
+def rk_split(c: float, seq_len: int, window: int, block: int, head_dim: int) -> dict:
+    out = RkSplitOut()
+    _check(_lib.rk_split(c, seq_len, window, block, head_dim, ctypes.byref(out)), "rk_split")
+    return {f: getattr(out, f) for f, _ in RkSplitOut._fields_}
+
+
+def rk_snapkv_workspace_bytes(shape: RkShape, seq_len: int, window: int) -> int:
+    return _lib.rk_snapkv_workspace_bytes(ctypes.byref(shape), seq_len, window)
+
+
+def rk_snapkv_evict(q_win, k, v, seq_len, window, pool_kernel, n_keep, kept_idx,
+                    k_out=None, v_out=None, pooled=None, ws=None, stream=None):
+    """Stage 1.  q_win [B,Hq,W,d]; k, v [B,Hkv,cap,d]; kept_idx [B,Hkv,n_keep] int32;
+    k_out, v_out [B,Hkv,out_cap,d] or None (RocketKV-MT); pooled [B,Hkv,S-W] fp32 or None."""
+    _need_contig(q_win, k, v, kept_idx, k_out, v_out, pooled)
+    B, Hq, W, d = q_win.shape
+    shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
+    nbytes = rk_snapkv_workspace_bytes(shape, seq_len, window)
+    ws = _ws(nbytes, k, ws)
+    out_cap = k_out.shape[2] if k_out is not None else 0
+    _check(_lib.rk_snapkv_evict(ctypes.byref(shape), _ptr(q_win), _ptr(k), _ptr(v), k.shape[2],
+                                seq_len, window, pool_kernel, n_keep, _ptr(kept_idx), _ptr(k_out),
+                                _ptr(v_out), out_cap, _ptr(pooled), _ptr(ws), ws.numel(),
+                                _stream(stream)), "rk_snapkv_evict")
+    return ws
+
+
+def rk_hsa_build_aux(k, n_tokens, first_token, block, kmax, kmin, n_q_heads=None, idx=None,
+                     stream=None):
+    """HSA step 1.  k [B,Hkv,cap,d]; kmax, kmin [B,Hkv,d,nblk_cap]; idx [B,Hkv,stride] int32
+    or None (page token n is row idx[n])."""
+    _need_contig(k, kmax, kmin, idx)
+    B, Hkv, cap, d = k.shape
+    shape = shape_of(B, n_q_heads or Hkv, Hkv, d, _dtype_code(k))
+    _check(_lib.rk_hsa_build_aux(ctypes.byref(shape), _ptr(k), cap, _ptr(idx),
+                                 idx.shape[2] if idx is not None else 0, n_tokens, first_token,
+                                 block, _ptr(kmax), _ptr(kmin), kmax.shape[3], _stream(stream)),
+           "rk_hsa_build_aux")
+
+
+def rk_hsa_workspace_bytes(shape: RkShape, n_tokens: int, block: int, k1: int, k2: int) -> int:
+    return _lib.rk_hsa_workspace_bytes(ctypes.byref(shape), n_tokens, block, k1, k2)
+
+
+def rk_hsa_decode(q, k, v, kmax, kmin, n_tokens, block, k1, k2, out, sel_blocks=None,
+                  sel_channels=None, block_scores=None, ws=None, stream=None):
+    """HSA steps 2-3.  q [B,Hq,d]; k, v [B,Hkv,cap,d]; kmax/kmin [B,Hkv,d,nblk_cap];
+    out [B,Hq,d] fp32; optional sel_blocks [B,Hkv,min(k2,nblk)], sel_channels [B,Hkv,k1],
+    block_scores [B,Hkv,nblk]."""
+    _need_contig(q, k, v, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    B, Hq, d = q.shape
+    shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
+    ws = _ws(rk_hsa_workspace_bytes(shape, n_tokens, block, k1, k2), k, ws)
+    _check(_lib.rk_hsa_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), k.shape[2],
+                              _ptr(kmax), _ptr(kmin), kmax.shape[3], n_tokens, block, k1, k2,
+                              _ptr(out), _ptr(sel_blocks), _ptr(sel_channels), _ptr(block_scores),
+                              _ptr(ws), ws.numel(), _stream(stream)), "rk_hsa_decode")
+    return ws
+
+
+def rk_hsa_decode_mt(q, k, v, cand_idx, n_cand, kmax, kmin, block, k1, k2, out, sel_blocks=None,
+                     sel_channels=None, block_scores=None, ws=None, stream=None):
+    """RocketKV-MT decode over the candidate rows cand_idx [B,Hkv,stride] of the full k, v."""
+    _need_contig(q, k, v, cand_idx, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    B, Hq, d = q.shape
+    shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
+    ws = _ws(rk_hsa_workspace_bytes(shape, n_cand, block, k1, k2), k, ws)
+    _check(_lib.rk_hsa_decode_mt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), k.shape[2],
+                                 _ptr(cand_idx), cand_idx.shape[2], n_cand, _ptr(kmax), _ptr(kmin),
+                                 kmax.shape[3], block, k1, k2, _ptr(out), _ptr(sel_blocks),
+                                 _ptr(sel_channels), _ptr(block_scores), _ptr(ws), ws.numel(),
+                                 _stream(stream)), "rk_hsa_decode_mt")
+    return ws
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def raw_library() -> ctypes.CDLL:
+    """The loaded ctypes library (for tests of the raw C ABI)."""
+    return _lib

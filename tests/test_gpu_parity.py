@@ -1,0 +1,185 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Every test prints the case it runs before launching, so a failure names it.
+Inputs are the seeded synthetic workloads; sizes are chosen so the oracle
+finishes in seconds while still spanning several tiles and a ragged tail.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import rk_testutil as U
+from sparse_decode_attention_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def rk():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_decode_attention_amd import rocketkv
+    return rocketkv
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def _pipeline(rk, w, layer=0, steps=None, seed=0):
+    """Stage 1 + aux + decode steps of one layer of workload w, checked stage-wise."""
+    s = rk.rk_split(w.c, w.seq, w.window, w.block, w.d)
+    k, v, pos = WL.layer_kv(w, layer, device=DEV, seed=seed)
+    qw = WL.window_queries(w, layer, device=DEV, seed=seed)
+    n_keep, k2 = s["n_keep"], s["k2_blocks"]
+    kept, kc, vc, pooled, sw1 = U.evict_and_check(rk, qw, k, v, w.seq, w.window, w.pool, n_keep)
+    kmax, kmin = U.aux_and_check(rk, kc, n_keep, w.block, w.n_q)
+    swaps = 0
+    for step in range(w.decode_steps if steps is None else steps):
+        q = WL.decode_query(w, layer, step, device=DEV, seed=seed)
+        _, _, sw = U.decode_and_check(rk, q, kc, vc, kmax, kmin, n_keep, w.block, w.k1, k2)
+        swaps += sw
+    return dict(kept=kept, pos=pos, swaps_evict=sw1, swaps_decode=swaps)
+
+
+def test_tiny_gqa_fp32_full_pipeline(rk):
+    w = WL.WORKLOADS["tiny-gqa-s2048-d64-fp32"]
+    say(w.name, "all 8 decode steps")
+    res = _pipeline(rk, w)
+    # the planted keys survive stage 1
+    kept = res["kept"].cpu().numpy()
+    for h in range(w.n_kv):
+        assert set(res["pos"][0, h].tolist()) <= set(kept[0, h].tolist())
+    say("swaps", res["swaps_evict"], res["swaps_decode"])
+
+
+def test_llama8b_layer_full_pipeline(rk):
+    w = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    say(w.name, "64 decode steps")
+    res = _pipeline(rk, w)
+    say("swaps", res["swaps_evict"], res["swaps_decode"])
+
+
+@pytest.mark.parametrize("dtype,d,G,S,W,pool", [
+    ("bf16", 128, 4, 1000, 32, 63),     # ragged S (tile 64), pool larger than gaps
+    ("bf16", 64, 2, 777, 16, 7),
+    ("f32", 128, 1, 513, 8, 3),
+    ("f32", 64, 8, 300, 4, 1),
+    ("bf16", 128, 8, 2100, 32, 63),
+])
+def test_shapes_and_ragged_tails(rk, dtype, d, G, S, W, pool):
+    say("shape", dtype, d, G, S, W, pool)
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=2, n_kv=2, n_q=2 * G, d=d, dtype=dtype, seq=S, window=W, pool=pool,
+                  n_plant=8, n_outlier=4, c=6.0, k1=min(16, d), decode_steps=3)
+    res = _pipeline(rk, w)
+    say("swaps", res["swaps_evict"], res["swaps_decode"])
+
+
+def test_keep_all_and_window_only(rk):
+    base = WL.WORKLOADS["tiny-gqa-s2048-d64-fp32"]
+    w = WL.scaled(base, seq=600, batch=2)
+    k, v, _ = WL.layer_kv(w, 0, device=DEV)
+    qw = WL.window_queries(w, 0, device=DEV)
+    say("keep all S=600")
+    kept, kc, vc, _, _ = U.evict_and_check(rk, qw, k, v, 600, w.window, w.pool, 600)
+    assert (kept.cpu().numpy() == np.arange(600)).all()
+    assert torch.equal(kc, k) and torch.equal(vc, v)
+    say("window only")
+    kept, _, _, _, _ = U.evict_and_check(rk, qw, k, v, 600, w.window, w.pool, w.window)
+    assert (kept.cpu().numpy() == np.arange(600 - w.window, 600)).all()
+    say("S == W")
+    w2 = WL.scaled(base, seq=16, window=16, batch=1)
+    k2, v2, _ = WL.layer_kv(WL.scaled(w2, n_plant=0), 0, device=DEV)
+    qw2 = WL.window_queries(w2, 0, device=DEV)
+    kept, _, _, _, _ = U.evict_and_check(rk, qw2, k2, v2, 16, 16, 7, 16)
+    assert (kept.cpu().numpy() == np.arange(16)).all()
+
+
+def test_decode_all_pages_is_dense_attention(rk):
+    """k2 >= pages: the output equals dense attention over the whole cache."""
+    say("dense special case")
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=2, seq=1000, n_plant=4)
+    kc, vc, _ = WL.layer_kv(w, 0, device=DEV)
+    n = 997                                              # ragged last page
+    kmax, kmin = U.aux_and_check(rk, kc, n, 16, w.n_q)
+    q = WL.decode_query(w, 0, 0, device=DEV)
+    out, sel, _ = U.decode_and_check(rk, q, kc, vc, kmax, kmin, n, 16, 128, 10 ** 6)
+    assert (sel.cpu().numpy() == np.arange(-(-n // 16))).all()
+    G = w.group
+    for b in range(2):
+        for h in range(w.n_kv):
+            want = O.attention(U.np32(q[b, h * G:(h + 1) * G]), U.np32(kc[b, h, :n]), U.np32(vc[b, h, :n]))
+            U.check_output(U.np32(out[b, h * G:(h + 1) * G]), want)
+
+
+def test_incremental_aux_equals_rebuild(rk):
+    say("incremental aux")
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=2, seq=700, n_plant=0)
+    kc, _, _ = WL.layer_kv(w, 0, device=DEV)
+    nblk = -(-700 // 16)
+    full_max = torch.empty(2, w.n_kv, 128, nblk + 3, dtype=kc.dtype, device=DEV)
+    full_min = torch.empty_like(full_max)
+    inc_max = torch.zeros_like(full_max)
+    inc_min = torch.zeros_like(full_max)
+    rk.rk_hsa_build_aux(kc, 700, 0, 16, full_max, full_min, n_q_heads=w.n_q)
+    rk.rk_hsa_build_aux(kc, 650, 0, 16, inc_max, inc_min, n_q_heads=w.n_q)
+    for n_old in range(650, 700, 7):
+        rk.rk_hsa_build_aux(kc, min(n_old + 7, 700), n_old, 16, inc_max, inc_min, n_q_heads=w.n_q)
+    torch.cuda.synchronize()
+    assert torch.equal(full_max[..., :nblk], inc_max[..., :nblk])
+    assert torch.equal(full_min[..., :nblk], inc_min[..., :nblk])
+
+
+def test_mt_decode_over_candidates(rk):
+    """RocketKV-MT: full cache kept, stage 2 restricted to the stage-1 candidates."""
+    base = WL.WORKLOADS["mt-mha-b8-s32k-c32"]
+    w = WL.scaled(base, batch=2, n_q=4, n_kv=4, seq=3000, n_plant=16, decode_steps=3)
+    s = rk.rk_split(w.c, w.seq, w.window, w.block, w.d)
+    cap = 3500                                          # full cache with spare capacity
+    k = torch.zeros(2, 4, cap, 128, dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros_like(k)
+    k0, v0, _ = WL.layer_kv(w, 0, device=DEV)
+    k[:, :, :3000] = k0
+    v[:, :, :3000] = v0
+    qw = WL.window_queries(w, 0, device=DEV)
+    say("MT evict indices only")
+    kept, _, _, _, _ = U.evict_and_check(rk, qw, k, v, 3000, w.window, w.pool, s["n_keep"], compact=False)
+    say("MT aux over candidates")
+    kmax, kmin = U.aux_and_check(rk, k, s["n_keep"], 16, w.n_q, idx=kept)
+    for step in range(3):
+        say("MT decode step", step)
+        q = WL.decode_query(w, 0, step, device=DEV)
+        U.decode_and_check(rk, q, k, v, kmax, kmin, s["n_keep"], 16, w.k1, s["k2_blocks"], cand=kept)
+
+
+def test_deterministic(rk):
+    say("run twice, bit-identical")
+    w = WL.scaled(WL.WORKLOADS["llama8b-layer-s32k-c16"], seq=4096, batch=1)
+    k, v, _ = WL.layer_kv(w, 0, device=DEV)
+    qw = WL.window_queries(w, 0, device=DEV)
+    q = WL.decode_query(w, 0, 0, device=DEV)
+    outs = []
+    for _ in range(2):
+        kept = torch.empty(1, 8, 1500, dtype=torch.int32, device=DEV)
+        kc = torch.empty(1, 8, 1500, 128, dtype=k.dtype, device=DEV)
+        vc = torch.empty_like(kc)
+        pooled = torch.empty(1, 8, 4096 - 32, device=DEV)
+        rk.rk_snapkv_evict(qw, k, v, 4096, 32, 63, 1500, kept, kc, vc, pooled)
+        kmax = torch.empty(1, 8, 128, 94, dtype=k.dtype, device=DEV)
+        kmin = torch.empty_like(kmax)
+        rk.rk_hsa_build_aux(kc, 1500, 0, 16, kmax, kmin, n_q_heads=32)
+        out = torch.empty(1, 32, 128, device=DEV)
+        rk.rk_hsa_decode(q, kc, vc, kmax, kmin, 1500, 16, 64, 32, out)
+        torch.cuda.synchronize()
+        outs.append((kept.clone(), pooled.clone(), out.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
