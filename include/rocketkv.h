@@ -134,12 +134,15 @@ rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* 
  *   idx_opt  [B, Hkv, idx_stride]   optional candidate rows (RocketKV-MT): page
  *                                   token n is key row idx_opt[n]; NULL means
  *                                   token n is row n
- *   kmax, kmin [B, Hkv, d, nblk_cap]  out, channel-major (page index fastest)
+ *   kmax, kmin [B, Hkv, d, nblk_cap]  out, channel-major (page index fastest);
+ *                                   nblk_cap must be a multiple of 8 so every
+ *                                   channel row starts 16-byte aligned
  * Pages first_token/block .. ceil(n_tokens/block)-1 are (re)computed from
  * tokens [page*block, min((page+1)*block, n_tokens)); other pages are left
  * untouched, so after appending tokens n_old..n_tokens-1 a call with
  * first_token = n_old equals a full rebuild bit for bit.  Exact: max/min only.
- * Requires 0 <= first_token < n_tokens, ceil(n_tokens/block) <= nblk_cap,
+ * Requires 0 <= first_token < n_tokens, ceil(n_tokens/block) <= nblk_cap
+ * (a multiple of 8),
  * n_tokens <= k_cap (identity map) or <= idx_stride (candidate map); every
  * idx_opt entry must lie in [0, k_cap).
  */
@@ -175,7 +178,8 @@ size_t rk_hsa_workspace_bytes(const rk_shape* shape, int64_t n_tokens, int32_t b
  *   sel_channels_opt [B, Hkv, k1] int32             out (optional): i1 ascending
  *   block_scores_opt [B, Hkv, nblk] float32         out (optional): s1
  * nblk = ceil(n_tokens / block).  Requires 1 <= n_tokens <= kv_cap,
- * nblk <= nblk_cap, nblk <= 16384, 1 <= k1 <= d, k2 >= 1, G in {1, 2, 4, 8}.
+ * nblk <= nblk_cap (a multiple of 8), nblk <= 12288, 1 <= k1 <= d, k2 >= 1,
+ * G in {1, 2, 4, 8}.
  */
 rk_status rk_hsa_decode(const rk_shape* shape, const void* q, const void* k, const void* v,
                         int64_t kv_cap, const void* kmax, const void* kmin, int64_t nblk_cap,
@@ -204,6 +208,25 @@ rk_status rk_hsa_decode_mt(const rk_shape* shape, const void* q, const void* k, 
                            int32_t* sel_blocks_opt, int32_t* sel_channels_opt,
                            float* block_scores_opt, void* ws, size_t ws_bytes,
                            rk_stream stream);
+
+/*
+ * Kernel timing (measurement support, not part of the method).
+ * Between rk_profile_begin() and rk_profile_end() every kernel the library
+ * launches is bracketed by a pair of HIP events recorded on the stream it is
+ * launched on.  rk_profile_end() waits for those events, stops recording and
+ * writes, per kernel name in order of first launch, the launch count and the
+ * summed event-to-event time into out[0 .. *n_out) (at most `cap` entries).
+ * Process-wide; not meant to be used concurrently from several threads.
+ * RK_EDEVICE if an event call fails, RK_EINVAL on NULL arguments.
+ */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} rk_kernel_time;
+
+rk_status rk_profile_begin(void);
+rk_status rk_profile_end(rk_kernel_time* out, int32_t cap, int32_t* n_out);
 
 /* Static name of a status code. */
 const char* rk_status_string(rk_status status);

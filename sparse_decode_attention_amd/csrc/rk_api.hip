@@ -73,8 +73,9 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
   if (st != RK_OK) return st;
   if (!q || !k || !v || !kmax || !kmin || !out) return fail(RK_EINVAL, "null tensor argument");
   if (mt && !cand) return fail(RK_EINVAL, "cand_idx is NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
-    return fail(RK_EINVAL, "q, k and v must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kmax) || !aligned16(kmin) ||
+      !aligned16(out))
+    return fail(RK_EINVAL, "q, k, v, kmax, kmin and out must be 16-byte aligned");
   if (d.G != 1 && d.G != 2 && d.G != 4 && d.G != 8)
     return fail(RK_EUNSUPPORTED, "group size %d not built (1, 2, 4, 8)", d.G);
   if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
@@ -89,6 +90,7 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
   }
   const int64_t nblk = (n_tokens + block - 1) / block;
   if (nblk > nblk_cap) return fail(RK_EINVAL, "pages (%lld) exceed nblk_cap", (long long)nblk);
+  if (nblk_cap % 8) return fail(RK_EINVAL, "nblk_cap must be a multiple of 8");
   if (nblk > rk::kMaxPages)
     return fail(RK_EUNSUPPORTED, "pages (%lld) above %lld", (long long)nblk,
                 (long long)rk::kMaxPages);
@@ -195,7 +197,8 @@ rk_status rk_hsa_build_aux(const rk_shape* shape, const void* k, int64_t k_cap,
   rk_status st = check_shape(shape, &d);
   if (st != RK_OK) return st;
   if (!k || !kmax || !kmin) return fail(RK_EINVAL, "null tensor argument");
-  if (!aligned16(k)) return fail(RK_EINVAL, "k must be 16-byte aligned");
+  if (!aligned16(k) || !aligned16(kmax) || !aligned16(kmin))
+    return fail(RK_EINVAL, "k, kmax and kmin must be 16-byte aligned");
   if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
   if (n_tokens < 1 || n_tokens > (int64_t(1) << 31) - 1)
     return fail(RK_EINVAL, "n_tokens outside [1, 2^31)");
@@ -205,6 +208,7 @@ rk_status rk_hsa_build_aux(const rk_shape* shape, const void* k, int64_t k_cap,
     return fail(RK_EINVAL, "n_tokens exceeds %s", idx_opt ? "idx_stride" : "k_cap");
   const int64_t nblk = (n_tokens + block - 1) / block;
   if (nblk > nblk_cap) return fail(RK_EINVAL, "pages (%lld) exceed nblk_cap", (long long)nblk);
+  if (nblk_cap % 8) return fail(RK_EINVAL, "nblk_cap must be a multiple of 8");
   return device_status(rk::launch_build_aux(d, k, k_cap, idx_opt, idx_stride, n_tokens,
                                             first_token / block, block, kmax, kmin, nblk_cap,
                                             static_cast<hipStream_t>(stream)),

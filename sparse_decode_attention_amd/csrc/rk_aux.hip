@@ -93,7 +93,7 @@ hipError_t launch_aux_t(const Dims& d, const void* k, int64_t k_cap, const int32
   const int64_t nblk = (n_tokens + block - 1) / block;
   const int64_t npages = nblk - first_block;
   dim3 grid(unsigned((npages + PPW - 1) / PPW), unsigned(d.units()));
-  hipLaunchKernelGGL((aux_build_kernel<T, D>), grid, dim3(256), 0, s,
+  RK_LAUNCH("aux_build", (aux_build_kernel<T, D>), grid, dim3(256), 0, s,
                      static_cast<const T*>(k), k_cap, idx, idx_stride, int(n_tokens),
                      int(first_block), int(nblk), block, static_cast<T*>(kmax),
                      static_cast<T*>(kmin), nblk_cap);

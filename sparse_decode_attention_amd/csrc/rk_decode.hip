@@ -9,12 +9,14 @@
 // cache).
 //
 // Three launches per call:
-//   hsa_select  one workgroup per unit: channel sums, top-k1, page scores
-//               over the k1 sign-selected aux rows (coalesced row reads), top-k2
-//   hsa_attn    split-K over the selected pages: a wave streams whole pages,
-//               16-byte K/V loads, online softmax in the exp2 domain, one
+//   hsa_select  one workgroup per unit: channel sums and top-k1; the k1
+//               sign-selected aux rows are staged into LDS with 16-byte loads
+//               (one memory round trip), pages are scored from LDS, top-k2 by
+//               radix select
+//   hsa_attn    split-K over the selected pages: a wave streams whole pages
+//               with 16-byte K/V loads, online softmax in the exp2 domain, one
 //               partial (m, l, o[d]) per head per workgroup
-//   hsa_combine merges the partials of each head in split order.
+//   hsa_combine one wave per (unit, head) merges the partials
 // HBM-bound: bytes per unit = q + k1*nblk aux elements + 2*d*|T| K/V elements.
 #include <math.h>
 
@@ -29,12 +31,18 @@ constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxi
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void hsa_select_kernel(
     const T* __restrict__ q, const T* __restrict__ kmax, const T* __restrict__ kmin,
-    int64_t nblk_cap, int nblk, int k1, int nsel, int32_t* __restrict__ sel_ws,
-    int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt) {
-  extern __shared__ uint32_t page_keys[];  // [nblk]
-  __shared__ uint32_t chan_keys[D];
+    int64_t nblk_cap, int nblk, int k1, int nsel, int npc, int32_t* __restrict__ sel_ws,
+    int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt,
+    float* __restrict__ s1_opt) {
+  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
+  extern __shared__ __align__(16) unsigned char dyn_lds[];
+  uint32_t* page_keys = reinterpret_cast<uint32_t*>(dyn_lds);  // [nblk rounded up to 4]
+  T* stage = reinterpret_cast<T*>(dyn_lds + (size_t((nblk + 3) & ~3) * 4 + 15) / 16 * 16);
+  __shared__ __align__(16) uint32_t chan_keys[D];
   __shared__ float qbar[D];
   __shared__ int i1[D];
+  __shared__ __align__(16) float i1_q[D];
+  __shared__ const T* i1_row[D];
   __shared__ TopkSmem<256> sm;
 
   const int u = blockIdx.x;
@@ -51,28 +59,81 @@ __global__ __launch_bounds__(256) void hsa_select_kernel(
     qbar[t] = qb;
   }
   __syncthreads();
-  wg_topk<256>([&](int i) { return chan_keys[i]; }, D, k1, [&](int r, int i) { i1[r] = i; }, sm);
+  wg_topk_rank<256>(chan_keys, D, k1, [&](int r, int i) { i1[r] = i; }, sm.tmp);
   __syncthreads();
-  if (chan_opt)
-    for (int j = t; j < k1; j += 256) chan_opt[size_t(u) * k1 + j] = i1[j];
-
   const T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
   const T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
-  for (int b = t; b < nblk; b += 256) {
-    // one rounded multiply and one rounded add per term: no fused multiply-add
-#pragma clang fp contract(off)
-    float s = 0.f;
-    for (int j = 0; j < k1; ++j) {
-      const int ch = i1[j];
-      const float qv = qbar[ch];
-      const T* row = (qv >= 0.f ? xu : nu) + size_t(ch) * nblk_cap;
-      const float prod = qv * to_f32(row[b]);
-      s = s + prod;
-    }
-    page_keys[b] = order_key(s);
-    if (s1_opt) s1_opt[size_t(u) * nblk + b] = s;
+  for (int j = t; j < k1; j += 256) {
+    const int ch = i1[j];
+    const float qv = qbar[ch];
+    i1_q[j] = qv;
+    i1_row[j] = (qv >= 0.f ? xu : nu) + size_t(ch) * nblk_cap;  // sign-selected aux row
+    if (chan_opt) chan_opt[size_t(u) * k1 + j] = ch;
   }
   __syncthreads();
+
+  // Pages in chunks of npc (a multiple of 8): stage the k1 rows' slices, then
+  // s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b] from LDS.
+  for (int p0 = 0; p0 < nblk; p0 += npc) {
+    const int np = min(npc, nblk - p0);
+    const int nv = (np + EPV - 1) / EPV;  // vectors per staged row (stays inside nblk_cap)
+    const int total = k1 * nv;
+    for (int e0 = t; e0 < total; e0 += 256 * 16) {
+      uint4 buf[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int e = e0 + x * 256;
+        if (e < total)
+          buf[x] = *reinterpret_cast<const uint4*>(i1_row[e / nv] + p0 + (e % nv) * EPV);
+      }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int e = e0 + x * 256;
+        if (e < total) *reinterpret_cast<uint4*>(stage + size_t(e / nv) * npc + (e % nv) * EPV) = buf[x];
+      }
+    }
+    __syncthreads();
+    // each thread scores up to 4 pages together; 4 channels per step, so a
+    // dozen independent LDS reads are in flight before the ordered adds
+    for (int b0 = t; b0 < np; b0 += 4 * 256) {
+      // one rounded multiply and one rounded add per term: no fused multiply-add
+#pragma clang fp contract(off)
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      int bb[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) bb[p] = min(b0 + p * 256, np - 1);
+      int j = 0;
+      for (; j + 4 <= k1; j += 4) {
+        const float4 qv = *reinterpret_cast<const float4*>(i1_q + j);
+        float sv[4][4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) sv[p][jj] = to_f32(stage[size_t(j + jj) * npc + bb[p]]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          acc[p] = acc[p] + qv.x * sv[p][0];
+          acc[p] = acc[p] + qv.y * sv[p][1];
+          acc[p] = acc[p] + qv.z * sv[p][2];
+          acc[p] = acc[p] + qv.w * sv[p][3];
+        }
+      }
+      for (; j < k1; ++j) {
+        const float qv = i1_q[j];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) acc[p] = acc[p] + qv * to_f32(stage[size_t(j) * npc + bb[p]]);
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int b = b0 + p * 256;
+        if (b < np) {
+          page_keys[p0 + b] = order_key(acc[p]);
+          if (s1_opt) s1_opt[size_t(u) * nblk + p0 + b] = acc[p];
+        }
+      }
+    }
+    __syncthreads();
+  }
   int32_t* su = sel_ws + size_t(u) * nsel;
   int32_t* so = sel_opt ? sel_opt + size_t(u) * nsel : nullptr;
   wg_topk<256>(
@@ -99,9 +160,10 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   constexpr int TPS = 4;
   constexpr int CHUNK = SLOTS * TPS;
   constexpr int NW = 4;
+  constexpr int PF = D + 4;  // floats per head partial: m, l, pad, pad, o[D]
   static_assert(kWave % LPR == 0, "row chunks must tile a wave");
   __shared__ float wm[NW][G], wl[NW][G];
-  __shared__ float wo[NW][G][D];
+  __shared__ __align__(16) float wo[NW][G][D];
 
   const int u = blockIdx.y;
   const int split = blockIdx.x;
@@ -223,7 +285,8 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   }
   __syncthreads();
   // merge the 4 waves in order and write this split's partial per head
-  float* pu = partials + (size_t(u) * n_split + split) * G * (D + 2);
+  float* pu = partials + size_t(u) * n_split * G * PF;
+  float* pw = pu + size_t(split) * G * PF;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int g = idx / D;
     const int ch = idx % D;
@@ -235,8 +298,8 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
       ll += wl[w][g] * a;
       oo += wo[w][g][ch] * a;
     }
-    float* pg = pu + size_t(g) * (D + 2);
-    pg[2 + ch] = oo;
+    float* pg = pw + size_t(g) * PF;
+    pg[4 + ch] = oo;
     if (ch == 0) {
       pg[0] = mm;
       pg[1] = ll;
@@ -244,24 +307,61 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   }
 }
 
+// One wave per (unit, head) merges the split partials.  Lane s (< n_split)
+// holds split s's (m, l); the o rows are read as float4, each lane covering
+// one 4-channel slice for one residue class of splits, all loads issued
+// before any use.  Classes are then merged with a fixed butterfly.
 template <int D, int G>
 __global__ __launch_bounds__(256) void hsa_combine_kernel(const float* __restrict__ partials,
-                                                          int n_split, float* __restrict__ out) {
-  const int u = blockIdx.x;
-  const float* pu = partials + size_t(u) * n_split * G * (D + 2);
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int g = idx / D;
-    const int ch = idx % D;
-    float mm = kNegBig;
-    for (int s = 0; s < n_split; ++s) mm = fmaxf(mm, pu[(size_t(s) * G + g) * (D + 2)]);
-    float ll = 0.f, oo = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float* pg = pu + (size_t(s) * G + g) * (D + 2);
-      const float a = exp2f(pg[0] - mm);
-      ll += pg[1] * a;
-      oo += pg[2 + ch] * a;
+                                                          int n_split, int units,
+                                                          float* __restrict__ out) {
+  constexpr int PF = D + 4;
+  constexpr int C4 = D / 4;               // float4 slices per head row
+  constexpr int CLASSES = kWave / C4;     // split residue classes per wave
+  constexpr int PER = kMaxSplits / CLASSES;
+  static_assert(kWave % C4 == 0, "head row must tile a wave");
+  const int wi = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (wi >= units * G) return;
+  const int lane = lane_id();
+  const int u = wi / G, g = wi % G;
+  const float* pu = partials + size_t(u) * n_split * G * PF + size_t(g) * PF;
+  const size_t stride = size_t(G) * PF;
+  const int c4 = lane % C4, cls = lane / C4;
+  float4 ov[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = cls + i * CLASSES;
+    ov[i] = s < n_split ? reinterpret_cast<const float4*>(pu + s * stride + 4)[c4]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const float2 ml = lane < n_split ? *reinterpret_cast<const float2*>(pu + lane * stride)
+                                   : make_float2(kNegBig, 0.f);
+  const float mm = wave_max(ml.x);
+  const float a = lane < n_split ? exp2f(ml.x - mm) : 0.f;
+  const float ll = wave_sum(ml.y * a);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = cls + i * CLASSES;
+    const float w = __shfl(a, s < kWave ? s : 0);
+    if (s < n_split) {
+      acc.x += ov[i].x * w;
+      acc.y += ov[i].y * w;
+      acc.z += ov[i].z * w;
+      acc.w += ov[i].w * w;
     }
-    out[(size_t(u) * G + g) * D + ch] = oo / ll;
+  }
+#pragma unroll
+  for (int off = C4; off < kWave; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+  if (cls == 0) {
+    const float inv = 1.0f / ll;
+    reinterpret_cast<float4*>(out + (size_t(u) * G + g) * D)[c4] =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
@@ -279,36 +379,51 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   float* part = reinterpret_cast<float*>(wsb + lay.partials);
   const int units = d.units();
 
-  const size_t lds = size_t(nblk) * sizeof(uint32_t);
-  hipLaunchKernelGGL((hsa_select_kernel<T, D, G>), dim3(units), dim3(256), lds, s,
-                     static_cast<const T*>(q), static_cast<const T*>(kmax),
-                     static_cast<const T*>(kmin), nblk_cap, nblk, k1, lay.nsel, sel, sel_opt,
-                     chan_opt, s1_opt);
+  // LDS of the select workgroup: page keys, then the staged aux slices
+  const size_t keys_bytes = (size_t((nblk + 3) & ~3) * 4 + 15) / 16 * 16;
+  const size_t stage_budget = kSelectLdsBudget - keys_bytes;
+  int npc = int(stage_budget / (size_t(k1) * sizeof(T))) / 8 * 8;
+  const int nblk8 = (nblk + 7) / 8 * 8;
+  npc = npc > nblk8 ? nblk8 : npc;
+  if (npc < 8) return hipErrorInvalidValue;
+  const size_t lds = keys_bytes + size_t(k1) * npc * sizeof(T);
+  static bool attr_set = false;  // once per template instantiation
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hsa_select_kernel<T, D, G>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       int(kSelectLdsBudget));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  RK_LAUNCH("hsa_select", (hsa_select_kernel<T, D, G>), dim3(units), dim3(256), lds, s,
+            static_cast<const T*>(q), static_cast<const T*>(kmax), static_cast<const T*>(kmin),
+            nblk_cap, nblk, k1, lay.nsel, npc, sel, sel_opt, chan_opt, s1_opt);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
   // split-K sizing: aim for ~2048 workgroups over the whole launch, at least
-  // kMinPagesPerSplit pages (one per wave) per workgroup
+  // kMinPagesPerSplit pages (one per wave) and at most kMaxSplits splits per unit
   const int64_t total_pages = int64_t(units) * lay.nsel;
   int pps = int((total_pages + 2047) / 2048);
   pps = pps < kMinPagesPerSplit ? kMinPagesPerSplit : pps;
+  const int pps_cap = (lay.nsel + kMaxSplits - 1) / kMaxSplits;
+  pps = pps < pps_cap ? pps_cap : pps;
   pps = (pps + 3) / 4 * 4;
   const int n_split = (lay.nsel + pps - 1) / pps;
   const float scale_log2 = float(1.4426950408889634 / sqrt(double(D)));
   if (cand)
-    hipLaunchKernelGGL((hsa_attn_kernel<T, D, G, true>), dim3(n_split, units), dim3(256), 0, s,
-                       static_cast<const T*>(q), static_cast<const T*>(k),
-                       static_cast<const T*>(v), kv_cap, cand, cand_stride, sel, lay.nsel, pps,
-                       n_split, int(n_tokens), block, scale_log2, part);
+    RK_LAUNCH("hsa_attn_mt", (hsa_attn_kernel<T, D, G, true>), dim3(n_split, units), dim3(256), 0,
+              s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+              kv_cap, cand, cand_stride, sel, lay.nsel, pps, n_split, int(n_tokens), block,
+              scale_log2, part);
   else
-    hipLaunchKernelGGL((hsa_attn_kernel<T, D, G, false>), dim3(n_split, units), dim3(256), 0, s,
-                       static_cast<const T*>(q), static_cast<const T*>(k),
-                       static_cast<const T*>(v), kv_cap, cand, cand_stride, sel, lay.nsel, pps,
-                       n_split, int(n_tokens), block, scale_log2, part);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((hsa_combine_kernel<D, G>), dim3(units), dim3(256), 0, s, part, n_split,
-                     out);
+    RK_LAUNCH("hsa_attn", (hsa_attn_kernel<T, D, G, false>), dim3(n_split, units), dim3(256), 0,
+              s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+              kv_cap, cand, cand_stride, sel, lay.nsel, pps, n_split, int(n_tokens), block,
+              scale_log2, part);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  RK_LAUNCH("hsa_combine", (hsa_combine_kernel<D, G>), dim3((units * G + 3) / 4), dim3(256), 0, s,
+            part, n_split, units, out);
   return hipGetLastError();
 }
 

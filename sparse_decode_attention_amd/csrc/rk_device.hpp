@@ -206,4 +206,54 @@ __device__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit, Topk
   }
 }
 
+// Workgroup top-k for a small key set held in LDS (n up to a few thousand):
+// element j is selected iff #{i : key_i > key_j or (key_i == key_j and
+// i < j)} < k, counted directly (4 keys per LDS read, broadcast to the wave);
+// emit(rank, j) in ascending j order as wg_topk.  `keys` must be 16-byte
+// aligned with room for n rounded up to 4 (the padding is never counted).
+template <int NT, typename EmitFn>
+__device__ void wg_topk_rank(const uint32_t* keys, int n, int k, const EmitFn& emit, int* tmp) {
+  const int t = threadIdx.x;
+  if (k <= 0) return;
+  if (k >= n) {
+    for (int i = t; i < n; i += NT) emit(i, i);
+    return;
+  }
+  const int n4 = n & ~3;
+  int base = 0;
+  for (int c0 = 0; c0 < n; c0 += NT) {
+    const int j = c0 + t;
+    bool sel = false;
+    if (j < n) {
+      const uint32_t kj = keys[j];
+      int rank = 0;
+      for (int i = 0; i < n4; i += 4) {
+        const uint4 kk = *reinterpret_cast<const uint4*>(keys + i);
+        rank += int(kk.x > kj || (kk.x == kj && i < j));
+        rank += int(kk.y > kj || (kk.y == kj && i + 1 < j));
+        rank += int(kk.z > kj || (kk.z == kj && i + 2 < j));
+        rank += int(kk.w > kj || (kk.w == kj && i + 3 < j));
+      }
+      for (int i = n4; i < n; ++i) rank += int(keys[i] > kj || (keys[i] == kj && i < j));
+      sel = rank < k;
+    }
+    int tot;
+    const int pos = base + wg_excl_count<NT>(sel, tmp, &tot);
+    if (sel) emit(pos, j);
+    base += tot;
+  }
+}
+
+// Wave-wide reductions (all 64 lanes take part).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
 }  // namespace rk

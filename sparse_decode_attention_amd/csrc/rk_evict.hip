@@ -125,27 +125,30 @@ __global__ __launch_bounds__(256) void ws_pass1_kernel(const T* __restrict__ q_w
     }
 #pragma unroll
     for (int off = 1; off < 8; off <<= 1) z += __shfl_xor(z, off);
-    if (part == 0 && r_all < M) partials[(size_t(u) * n_tiles + tile) * M + r_all] = make_float2(mx, z);
+    if (part == 0 && r_all < M) partials[(size_t(u) * M + r_all) * n_tiles + tile] = make_float2(mx, z);
     __syncthreads();
   }
 }
 
-// Merge the tile partials of every row, in tile order: (m, 1/Z).
+// Merge the tile partials of every row: (m, 1/Z).  One wave per (unit, row);
+// lane l takes tiles l, l+64, ... in order, then a fixed butterfly merges lanes.
 __global__ __launch_bounds__(256) void ws_stats_kernel(const float2* __restrict__ partials,
-                                                       int M, int n_tiles,
+                                                       int M, int n_tiles, int units,
                                                        float2* __restrict__ stats) {
-  const int u = blockIdx.y;
-  const int row = blockIdx.x * 256 + threadIdx.x;
-  if (row >= M) return;
-  const float2* pu = partials + size_t(u) * n_tiles * M + row;
+  const int wi = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (wi >= units * M) return;
+  const int lane = lane_id();
+  const float2* pr = partials + size_t(wi) * n_tiles;
   float mm = kNegBig;
-  for (int t = 0; t < n_tiles; ++t) mm = fmaxf(mm, pu[size_t(t) * M].x);
+  for (int t = lane; t < n_tiles; t += kWave) mm = fmaxf(mm, pr[t].x);
+  mm = wave_max(mm);
   float z = 0.f;
-  for (int t = 0; t < n_tiles; ++t) {
-    const float2 p = pu[size_t(t) * M];
+  for (int t = lane; t < n_tiles; t += kWave) {
+    const float2 p = pr[t];
     z += p.y * exp2f(p.x - mm);
   }
-  stats[size_t(u) * M + row] = make_float2(mm, 1.0f / z);
+  z = wave_sum(z);
+  if (lane == 0) stats[wi] = make_float2(mm, 1.0f / z);
 }
 
 // Pass 2: score[j] = sum over the G*W rows of exp2(x - m) / Z, prefix keys only.
@@ -251,6 +254,166 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k,
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 window scoring on the matrix cores (v_mfma_f32_32x32x16_bf16).
+//
+// A workgroup (4 waves) owns 256 consecutive keys of one unit.  The G*W window
+// rows are cut into 32-row groups; a wave keeps the A operand of its row group
+// (32 rows x d, bf16) in registers for the whole tile and streams 32-key
+// chunks of K straight from memory as the B operand (each lane fetches 16
+// contiguous bytes of one key row), prefetching the next chunk while the
+// current one is multiplied.  With fewer than 4 row groups the waves split
+// the tile's chunks instead.  Accumulator lane layout (verified on gfx950):
+// lane l, element i holds row 8*(i/4) + 4*(l/32) + i%4 of the group and key
+// column l%32 of the chunk.
+//   pass 1: per row, online max / sum of exp2 over the tile -> partials
+//   pass 2: exp2(x - m_row) / Z_row summed over all rows of the group for each
+//           key, then over the row groups in order -> score
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int TNM = 256;             // keys per workgroup
+constexpr int NCH = TNM / 32;        // 32-key chunks per workgroup
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p, bool ok) {
+  uint4 r = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+template <int D, int PASS>
+__global__ __launch_bounds__(256) void ws_mfma_kernel(
+    const bf16_t* __restrict__ q_win, const bf16_t* __restrict__ k, int64_t kv_cap, int S, int W,
+    int G, int n_tiles, float scale_log2, float2* __restrict__ partials,
+    const float2* __restrict__ stats, float* __restrict__ scores) {
+  constexpr int KS = D / 16;
+  extern __shared__ float smem[];  // pass 1: items x 32 float2; pass 2: RG x TNM floats
+  const int M = G * W;
+  const int RG = (M + 31) / 32;
+  const int CS = RG >= 4 ? 1 : 4 / RG;  // waves sharing one row group
+  const int items = RG * CS;
+  const int u = blockIdx.y;
+  const int tile = blockIdx.x;
+  const int j0 = tile * TNM;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int half = lane >> 5;
+  const int P = S - W;
+  const int jlim = PASS == 1 ? S : P;
+  const bf16_t* qg = q_win + size_t(u) * M * D;
+  const bf16_t* ku = k + size_t(u) * size_t(kv_cap) * D + half * 8;
+
+  for (int it = wave; it < items; it += 4) {
+    const int rg = it / CS;
+    const int cs = it % CS;
+    bf16x8_t a[KS];
+    {
+      const int arow = rg * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        a[ks] = load_bf16x8(qg + size_t(arow) * D + ks * 16 + half * 8, arow < M);
+    }
+    float m[16], z[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = rg * 32 + 8 * (i / 4) + 4 * half + (i & 3);
+      if (PASS == 1) {
+        m[i] = kNegBig;
+        z[i] = 0.f;
+      } else {
+        const float2 st = row < M ? stats[size_t(u) * M + row] : make_float2(1.0e30f, 0.f);
+        m[i] = st.x;  // row max (log2 domain)
+        z[i] = st.y;  // 1 / row sum
+      }
+    }
+    int cc = cs;
+    int col = j0 + cc * 32 + (lane & 31);
+    bf16x8_t b[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) b[ks] = load_bf16x8(ku + size_t(col) * D + ks * 16, col < jlim);
+    for (; cc < NCH && j0 + cc * 32 < jlim; cc += CS) {
+      const int ncol = col + 32 * CS;
+      const bool more = cc + CS < NCH && j0 + (cc + CS) * 32 < jlim;
+      bf16x8_t bn[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        bn[ks] = load_bf16x8(ku + size_t(ncol) * D + ks * 16, more && ncol < jlim);
+      f32x16_t acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b[ks], acc, 0, 0, 0);
+      if (PASS == 1) {
+        const bool edge = j0 + cc * 32 + 32 > S - W;  // chunk reaches the causal window or S
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = acc[i] * scale_log2;
+          bool ok = true;
+          if (edge) {
+            const int row = rg * 32 + 8 * (i / 4) + 4 * half + (i & 3);
+            ok = col < S && col <= S - W + (row % W);
+          }
+          if (ok) {
+            const float mn = fmaxf(m[i], x);
+            z[i] = z[i] * exp2f(m[i] - mn) + exp2f(x - mn);
+            m[i] = mn;
+          }
+        }
+      } else {
+        float cs_sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cs_sum += exp2f(acc[i] * scale_log2 - m[i]) * z[i];
+        cs_sum += __shfl_xor(cs_sum, 32);
+        if (lane < 32) smem[rg * TNM + cc * 32 + lane] = cs_sum;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) b[ks] = bn[ks];
+      col = ncol;
+    }
+    if (PASS == 1) {
+      // merge the 32 key columns held by the lanes of each half-wave
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float mo = __shfl_xor(m[i], off);
+          const float zo = __shfl_xor(z[i], off);
+          const float mn = fmaxf(m[i], mo);
+          z[i] = z[i] * exp2f(m[i] - mn) + zo * exp2f(mo - mn);
+          m[i] = mn;
+        }
+      }
+      if ((lane & 31) == 0) {
+        float2* mz = reinterpret_cast<float2*>(smem) + it * 32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mz[8 * (i / 4) + 4 * half + (i & 3)] = make_float2(m[i], z[i]);
+      }
+    }
+  }
+  __syncthreads();
+  if (PASS == 1) {
+    const float2* mz = reinterpret_cast<const float2*>(smem);
+    for (int r = threadIdx.x; r < RG * 32; r += 256) {
+      if (r >= M) continue;
+      const int rg = r / 32, rl = r % 32;
+      float mm = kNegBig, zz = 0.f;
+      for (int c = 0; c < CS; ++c) {  // column splits in order
+        const float2 p = mz[(rg * CS + c) * 32 + rl];
+        const float mn = fmaxf(mm, p.x);
+        zz = zz * exp2f(mm - mn) + p.y * exp2f(p.x - mn);
+        mm = mn;
+      }
+      partials[(size_t(u) * M + r) * n_tiles + tile] = make_float2(mm, zz);
+    }
+  } else {
+    for (int c = threadIdx.x; c < TNM; c += 256) {
+      const int j = j0 + c;
+      if (j >= P) continue;
+      float sacc = 0.f;
+      for (int rg = 0; rg < RG; ++rg) sacc += smem[rg * TNM + c];
+      scores[size_t(u) * P + j] = sacc;
+    }
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const void* v,
                           int64_t kv_cap, int64_t S64, int W, int pool_kernel, int64_t n_keep,
@@ -270,27 +433,45 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   const T* qw = static_cast<const T*>(q_win);
   const T* kk = static_cast<const T*>(k);
 
-  hipLaunchKernelGGL((ws_pass1_kernel<T, D>), dim3(lay.n_tiles, units), dim3(256), 0, s, qw, kk,
-                     kv_cap, S, W, d.G, lay.n_tiles, scale_log2, partials);
+  constexpr bool kMfma = sizeof(T) == 2;  // bf16 on the matrix cores, float32 on the vector ALUs
+  const int n_tiles = kMfma ? (S + TNM - 1) / TNM : lay.n_tiles;
+  const int RG = (M + 31) / 32;
+  const int CS = RG >= 4 ? 1 : 4 / RG;
+  const size_t lds1 = size_t(RG * CS) * 32 * sizeof(float2);
+  const size_t lds2 = size_t(RG) * TNM * sizeof(float);
+  if constexpr (kMfma) {
+    RK_LAUNCH("ws_pass1", (ws_mfma_kernel<D, 1>), dim3(n_tiles, units), dim3(256), lds1, s,
+              reinterpret_cast<const bf16_t*>(qw), reinterpret_cast<const bf16_t*>(kk), kv_cap, S,
+              W, d.G, n_tiles, scale_log2, partials, nullptr, nullptr);
+  } else {
+    RK_LAUNCH("ws_pass1", (ws_pass1_kernel<T, D>), dim3(n_tiles, units), dim3(256), 0, s, qw, kk,
+              kv_cap, S, W, d.G, n_tiles, scale_log2, partials);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(ws_stats_kernel, dim3((M + 255) / 256, units), dim3(256), 0, s, partials, M,
-                     lay.n_tiles, stats);
+  RK_LAUNCH("ws_stats", ws_stats_kernel, dim3((units * M + 3) / 4), dim3(256), 0, s, partials, M,
+            n_tiles, units, stats);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (P > 0) {
-    hipLaunchKernelGGL((ws_pass2_kernel<T, D>), dim3((P + TN - 1) / TN, units), dim3(256), 0, s,
-                       qw, kk, kv_cap, S, W, d.G, scale_log2, stats, scores);
+    if constexpr (kMfma) {
+      RK_LAUNCH("ws_pass2", (ws_mfma_kernel<D, 2>), dim3((P + TNM - 1) / TNM, units), dim3(256),
+                lds2, s, reinterpret_cast<const bf16_t*>(qw), reinterpret_cast<const bf16_t*>(kk),
+                kv_cap, S, W, d.G, n_tiles, scale_log2, nullptr, stats, scores);
+    } else {
+      RK_LAUNCH("ws_pass2", (ws_pass2_kernel<T, D>), dim3((P + TN - 1) / TN, units), dim3(256), 0,
+                s, qw, kk, kv_cap, S, W, d.G, scale_log2, stats, scores);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const int h = (pool_kernel - 1) / 2;
-    hipLaunchKernelGGL(pool_sum_kernel, dim3((P + 255) / 256, units), dim3(256),
+    RK_LAUNCH("pool_sum", pool_sum_kernel, dim3((P + 255) / 256, units), dim3(256),
                        size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(select_kernel, dim3(units), dim3(1024), 0, s, pooled, S, W, int(n_keep),
+  RK_LAUNCH("select_tokens", select_kernel, dim3(units), dim3(1024), 0, s, pooled, S, W, int(n_keep),
                      kept);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (k_out) {
-    hipLaunchKernelGGL((gather_kernel<T, D>), dim3(unsigned((n_keep + 63) / 64), units),
+    RK_LAUNCH("gather_kv", (gather_kernel<T, D>), dim3(unsigned((n_keep + 63) / 64), units),
                        dim3(256), 0, s, kk, static_cast<const T*>(v), kv_cap, kept, int(n_keep),
                        static_cast<T*>(k_out), static_cast<T*>(v_out), out_cap);
     err = hipGetLastError();

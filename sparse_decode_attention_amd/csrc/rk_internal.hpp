@@ -13,8 +13,12 @@ namespace rk {
 constexpr int64_t kMaxPages = 12288;
 // Stage-1 column tile of the window-score passes (partials are sized by it).
 constexpr int kWsTile = 64;
-// Pages handled by one attention workgroup at least (split-K granularity).
+// Pages handled by one attention workgroup at least (split-K granularity),
+// and the most workgroups one unit's attention is split over.
 constexpr int kMinPagesPerSplit = 4;
+constexpr int kMaxSplits = 64;
+// LDS budget of the page-selection workgroup (gfx950: 160 KB per workgroup).
+constexpr size_t kSelectLdsBudget = 160 * 1024 - 16 * 1024;
 
 struct Dims {
   int B, Hq, Hkv, G, D;
@@ -43,6 +47,9 @@ inline EvictWs evict_ws_layout(const Dims& d, int64_t S, int W) {
   return w;
 }
 
+// Split-K partial of one head: m, l, two pad floats, then o[D] (16-byte aligned).
+inline int partial_floats(int D) { return D + 4; }
+
 struct DecodeWs {
   size_t sel, partials, total;
   int n_split_max, nsel;
@@ -50,14 +57,30 @@ struct DecodeWs {
 inline DecodeWs decode_ws_layout(const Dims& d, int64_t nblk, int k2) {
   DecodeWs w{};
   w.nsel = int(nblk < k2 ? nblk : k2);
-  w.n_split_max = (w.nsel + kMinPagesPerSplit - 1) / kMinPagesPerSplit;
+  const int by_pages = (w.nsel + kMinPagesPerSplit - 1) / kMinPagesPerSplit;
+  w.n_split_max = by_pages < kMaxSplits ? by_pages : kMaxSplits;
   const size_t u = size_t(d.units());
   size_t off = 0;
   w.sel = off;      off += align256(u * w.nsel * sizeof(int32_t));
-  w.partials = off; off += align256(u * w.n_split_max * d.G * (d.D + 2) * sizeof(float));
+  w.partials = off; off += align256(u * w.n_split_max * d.G * partial_floats(d.D) * sizeof(float));
   w.total = off;
   return w;
 }
+
+// ---- kernel timing (rk_profile_begin / rk_profile_end) ----
+bool prof_enabled();
+void prof_before(const char* name, hipStream_t s);
+void prof_after(hipStream_t s);
+
+// Launch a kernel; when kernel timing is on, bracket it with HIP events on
+// its stream.  `kern` must be parenthesised if it contains commas.
+#define RK_LAUNCH(name, kern, grid, block, lds, stream, ...)        \
+  do {                                                              \
+    const bool rk_prof_on_ = ::rk::prof_enabled();                  \
+    if (rk_prof_on_) ::rk::prof_before(name, stream);               \
+    hipLaunchKernelGGL(kern, grid, block, lds, stream, __VA_ARGS__); \
+    if (rk_prof_on_) ::rk::prof_after(stream);                      \
+  } while (0)
 
 // ---- launchers ----
 hipError_t launch_build_aux(const Dims& d, const void* k, int64_t k_cap, const int32_t* idx,

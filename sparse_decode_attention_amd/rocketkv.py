@@ -181,6 +181,11 @@ def rk_hsa_decode_mt(q, k, v, cand_idx, n_cand, kmax, kmin, block, k1, k2, out, 
     return ws
 
 
+def aux_capacity(n_tokens: int, block: int) -> int:
+    """Smallest valid nblk_cap for n_tokens: the page count rounded up to 8."""
+    return (-(-n_tokens // block) + 7) // 8 * 8
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -188,3 +193,26 @@ def library_path() -> str:
 def raw_library() -> ctypes.CDLL:
     """The loaded ctypes library (for tests of the raw C ABI)."""
     return _lib
+
+
+class RkKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+_lib.rk_profile_begin.argtypes = []
+_lib.rk_profile_begin.restype = ctypes.c_int
+_lib.rk_profile_end.argtypes = [ctypes.POINTER(RkKernelTime), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+_lib.rk_profile_end.restype = ctypes.c_int
+
+
+def rk_profile_begin():
+    """Start bracketing every library kernel with HIP events on its stream."""
+    _check(_lib.rk_profile_begin(), "rk_profile_begin")
+
+
+def rk_profile_end(cap: int = 64) -> dict:
+    """Stop, wait for the events and return {kernel: (launches, total_ms)}."""
+    arr = (RkKernelTime * cap)()
+    n = ctypes.c_int32(0)
+    _check(_lib.rk_profile_end(arr, cap, ctypes.byref(n)), "rk_profile_end")
+    return {arr[i].name.decode(): (int(arr[i].launches), float(arr[i].total_ms)) for i in range(n.value)}

@@ -103,7 +103,7 @@ def aux_and_check(rk, kc, n_tokens, block, n_q_heads, idx=None, units_to_check=N
     """Run rk_hsa_build_aux over kc (or the rows idx of kc) and check bit-exactly."""
     B, Hkv, _, d = kc.shape
     nblk = -(-n_tokens // block)
-    kmax = torch.empty(B, Hkv, d, nblk, dtype=kc.dtype, device=kc.device)
+    kmax = torch.empty(B, Hkv, d, rk.aux_capacity(n_tokens, block), dtype=kc.dtype, device=kc.device)
     kmin = torch.empty_like(kmax)
     rk.rk_hsa_build_aux(kc, n_tokens, 0, block, kmax, kmin, n_q_heads=n_q_heads, idx=idx)
     torch.cuda.synchronize()
@@ -111,8 +111,8 @@ def aux_and_check(rk, kc, n_tokens, block, n_q_heads, idx=None, units_to_check=N
     for b, h in units:
         rows = kc[b, h] if idx is None else kc[b, h, idx[b, h, :n_tokens].long()]
         wmax, wmin = O.build_aux(rows[:n_tokens].cpu().float().numpy(), n_tokens, block)
-        assert np.array_equal(np32(kmax[b, h]), wmax), (b, h)
-        assert np.array_equal(np32(kmin[b, h]), wmin), (b, h)
+        assert np.array_equal(np32(kmax[b, h, :, :nblk]), wmax), (b, h)
+        assert np.array_equal(np32(kmin[b, h, :, :nblk]), wmin), (b, h)
     return kmax, kmin
 
 
@@ -141,7 +141,7 @@ def decode_and_check(rk, q, kc, vc, kmax, kmin, n_tokens, block, k1, k2, cand=No
         qg = np32(q[b, h * G:(h + 1) * G])
         i1, qbar = O.channel_select(qg, k1)
         assert np.array_equal(chan[b, h].cpu().numpy(), i1), (b, h)
-        ws1 = O.block_scores(qbar, i1, np32(kmax[b, h]), np32(kmin[b, h]))
+        ws1 = O.block_scores(qbar, i1, np32(kmax[b, h, :, :nblk]), np32(kmin[b, h, :, :nblk]))
         assert np.array_equal(np32(s1[b, h]), ws1), (b, h)           # same float32 ops, same order
         gsel = sel[b, h].cpu().numpy()
         assert ascending(gsel) or nsel == 1

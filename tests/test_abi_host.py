@@ -111,6 +111,7 @@ def test_error_codes_before_any_launch(rk):
     assert decode(k2=0) == rk.RK_EINVAL
     assert decode(n=0) == rk.RK_EINVAL and decode(n=1025) == rk.RK_EINVAL
     assert decode(nblk_cap=62) == rk.RK_EINVAL
+    assert decode(nblk_cap=66) == rk.RK_EINVAL                         # not a multiple of 8
     assert decode(block=0) == rk.RK_EINVAL
     assert decode(ws_bytes=16) == rk.RK_EWORKSPACE
     assert b"workspace" in lib.rk_last_error()
@@ -143,12 +144,13 @@ def test_error_codes_before_any_launch(rk):
     assert need > 0 and evict(wsb=need - 1) == rk.RK_EWORKSPACE
 
     def aux(**kw):
-        a = dict(k=_vp(FAKE), cap=1024, idx=None, stride=0, n=1000, first=0, block=16, nblk_cap=63)
+        a = dict(k=_vp(FAKE), cap=1024, idx=None, stride=0, n=1000, first=0, block=16, nblk_cap=64)
         a.update(kw)
         return lib.rk_hsa_build_aux(byref(sh), a["k"], a["cap"], a["idx"], a["stride"], a["n"],
                                     a["first"], a["block"], _vp(FAKE), _vp(FAKE), a["nblk_cap"], None)
 
     assert aux(nblk_cap=62) == rk.RK_EINVAL
+    assert aux(nblk_cap=63) == rk.RK_EINVAL                            # not a multiple of 8
     assert aux(first=1000) == rk.RK_EINVAL and aux(first=-1) == rk.RK_EINVAL
     assert aux(n=1025) == rk.RK_EINVAL
     assert aux(idx=_vp(FAKE), stride=999) == rk.RK_EINVAL

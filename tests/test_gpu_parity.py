@@ -126,7 +126,7 @@ def test_incremental_aux_equals_rebuild(rk):
     w = WL.scaled(base, batch=2, seq=700, n_plant=0)
     kc, _, _ = WL.layer_kv(w, 0, device=DEV)
     nblk = -(-700 // 16)
-    full_max = torch.empty(2, w.n_kv, 128, nblk + 3, dtype=kc.dtype, device=DEV)
+    full_max = torch.empty(2, w.n_kv, 128, nblk + 4, dtype=kc.dtype, device=DEV)
     full_min = torch.empty_like(full_max)
     inc_max = torch.zeros_like(full_max)
     inc_min = torch.zeros_like(full_max)
@@ -174,7 +174,7 @@ def test_deterministic(rk):
         vc = torch.empty_like(kc)
         pooled = torch.empty(1, 8, 4096 - 32, device=DEV)
         rk.rk_snapkv_evict(qw, k, v, 4096, 32, 63, 1500, kept, kc, vc, pooled)
-        kmax = torch.empty(1, 8, 128, 94, dtype=k.dtype, device=DEV)
+        kmax = torch.empty(1, 8, 128, 96, dtype=k.dtype, device=DEV)
         kmin = torch.empty_like(kmax)
         rk.rk_hsa_build_aux(kc, 1500, 0, 16, kmax, kmin, n_q_heads=32)
         out = torch.empty(1, 32, 128, device=DEV)
@@ -183,3 +183,72 @@ def test_deterministic(rk):
         outs.append((kept.clone(), pooled.clone(), out.clone()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_graph_replay_matches_eager(rk):
+    """Decode calls captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager result bit for bit."""
+    say("graph capture / replay")
+    w = WL.scaled(WL.WORKLOADS["llama8b-layer-s32k-c16"], seq=4096, batch=2)
+    s = rk.rk_split(w.c, w.seq, w.window, w.block, w.d)
+    n_keep, k2 = s["n_keep"], s["k2_blocks"]
+    k, v, _ = WL.layer_kv(w, 0, device=DEV)
+    qw = WL.window_queries(w, 0, device=DEV)
+    kept = torch.empty(2, 8, n_keep, dtype=torch.int32, device=DEV)
+    kc = torch.empty(2, 8, n_keep, 128, dtype=k.dtype, device=DEV)
+    vc = torch.empty_like(kc)
+    nblk = -(-n_keep // 16)
+    kmax = torch.empty(2, 8, 128, rk.aux_capacity(n_keep, 16), dtype=k.dtype, device=DEV)
+    kmin = torch.empty_like(kmax)
+    shape = rk.shape_of(2, 32, 8, 128, k.dtype)
+    ws_e = torch.empty(rk.rk_snapkv_workspace_bytes(shape, w.seq, w.window), dtype=torch.uint8, device=DEV)
+    ws_d = torch.empty(rk.rk_hsa_workspace_bytes(shape, n_keep, 16, w.k1, k2), dtype=torch.uint8, device=DEV)
+    qs = torch.stack([WL.decode_query(w, 0, i, device=DEV) for i in range(4)])
+    out = torch.empty(4, 2, 32, 128, device=DEV)
+
+    def body():
+        rk.rk_snapkv_evict(qw, k, v, w.seq, w.window, w.pool, n_keep, kept, kc, vc, None, ws=ws_e)
+        rk.rk_hsa_build_aux(kc, n_keep, 0, 16, kmax, kmin, n_q_heads=32)
+        for i in range(4):
+            rk.rk_hsa_decode(qs[i], kc, vc, kmax, kmin, n_keep, 16, w.k1, k2, out[i], ws=ws_d)
+
+    body()
+    torch.cuda.synchronize()
+    ref = (kept.clone(), kc.clone(), kmax[..., :nblk].clone(), out.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        kept.zero_()
+        out.zero_()
+        kmax.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, (kept, kc, kmax[..., :nblk], out)):
+            assert torch.equal(a, b), rep
+        body()                                               # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_kernel_timing_hooks(rk):
+    say("rk_profile_begin/end")
+    w = WL.scaled(WL.WORKLOADS["tiny-gqa-s2048-d64-fp32"], seq=512)
+    kc, vc, _ = WL.layer_kv(w, 0, device=DEV)
+    kmax = torch.empty(1, 2, 64, 32, device=DEV)
+    kmin = torch.empty_like(kmax)
+    rk.rk_profile_begin()
+    for _ in range(3):
+        rk.rk_hsa_build_aux(kc, 512, 0, 16, kmax, kmin, n_q_heads=8)
+    q = WL.decode_query(w, 0, 0, device=DEV)
+    out = torch.empty(1, 8, 64, device=DEV)
+    rk.rk_hsa_decode(q, kc, vc, kmax, kmin, 512, 16, 16, 4, out)
+    prof = rk.rk_profile_end()
+    assert prof["aux_build"][0] == 3 and prof["aux_build"][1] > 0
+    assert set(prof) == {"aux_build", "hsa_select", "hsa_attn", "hsa_combine"}
+    assert rk.rk_profile_end() == {}
