@@ -26,8 +26,6 @@
 namespace rk {
 namespace {
 
-constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
-
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void hsa_select_kernel(
     const T* __restrict__ q, const T* __restrict__ kmax, const T* __restrict__ kmin,
@@ -41,12 +39,13 @@ __global__ __launch_bounds__(256) void hsa_select_kernel(
   __shared__ __align__(16) uint32_t chan_keys[D];
   __shared__ float qbar[D];
   __shared__ int i1[D];
-  __shared__ __align__(16) float i1_q[D];
-  __shared__ const T* i1_row[D];
+  __shared__ __align__(16) float i1_q[D + 16];
+  __shared__ int i1_off[D];  // element offset of the sign-selected row; < 0: Kmin
   __shared__ TopkSmem<256> sm;
 
   const int u = blockIdx.x;
   const int t = threadIdx.x;
+  RK_PHASE(0);
   if (t < D) {
     float a = 0.f, qb = 0.f;
 #pragma unroll
@@ -61,78 +60,106 @@ __global__ __launch_bounds__(256) void hsa_select_kernel(
   __syncthreads();
   wg_topk_rank<256>(chan_keys, D, k1, [&](int r, int i) { i1[r] = i; }, sm.tmp);
   __syncthreads();
+  RK_PHASE(8);
   const T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
   const T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
   for (int j = t; j < k1; j += 256) {
     const int ch = i1[j];
     const float qv = qbar[ch];
     i1_q[j] = qv;
-    i1_row[j] = (qv >= 0.f ? xu : nu) + size_t(ch) * nblk_cap;  // sign-selected aux row
+    i1_off[j] = qv >= 0.f ? ch : -1 - ch;  // sign selects the Kmax or the Kmin row
     if (chan_opt) chan_opt[size_t(u) * k1 + j] = ch;
   }
   __syncthreads();
 
-  // Pages in chunks of npc (a multiple of 8): stage the k1 rows' slices, then
-  // s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b] from LDS.
+  // Pages in chunks of npc (a multiple of 8).  Staging: thread (channel j,
+  // vector slot) fetches 16-byte runs of row j (EPV consecutive pages) with
+  // all of its loads in flight, and scatters them transposed into LDS as
+  // stage[page][channel] (row pitch k1p, a multiple of EPV plus one vector of
+  // padding).  Scoring: s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b],
+  // read back as 16-byte vectors of channels.
+  const int k1p = (k1 + 15) / 16 * 16 + EPV;  // 16-channel blocks plus one vector of padding
+  const int groups = 256 / k1;  // vector slots per channel (k1 <= 128)
   for (int p0 = 0; p0 < nblk; p0 += npc) {
     const int np = min(npc, nblk - p0);
-    const int nv = (np + EPV - 1) / EPV;  // vectors per staged row (stays inside nblk_cap)
-    const int total = k1 * nv;
-    for (int e0 = t; e0 < total; e0 += 256 * 16) {
-      uint4 buf[16];
+    const int nv = (np + EPV - 1) / EPV;  // vectors per row slice (stays inside nblk_cap)
+    if (t < groups * k1) {
+      const int j = t % k1;
+      const int off = i1_off[j];
+      const T* row = (off >= 0 ? xu + size_t(off) * nblk_cap : nu + size_t(-1 - off) * nblk_cap) + p0;
+      constexpr int NB = 20;
+      for (int v0 = t / k1; v0 < nv; v0 += groups * NB) {
+        Vec16<T> buf[NB];
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int e = e0 + x * 256;
-        if (e < total)
-          buf[x] = *reinterpret_cast<const uint4*>(i1_row[e / nv] + p0 + (e % nv) * EPV);
-      }
+        for (int x = 0; x < NB; ++x) {
+          const int vi = v0 + x * groups;
+          if (vi < nv) buf[x] = load16(row + vi * EPV);
+        }
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int e = e0 + x * 256;
-        if (e < total) *reinterpret_cast<uint4*>(stage + size_t(e / nv) * npc + (e % nv) * EPV) = buf[x];
+        for (int x = 0; x < NB; ++x) {
+          const int vi = v0 + x * groups;
+          if (vi < nv) {
+            const T* src = reinterpret_cast<const T*>(&buf[x].raw);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) stage[size_t(vi * EPV + e) * k1p + j] = src[e];
+          }
+        }
       }
     }
     __syncthreads();
-    // each thread scores up to 4 pages together; 4 channels per step, so a
-    // dozen independent LDS reads are in flight before the ordered adds
-    for (int b0 = t; b0 < np; b0 += 4 * 256) {
-      // one rounded multiply and one rounded add per term: no fused multiply-add
+    RK_PHASE(9);
+    {
+      // Each thread scores up to 4 pages (b = t + 256 p) together.  Channels go
+      // in blocks of 16: the block's q_bar values come from LDS once (float4
+      // broadcasts) and each page's 16 staged values as 16-byte reads, so all
+      // reads of a block are in flight before the ordered multiply-adds.
+      // One rounded multiply and one rounded add per term: no fused multiply-add.
 #pragma clang fp contract(off)
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      int bb[4];
+      const T* sp[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) bb[p] = min(b0 + p * 256, np - 1);
-      int j = 0;
-      for (; j + 4 <= k1; j += 4) {
-        const float4 qv = *reinterpret_cast<const float4*>(i1_q + j);
-        float sv[4][4];
+      for (int p = 0; p < 4; ++p) sp[p] = stage + size_t(min(t + 256 * p, np - 1)) * k1p;
+      const int npp = np > t ? (np - t + 255) / 256 : 0;  // pages of this thread (<= 4 when np <= npc)
+      for (int j0 = 0; j0 < k1; j0 += 16) {
+        float qv[16];
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) sv[p][jj] = to_f32(stage[size_t(j + jj) * npc + bb[p]]);
+        for (int x = 0; x < 4; ++x) {
+          const float4 q4 = *reinterpret_cast<const float4*>(i1_q + j0 + 4 * x);
+          qv[4 * x] = q4.x;
+          qv[4 * x + 1] = q4.y;
+          qv[4 * x + 2] = q4.z;
+          qv[4 * x + 3] = q4.w;
+        }
+        float sv[4][16];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          acc[p] = acc[p] + qv.x * sv[p][0];
-          acc[p] = acc[p] + qv.y * sv[p][1];
-          acc[p] = acc[p] + qv.z * sv[p][2];
-          acc[p] = acc[p] + qv.w * sv[p][3];
-        }
-      }
-      for (; j < k1; ++j) {
-        const float qv = i1_q[j];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) acc[p] = acc[p] + qv * to_f32(stage[size_t(j) * npc + bb[p]]);
+          for (int x = 0; x < 16 / EPV; ++x) {
+            const Vec16<T> vv = load16(sp[p] + j0 + x * EPV);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) sv[p][x * EPV + e] = vv.get(e);
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          if (p < npp) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              if (j0 + e < k1) acc[p] = acc[p] + qv[e] * sv[p][e];
+          }
+        }
       }
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int b = b0 + p * 256;
-        if (b < np) {
+        const int b = t + 256 * p;
+        if (p < npp) {
           page_keys[p0 + b] = order_key(acc[p]);
           if (s1_opt) s1_opt[size_t(u) * nblk + p0 + b] = acc[p];
         }
       }
     }
     __syncthreads();
+    RK_PHASE(10);
   }
   int32_t* su = sel_ws + size_t(u) * nsel;
   int32_t* so = sel_opt ? sel_opt + size_t(u) * nsel : nullptr;
@@ -382,11 +409,14 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   // LDS of the select workgroup: page keys, then the staged aux slices
   const size_t keys_bytes = (size_t((nblk + 3) & ~3) * 4 + 15) / 16 * 16;
   const size_t stage_budget = kSelectLdsBudget - keys_bytes;
-  int npc = int(stage_budget / (size_t(k1) * sizeof(T))) / 8 * 8;
+  constexpr int EPV = 16 / sizeof(T);
+  const int k1p = (k1 + 15) / 16 * 16 + EPV;
+  int npc = int(stage_budget / (size_t(k1p) * sizeof(T))) / 8 * 8;
+  npc = npc > 1024 ? 1024 : npc;  // at most 4 pages per scoring thread
   const int nblk8 = (nblk + 7) / 8 * 8;
   npc = npc > nblk8 ? nblk8 : npc;
   if (npc < 8) return hipErrorInvalidValue;
-  const size_t lds = keys_bytes + size_t(k1) * npc * sizeof(T);
+  const size_t lds = keys_bytes + size_t(k1p) * npc * sizeof(T);
   static bool attr_set = false;  // once per template instantiation
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hsa_select_kernel<T, D, G>),

@@ -7,9 +7,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Phase marker for external timing probes; compiles to nothing in the library.
+#ifndef RK_PHASE
+#define RK_PHASE(slot)
+#endif
+
 namespace rk {
 
 constexpr int kWave = 64;
+constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
 
 // bf16 is carried as raw uint16 bits (the upper half of an IEEE float32).
 struct bf16_t {
@@ -100,6 +106,42 @@ __device__ __forceinline__ int wg_excl_scan(int v, int* tmp, int* total) {
   return res;
 }
 
+// Exclusive prefix sums of a pair (a, b) over the workgroup in one pass.
+template <int NT>
+__device__ __forceinline__ int2 wg_excl_scan2(int a, int b, int* tmp) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  int xa = a, xb = b;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int ta = __shfl_up(xa, off);
+    const int tb = __shfl_up(xb, off);
+    if (lane >= off) {
+      xa += ta;
+      xb += tb;
+    }
+  }
+  if (lane == kWave - 1) {
+    tmp[2 * wave] = xa;
+    tmp[2 * wave + 1] = xb;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ra = 0, rb = 0;
+    for (int w = 0; w < NT / kWave; ++w) {
+      const int ta = tmp[2 * w], tb = tmp[2 * w + 1];
+      tmp[2 * w] = ra;
+      tmp[2 * w + 1] = rb;
+      ra += ta;
+      rb += tb;
+    }
+  }
+  __syncthreads();
+  const int2 res = make_int2(tmp[2 * wave] + xa - a, tmp[2 * wave + 1] + xb - b);
+  __syncthreads();
+  return res;
+}
+
 // Exclusive prefix count of a predicate over the workgroup (ballot based).
 template <int NT>
 __device__ __forceinline__ int wg_excl_count(bool p, int* tmp, int* total) {
@@ -129,7 +171,7 @@ template <int NT>
 struct TopkSmem {
   static constexpr int kBins = 2048;
   uint32_t hist[kBins];
-  int tmp[NT / kWave + 1];
+  int tmp[2 * (NT / kWave) + 2];
   int found[2];
 };
 
@@ -153,17 +195,27 @@ __device__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit, Topk
   constexpr int kBits[3] = {11, 11, 10};
   constexpr int kPer = TopkSmem<NT>::kBins / NT;  // bins owned by one thread
   static_assert(kPer >= 1 && TopkSmem<NT>::kBins % NT == 0, "bins per thread");
+  // Histogram order: lane l of every wave walks the run [l*rows, (l+1)*rows)
+  // (rows odd), so the 64 lanes of one instruction touch keys far apart.
+  // Neighbouring keys are often nearly equal (pooled scores), and a wave whose
+  // lanes all hit one bin would serialise its LDS atomics.
+  const int rows = ((n + kWave - 1) / kWave) | 1;
+  const int lane = lane_id();
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = kShift[pass];
     const uint32_t dmask = (1u << kBits[pass]) - 1u;
     for (int b = t; b < TopkSmem<NT>::kBins; b += NT) sm.hist[b] = 0u;
     __syncthreads();
-    for (int i = t; i < n; i += NT) {
-      const uint32_t kk = key(i);
-      if ((kk & mask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & dmask], 1u);
+    for (int c = t / kWave; c < rows; c += NT / kWave) {
+      const int i = lane * rows + c;
+      if (i < n) {
+        const uint32_t kk = key(i);
+        if ((kk & mask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & dmask], 1u);
+      }
     }
     __syncthreads();
+    RK_PHASE(1 + pass);
     // Thread t owns bins [top - (t+1)*kPer, top - t*kPer): thread 0 the highest.
     const int hi = TopkSmem<NT>::kBins - t * kPer;
     int own = 0;
@@ -187,23 +239,35 @@ __device__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit, Topk
     __syncthreads();
   }
   // prefix == T (the k-th largest key); take `need` of the keys equal to T,
-  // lowest positions first, and every key above T.
+  // lowest positions first, and every key above T.  Thread t owns the
+  // contiguous positions [t*seg, (t+1)*seg): it counts its keys above and
+  // equal to T, one workgroup scan gives the counts before it, then it emits
+  // its selected positions in order.
   const uint32_t T = prefix;
   const int need_eq = need;
-  int base_sel = 0, base_eq = 0;
-  for (int c0 = 0; c0 < n && base_sel < k; c0 += NT) {
-    const int i = c0 + t;
-    const uint32_t kk = i < n ? key(i) : 0u;
-    const bool is_eq = i < n && kk == T;
-    const bool is_gt = i < n && kk > T;
-    int eq_tot, sel_tot;
-    const int eq_before = base_eq + wg_excl_count<NT>(is_eq, sm.tmp, &eq_tot);
-    const bool sel = is_gt || (is_eq && eq_before < need_eq);
-    const int pos = base_sel + wg_excl_count<NT>(sel, sm.tmp, &sel_tot);
-    if (sel) emit(pos, i);
-    base_eq += eq_tot;
-    base_sel += sel_tot;
+  const int seg = ((n + NT - 1) / NT) | 1;  // odd: spreads LDS banks
+  const int lo = min(t * seg, n);
+  const int hi = min(lo + seg, n);
+  int n_gt = 0, n_eq = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t kk = key(i);
+    n_gt += kk > T;
+    n_eq += kk == T;
   }
+  RK_PHASE(4);
+  const int2 before = wg_excl_scan2<NT>(n_gt, n_eq, sm.tmp);
+  int eq_seen = before.y;
+  int pos = before.x + min(before.y, need_eq);
+  for (int i = lo; i < hi; ++i) {
+    const uint32_t kk = key(i);
+    bool sel = kk > T;
+    if (kk == T) {
+      sel = eq_seen < need_eq;
+      ++eq_seen;
+    }
+    if (sel) emit(pos++, i);
+  }
+  RK_PHASE(5);
 }
 
 // Workgroup top-k for a small key set held in LDS (n up to a few thousand):
@@ -227,14 +291,29 @@ __device__ void wg_topk_rank(const uint32_t* keys, int n, int k, const EmitFn& e
     if (j < n) {
       const uint32_t kj = keys[j];
       int rank = 0;
-      for (int i = 0; i < n4; i += 4) {
+      const int n32 = n & ~31;
+      int i = 0;
+      for (; i < n32; i += 32) {  // eight 16-byte LDS reads in flight
+        uint4 kk[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) kk[x] = *reinterpret_cast<const uint4*>(keys + i + 4 * x);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int b = i + 4 * x;
+          rank += int(kk[x].x > kj || (kk[x].x == kj && b < j));
+          rank += int(kk[x].y > kj || (kk[x].y == kj && b + 1 < j));
+          rank += int(kk[x].z > kj || (kk[x].z == kj && b + 2 < j));
+          rank += int(kk[x].w > kj || (kk[x].w == kj && b + 3 < j));
+        }
+      }
+      for (; i < n4; i += 4) {
         const uint4 kk = *reinterpret_cast<const uint4*>(keys + i);
         rank += int(kk.x > kj || (kk.x == kj && i < j));
         rank += int(kk.y > kj || (kk.y == kj && i + 1 < j));
         rank += int(kk.z > kj || (kk.z == kj && i + 2 < j));
         rank += int(kk.w > kj || (kk.w == kj && i + 3 < j));
       }
-      for (int i = n4; i < n; ++i) rank += int(keys[i] > kj || (keys[i] == kj && i < j));
+      for (; i < n; ++i) rank += int(keys[i] > kj || (keys[i] == kj && i < j));
       sel = rank < k;
     }
     int tot;

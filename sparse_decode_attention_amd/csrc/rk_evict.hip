@@ -25,7 +25,6 @@
 namespace rk {
 namespace {
 
-constexpr float kNegBig = -1.0e30f;
 constexpr int TN = kWsTile;  // keys per tile
 constexpr int RC = 32;       // window rows per chunk
 
@@ -216,16 +215,47 @@ __global__ __launch_bounds__(256) void pool_sum_kernel(const float* __restrict__
 }
 
 // Top (n_keep - W) prefix positions by pooled score, ascending, then the window.
+// When the P = S - W keys fit, they are converted to order keys once and held
+// in LDS (dynamic, P words) for all radix passes and the compaction.
 __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ pooled, int S,
-                                                      int W, int n_keep,
+                                                      int W, int n_keep, int staged,
                                                       int32_t* __restrict__ kept) {
+  extern __shared__ uint32_t skeys[];
   __shared__ TopkSmem<1024> sm;
   const int u = blockIdx.x;
   const int P = S - W;
   const float* pu = pooled + size_t(u) * P;
   int32_t* ku = kept + size_t(u) * n_keep;
-  wg_topk<1024>([&](int i) { return order_key(pu[i]); }, P, n_keep - W,
-                [&](int r, int i) { ku[r] = i; }, sm);
+  auto emit = [&](int r, int i) { ku[r] = i; };
+  RK_PHASE(0);
+  if (staged) {
+    // 16-byte loads where the row allows it, all of a thread's loads in flight
+    const bool vec = (reinterpret_cast<uintptr_t>(pu) & 15u) == 0;
+    const int P4 = vec ? P / 4 : 0;
+    for (int i0 = threadIdx.x; i0 < P4; i0 += 1024 * 16) {
+      float4 buf[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int i = i0 + x * 1024;
+        if (i < P4) buf[x] = reinterpret_cast<const float4*>(pu)[i];
+      }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int i = i0 + x * 1024;
+        if (i < P4) {
+          skeys[4 * i] = order_key(buf[x].x);
+          skeys[4 * i + 1] = order_key(buf[x].y);
+          skeys[4 * i + 2] = order_key(buf[x].z);
+          skeys[4 * i + 3] = order_key(buf[x].w);
+        }
+      }
+    }
+    for (int i = 4 * P4 + threadIdx.x; i < P; i += 1024) skeys[i] = order_key(pu[i]);
+    __syncthreads();
+    wg_topk<1024>([&](int i) { return skeys[i]; }, P, n_keep - W, emit, sm);
+  } else {
+    wg_topk<1024>([&](int i) { return order_key(pu[i]); }, P, n_keep - W, emit, sm);
+  }
   for (int r = threadIdx.x; r < W; r += 1024) ku[n_keep - W + r] = P + r;
 }
 
@@ -467,8 +497,17 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
                        size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  RK_LAUNCH("select_tokens", select_kernel, dim3(units), dim3(1024), 0, s, pooled, S, W, int(n_keep),
-                     kept);
+  const int staged = size_t(P) * 4 <= kSelectKeysLds ? 1 : 0;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       int(kSelectKeysLds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  RK_LAUNCH("select_tokens", select_kernel, dim3(units), dim3(1024),
+            staged ? size_t(P) * 4 : size_t(0), s, pooled, S, W, int(n_keep), staged, kept);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (k_out) {
     RK_LAUNCH("gather_kv", (gather_kernel<T, D>), dim3(unsigned((n_keep + 63) / 64), units),

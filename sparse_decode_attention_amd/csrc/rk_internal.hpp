@@ -17,6 +17,9 @@ constexpr int kWsTile = 64;
 // and the most workgroups one unit's attention is split over.
 constexpr int kMinPagesPerSplit = 4;
 constexpr int kMaxSplits = 64;
+// Stage-1 selection keeps the order keys of up to this many bytes in LDS
+// (160 KB per workgroup on gfx950, minus the radix histogram and scan space).
+constexpr size_t kSelectKeysLds = 160 * 1024 - 10 * 1024;
 // LDS budget of the page-selection workgroup (gfx950: 160 KB per workgroup).
 constexpr size_t kSelectLdsBudget = 160 * 1024 - 16 * 1024;
 
