@@ -61,7 +61,7 @@ def ascending(x) -> bool:
 
 
 # --------------------------------------------------------------------------
-def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compact=True):
+def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compact=True, out_cap=None):
     """Run rk_snapkv_evict and check every (or the given) unit against the oracle.
     Returns (kept, k_out, v_out, pooled, swaps)."""
     B, Hq, _, d = qw.shape
@@ -72,7 +72,7 @@ def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compa
     pooled = torch.empty(B, Hkv, S - W, dtype=torch.float32, device=dev)
     ko = vo = None
     if compact:
-        ko = torch.empty(B, Hkv, n_keep, d, dtype=k.dtype, device=dev)
+        ko = torch.empty(B, Hkv, out_cap or n_keep, d, dtype=k.dtype, device=dev)
         vo = torch.empty_like(ko)
     rk.rk_snapkv_evict(qw, k, v, S, W, pool, n_keep, kept, ko, vo, pooled)
     torch.cuda.synchronize()
@@ -95,7 +95,7 @@ def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compa
         swaps += compare_sets(got[: n_keep - W], want[: n_keep - W], pl)
         if compact:
             idx = torch.as_tensor(got, dtype=torch.long, device=dev)
-            assert torch.equal(ko[b, h], k[b, h, idx]) and torch.equal(vo[b, h], v[b, h, idx])
+            assert torch.equal(ko[b, h, :n_keep], k[b, h, idx]) and torch.equal(vo[b, h, :n_keep], v[b, h, idx])
     return kept, ko, vo, pooled, swaps
 
 
@@ -155,3 +155,13 @@ def decode_and_check(rk, q, kc, vc, kmax, kmin, n_tokens, block, k1, k2, cand=No
         want = O.attention(qg, np32(kc[b, h, ridx]), np32(vc[b, h, ridx]))
         check_output(np32(out[b, h * G:(h + 1) * G]), want)
     return out, sel, swaps
+
+
+def check_aux_units(kmax, kmin, kc, n_tokens, block, units, idx=None):
+    """Bit-exact Kmax/Kmin of the given units against the oracle rebuilt from scratch."""
+    nblk = -(-n_tokens // block)
+    for b, h in units:
+        rows = kc[b, h, :n_tokens] if idx is None else kc[b, h, idx[b, h, :n_tokens].long()]
+        wmax, wmin = O.build_aux(rows.cpu().float().numpy(), n_tokens, block)
+        assert np.array_equal(np32(kmax[b, h, :, :nblk]), wmax), (b, h)
+        assert np.array_equal(np32(kmin[b, h, :, :nblk]), wmin), (b, h)

@@ -1,0 +1,184 @@
+"""GPU parity at the full per-layer sizes of the large workloads, in the
+launch configurations the benchmark uses, with the oracle on sampled units
+(and the needle property on every layer and step of the 109K workload)."""
+
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import rk_testutil as U
+from sparse_decode_attention_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def rk():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_decode_attention_amd import rocketkv
+    return rocketkv
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_llama8b_stack_batch32_appends(rk):
+    """Batch 32 x 32K, c = 64: eviction, aux, then 32 steps of append +
+    incremental aux + decode; layers 0 and 31; oracle on batches {0, 31}."""
+    w = WL.WORKLOADS["llama8b-stack-b32-s32k-c64"]
+    s = rk.rk_split(w.c, w.seq, w.window, w.block, w.d)
+    n_keep, k2 = s["n_keep"], s["k2_blocks"]
+    assert (n_keep, k2) == (3192, 32)
+    cap = n_keep + w.decode_steps
+    units = [(b, h) for b in (0, w.batch - 1) for h in range(w.n_kv)]
+    for layer in (0, w.layers - 1):
+        t0 = time.time()
+        say(w.name, "layer", layer)
+        k, v, _ = WL.layer_kv(w, layer, device=DEV)
+        qw = WL.window_queries(w, layer, device=DEV)
+        kept, kc, vc, _, sw = U.evict_and_check(rk, qw, k, v, w.seq, w.window, w.pool, n_keep,
+                                                units_to_check=units, out_cap=cap)
+        del k, v
+        _free()
+        kmax = torch.empty(w.batch, w.n_kv, w.d, rk.aux_capacity(cap, w.block), dtype=kc.dtype, device=DEV)
+        kmin = torch.empty_like(kmax)
+        rk.rk_hsa_build_aux(kc, n_keep, 0, w.block, kmax, kmin, n_q_heads=w.n_q)
+        U.check_aux_units(kmax, kmin, kc, n_keep, w.block, units)
+        swaps = 0
+        for step in range(w.decode_steps):
+            n = n_keep + step
+            ka, va = WL.append_kv(w, layer, step, device=DEV)
+            kc[:, :, n] = ka
+            vc[:, :, n] = va
+            rk.rk_hsa_build_aux(kc, n + 1, n, w.block, kmax, kmin, n_q_heads=w.n_q)
+            q = WL.decode_query(w, layer, step, device=DEV)
+            if step in (0, 1, w.decode_steps - 1) or step % 8 == 0:
+                U.check_aux_units(kmax, kmin, kc, n + 1, w.block, units)
+            _, _, sw2 = U.decode_and_check(rk, q, kc, vc, kmax, kmin, n + 1, w.block, w.k1, k2,
+                                           units_to_check=units)
+            swaps += sw2
+        say("layer", layer, "evict swaps", sw, "decode swaps", swaps, f"{time.time() - t0:.1f}s")
+        del kc, vc, kmax, kmin, kept
+        _free()
+
+
+def test_needle_109k_every_layer_and_step(rk):
+    """109K prompt, budget 256 (c = 428): the planted key survives stage 1 and
+    its page is chosen at every decode step of every layer and KV head; the
+    oracle checks layers 0 and 31."""
+    w = WL.WORKLOADS["needle-s109k-c428"]
+    s = rk.rk_split(w.c, w.seq, w.window, w.block, w.d)
+    n_keep, k2 = s["n_keep"], s["k2_blocks"]
+    assert (n_keep, k2) == (1360, 16)
+    units = [(0, h) for h in range(w.n_kv)]
+    shape = rk.shape_of(1, w.n_q, w.n_kv, w.d, w.torch_dtype)
+    ws_e = torch.empty(rk.rk_snapkv_workspace_bytes(shape, w.seq, w.window), dtype=torch.uint8, device=DEV)
+    ws_d = torch.empty(rk.rk_hsa_workspace_bytes(shape, n_keep, w.block, w.k1, k2), dtype=torch.uint8, device=DEV)
+    nblk = -(-n_keep // w.block)
+    t0 = time.time()
+    for layer in range(w.layers):
+        check = layer in (0, w.layers - 1)
+        k, v, pos = WL.layer_kv(w, layer, device=DEV)
+        qw = WL.window_queries(w, layer, device=DEV)
+        if check:
+            say(w.name, "layer", layer, "with oracle")
+            kept, kc, vc, _, _ = U.evict_and_check(rk, qw, k, v, w.seq, w.window, w.pool, n_keep)
+        else:
+            kept = torch.empty(1, w.n_kv, n_keep, dtype=torch.int32, device=DEV)
+            kc = torch.empty(1, w.n_kv, n_keep, w.d, dtype=k.dtype, device=DEV)
+            vc = torch.empty_like(kc)
+            rk.rk_snapkv_evict(qw, k, v, w.seq, w.window, w.pool, n_keep, kept, kc, vc, None, ws=ws_e)
+        kmax = torch.empty(1, w.n_kv, w.d, rk.aux_capacity(n_keep, w.block), dtype=k.dtype, device=DEV)
+        kmin = torch.empty_like(kmax)
+        rk.rk_hsa_build_aux(kc, n_keep, 0, w.block, kmax, kmin, n_q_heads=w.n_q)
+        if check:
+            U.check_aux_units(kmax, kmin, kc, n_keep, w.block, units)
+        kept_h = kept.cpu().numpy()
+        pos_h = pos.cpu().numpy()
+        page = np.zeros(w.n_kv, np.int64)
+        for h in range(w.n_kv):
+            hit = np.nonzero(kept_h[0, h] == pos_h[0, h, 0])[0]
+            assert hit.size == 1, f"layer {layer} head {h}: needle {pos_h[0, h, 0]} evicted"
+            page[h] = hit[0] // w.block
+        sels = torch.empty(w.decode_steps, 1, w.n_kv, min(k2, nblk), dtype=torch.int32, device=DEV)
+        out = torch.empty(1, w.n_q, w.d, device=DEV)
+        for step in range(w.decode_steps):
+            q = WL.decode_query(w, layer, step, device=DEV)
+            if check and step in (0, w.decode_steps - 1):
+                _, sel, _ = U.decode_and_check(rk, q, kc, vc, kmax, kmin, n_keep, w.block, w.k1, k2)
+                sels[step] = sel
+            else:
+                rk.rk_hsa_decode(q, kc, vc, kmax, kmin, n_keep, w.block, w.k1, k2, out, sels[step], ws=ws_d)
+        sel_h = sels.cpu().numpy()
+        for h in range(w.n_kv):
+            missing = [st for st in range(w.decode_steps) if page[h] not in sel_h[st, 0, h]]
+            assert not missing, f"layer {layer} head {h}: needle page not chosen at steps {missing[:5]}"
+        del k, v, kc, vc, kmax, kmin
+        _free()
+    say("needle found in every layer/head/step", f"{time.time() - t0:.1f}s")
+
+
+def test_mt_mha_batch8_turns(rk):
+    """RocketKV-MT, MHA, batch 8 x 32 heads: 4 turns, each appending 1024
+    tokens to the resident full cache, re-running stage 1 over the whole cache
+    (indices only), building aux over the candidates and decoding 64 steps;
+    layers 0 and 31; oracle on batches {0, 7}, all heads."""
+    w = WL.WORKLOADS["mt-mha-b8-s32k-c32"]
+    cap = w.seq + w.mt_turns * w.mt_append
+    units = [(b, h) for b in (0, w.batch - 1) for h in range(w.n_kv)]
+    for layer in (0, w.layers - 1):
+        t0 = time.time()
+        kf = torch.zeros(w.batch, w.n_kv, cap, w.d, dtype=w.torch_dtype, device=DEV)
+        vf = torch.zeros_like(kf)
+        k0, v0, _ = WL.layer_kv(w, layer, device=DEV)
+        kf[:, :, :w.seq] = k0
+        vf[:, :, :w.seq] = v0
+        del k0, v0
+        _free()
+        S = w.seq
+        for turn in range(w.mt_turns):
+            kt, vt = WL.turn_kv(w, layer, turn, device=DEV)
+            kf[:, :, S:S + w.mt_append] = kt
+            vf[:, :, S:S + w.mt_append] = vt
+            S += w.mt_append
+            s = rk.rk_split(w.c, S, w.window, w.block, w.d)
+            n_keep, k2 = s["n_keep"], s["k2_blocks"]
+            say(w.name, "layer", layer, "turn", turn, "S", S, "n_keep", n_keep, "k2", k2)
+            qw = WL.window_queries(w, layer, device=DEV, turn=turn)
+            oracle_units = units if turn in (0, w.mt_turns - 1) else units[::5]
+            kept, _, _, _, sw = U.evict_and_check(rk, qw, kf, vf, S, w.window, w.pool, n_keep,
+                                                  units_to_check=oracle_units, compact=False)
+            kmax = torch.empty(w.batch, w.n_kv, w.d, rk.aux_capacity(n_keep, w.block), dtype=kf.dtype, device=DEV)
+            kmin = torch.empty_like(kmax)
+            rk.rk_hsa_build_aux(kf, n_keep, 0, w.block, kmax, kmin, n_q_heads=w.n_q, idx=kept)
+            U.check_aux_units(kmax, kmin, kf, n_keep, w.block, oracle_units, idx=kept)
+            shape = rk.shape_of(w.batch, w.n_q, w.n_kv, w.d, kf.dtype)
+            ws_d = torch.empty(rk.rk_hsa_workspace_bytes(shape, n_keep, w.block, w.k1, k2),
+                               dtype=torch.uint8, device=DEV)
+            out = torch.empty(w.batch, w.n_q, w.d, device=DEV)
+            swaps = 0
+            for step in range(w.decode_steps):
+                q = WL.decode_query(w, layer, turn * w.decode_steps + step, device=DEV)
+                if step in (0, w.decode_steps - 1):
+                    _, _, sw2 = U.decode_and_check(rk, q, kf, vf, kmax, kmin, n_keep, w.block, w.k1, k2,
+                                                   cand=kept, units_to_check=oracle_units)
+                    swaps += sw2
+                else:
+                    rk.rk_hsa_decode_mt(q, kf, vf, kept, n_keep, kmax, kmin, w.block, w.k1, k2, out, ws=ws_d)
+            torch.cuda.synchronize()
+            say("turn", turn, "evict swaps", sw, "decode swaps", swaps)
+        say("layer", layer, f"{time.time() - t0:.1f}s")
+        del kf, vf
+        _free()
