@@ -1,22 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the RocketKV hot path on one MI355X.
 
-A step is one pass of the whole hot path over one batch of synthetic input of
-the Llama-3.1-8B-shaped single-layer workload (batch 1, 32K prompt, 32 query /
-8 KV heads, d 128, bf16, c = 16): the adaptive split, SnapKV eviction of the
-layer (window scoring, pooling, top-k, compaction), the Kmax/Kmin build and
-the 64 HSA decode steps of the workload.  Inputs are resident in HBM before
-timing; steps rotate over several prompt replicas so the eviction does not
-re-read a cache-resident K.  Each step is replayed from two HIP graphs (evict +
-aux, then the 64 decode calls) with HIP events between them.
+Default workload: the Llama-3.1-8B-shaped single layer (batch 1, 32K prompt,
+32 query / 8 KV heads, d 128, bf16, c = 16).  A step is one pass of the whole
+hot path over one batch of synthetic input: the adaptive split, SnapKV
+eviction of the layer (window scoring, pooling, top-k, compaction), the
+Kmax/Kmin build and the workload's HSA decode steps.  `--workload` runs one
+layer of another workload instead (the batch-32 stack: append + decode per
+step; the 109K needle; the last RocketKV-MT turn: index-only eviction of the
+resident full cache, aux over the candidates, MT decode).
 
-Reported: `value` = HSA decode time per decode step (us), `ms_per_step` = one
-whole pass, plus SnapKV eviction ms/layer, decode HBM GB/s and the roofline of
-the dominant kernel (per-kernel durations from the library's own HIP-event
-timing over an eager pass of the same steps), and the CPU oracle timed on a
-bounded sample on the host.
+Inputs are resident in HBM before timing; steps rotate over enough prompt
+replicas that eviction does not re-read a cache-resident K.  Each step is
+replayed from two HIP graphs (eviction + aux, then the decode calls) with HIP
+events between them.  Reported: `value` = HSA decode time per decode step
+(us), `ms_per_step` = one whole pass, SnapKV eviction ms/layer, decode HBM
+GB/s, the roofline of the dominant kernel (per-kernel durations from the
+library's HIP-event timing over an eager pass of the same steps) and the CPU
+oracle timed on a bounded sample on the host.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 
 from __future__ import annotations
@@ -24,7 +27,6 @@ from __future__ import annotations
 import argparse
 import json
 import math
-import os
 import sys
 import time
 
@@ -37,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b-layer-s32k-c16")
-    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--replicas", type=int, default=0, help="prompt replicas (0: enough to exceed 512 MB)")
     ap.add_argument("--no-graph", action="store_true", help="issue every call eagerly instead of graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -46,6 +48,108 @@ def parse():
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Path:
+    """Buffers and calls of one layer of a workload (one replica per prompt)."""
+
+    def __init__(self, rk, WL, w, dev, replicas):
+        import torch
+
+        self.rk, self.w = rk, w
+        self.mt = w.mt_turns > 0
+        self.S = w.seq + (w.mt_turns * w.mt_append if self.mt else 0)   # MT: the last turn
+        sp = rk.rk_split(w.c, self.S, w.window, w.block, w.d)
+        self.n_keep, self.k2 = sp["n_keep"], sp["k2_blocks"]
+        self.steps = w.decode_steps
+        B, Hq, Hkv, d = w.batch, w.n_q, w.n_kv, w.d
+        cap_c = self.n_keep + (self.steps if w.appends else 0)
+        self.nblk = -(-cap_c // w.block)
+        esize = 2 if w.dtype == "bf16" else 4
+        kv_bytes = 2 * B * Hkv * self.S * d * esize
+        R = replicas or max(1, min(4, math.ceil(512e6 / kv_bytes)))
+        self.R = R
+        self.reps = []
+        for r in range(R):
+            if self.mt:
+                k = torch.empty(B, Hkv, self.S, d, dtype=w.torch_dtype, device=dev)
+                v = torch.empty_like(k)
+                k0, v0, _ = WL.layer_kv(w, r, device=dev)
+                k[:, :, :w.seq], v[:, :, :w.seq] = k0, v0
+                del k0, v0
+                s0 = w.seq
+                for t in range(w.mt_turns):
+                    kt, vt = WL.turn_kv(w, r, t, device=dev)
+                    k[:, :, s0:s0 + w.mt_append], v[:, :, s0:s0 + w.mt_append] = kt, vt
+                    s0 += w.mt_append
+                qw = WL.window_queries(w, r, device=dev, turn=w.mt_turns - 1)
+                qs = torch.stack([WL.decode_query(w, r, (w.mt_turns - 1) * self.steps + s, device=dev)
+                                  for s in range(self.steps)])
+            else:
+                k, v, _ = WL.layer_kv(w, r, device=dev)
+                qw = WL.window_queries(w, r, device=dev)
+                qs = torch.stack([WL.decode_query(w, r, s, device=dev) for s in range(self.steps)])
+            app = None
+            if w.appends:
+                app = [WL.append_kv(w, r, s, device=dev) for s in range(self.steps)]
+            self.reps.append((k, v, qw, qs, app))
+        self.kept = torch.empty(B, Hkv, self.n_keep, dtype=torch.int32, device=dev)
+        self.kc = self.vc = None
+        if not self.mt:
+            self.kc = torch.empty(B, Hkv, cap_c, d, dtype=w.torch_dtype, device=dev)
+            self.vc = torch.empty_like(self.kc)
+        self.kmax = torch.empty(B, Hkv, d, rk.aux_capacity(cap_c, w.block), dtype=w.torch_dtype, device=dev)
+        self.kmin = torch.empty_like(self.kmax)
+        self.out = torch.empty(self.steps, B, Hq, d, dtype=torch.float32, device=dev)
+        shape = rk.shape_of(B, Hq, Hkv, d, w.torch_dtype)
+        self.ws_e = torch.empty(rk.rk_snapkv_workspace_bytes(shape, self.S, w.window), dtype=torch.uint8, device=dev)
+        self.ws_d = torch.empty(rk.rk_hsa_workspace_bytes(shape, cap_c, w.block, w.k1, self.k2),
+                                dtype=torch.uint8, device=dev)
+        # algorithmic bytes per launch (what the method must move)
+        units = B * Hkv
+        nb0 = -(-self.n_keep // w.block)
+        nsel = min(self.k2, self.nblk)
+        G = w.group
+        self.alg = {
+            "hsa_attn": units * nsel * w.block * 2 * d * esize + B * Hq * d * esize,
+            "hsa_attn_mt": units * nsel * w.block * (2 * d * esize + 4) + B * Hq * d * esize,
+            "hsa_select": units * w.k1 * nb0 * esize + B * Hq * d * esize,
+            "aux_build": units * self.n_keep * d * esize + 2 * units * d * nb0 * esize,
+            "gather_kv": 2 * 2 * units * self.n_keep * d * esize,
+            "ws_pass1": units * self.S * d * esize + B * Hq * w.window * d * esize,
+            "ws_pass2": units * (self.S - w.window) * d * esize + B * Hq * w.window * d * esize,
+            "append_kv": units * d * esize * 5,
+        }
+        self.flops_ws = 2.0 * units * G * w.window * self.S * d
+        self.dec_bytes = self.alg["hsa_attn_mt" if self.mt else "hsa_attn"] + self.alg["hsa_select"]
+
+    def evict_part(self, r):
+        rk, w = self.rk, self.w
+        k, v, qw = self.reps[r][:3]
+        if self.mt:
+            rk.rk_snapkv_evict(qw, k, v, self.S, w.window, w.pool, self.n_keep, self.kept, None, None, None,
+                               ws=self.ws_e)
+            rk.rk_hsa_build_aux(k, self.n_keep, 0, w.block, self.kmax, self.kmin, n_q_heads=w.n_q, idx=self.kept)
+        else:
+            rk.rk_snapkv_evict(qw, k, v, self.S, w.window, w.pool, self.n_keep, self.kept, self.kc, self.vc,
+                               None, ws=self.ws_e)
+            rk.rk_hsa_build_aux(self.kc, self.n_keep, 0, w.block, self.kmax, self.kmin, n_q_heads=w.n_q)
+
+    def decode_part(self, r):
+        rk, w = self.rk, self.w
+        k, v, _, qs, app = self.reps[r]
+        for s in range(self.steps):
+            if self.mt:
+                rk.rk_hsa_decode_mt(qs[s], k, v, self.kept, self.n_keep, self.kmax, self.kmin, w.block, w.k1,
+                                    self.k2, self.out[s], ws=self.ws_d)
+            else:
+                n = self.n_keep
+                if app is not None:
+                    rk.rk_append_kv(app[s][0], app[s][1], self.kc, self.vc, n + s, self.kmax, self.kmin, w.block,
+                                    n_q_heads=w.n_q)
+                    n = n + s + 1
+                rk.rk_hsa_decode(qs[s], self.kc, self.vc, self.kmax, self.kmin, n, w.block, w.k1, self.k2,
+                                 self.out[s], ws=self.ws_d)
 
 
 def main():
@@ -64,49 +168,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = WL.WORKLOADS[args.workload]
-    assert w.layers == 1 and w.mt_turns == 0, "bench runs a single-layer RocketKV workload"
-    sp = rk.rk_split(w.c, w.seq, w.window, w.block, w.d)
-    S, W, B, Hq, Hkv, d = w.seq, w.window, w.batch, w.n_q, w.n_kv, w.d
-    n_keep, k2, blk, k1 = sp["n_keep"], sp["k2_blocks"], w.block, w.k1
-    nblk = -(-n_keep // blk)
-    nsel = min(k2, nblk)
-    R = max(1, args.replicas)
-    steps_dec = w.decode_steps
-    esize = 2 if w.dtype == "bf16" else 4
-    log(f"workload {w.name}: S={S} n_keep={n_keep} pages={nblk} k1={k1} k2={k2} replicas={R}")
-
-    # ---- inputs, resident in HBM ----
-    reps = []
-    for r in range(R):
-        k, v, _ = WL.layer_kv(w, r, device=dev)
-        qw = WL.window_queries(w, r, device=dev)
-        qs = torch.stack([WL.decode_query(w, r, s, device=dev) for s in range(steps_dec)])
-        reps.append((k, v, qw, qs))
-    kept = torch.empty(B, Hkv, n_keep, dtype=torch.int32, device=dev)
-    kc = torch.empty(B, Hkv, n_keep, d, dtype=w.torch_dtype, device=dev)
-    vc = torch.empty_like(kc)
-    kmax = torch.empty(B, Hkv, d, rk.aux_capacity(n_keep, blk), dtype=w.torch_dtype, device=dev)
-    kmin = torch.empty_like(kmax)
-    out = torch.empty(steps_dec, B, Hq, d, dtype=torch.float32, device=dev)
-    shape = rk.shape_of(B, Hq, Hkv, d, w.torch_dtype)
-    ws_e = torch.empty(rk.rk_snapkv_workspace_bytes(shape, S, W), dtype=torch.uint8, device=dev)
-    ws_d = torch.empty(rk.rk_hsa_workspace_bytes(shape, n_keep, blk, k1, k2), dtype=torch.uint8, device=dev)
+    p = Path(rk, WL, w, dev, args.replicas)
+    R = p.R
+    log(f"workload {w.name} (one layer): S={p.S} n_keep={p.n_keep} k1={w.k1} k2={p.k2} "
+        f"decode steps={p.steps} replicas={R}")
     torch.cuda.synchronize()
 
-    def evict_part(r):
-        k, v, qw, _ = reps[r]
-        rk.rk_snapkv_evict(qw, k, v, S, W, w.pool, n_keep, kept, kc, vc, None, ws=ws_e)
-        rk.rk_hsa_build_aux(kc, n_keep, 0, blk, kmax, kmin, n_q_heads=Hq)
-
-    def decode_part(r):
-        qs = reps[r][3]
-        for s in range(steps_dec):
-            rk.rk_hsa_decode(qs[s], kc, vc, kmax, kmin, n_keep, blk, k1, k2, out[s], ws=ws_d)
-
-    # eager warm-up (also before capture)
-    for i in range(max(1, args.warmup)):
-        evict_part(i % R)
-        decode_part(i % R)
+    for i in range(max(1, args.warmup)):           # eager warm-up (also before capture)
+        p.evict_part(i % R)
+        p.decode_part(i % R)
     torch.cuda.synchronize()
 
     use_graph = not args.no_graph
@@ -118,9 +188,9 @@ def main():
             for r in range(R):
                 ge, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
                 with torch.cuda.graph(ge, stream=stream):
-                    evict_part(r)
+                    p.evict_part(r)
                 with torch.cuda.graph(gd, stream=stream):
-                    decode_part(r)
+                    p.decode_part(r)
                 graphs.append((ge, gd))
         torch.cuda.current_stream().wait_stream(stream)
         torch.cuda.synchronize()
@@ -128,15 +198,9 @@ def main():
     def run_step(i, ev):
         r = i % R
         ev[0].record()
-        if use_graph:
-            graphs[r][0].replay()
-        else:
-            evict_part(r)
+        graphs[r][0].replay() if use_graph else p.evict_part(r)
         ev[1].record()
-        if use_graph:
-            graphs[r][1].replay()
-        else:
-            decode_part(r)
+        graphs[r][1].replay() if use_graph else p.decode_part(r)
         ev[2].record()
 
     for i in range(args.warmup):
@@ -152,49 +216,38 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    evict_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    evict_ms_layer = sum(evict_ms) / len(evict_ms)
-    dec_us_step = sum(dec_ms) / len(dec_ms) * 1e3 / steps_dec
-    log(f"wall {ms_per_step:.3f} ms/step; evict+aux {evict_ms_layer:.3f} ms/layer; "
-        f"decode {dec_us_step:.2f} us/step")
+    evict_ms_layer = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_us_step = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e3 / p.steps
+    log(f"wall {ms_per_step:.3f} ms/step; evict+aux {evict_ms_layer:.3f} ms/layer; decode {dec_us_step:.2f} us/step")
 
     # ---- per-kernel durations: library HIP-event timing over an eager pass ----
     rk.rk_profile_begin()
     for i in range(args.steps):
-        evict_part(i % R)
-        decode_part(i % R)
+        p.evict_part(i % R)
+        p.decode_part(i % R)
     prof = rk.rk_profile_end()
     torch.cuda.synchronize()
     per_step = {n: (c / args.steps, t / args.steps, t / c) for n, (c, t) in prof.items()}
     for n, (cps, tps, avg) in per_step.items():
         log(f"kernel {n:14s} {cps:6.1f} launches/step {tps:8.4f} ms/step avg {avg * 1e3:8.2f} us")
 
-    # algorithmic bytes per launch (what the method must move)
-    units = B * Hkv
-    alg = {
-        "hsa_attn": units * nsel * blk * 2 * d * esize + B * Hq * d * (esize + 4),
-        "hsa_select": units * k1 * nblk * esize + B * Hq * d * esize,
-        "aux_build": units * n_keep * d * esize + 2 * units * d * nblk * esize,
-        "gather_kv": 2 * 2 * units * n_keep * d * esize,
-        "ws_pass1": units * S * d * esize + B * Hq * W * d * esize,
-        "ws_pass2": units * (S - W) * d * esize + B * Hq * W * d * esize,
-    }
     dominant = max(per_step, key=lambda n: per_step[n][1])
     avg_ms = per_step[dominant][2]
     roof = None
-    if dominant in alg:
-        achieved = alg[dominant] / (avg_ms * 1e-3) / 1e9
+    if dominant in p.alg:
+        achieved = p.alg[dominant] / (avg_ms * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "bytes_per_launch": alg[dominant], "avg_launch_us": round(avg_ms * 1e3, 3)}
-    attn_avg = per_step.get("hsa_attn", (0, 0, float("nan")))[2]
-    dec_bytes = alg["hsa_attn"] + alg["hsa_select"]
-    dec_gbps = dec_bytes / (dec_us_step * 1e-6) / 1e9
+                "bytes_per_launch": p.alg[dominant], "avg_launch_us": round(avg_ms * 1e3, 3)}
+    attn_name = "hsa_attn_mt" if p.mt else "hsa_attn"
+    attn_avg = per_step.get(attn_name, (0, 0, float("nan")))[2]
+    attn_gbps = p.alg[attn_name] / (attn_avg * 1e-3) / 1e9 if attn_avg == attn_avg else None
+    ws1 = per_step.get("ws_pass1", (0, 0, float("nan")))[2]
+    dec_gbps = p.dec_bytes / (dec_us_step * 1e-6) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, reps[0], n_keep, k1, k2, args.cpu_seconds)
+        cpu = cpu_baseline(w, p, args.cpu_seconds)
 
     line = {
         "metric": "HSA decode us/step + HBM GB/s (% peak); SnapKV evict ms/layer",
@@ -207,16 +260,18 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "seq_len": S, "n_q_heads": Hq, "n_kv_heads": Hkv,
-                   "head_dim": d, "kv_dtype": w.dtype, "compression": w.c, "n_keep": n_keep,
-                   "k1": k1, "k2_pages": k2, "page": blk, "decode_steps": steps_dec,
-                   "replicas": R, "graph_replay": use_graph},
+        "config": {"workload": w.name, "layers_timed": 1, "batch": w.batch, "seq_len": p.S, "n_q_heads": w.n_q,
+                   "n_kv_heads": w.n_kv, "head_dim": w.d, "kv_dtype": w.dtype, "compression": round(w.c, 3),
+                   "n_keep": p.n_keep, "k1": w.k1, "k2_pages": p.k2, "page": w.block, "decode_steps": p.steps,
+                   "appends": w.appends, "rocketkv_mt": p.mt, "replicas": R, "graph_replay": use_graph},
         "snapkv_evict_ms_per_layer": round(evict_ms_layer, 4),
         "hsa_decode_GBps": round(dec_gbps, 1),
         "hsa_decode_hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "hsa_attn_avg_us": round(attn_avg * 1e3, 3),
+        "hsa_attn_GBps": round(attn_gbps, 1) if attn_gbps else None,
+        "window_scoring_TFLOPs": round(p.flops_ws / (ws1 * 1e-3) / 1e12, 2) if ws1 == ws1 else None,
         "kernels_ms_per_step": {n: round(v[1], 5) for n, v in per_step.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -224,10 +279,8 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, rep, n_keep, k1, k2, budget_s):
+def cpu_baseline(w, p, budget_s):
     """The oracle, as it stands, on a bounded sample of the same workload."""
-    import numpy as np
-
     import oracle as O
 
     try:
@@ -235,46 +288,41 @@ def cpu_baseline(w, rep, n_keep, k1, k2, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = 1
-    k, v, qw, qs = rep
+    k, v, qw, qs, _ = p.reps[0]
     G = w.group
-    # stage 1 on one unit, extrapolated to the layer
+    S, W = p.S, w.window
+    units_all = [(b, h) for b in range(w.batch) for h in range(w.n_kv)]
+
+    def stage1(b, h):
+        kn = k[b, h, :S].float().cpu().numpy()
+        vn = v[b, h, :S].float().cpu().numpy()
+        pl = O.pool_sum(O.window_scores(qw[b, h * G:(h + 1) * G].float().cpu().numpy(), kn), w.pool)
+        kept = O.snapkv_select(pl, S, W, p.n_keep)
+        kc, vc = kn[kept], vn[kept]
+        kmax, kmin = O.build_aux(kc, p.n_keep, w.block)
+        return kc, vc, kmax, kmin
+
     t0 = time.perf_counter()
-    kn = k[0, 0].float().cpu().numpy()
-    vn = v[0, 0].float().cpu().numpy()
-    qn = qw[0, :G].float().cpu().numpy()
-    sc = O.window_scores(qn, kn)
-    pl = O.pool_sum(sc, w.pool)
-    kept = O.snapkv_select(pl, w.seq, w.window, n_keep)
-    kc, vc = kn[kept], vn[kept]
-    kmax, kmin = O.build_aux(kc, n_keep, w.block)
+    caches = {units_all[0]: stage1(*units_all[0])}
     evict_unit_ms = (time.perf_counter() - t0) * 1e3
-    # decode: all units of the batch, as many steps as the budget allows
-    units = [(0, h) for h in range(w.n_kv)]
-    caches = {}
-    for b, h in units:
-        if (b, h) == (0, 0):
-            caches[(b, h)] = (kc, vc, kmax, kmin)
-            continue
-        kk = k[b, h].float().cpu().numpy()
-        vv = v[b, h].float().cpu().numpy()
-        pl2 = O.pool_sum(O.window_scores(qw[b, h * G:(h + 1) * G].float().cpu().numpy(), kk), w.pool)
-        kp = O.snapkv_select(pl2, w.seq, w.window, n_keep)
-        ka, kb = O.build_aux(kk[kp], n_keep, w.block)
-        caches[(b, h)] = (kk[kp], vv[kp], ka, kb)
-    qn_all = qs.float().cpu().numpy()
+    # decode over the units of batch 0 (all of them for single-sequence workloads)
+    units = [u for u in units_all if u[0] == 0]
+    for u in units[1:]:
+        caches[u] = stage1(*u)
+    qn = qs.float().cpu().numpy()
     t0 = time.perf_counter()
     done = 0
-    while done < qn_all.shape[0] and time.perf_counter() - t0 < budget_s:
+    while done < p.steps and time.perf_counter() - t0 < budget_s:
         for b, h in units:
             c = caches[(b, h)]
-            O.hsa_unit(qn_all[done, b, h * G:(h + 1) * G], c[0], c[1], c[2], c[3], n_keep, w.block, k1, k2)
+            O.hsa_unit(qn[done, b, h * G:(h + 1) * G], c[0], c[1], c[2], c[3], p.n_keep, w.block, w.k1, p.k2)
         done += 1
-    dec_us = (time.perf_counter() - t0) * 1e6 / max(done, 1)
-    return {"value": round(dec_us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
-            "sample": f"HSA decode of all {len(units)} units for {done} of {w.decode_steps} steps "
-                      f"(aux built once); stage 1 of one unit {evict_unit_ms:.0f} ms, "
-                      f"x{w.batch * w.n_kv} units = {evict_unit_ms * w.batch * w.n_kv:.0f} ms/layer (extrapolated)",
-            "evict_ms_per_layer_extrapolated": round(evict_unit_ms * w.batch * w.n_kv, 1)}
+    per_step_us = (time.perf_counter() - t0) * 1e6 / max(done, 1) * (len(units_all) / len(units))
+    return {"value": round(per_step_us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"HSA decode of {len(units)} of {len(units_all)} units for {done} of {p.steps} steps, "
+                      f"scaled to all units (aux built once); stage 1 of one unit {evict_unit_ms:.0f} ms, "
+                      f"x{len(units_all)} units = {evict_unit_ms * len(units_all):.0f} ms/layer (extrapolated)",
+            "evict_ms_per_layer_extrapolated": round(evict_unit_ms * len(units_all), 1)}
 
 
 if __name__ == "__main__":

@@ -152,6 +152,24 @@ rk_status rk_hsa_build_aux(const rk_shape* shape, const void* k, int64_t k_cap,
                            int64_t nblk_cap, rk_stream stream);
 
 /*
+ * rk_append_kv -- append one decode token per unit and refresh its page.
+ * [RKV] method details, HSA step 1: the auxiliary max/min data is updated
+ * whenever a new key is generated.
+ *
+ *   k_new, v_new [B, Hkv, d]         the new key / value rows
+ *   k, v     [B, Hkv, kv_cap, d]     compact cache; row `pos` is written
+ *   kmax, kmin [B, Hkv, d, nblk_cap] page pos/block becomes the element-wise
+ *                                    max / min of its old value and k_new, or
+ *                                    k_new itself when pos starts the page
+ * Pages before pos/block are untouched.  If the aux data was valid for tokens
+ * [0, pos), it equals rk_hsa_build_aux over [0, pos] bit for bit afterwards.
+ * Requires 0 <= pos < kv_cap, pos/block < nblk_cap (a multiple of 8).
+ */
+rk_status rk_append_kv(const rk_shape* shape, const void* k_new, const void* v_new, void* k,
+                       void* v, int64_t kv_cap, int64_t pos, void* kmax, void* kmin,
+                       int64_t nblk_cap, int32_t block, rk_stream stream);
+
+/*
  * rk_hsa_workspace_bytes -- workspace needed by rk_hsa_decode / _mt for this
  * shape, token count, page size and k1/k2 (0 if the arguments are invalid).
  */

@@ -215,6 +215,22 @@ rk_status rk_hsa_build_aux(const rk_shape* shape, const void* k, int64_t k_cap,
                        "rk_hsa_build_aux launch");
 }
 
+rk_status rk_append_kv(const rk_shape* shape, const void* k_new, const void* v_new, void* k,
+                       void* v, int64_t kv_cap, int64_t pos, void* kmax, void* kmin,
+                       int64_t nblk_cap, int32_t block, rk_stream stream) {
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  if (!k_new || !v_new || !k || !v || !kmax || !kmin) return fail(RK_EINVAL, "null tensor argument");
+  if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
+  if (pos < 0 || pos >= kv_cap) return fail(RK_EINVAL, "pos outside [0, kv_cap)");
+  if (pos / block >= nblk_cap) return fail(RK_EINVAL, "page of pos beyond nblk_cap");
+  if (nblk_cap % 8) return fail(RK_EINVAL, "nblk_cap must be a multiple of 8");
+  return device_status(rk::launch_append_kv(d, k_new, v_new, k, v, kv_cap, pos, kmax, kmin,
+                                            nblk_cap, block, static_cast<hipStream_t>(stream)),
+                       "rk_append_kv launch");
+}
+
 size_t rk_hsa_workspace_bytes(const rk_shape* shape, int64_t n_tokens, int32_t block, int32_t k1,
                               int32_t k2) {
   rk::Dims d;

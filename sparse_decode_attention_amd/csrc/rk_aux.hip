@@ -4,7 +4,8 @@
 // via Two-Stage KV Cache Compression", method details, HSA step 1 (pages of
 // consecutive keys, element-wise max/min kept as auxiliary data laid out
 // along the head dimension, refreshed as new keys arrive) and RocketKV-MT
-// (pages over the stage-1 candidate list of the full cache).
+// (pages over the stage-1 candidate list of the full cache).  Also the
+// decode-time append: one new row per unit folded into its page.
 //
 // One workgroup covers kPagesPerWg consecutive pages of one unit.  Each thread
 // owns one 16-byte channel chunk of one page: it streams the page's rows
@@ -100,7 +101,62 @@ hipError_t launch_aux_t(const Dims& d, const void* k, int64_t k_cap, const int32
   return hipGetLastError();
 }
 
+// One thread per (unit, channel): write the new K/V element at row pos and
+// fold it into the page's max/min (a fresh page takes the value itself).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void append_kv_kernel(const T* __restrict__ k_new,
+                                                        const T* __restrict__ v_new,
+                                                        T* __restrict__ k, T* __restrict__ v,
+                                                        int64_t kv_cap, int64_t pos, int units,
+                                                        T* __restrict__ kmax, T* __restrict__ kmin,
+                                                        int64_t nblk_cap, int block) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  if (gid >= units * D) return;
+  const int u = gid / D, ch = gid % D;
+  const T kn = k_new[size_t(u) * D + ch];
+  k[(size_t(u) * kv_cap + pos) * D + ch] = kn;
+  v[(size_t(u) * kv_cap + pos) * D + ch] = v_new[size_t(u) * D + ch];
+  const size_t a = (size_t(u) * D + ch) * nblk_cap + pos / block;
+  if (pos % block == 0) {
+    kmax[a] = kn;
+    kmin[a] = kn;
+  } else {
+    const float x = to_f32(kn);
+    if (x > to_f32(kmax[a])) kmax[a] = kn;
+    if (x < to_f32(kmin[a])) kmin[a] = kn;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_append_t(const Dims& d, const void* k_new, const void* v_new, void* k, void* v,
+                           int64_t kv_cap, int64_t pos, void* kmax, void* kmin, int64_t nblk_cap,
+                           int block, hipStream_t s) {
+  const int units = d.units();
+  RK_LAUNCH("append_kv", (append_kv_kernel<T, D>), dim3((units * D + 255) / 256), dim3(256), 0, s,
+            static_cast<const T*>(k_new), static_cast<const T*>(v_new), static_cast<T*>(k),
+            static_cast<T*>(v), kv_cap, pos, units, static_cast<T*>(kmax), static_cast<T*>(kmin),
+            nblk_cap, block);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_append_kv(const Dims& d, const void* k_new, const void* v_new, void* k, void* v,
+                            int64_t kv_cap, int64_t pos, void* kmax, void* kmin,
+                            int64_t nblk_cap, int block, hipStream_t s) {
+  if (d.bf16) {
+    if (d.D == 128)
+      return launch_append_t<bf16_t, 128>(d, k_new, v_new, k, v, kv_cap, pos, kmax, kmin, nblk_cap,
+                                          block, s);
+    return launch_append_t<bf16_t, 64>(d, k_new, v_new, k, v, kv_cap, pos, kmax, kmin, nblk_cap,
+                                       block, s);
+  }
+  if (d.D == 128)
+    return launch_append_t<float, 128>(d, k_new, v_new, k, v, kv_cap, pos, kmax, kmin, nblk_cap,
+                                       block, s);
+  return launch_append_t<float, 64>(d, k_new, v_new, k, v, kv_cap, pos, kmax, kmin, nblk_cap, block,
+                                    s);
+}
 
 hipError_t launch_build_aux(const Dims& d, const void* k, int64_t k_cap, const int32_t* idx,
                             int64_t idx_stride, int64_t n_tokens, int64_t first_block,

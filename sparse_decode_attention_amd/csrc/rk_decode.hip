@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPR = D / EPL;
   constexpr int SLOTS = kWave / LPR;
-  constexpr int TPS = 4;
+  constexpr int TPS = G >= 4 ? 2 : 4;  // fewer tokens per step for wide groups (registers)
   constexpr int CHUNK = SLOTS * TPS;
   constexpr int NW = 4;
   constexpr int PF = D + 4;  // floats per head partial: m, l, pad, pad, o[D]
@@ -248,9 +248,7 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
           float s = 0.f;
 #pragma unroll
           for (int ee = 0; ee < EPL; ++ee) s += qf[g][ee] * kf[ee];
-#pragma unroll
-          for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off);
-          x[g][i] = s * scale_log2;
+          x[g][i] = group_sum<LPR>(s) * scale_log2;
         }
       }
 #pragma unroll
@@ -260,12 +258,12 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
         for (int i = 0; i < TPS; ++i)
           if (ok[i]) cm = fmaxf(cm, x[g][i]);
         const float mn = fmaxf(m[g], cm);
-        const float corr = exp2f(m[g] - mn);
+        const float corr = fast_exp2(m[g] - mn);
         float p[TPS];
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < TPS; ++i) {
-          p[i] = ok[i] ? exp2f(x[g][i] - mn) : 0.f;
+          p[i] = ok[i] ? fast_exp2(x[g][i] - mn) : 0.f;
           ps += p[i];
         }
         l[g] = l[g] * corr + ps;
@@ -289,7 +287,7 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
       const float mo = __shfl_xor(m[g], off);
       const float lo = __shfl_xor(l[g], off);
       const float mn = fmaxf(m[g], mo);
-      const float a = exp2f(m[g] - mn), b = exp2f(mo - mn);
+      const float a = fast_exp2(m[g] - mn), b = fast_exp2(mo - mn);
       l[g] = l[g] * a + lo * b;
 #pragma unroll
       for (int ee = 0; ee < EPL; ++ee) {
@@ -321,7 +319,7 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
     for (int w = 0; w < NW; ++w) mm = fmaxf(mm, wm[w][g]);
     float ll = 0.f, oo = 0.f;
     for (int w = 0; w < NW; ++w) {
-      const float a = exp2f(wm[w][g] - mm);
+      const float a = fast_exp2(wm[w][g] - mm);
       ll += wl[w][g] * a;
       oo += wo[w][g][ch] * a;
     }
@@ -364,7 +362,7 @@ __global__ __launch_bounds__(256) void hsa_combine_kernel(const float* __restric
   const float2 ml = lane < n_split ? *reinterpret_cast<const float2*>(pu + lane * stride)
                                    : make_float2(kNegBig, 0.f);
   const float mm = wave_max(ml.x);
-  const float a = lane < n_split ? exp2f(ml.x - mm) : 0.f;
+  const float a = lane < n_split ? fast_exp2(ml.x - mm) : 0.f;
   const float ll = wave_sum(ml.y * a);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll

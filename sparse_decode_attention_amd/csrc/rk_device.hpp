@@ -22,6 +22,11 @@ struct bf16_t {
   uint16_t bits;
 };
 
+// 2^x with the hardware instruction alone.  Used where x <= 0 (arguments are
+// differences from a running maximum): results below 2^-126, if flushed,
+// are negligible next to the sums of >= 1 they are added to.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x.bits) << 16); }
 
@@ -321,6 +326,21 @@ __device__ void wg_topk_rank(const uint32_t* keys, int n, int k, const EmitFn& e
     if (sel) emit(pos, j);
     base += tot;
   }
+}
+
+// Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32), result in every
+// lane of the group.  Up to 16 lanes it uses DPP row permutations (quad swaps,
+// then the half-row and row mirrors), which stay in the ALU; the step across
+// 16-lane rows uses a lane shuffle.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  if (N >= 2) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
+  if (N >= 4) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
+  if (N >= 8) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false)); // row_half_mirror
+  if (N >= 16) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false)); // row_mirror
+  if (N >= 32) x += __shfl_xor(x, 16);
+  return x;
 }
 
 // Wave-wide reductions (all 64 lanes take part).

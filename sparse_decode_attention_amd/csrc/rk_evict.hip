@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void ws_pass1_kernel(const T* __restrict__ q_w
     for (int i = 0; i < 8; ++i) {
       const int col = part * 8 + i;
       const int j = j0 + col;
-      if (j < S && j <= lim) z += exp2f(Ls[row][col] - mx);
+      if (j < S && j <= lim) z += fast_exp2(Ls[row][col] - mx);
     }
 #pragma unroll
     for (int off = 1; off < 8; off <<= 1) z += __shfl_xor(z, off);
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void ws_stats_kernel(const float2* __restrict_
   float z = 0.f;
   for (int t = lane; t < n_tiles; t += kWave) {
     const float2 p = pr[t];
-    z += p.y * exp2f(p.x - mm);
+    z += p.y * fast_exp2(p.x - mm);
   }
   z = wave_sum(z);
   if (lane == 0) stats[wi] = make_float2(mm, 1.0f / z);
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void ws_pass2_kernel(const T* __restrict__ q_w
       const int r_all = r0 + part * 8 + i;
       if (r_all < M) {
         const float2 mz = st[r_all];
-        s += exp2f(Ls[part * 8 + i][col] - mz.x) * mz.y;
+        s += fast_exp2(Ls[part * 8 + i][col] - mz.x) * mz.y;
       }
     }
     red[part][col] = s;
@@ -287,24 +287,27 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k,
 // ---------------------------------------------------------------------------
 // bf16 window scoring on the matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// A workgroup (4 waves) owns 256 consecutive keys of one unit.  The G*W window
-// rows are cut into 32-row groups; a wave keeps the A operand of its row group
-// (32 rows x d, bf16) in registers for the whole tile and streams 32-key
-// chunks of K straight from memory as the B operand (each lane fetches 16
-// contiguous bytes of one key row), prefetching the next chunk while the
-// current one is multiplied.  With fewer than 4 row groups the waves split
-// the tile's chunks instead.  Accumulator lane layout (verified on gfx950):
-// lane l, element i holds row 8*(i/4) + 4*(l/32) + i%4 of the group and key
-// column l%32 of the chunk.
-//   pass 1: per row, online max / sum of exp2 over the tile -> partials
-//   pass 2: exp2(x - m_row) / Z_row summed over all rows of the group for each
-//           key, then over the row groups in order -> score
+// A workgroup (4 waves) walks a range of keys of one unit in 128-key tiles.
+// Each tile is fetched with fully coalesced 16-byte loads (consecutive
+// threads, consecutive bytes) into LDS with a padded row pitch, the next tile
+// is prefetched into registers while the current one is multiplied, and the
+// waves read their MFMA operand fragments from LDS.  The G*W window rows are
+// cut into 32-row groups; a wave keeps its group's Q fragments (32 rows x d,
+// bf16) in registers for the whole range.  With fewer than 4 row groups the
+// waves split each tile's 32-key chunks instead.  Accumulator lane layout of
+// v_mfma_f32_32x32x16_bf16 (verified on gfx950): lane l, element i holds row
+// 8*(i/4) + 4*(l/32) + i%4 and column l%32 of the 32x32 product.
+//   pass 1: product K_chunk * Q^T, so lane l owns window row l%32 of its group
+//           and keeps that row's running (max, sum of exp2) in two registers
+//   pass 2: product Q * K_chunk^T, so lane l owns key l%32 and sums
+//           exp2(x - m_row) / Z_row over its 16 rows; row groups are then
+//           added in order -> score
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int TNM = 256;             // keys per workgroup
-constexpr int NCH = TNM / 32;        // 32-key chunks per workgroup
+constexpr int TK = 128;              // keys per LDS tile
+constexpr int TCH = TK / 32;         // 32-key chunks per tile
 
 __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p, bool ok) {
   uint4 r = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
@@ -314,132 +317,171 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p, bool ok) {
 template <int D, int PASS>
 __global__ __launch_bounds__(256) void ws_mfma_kernel(
     const bf16_t* __restrict__ q_win, const bf16_t* __restrict__ k, int64_t kv_cap, int S, int W,
-    int G, int n_tiles, float scale_log2, float2* __restrict__ partials,
+    int G, int n_wg, int keys_per_wg, float scale_log2, float2* __restrict__ partials,
     const float2* __restrict__ stats, float* __restrict__ scores) {
   constexpr int KS = D / 16;
-  extern __shared__ float smem[];  // pass 1: items x 32 float2; pass 2: RG x TNM floats
+  constexpr int ROWB = D * 2 + 16;         // LDS row pitch in bytes (16 bytes of padding)
+  constexpr int VPR = D * 2 / 16;          // 16-byte vectors per key row
+  constexpr int LPT = TK * VPR / 256;      // vectors per thread per tile
+  static_assert(TK * VPR % 256 == 0, "tile must split evenly over the workgroup");
+  __shared__ __align__(16) unsigned char ktile[TK * ROWB];
+  extern __shared__ float smem[];  // pass 1: items x 32 float2; pass 2: RG x TK floats
   const int M = G * W;
   const int RG = (M + 31) / 32;
   const int CS = RG >= 4 ? 1 : 4 / RG;  // waves sharing one row group
   const int items = RG * CS;
   const int u = blockIdx.y;
-  const int tile = blockIdx.x;
-  const int j0 = tile * TNM;
+  const int wgi = blockIdx.x;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int half = lane >> 5;
   const int P = S - W;
   const int jlim = PASS == 1 ? S : P;
+  const int kb = wgi * keys_per_wg;
+  const int ke = min(kb + keys_per_wg, jlim);
   const bf16_t* qg = q_win + size_t(u) * M * D;
-  const bf16_t* ku = k + size_t(u) * size_t(kv_cap) * D + half * 8;
-
-  for (int it = wave; it < items; it += 4) {
-    const int rg = it / CS;
-    const int cs = it % CS;
-    bf16x8_t a[KS];
-    {
-      const int arow = rg * 32 + (lane & 31);
+  const bf16_t* ku = k + size_t(u) * size_t(kv_cap) * D;
+  // Wave w owns item w (row group it / CS, chunk class it % CS); the launcher
+  // guarantees at most 4 items.  Its Q fragments stay in registers.
+  const bool active = wave < items;
+  const int rg = wave / CS, cs = wave % CS;
+  bf16x8_t a[KS];
+  {
+    const int arow = rg * 32 + (lane & 31);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        a[ks] = load_bf16x8(qg + size_t(arow) * D + ks * 16 + half * 8, arow < M);
-    }
-    float m[16], z[16];
+    for (int ks = 0; ks < KS; ++ks)
+      a[ks] = load_bf16x8(qg + size_t(arow) * D + ks * 16 + half * 8, active && arow < M);
+  }
+  // pass 1: (max, sum) of this lane's row; pass 2: (m, 1/Z) of its 16 rows
+  float m1 = kNegBig, z1 = 0.f;
+  float m2[16], z2[16];
+  if (PASS == 2 && active) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = rg * 32 + 8 * (i / 4) + 4 * half + (i & 3);
-      if (PASS == 1) {
-        m[i] = kNegBig;
-        z[i] = 0.f;
-      } else {
-        const float2 st = row < M ? stats[size_t(u) * M + row] : make_float2(1.0e30f, 0.f);
-        m[i] = st.x;  // row max (log2 domain)
-        z[i] = st.y;  // 1 / row sum
-      }
-    }
-    int cc = cs;
-    int col = j0 + cc * 32 + (lane & 31);
-    bf16x8_t b[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) b[ks] = load_bf16x8(ku + size_t(col) * D + ks * 16, col < jlim);
-    for (; cc < NCH && j0 + cc * 32 < jlim; cc += CS) {
-      const int ncol = col + 32 * CS;
-      const bool more = cc + CS < NCH && j0 + (cc + CS) * 32 < jlim;
-      bf16x8_t bn[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        bn[ks] = load_bf16x8(ku + size_t(ncol) * D + ks * 16, more && ncol < jlim);
-      f32x16_t acc = {};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b[ks], acc, 0, 0, 0);
-      if (PASS == 1) {
-        const bool edge = j0 + cc * 32 + 32 > S - W;  // chunk reaches the causal window or S
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = acc[i] * scale_log2;
-          bool ok = true;
-          if (edge) {
-            const int row = rg * 32 + 8 * (i / 4) + 4 * half + (i & 3);
-            ok = col < S && col <= S - W + (row % W);
-          }
-          if (ok) {
-            const float mn = fmaxf(m[i], x);
-            z[i] = z[i] * exp2f(m[i] - mn) + exp2f(x - mn);
-            m[i] = mn;
-          }
-        }
-      } else {
-        float cs_sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) cs_sum += exp2f(acc[i] * scale_log2 - m[i]) * z[i];
-        cs_sum += __shfl_xor(cs_sum, 32);
-        if (lane < 32) smem[rg * TNM + cc * 32 + lane] = cs_sum;
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) b[ks] = bn[ks];
-      col = ncol;
-    }
-    if (PASS == 1) {
-      // merge the 32 key columns held by the lanes of each half-wave
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float mo = __shfl_xor(m[i], off);
-          const float zo = __shfl_xor(z[i], off);
-          const float mn = fmaxf(m[i], mo);
-          z[i] = z[i] * exp2f(m[i] - mn) + zo * exp2f(mo - mn);
-          m[i] = mn;
-        }
-      }
-      if ((lane & 31) == 0) {
-        float2* mz = reinterpret_cast<float2*>(smem) + it * 32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mz[8 * (i / 4) + 4 * half + (i & 3)] = make_float2(m[i], z[i]);
-      }
+      const float2 st = row < M ? stats[size_t(u) * M + row] : make_float2(1.0e30f, 0.f);
+      m2[i] = st.x;
+      z2[i] = st.y;
     }
   }
+
+  uint4 pre[LPT];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int x = 0; x < LPT; ++x) {
+      const int vidx = threadIdx.x + 256 * x;
+      const int key = t0 + vidx / VPR;
+      pre[x] = key < ke ? reinterpret_cast<const uint4*>(ku + size_t(key) * D)[vidx % VPR]
+                        : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int x = 0; x < LPT; ++x) {
+      const int vidx = threadIdx.x + 256 * x;
+      *reinterpret_cast<uint4*>(ktile + (vidx / VPR) * ROWB + (vidx % VPR) * 16) = pre[x];
+    }
+  };
+  if (kb < ke) {
+    fetch(kb);
+    stash();
+  }
   __syncthreads();
+  for (int t0 = kb; t0 < ke; t0 += TK) {
+    const bool next = t0 + TK < ke;
+    if (next) fetch(t0 + TK);             // in flight while this tile is multiplied
+    const int nch = (min(t0 + TK, ke) - t0 + 31) / 32;
+    if (active) {
+      const int row1 = rg * 32 + (lane & 31);
+      const int lim1 = S - W + (row1 % W);   // last key row1 may see
+      for (int c = cs; c < nch; c += CS) {
+        const unsigned char* fr = ktile + (c * 32 + (lane & 31)) * ROWB + half * 16;
+        bf16x8_t b[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) b[ks] = *reinterpret_cast<const bf16x8_t*>(fr + ks * 32);
+        f32x16_t acc = {};
+        if (PASS == 1) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[ks], a[ks], acc, 0, 0, 0);
+          if (t0 + c * 32 + 32 <= S - W) {
+            // every key of the chunk is visible to every window row
+            float cm = acc[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) cm = fmaxf(cm, acc[i]);
+            const float mn = fmaxf(m1, cm * scale_log2);
+            float zz = z1 * fast_exp2(m1 - mn);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) zz += fast_exp2(fmaf(acc[i], scale_log2, -mn));
+            z1 = zz;
+            m1 = mn;
+          } else {
+            // causal window / past S: masked without branches
+            const int kbase = t0 + c * 32 + 4 * half;  // key of element i: kbase + 8*(i/4) + i%4
+            bool ok[16];
+            float cm = kNegBig;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kbase + 8 * (i / 4) + (i & 3);
+              ok[i] = key < S && key <= lim1;
+              cm = fmaxf(cm, ok[i] ? acc[i] : kNegBig);
+            }
+            const float mn = fmaxf(m1, cm * scale_log2);
+            float zz = z1 * fast_exp2(m1 - mn);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float e = fast_exp2(fmaf(acc[i], scale_log2, -mn));
+              zz += ok[i] ? e : 0.f;
+            }
+            z1 = zz;
+            m1 = mn;
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b[ks], acc, 0, 0, 0);
+          float cs_sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) cs_sum += fast_exp2(fmaf(acc[i], scale_log2, -m2[i])) * z2[i];
+          cs_sum += __shfl_xor(cs_sum, 32);
+          if (lane < 32) smem[rg * TK + c * 32 + lane] = cs_sum;
+        }
+      }
+    }
+    __syncthreads();
+    if (PASS == 2) {
+      for (int cidx = threadIdx.x; cidx < TK; cidx += 256) {
+        const int j = t0 + cidx;
+        if (j >= ke) continue;
+        float sacc = 0.f;
+        for (int rg = 0; rg < RG; ++rg) sacc += smem[rg * TK + cidx];
+        scores[size_t(u) * P + j] = sacc;
+      }
+    }
+    if (next) stash();
+    __syncthreads();
+  }
   if (PASS == 1) {
+    if (wave < items) {
+      // the two half-waves hold disjoint keys of the same 32 rows
+      const float mo = __shfl_xor(m1, 32);
+      const float zo = __shfl_xor(z1, 32);
+      const float mn = fmaxf(m1, mo);
+      const float zz = (lane < 32) ? z1 * fast_exp2(m1 - mn) + zo * fast_exp2(mo - mn)
+                                   : zo * fast_exp2(mo - mn) + z1 * fast_exp2(m1 - mn);
+      if (lane < 32) reinterpret_cast<float2*>(smem)[wave * 32 + lane] = make_float2(mn, zz);
+    }
+    __syncthreads();
     const float2* mz = reinterpret_cast<const float2*>(smem);
     for (int r = threadIdx.x; r < RG * 32; r += 256) {
       if (r >= M) continue;
       const int rg = r / 32, rl = r % 32;
       float mm = kNegBig, zz = 0.f;
       for (int c = 0; c < CS; ++c) {  // column splits in order
-        const float2 p = mz[(rg * CS + c) * 32 + rl];
-        const float mn = fmaxf(mm, p.x);
-        zz = zz * exp2f(mm - mn) + p.y * exp2f(p.x - mn);
+        const float2 pz = mz[(rg * CS + c) * 32 + rl];
+        const float mn = fmaxf(mm, pz.x);
+        zz = zz * fast_exp2(mm - mn) + pz.y * fast_exp2(pz.x - mn);
         mm = mn;
       }
-      partials[(size_t(u) * M + r) * n_tiles + tile] = make_float2(mm, zz);
-    }
-  } else {
-    for (int c = threadIdx.x; c < TNM; c += 256) {
-      const int j = j0 + c;
-      if (j >= P) continue;
-      float sacc = 0.f;
-      for (int rg = 0; rg < RG; ++rg) sacc += smem[rg * TNM + c];
-      scores[size_t(u) * P + j] = sacc;
+      partials[(size_t(u) * M + r) * n_wg + wgi] = make_float2(mm, zz);
     }
   }
 }
@@ -463,16 +505,28 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   const T* qw = static_cast<const T*>(q_win);
   const T* kk = static_cast<const T*>(k);
 
-  constexpr bool kMfma = sizeof(T) == 2;  // bf16 on the matrix cores, float32 on the vector ALUs
-  const int n_tiles = kMfma ? (S + TNM - 1) / TNM : lay.n_tiles;
+  // bf16 on the matrix cores when G*W fits 4 waves of 32-row groups (one
+  // group per wave), otherwise (and for float32) on the vector ALUs
+  constexpr bool kBf16 = sizeof(T) == 2;
+  const bool mfma = kBf16 && M <= 128;
   const int RG = (M + 31) / 32;
   const int CS = RG >= 4 ? 1 : 4 / RG;
+  // keys per workgroup: about 2048 workgroups per pass, in whole 128-key tiles
+  auto range = [&](int keys) {
+    const int wpu = (2048 + units - 1) / units;
+    int kpw = (keys + wpu - 1) / wpu;
+    kpw = (kpw + TK - 1) / TK * TK;
+    return kpw < TK ? TK : kpw;
+  };
+  const int kpw1 = range(S);
+  const int n_wg1 = mfma ? (S + kpw1 - 1) / kpw1 : lay.n_tiles;
+  const int n_tiles = n_wg1;
   const size_t lds1 = size_t(RG * CS) * 32 * sizeof(float2);
-  const size_t lds2 = size_t(RG) * TNM * sizeof(float);
-  if constexpr (kMfma) {
-    RK_LAUNCH("ws_pass1", (ws_mfma_kernel<D, 1>), dim3(n_tiles, units), dim3(256), lds1, s,
+  const size_t lds2 = size_t(RG) * TK * sizeof(float);
+  if (mfma) {
+    RK_LAUNCH("ws_pass1", (ws_mfma_kernel<D, 1>), dim3(n_wg1, units), dim3(256), lds1, s,
               reinterpret_cast<const bf16_t*>(qw), reinterpret_cast<const bf16_t*>(kk), kv_cap, S,
-              W, d.G, n_tiles, scale_log2, partials, nullptr, nullptr);
+              W, d.G, n_wg1, kpw1, scale_log2, partials, nullptr, nullptr);
   } else {
     RK_LAUNCH("ws_pass1", (ws_pass1_kernel<T, D>), dim3(n_tiles, units), dim3(256), 0, s, qw, kk,
               kv_cap, S, W, d.G, n_tiles, scale_log2, partials);
@@ -483,10 +537,11 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
             n_tiles, units, stats);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (P > 0) {
-    if constexpr (kMfma) {
-      RK_LAUNCH("ws_pass2", (ws_mfma_kernel<D, 2>), dim3((P + TNM - 1) / TNM, units), dim3(256),
+    if (mfma) {
+      const int kpw2 = range(P);
+      RK_LAUNCH("ws_pass2", (ws_mfma_kernel<D, 2>), dim3((P + kpw2 - 1) / kpw2, units), dim3(256),
                 lds2, s, reinterpret_cast<const bf16_t*>(qw), reinterpret_cast<const bf16_t*>(kk),
-                kv_cap, S, W, d.G, n_tiles, scale_log2, nullptr, stats, scores);
+                kv_cap, S, W, d.G, 0, kpw2, scale_log2, nullptr, stats, scores);
     } else {
       RK_LAUNCH("ws_pass2", (ws_pass2_kernel<T, D>), dim3((P + TN - 1) / TN, units), dim3(256), 0,
                 s, qw, kk, kv_cap, S, W, d.G, scale_log2, stats, scores);

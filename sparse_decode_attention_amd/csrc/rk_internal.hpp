@@ -91,6 +91,10 @@ hipError_t launch_build_aux(const Dims& d, const void* k, int64_t k_cap, const i
                             int block, void* kmax, void* kmin, int64_t nblk_cap,
                             hipStream_t s);
 
+hipError_t launch_append_kv(const Dims& d, const void* k_new, const void* v_new, void* k, void* v,
+                            int64_t kv_cap, int64_t pos, void* kmax, void* kmin,
+                            int64_t nblk_cap, int block, hipStream_t s);
+
 hipError_t launch_hsa_decode(const Dims& d, const void* q, const void* k, const void* v,
                              int64_t kv_cap, const int32_t* cand, int64_t cand_stride,
                              const void* kmax, const void* kmin, int64_t nblk_cap,

@@ -146,6 +146,20 @@ def rk_hsa_build_aux(k, n_tokens, first_token, block, kmax, kmin, n_q_heads=None
            "rk_hsa_build_aux")
 
 
+_lib.rk_append_kv.argtypes = [_SP, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _i32, _vp]
+_lib.rk_append_kv.restype = ctypes.c_int
+
+
+def rk_append_kv(k_new, v_new, k, v, pos, kmax, kmin, block, n_q_heads=None, stream=None):
+    """Append row `pos` (k_new, v_new [B,Hkv,d]) to k, v [B,Hkv,cap,d] and fold it
+    into page pos // block of kmax, kmin [B,Hkv,d,nblk_cap]."""
+    _need_contig(k_new, v_new, k, v, kmax, kmin)
+    B, Hkv, cap, d = k.shape
+    shape = shape_of(B, n_q_heads or Hkv, Hkv, d, _dtype_code(k))
+    _check(_lib.rk_append_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k), _ptr(v), cap, pos,
+                             _ptr(kmax), _ptr(kmin), kmax.shape[3], block, _stream(stream)), "rk_append_kv")
+
+
 def rk_hsa_workspace_bytes(shape: RkShape, n_tokens: int, block: int, k1: int, k2: int) -> int:
     return _lib.rk_hsa_workspace_bytes(ctypes.byref(shape), n_tokens, block, k1, k2)
 

@@ -156,6 +156,16 @@ def test_error_codes_before_any_launch(rk):
     assert aux(idx=_vp(FAKE), stride=999) == rk.RK_EINVAL
     assert aux(k=None) == rk.RK_EINVAL
 
+    def app(**kw):
+        a = dict(kn=_vp(FAKE), cap=1024, pos=1000, nblk_cap=64, block=16)
+        a.update(kw)
+        return lib.rk_append_kv(byref(sh), a["kn"], _vp(FAKE), _vp(FAKE), _vp(FAKE), a["cap"], a["pos"],
+                                _vp(FAKE), _vp(FAKE), a["nblk_cap"], a["block"], None)
+
+    assert app(pos=1024) == rk.RK_EINVAL and app(pos=-1) == rk.RK_EINVAL
+    assert app(nblk_cap=62) == rk.RK_EINVAL and app(nblk_cap=63) == rk.RK_EINVAL
+    assert app(kn=None) == rk.RK_EINVAL and app(block=0) == rk.RK_EINVAL
+
     assert lib.rk_hsa_decode_mt(byref(sh), _vp(FAKE), _vp(FAKE), _vp(FAKE), 4096, None, 1000, 1000,
                                 _vp(FAKE), _vp(FAKE), 63, 16, 16, 16, _vp(FAKE), None, None, None,
                                 _vp(FAKE), 1 << 30, None) == rk.RK_EINVAL

@@ -60,9 +60,9 @@ def test_llama8b_stack_batch32_appends(rk):
         for step in range(w.decode_steps):
             n = n_keep + step
             ka, va = WL.append_kv(w, layer, step, device=DEV)
-            kc[:, :, n] = ka
-            vc[:, :, n] = va
-            rk.rk_hsa_build_aux(kc, n + 1, n, w.block, kmax, kmin, n_q_heads=w.n_q)
+            rk.rk_append_kv(ka, va, kc, vc, n, kmax, kmin, w.block, n_q_heads=w.n_q)
+            if step == 0:
+                assert torch.equal(kc[:, :, n], ka) and torch.equal(vc[:, :, n], va)
             q = WL.decode_query(w, layer, step, device=DEV)
             if step in (0, 1, w.decode_steps - 1) or step % 8 == 0:
                 U.check_aux_units(kmax, kmin, kc, n + 1, w.block, units)

@@ -252,3 +252,26 @@ def test_kernel_timing_hooks(rk):
     assert prof["aux_build"][0] == 3 and prof["aux_build"][1] > 0
     assert set(prof) == {"aux_build", "hsa_select", "hsa_attn", "hsa_combine"}
     assert rk.rk_profile_end() == {}
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_append_equals_rebuild(rk, dtype, d):
+    """rk_append_kv writes the rows and leaves Kmax/Kmin equal to a full rebuild."""
+    say("append", dtype, d)
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=3, n_kv=2, n_q=4, d=d, dtype=dtype, seq=200, n_plant=0)
+    kc0, vc0, _ = WL.layer_kv(w, 0, device=DEV)
+    cap = 240
+    kc = torch.zeros(3, 2, cap, d, dtype=kc0.dtype, device=DEV)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :200] = kc0
+    vc[:, :, :200] = vc0
+    kmax = torch.empty(3, 2, d, rk.aux_capacity(cap, 16), dtype=kc.dtype, device=DEV)
+    kmin = torch.empty_like(kmax)
+    rk.rk_hsa_build_aux(kc, 200, 0, 16, kmax, kmin)
+    for step in range(40):                       # crosses page boundaries at 208, 224
+        ka, va = WL.append_kv(w, 0, step, device=DEV)
+        rk.rk_append_kv(ka, va, kc, vc, 200 + step, kmax, kmin, 16)
+        torch.cuda.synchronize()
+        assert torch.equal(kc[:, :, 200 + step], ka) and torch.equal(vc[:, :, 200 + step], va)
+        U.check_aux_units(kmax, kmin, kc, 201 + step, 16, [(b, h) for b in range(3) for h in range(2)])
