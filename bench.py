@@ -113,7 +113,7 @@ class Path:
         self.alg = {
             "hsa_attn": units * nsel * w.block * 2 * d * esize + B * Hq * d * esize,
             "hsa_attn_mt": units * nsel * w.block * (2 * d * esize + 4) + B * Hq * d * esize,
-            "hsa_select": units * w.k1 * nb0 * esize + B * Hq * d * esize,
+            "hsa_score": units * w.k1 * nb0 * esize + B * Hq * d * esize,
             "aux_build": units * self.n_keep * d * esize + 2 * units * d * nb0 * esize,
             "gather_kv": 2 * 2 * units * self.n_keep * d * esize,
             "ws_pass1": units * self.S * d * esize + B * Hq * w.window * d * esize,
@@ -121,7 +121,7 @@ class Path:
             "append_kv": units * d * esize * 5,
         }
         self.flops_ws = 2.0 * units * G * w.window * self.S * d
-        self.dec_bytes = self.alg["hsa_attn_mt" if self.mt else "hsa_attn"] + self.alg["hsa_select"]
+        self.dec_bytes = self.alg["hsa_attn_mt" if self.mt else "hsa_attn"] + self.alg["hsa_score"]
 
     def evict_part(self, r):
         rk, w = self.rk, self.w

@@ -9,13 +9,13 @@
 // cache).
 //
 // Three launches per call:
-//   hsa_select  one workgroup per unit: channel sums and top-k1; the k1
-//               sign-selected aux rows are staged into LDS with 16-byte loads
-//               (one memory round trip), pages are scored from LDS, top-k2 by
-//               radix select
-//   hsa_attn    split-K over the selected pages: a wave streams whole pages
-//               with 16-byte K/V loads, online softmax in the exp2 domain, one
-//               partial (m, l, o[d]) per head per workgroup
+//   hsa_score   one workgroup per (page range, unit): channel sums and top-k1;
+//               the range's k1 sign-selected aux rows are staged into LDS with
+//               16-byte loads (one memory round trip) and its pages scored
+//   hsa_attn    top-k2 of the unit's page scores (radix select, in every
+//               workgroup), then split-K over the selected pages: a wave streams
+//               whole pages with 16-byte K/V loads, online softmax in the exp2
+//               domain, one partial (m, l, o[d]) per head per workgroup
 //   hsa_combine one wave per (unit, head) merges the partials
 // HBM-bound: bytes per unit = q + k1*nblk aux elements + 2*d*|T| K/V elements.
 #include <math.h>
@@ -26,102 +26,168 @@
 namespace rk {
 namespace {
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void hsa_select_kernel(
+// Step 2a: one workgroup per (page range, unit).  Every workgroup of a unit
+// makes the same channel choice (group sums of |q| in g order, top-k1 with
+// ties toward the lower channel), then stages its pages' sign-selected aux
+// rows into LDS with all 16-byte loads in flight and scores them.  Spreading
+// a unit's pages over many workgroups keeps the aux fetch of a small batch
+// from queueing behind one CU's outstanding-load limit.  ALL (small launches,
+// where latency rules and bytes are cheap): the range's Kmax and Kmin rows of
+// every channel are fetched together with q, so the channel choice no longer
+// sits between two memory round trips.
+template <typename T, int D, int G, bool ALL>
+__global__ __launch_bounds__(256) void hsa_score_kernel(
     const T* __restrict__ q, const T* __restrict__ kmax, const T* __restrict__ kmin,
-    int64_t nblk_cap, int nblk, int k1, int nsel, int npc, int32_t* __restrict__ sel_ws,
-    int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt,
-    float* __restrict__ s1_opt) {
+    int64_t nblk_cap, int nblk, int k1, int ppw, uint32_t* __restrict__ keys, int keys_pitch,
+    int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt) {
   constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
   extern __shared__ __align__(16) unsigned char dyn_lds[];
-  uint32_t* page_keys = reinterpret_cast<uint32_t*>(dyn_lds);  // [nblk rounded up to 4]
-  T* stage = reinterpret_cast<T*>(dyn_lds + (size_t((nblk + 3) & ~3) * 4 + 15) / 16 * 16);
-  __shared__ __align__(16) uint32_t chan_keys[D];
-  __shared__ float qbar[D];
-  __shared__ int i1[D];
+  T* stage = reinterpret_cast<T*>(dyn_lds);  // [ppw][k1p]
   __shared__ __align__(16) float i1_q[D + 16];
-  __shared__ int i1_off[D];  // element offset of the sign-selected row; < 0: Kmin
-  __shared__ TopkSmem<256> sm;
+  __shared__ __align__(16) int i1_off[D + 16];  // sign-selected row of i1[j]: ch (Kmax) or -1-ch (Kmin)
+  __shared__ __align__(16) uint32_t hist[1024];
 
-  const int u = blockIdx.x;
+  constexpr int R = D / kWave;  // channels per lane of wave 0
+  constexpr int NBA = 8;        // 16-byte vectors per thread in ALL mode (one round)
+  const int u = blockIdx.y;
+  const int p0 = blockIdx.x * ppw;
+  const int np = min(ppw, nblk - p0);
   const int t = threadIdx.x;
-  RK_PHASE(0);
-  if (t < D) {
-    float a = 0.f, qb = 0.f;
+  const int wave = t / kWave, lane = lane_id();
+  RK_PHASE(16);
+  const T* xu = kmax + size_t(u) * D * size_t(nblk_cap) + p0;
+  const T* nu = kmin + size_t(u) * D * size_t(nblk_cap) + p0;
+  const int nv = (np + EPV - 1) / EPV;  // 16-byte vectors per row slice
+  float qx[R][G];
+  if (wave == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {  // g ascending, float32, as the group sums are defined
-      const float x = to_f32(q[(size_t(u) * G + g) * D + t]);
-      a = __fadd_rn(a, fabsf(x));
-      qb = __fadd_rn(qb, x);
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int g = 0; g < G; ++g) qx[r][g] = to_f32(q[(size_t(u) * G + g) * D + r * kWave + lane]);
+  }
+  // ALL: rows r < D are Kmax channel r, rows r >= D Kmin channel r - D;
+  // stage[r][page] with pitch ppw (2*D*nv <= 256*NBA, set by the launcher)
+  Vec16<T> buf[NBA];
+  if (ALL) {
+#pragma unroll
+    for (int x = 0; x < NBA; ++x) {
+      const int id = x * 256 + t;
+      if (id < 2 * D * nv) {
+        const int r = id / nv, vi = id % nv;
+        buf[x] = load16((r < D ? xu + size_t(r) * nblk_cap : nu + size_t(r - D) * nblk_cap) + vi * EPV);
+      }
     }
-    chan_keys[t] = order_key(a);
-    qbar[t] = qb;
   }
-  __syncthreads();
-  wg_topk_rank<256>(chan_keys, D, k1, [&](int r, int i) { i1[r] = i; }, sm.tmp);
-  __syncthreads();
-  RK_PHASE(8);
-  const T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
-  const T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
-  for (int j = t; j < k1; j += 256) {
-    const int ch = i1[j];
-    const float qv = qbar[ch];
-    i1_q[j] = qv;
-    i1_off[j] = qv >= 0.f ? ch : -1 - ch;  // sign selects the Kmax or the Kmin row
-    if (chan_opt) chan_opt[size_t(u) * k1 + j] = ch;
-  }
-  __syncthreads();
-
-  // Pages in chunks of npc (a multiple of 8).  Staging: thread (channel j,
-  // vector slot) fetches 16-byte runs of row j (EPV consecutive pages) with
-  // all of its loads in flight, and scatters them transposed into LDS as
-  // stage[page][channel] (row pitch k1p, a multiple of EPV plus one vector of
-  // padding).  Scoring: s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b],
-  // read back as 16-byte vectors of channels.
-  const int k1p = (k1 + 15) / 16 * 16 + EPV;  // 16-channel blocks plus one vector of padding
-  const int groups = 256 / k1;  // vector slots per channel (k1 <= 128)
-  for (int p0 = 0; p0 < nblk; p0 += npc) {
-    const int np = min(npc, nblk - p0);
-    const int nv = (np + EPV - 1) / EPV;  // vectors per row slice (stays inside nblk_cap)
-    if (t < groups * k1) {
-      const int j = t % k1;
-      const int off = i1_off[j];
-      const T* row = (off >= 0 ? xu + size_t(off) * nblk_cap : nu + size_t(-1 - off) * nblk_cap) + p0;
-      constexpr int NB = 20;
-      for (int v0 = t / k1; v0 < nv; v0 += groups * NB) {
-        Vec16<T> buf[NB];
+  if (wave == 0) {
+    // group sums of |q| and q per channel (g ascending, float32), then the
+    // top-k1 channels by one wave; the emitting lane holds the channel's q_bar
+    float qb[R];
+    uint32_t kr[R];
 #pragma unroll
-        for (int x = 0; x < NB; ++x) {
-          const int vi = v0 + x * groups;
-          if (vi < nv) buf[x] = load16(row + vi * EPV);
+    for (int r = 0; r < R; ++r) {
+      float a = 0.f, s = 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        a = __fadd_rn(a, fabsf(qx[r][g]));
+        s = __fadd_rn(s, qx[r][g]);
+      }
+      kr[r] = order_key(a);
+      qb[r] = s;
+    }
+    wave_topk<R, 1024>(kr, D, k1, [&](int rank, int ch) {
+      float qv = qb[0];
+#pragma unroll
+      for (int r = 1; r < R; ++r)
+        if ((ch >> 6) == r) qv = qb[r];
+      i1_q[rank] = qv;
+      i1_off[rank] = qv >= 0.f ? ch : -1 - ch;  // the sign picks the Kmax or the Kmin row
+      if (chan_opt && blockIdx.x == 0) chan_opt[size_t(u) * k1 + rank] = ch;
+    }, hist);
+  }
+  if (ALL) {
+#pragma unroll
+    for (int x = 0; x < NBA; ++x) {
+      const int id = x * 256 + t;
+      if (id < 2 * D * nv) {
+        const int r = id / nv, vi = id % nv;
+        *reinterpret_cast<decltype(buf[x].raw)*>(stage + size_t(r) * ppw + vi * EPV) = buf[x].raw;
+      }
+    }
+  }
+  __syncthreads();
+  RK_PHASE(18);
+  uint32_t* ku = keys + size_t(u) * keys_pitch + p0;
+  if (ALL) {
+    // s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b], P_i read from the
+    // Kmax or Kmin row the sign picked; four channels' reads in flight before
+    // their ordered terms; no fused multiply-add.
+#pragma clang fp contract(off)
+    for (int b = t; b < np; b += 256) {
+      float acc = 0.f;
+      for (int j0 = 0; j0 < k1; j0 += 4) {
+        const int4 o4 = *reinterpret_cast<const int4*>(i1_off + j0);
+        const float4 q4 = *reinterpret_cast<const float4*>(i1_q + j0);
+        const int oo[4] = {o4.x, o4.y, o4.z, o4.w};
+        const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = oo[e] >= 0 ? oo[e] : D + (-1 - oo[e]);
+          pv[e] = j0 + e < k1 ? to_f32(stage[size_t(r) * ppw + b]) : 0.f;
         }
 #pragma unroll
-        for (int x = 0; x < NB; ++x) {
-          const int vi = v0 + x * groups;
-          if (vi < nv) {
-            const T* src = reinterpret_cast<const T*>(&buf[x].raw);
+        for (int e = 0; e < 4; ++e)
+          if (j0 + e < k1) acc = acc + qq[e] * pv[e];
+      }
+      ku[b] = order_key(acc);
+      if (s1_opt) s1_opt[size_t(u) * nblk + p0 + b] = acc;
+    }
+    RK_PHASE(20);
+    return;
+  }
+
+  // Staging: thread (channel j, vector slot) fetches 16-byte runs of row j
+  // (EPV consecutive pages; p0 and nblk_cap are multiples of 8, so runs stay
+  // aligned and inside the row) and scatters them transposed into LDS as
+  // stage[page][channel] (row pitch k1p: 16-channel blocks plus one vector of
+  // padding).  Scoring: s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b].
+  const int k1p = (k1 + 15) / 16 * 16 + EPV;
+  const int groups = 256 / k1;  // vector slots per channel (k1 <= 128)
+  if (t < groups * k1) {
+    const int j = t % k1;
+    const int off = i1_off[j];
+    const T* row = off >= 0 ? xu + size_t(off) * nblk_cap : nu + size_t(-1 - off) * nblk_cap;
+    constexpr int NB = 4;
+    for (int v0 = t / k1; v0 < nv; v0 += groups * NB) {
+      Vec16<T> buf[NB];
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) stage[size_t(vi * EPV + e) * k1p + j] = src[e];
-          }
+      for (int x = 0; x < NB; ++x) {
+        const int vi = v0 + x * groups;
+        if (vi < nv) buf[x] = load16(row + vi * EPV);
+      }
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        const int vi = v0 + x * groups;
+        if (vi < nv) {
+          const T* src = reinterpret_cast<const T*>(&buf[x].raw);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) stage[size_t(vi * EPV + e) * k1p + j] = src[e];
         }
       }
     }
-    __syncthreads();
-    RK_PHASE(9);
-    {
-      // Each thread scores up to 4 pages (b = t + 256 p) together.  Channels go
-      // in blocks of 16: the block's q_bar values come from LDS once (float4
-      // broadcasts) and each page's 16 staged values as 16-byte reads, so all
-      // reads of a block are in flight before the ordered multiply-adds.
-      // One rounded multiply and one rounded add per term: no fused multiply-add.
+  }
+  __syncthreads();
+  {
+    // Thread t scores pages b = t, t + 256, ...  Channels go in blocks of 16:
+    // the block's q_bar values come from LDS as float4 broadcasts and the
+    // page's 16 staged values as 16-byte reads, then the ordered terms.
+    // One rounded multiply and one rounded add per term: no fused multiply-add.
 #pragma clang fp contract(off)
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      const T* sp[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) sp[p] = stage + size_t(min(t + 256 * p, np - 1)) * k1p;
-      const int npp = np > t ? (np - t + 255) / 256 : 0;  // pages of this thread (<= 4 when np <= npc)
+    for (int b = t; b < np; b += 256) {
+      const T* sp = stage + size_t(b) * k1p;
+      float acc = 0.f;
       for (int j0 = 0; j0 < k1; j0 += 16) {
-        float qv[16];
+        float qv[16], sv[16];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const float4 q4 = *reinterpret_cast<const float4*>(i1_q + j0 + 4 * x);
@@ -130,57 +196,35 @@ __global__ __launch_bounds__(256) void hsa_select_kernel(
           qv[4 * x + 2] = q4.z;
           qv[4 * x + 3] = q4.w;
         }
-        float sv[4][16];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int x = 0; x < 16 / EPV; ++x) {
+          const Vec16<T> vv = load16(sp + j0 + x * EPV);
 #pragma unroll
-          for (int x = 0; x < 16 / EPV; ++x) {
-            const Vec16<T> vv = load16(sp[p] + j0 + x * EPV);
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) sv[p][x * EPV + e] = vv.get(e);
-          }
+          for (int e = 0; e < EPV; ++e) sv[x * EPV + e] = vv.get(e);
         }
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          if (p < npp) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (j0 + e < k1) acc[p] = acc[p] + qv[e] * sv[p][e];
-          }
-        }
+        for (int e = 0; e < 16; ++e)
+          if (j0 + e < k1) acc = acc + qv[e] * sv[e];
       }
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int b = t + 256 * p;
-        if (p < npp) {
-          page_keys[p0 + b] = order_key(acc[p]);
-          if (s1_opt) s1_opt[size_t(u) * nblk + p0 + b] = acc[p];
-        }
-      }
+      ku[b] = order_key(acc);
+      if (s1_opt) s1_opt[size_t(u) * nblk + p0 + b] = acc;
     }
-    __syncthreads();
-    RK_PHASE(10);
   }
-  int32_t* su = sel_ws + size_t(u) * nsel;
-  int32_t* so = sel_opt ? sel_opt + size_t(u) * nsel : nullptr;
-  wg_topk<256>(
-      [&](int i) { return page_keys[i]; }, nblk, nsel,
-      [&](int r, int i) {
-        su[r] = i;
-        if (so) so[r] = i;
-      },
-      sm);
 }
 
-// One workgroup = 4 waves; a wave streams whole pages.  Lanes split a row into
-// LPR 16-byte chunks, so SLOTS tokens are in flight per wave and each slot
-// takes TPS tokens per chunk before one softmax rescale.
+// Step 2b + step 3.  Every workgroup of a unit first takes the top-k2 of the
+// unit's page scores itself (the same radix select in each, so all agree;
+// ties toward the lower page, pages in ascending order) and keeps the pages
+// of its own split: this saves a launch and a memory round trip between the
+// choice and the K/V fetch.  Then 4 waves stream whole pages.  Lanes split a
+// row into LPR 16-byte chunks, so SLOTS tokens are in flight per wave and each
+// slot takes TPS tokens per chunk before one softmax rescale.
 template <typename T, int D, int G, bool MT>
 __global__ __launch_bounds__(256) void hsa_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
-    const int32_t* __restrict__ cand, int64_t cand_stride, const int32_t* __restrict__ sel,
-    int nsel, int pages_per_split, int n_split, int n_tokens, int block, float scale_log2,
-    float* __restrict__ partials) {
+    const int32_t* __restrict__ cand, int64_t cand_stride, const uint32_t* __restrict__ keys,
+    int keys_pitch, int nblk, int nsel, int pages_per_split, int n_split, int n_tokens,
+    int block, float scale_log2, float* __restrict__ partials, int32_t* __restrict__ sel_opt) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPR = D / EPL;
   constexpr int SLOTS = kWave / LPR;
@@ -191,6 +235,8 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   static_assert(kWave % LPR == 0, "row chunks must tile a wave");
   __shared__ float wm[NW][G], wl[NW][G];
   __shared__ __align__(16) float wo[NW][G][D];
+  __shared__ TopkSmem<256, 1024, 1> tsm;
+  extern __shared__ __align__(16) uint32_t attn_lds[];  // the split's pages, then (many pages) the keys
 
   const int u = blockIdx.y;
   const int split = blockIdx.x;
@@ -215,12 +261,38 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   const T* ku = k + size_t(u) * size_t(kv_cap) * D + c * EPL;
   const T* vu = v + size_t(u) * size_t(kv_cap) * D + c * EPL;
   const int32_t* cu = MT ? cand + size_t(u) * size_t(cand_stride) : nullptr;
-  const int32_t* su = sel + size_t(u) * nsel;
-  const int e0 = split * pages_per_split;
-  const int e1 = min(e0 + pages_per_split, nsel);
 
-  for (int e = e0 + wave; e < e1; e += NW) {
-    const int t0 = su[e] * block;
+  RK_PHASE(8);
+  int* pages = reinterpret_cast<int*>(attn_lds);  // [pages_per_split]
+  const int e0 = split * pages_per_split;
+  const int np = min(e0 + pages_per_split, nsel) - e0;
+  int32_t* so = sel_opt && split == 0 ? sel_opt + size_t(u) * nsel : nullptr;
+  const uint32_t* kg = keys + size_t(u) * keys_pitch;
+  auto emit = [&](int r, int i) {
+    if (r >= e0 && r < e0 + np) pages[r - e0] = i;
+    if (so) so[r] = i;
+  };
+  if (nblk <= kWaveTopkPages) {
+    // one wave selects from keys held in registers; no barrier inside
+    if (wave == 0) {
+      constexpr int RK = kWaveTopkPages / kWave;
+      uint32_t kr[RK];
+#pragma unroll
+      for (int r = 0; r < RK; ++r) kr[r] = r * kWave + lane < nblk ? kg[r * kWave + lane] : 0u;
+      wave_topk<RK, 1024>(kr, nblk, nsel, emit, tsm.hist[0]);
+    }
+  } else {
+    uint32_t* kl = attn_lds + pages_per_split;  // [keys_pitch]
+    for (int i = threadIdx.x; i < keys_pitch / 4; i += 256)
+      reinterpret_cast<uint4*>(kl)[i] = reinterpret_cast<const uint4*>(kg)[i];
+    __syncthreads();
+    wg_topk<256, 1024>([&](int i) { return kl[i]; }, nblk, nsel, emit, tsm);
+  }
+  __syncthreads();
+  RK_PHASE(10);
+
+  for (int e = wave; e < np; e += NW) {
+    const int t0 = pages[e] * block;
     const int t1 = min(t0 + block, n_tokens);
     for (int tc = t0; tc < t1; tc += CHUNK) {
       Vec16<T> kr[TPS], vr[TPS];
@@ -309,6 +381,7 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
     }
   }
   __syncthreads();
+  RK_PHASE(11);
   // merge the 4 waves in order and write this split's partial per head
   float* pu = partials + size_t(u) * n_split * G * PF;
   float* pw = pu + size_t(split) * G * PF;
@@ -400,34 +473,50 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   const int nblk = int((n_tokens + block - 1) / block);
   const DecodeWs lay = decode_ws_layout(d, nblk, k2);
   char* wsb = static_cast<char*>(ws);
-  int32_t* sel = reinterpret_cast<int32_t*>(wsb + lay.sel);
   float* part = reinterpret_cast<float*>(wsb + lay.partials);
   const int units = d.units();
 
-  // LDS of the select workgroup: page keys, then the staged aux slices
-  const size_t keys_bytes = (size_t((nblk + 3) & ~3) * 4 + 15) / 16 * 16;
-  const size_t stage_budget = kSelectLdsBudget - keys_bytes;
+  // Step 2a grid: page ranges of ppw pages (a multiple of 8, the staged
+  // slice within the LDS budget) so the launch has about 1024 workgroups, at
+  // least 16 pages each.  Launches whose full aux slices come to at most
+  // kScoreAllBytes fetch every channel's rows up front (ALL).
   constexpr int EPV = 16 / sizeof(T);
   const int k1p = (k1 + 15) / 16 * 16 + EPV;
-  int npc = int(stage_budget / (size_t(k1p) * sizeof(T))) / 8 * 8;
-  npc = npc > 1024 ? 1024 : npc;  // at most 4 pages per scoring thread
-  const int nblk8 = (nblk + 7) / 8 * 8;
-  npc = npc > nblk8 ? nblk8 : npc;
-  if (npc < 8) return hipErrorInvalidValue;
-  const size_t lds = keys_bytes + size_t(k1p) * npc * sizeof(T);
+  const int ppw_max = int(kSelectLdsBudget / (size_t(k1p) * sizeof(T))) / 8 * 8;
+  if (ppw_max < 8) return hipErrorInvalidValue;
+  int ppw = int((int64_t(nblk) * units + 1023) / 1024);
+  ppw = ppw < 16 ? 16 : ppw;
+  ppw = (ppw + 7) / 8 * 8;
+  ppw = ppw > ppw_max ? ppw_max : ppw;
+  // ALL also needs the range to come in one round of 8 vectors per thread
+  const bool all = size_t(2) * D * nblk * units * sizeof(T) <= kScoreAllBytes &&
+                   2 * D * (ppw / EPV) <= 256 * 8;
+  const int n_ranges = (nblk + ppw - 1) / ppw;
+  const size_t lds = (all ? size_t(2) * D : size_t(k1p)) * sizeof(T) * ppw;
   static bool attr_set = false;  // once per template instantiation
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&hsa_select_kernel<T, D, G>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       int(kSelectLdsBudget));
-    if (e != hipSuccess) return e;
+    for (const void* f : {reinterpret_cast<const void*>(&hsa_score_kernel<T, D, G, true>),
+                          reinterpret_cast<const void*>(&hsa_score_kernel<T, D, G, false>)}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         int(kSelectLdsBudget));
+      if (e != hipSuccess) return e;
+    }
     attr_set = true;
   }
-  RK_LAUNCH("hsa_select", (hsa_select_kernel<T, D, G>), dim3(units), dim3(256), lds, s,
-            static_cast<const T*>(q), static_cast<const T*>(kmax), static_cast<const T*>(kmin),
-            nblk_cap, nblk, k1, lay.nsel, npc, sel, sel_opt, chan_opt, s1_opt);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(wsb + lay.keys);
+  if (all)
+    RK_LAUNCH("hsa_score", (hsa_score_kernel<T, D, G, true>), dim3(n_ranges, units), dim3(256),
+              lds, s, static_cast<const T*>(q), static_cast<const T*>(kmax),
+              static_cast<const T*>(kmin), nblk_cap, nblk, k1, ppw, keys, lay.keys_pitch,
+              chan_opt, s1_opt);
+  else
+    RK_LAUNCH("hsa_score", (hsa_score_kernel<T, D, G, false>), dim3(n_ranges, units), dim3(256),
+              lds, s, static_cast<const T*>(q), static_cast<const T*>(kmax),
+              static_cast<const T*>(kmin), nblk_cap, nblk, k1, ppw, keys, lay.keys_pitch,
+              chan_opt, s1_opt);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if ((err = hipGetLastError()) != hipSuccess) return err;
 
   // split-K sizing: aim for ~2048 workgroups over the whole launch, at least
   // kMinPagesPerSplit pages (one per wave) and at most kMaxSplits splits per unit
@@ -437,18 +526,33 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   const int pps_cap = (lay.nsel + kMaxSplits - 1) / kMaxSplits;
   pps = pps < pps_cap ? pps_cap : pps;
   pps = (pps + 3) / 4 * 4;
+  const int nsel4 = (lay.nsel + 3) / 4 * 4;
+  pps = pps > nsel4 ? nsel4 : pps;
   const int n_split = (lay.nsel + pps - 1) / pps;
   const float scale_log2 = float(1.4426950408889634 / sqrt(double(D)));
+  const size_t attn_lds =
+      size_t(pps + (nblk > kWaveTopkPages ? lay.keys_pitch : 0)) * sizeof(uint32_t);  // <= 96 KB
+  static bool attn_attr_set = false;  // once per template instantiation
+  if (!attn_attr_set) {
+    for (const void* f : {reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, true>),
+                          reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, false>)}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         int(kAttnDynLds));
+      if (e != hipSuccess) return e;
+    }
+    attn_attr_set = true;
+  }
+  if (attn_lds > kAttnDynLds) return hipErrorInvalidValue;
   if (cand)
-    RK_LAUNCH("hsa_attn_mt", (hsa_attn_kernel<T, D, G, true>), dim3(n_split, units), dim3(256), 0,
-              s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-              kv_cap, cand, cand_stride, sel, lay.nsel, pps, n_split, int(n_tokens), block,
-              scale_log2, part);
+    RK_LAUNCH("hsa_attn_mt", (hsa_attn_kernel<T, D, G, true>), dim3(n_split, units), dim3(256),
+              attn_lds, s, static_cast<const T*>(q), static_cast<const T*>(k),
+              static_cast<const T*>(v), kv_cap, cand, cand_stride, keys, lay.keys_pitch, nblk,
+              lay.nsel, pps, n_split, int(n_tokens), block, scale_log2, part, sel_opt);
   else
-    RK_LAUNCH("hsa_attn", (hsa_attn_kernel<T, D, G, false>), dim3(n_split, units), dim3(256), 0,
-              s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-              kv_cap, cand, cand_stride, sel, lay.nsel, pps, n_split, int(n_tokens), block,
-              scale_log2, part);
+    RK_LAUNCH("hsa_attn", (hsa_attn_kernel<T, D, G, false>), dim3(n_split, units), dim3(256),
+              attn_lds, s, static_cast<const T*>(q), static_cast<const T*>(k),
+              static_cast<const T*>(v), kv_cap, cand, cand_stride, keys, lay.keys_pitch, nblk,
+              lay.nsel, pps, n_split, int(n_tokens), block, scale_log2, part, sel_opt);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   RK_LAUNCH("hsa_combine", (hsa_combine_kernel<D, G>), dim3((units * G + 3) / 4), dim3(256), 0, s,
             part, n_split, units, out);

@@ -80,176 +80,101 @@ __device__ __forceinline__ int clamp_row(int32_t row, int64_t cap) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts build the
+// sums inside each 16-lane row (zero fill at the row edge), then the totals of
+// the earlier rows come in through lane reads.  No LDS traffic.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane_id() >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+// Minimum / maximum of uint32 over the wave (DPP inside rows, lane reads across).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0xB1, 0xf, 0xf, false)));
+  x = min(x, uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0x4E, 0xf, 0xf, false)));
+  x = min(x, uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0x141, 0xf, 0xf, false)));
+  x = min(x, uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0x140, 0xf, 0xf, false)));
+  const uint32_t a = uint32_t(__builtin_amdgcn_readlane(int(x), 0));
+  const uint32_t b = uint32_t(__builtin_amdgcn_readlane(int(x), 16));
+  const uint32_t c = uint32_t(__builtin_amdgcn_readlane(int(x), 32));
+  const uint32_t d = uint32_t(__builtin_amdgcn_readlane(int(x), 48));
+  return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0xB1, 0xf, 0xf, false)));
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0x4E, 0xf, 0xf, false)));
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0x141, 0xf, 0xf, false)));
+  x = max(x, uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), 0x140, 0xf, 0xf, false)));
+  const uint32_t a = uint32_t(__builtin_amdgcn_readlane(int(x), 0));
+  const uint32_t b = uint32_t(__builtin_amdgcn_readlane(int(x), 16));
+  const uint32_t c = uint32_t(__builtin_amdgcn_readlane(int(x), 32));
+  const uint32_t d = uint32_t(__builtin_amdgcn_readlane(int(x), 48));
+  return max(max(a, b), max(c, d));
+}
+
 // Exclusive prefix sum of v over the workgroup (NT threads, wave64).  `tmp`
-// must hold NT/64 + 1 ints of LDS.  Returns the exclusive prefix; *total gets
-// the workgroup sum.  Contains barriers: every thread must call it.
+// must hold 2*(NT/64) + 2 ints of LDS.  Returns the exclusive prefix; *total
+// gets the workgroup sum.  Every thread reads the wave totals itself (no
+// serial pass).  Contains barriers: every thread must call it.
 template <int NT>
 __device__ __forceinline__ int wg_excl_scan(int v, int* tmp, int* total) {
-  const int lane = lane_id();
+  constexpr int NW = NT / kWave;
   const int wave = threadIdx.x / kWave;
-  int x = v;
+  const int x = wave_incl_scan(v);
+  if (lane_id() == kWave - 1) tmp[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int t = __shfl_up(x, off);
-    if (lane >= off) x += t;
+  for (int w = 0; w < NW; ++w) {
+    const int c = tmp[w];
+    before += w < wave ? c : 0;
+    all += c;
   }
-  if (lane == kWave - 1) tmp[wave] = x;
+  *total = all;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < NT / kWave; ++w) {
-      const int t = tmp[w];
-      tmp[w] = run;
-      run += t;
-    }
-    tmp[NT / kWave] = run;
-  }
-  __syncthreads();
-  const int res = tmp[wave] + x - v;
-  *total = tmp[NT / kWave];
-  __syncthreads();
-  return res;
+  return before + x - v;
 }
 
 // Exclusive prefix sums of a pair (a, b) over the workgroup in one pass.
 template <int NT>
 __device__ __forceinline__ int2 wg_excl_scan2(int a, int b, int* tmp) {
-  const int lane = lane_id();
+  constexpr int NW = NT / kWave;
   const int wave = threadIdx.x / kWave;
-  int xa = a, xb = b;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int ta = __shfl_up(xa, off);
-    const int tb = __shfl_up(xb, off);
-    if (lane >= off) {
-      xa += ta;
-      xb += tb;
-    }
-  }
-  if (lane == kWave - 1) {
+  const int xa = wave_incl_scan(a);
+  const int xb = wave_incl_scan(b);
+  if (lane_id() == kWave - 1) {
     tmp[2 * wave] = xa;
     tmp[2 * wave + 1] = xb;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int ra = 0, rb = 0;
-    for (int w = 0; w < NT / kWave; ++w) {
-      const int ta = tmp[2 * w], tb = tmp[2 * w + 1];
-      tmp[2 * w] = ra;
-      tmp[2 * w + 1] = rb;
-      ra += ta;
-      rb += tb;
+  int ba = 0, bb = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) {
+      ba += tmp[2 * w];
+      bb += tmp[2 * w + 1];
     }
   }
   __syncthreads();
-  const int2 res = make_int2(tmp[2 * wave] + xa - a, tmp[2 * wave + 1] + xb - b);
-  __syncthreads();
-  return res;
+  return make_int2(ba + xa - a, bb + xb - b);
 }
 
-// Exclusive prefix count of a predicate over the workgroup (ballot based).
-template <int NT>
-__device__ __forceinline__ int wg_excl_count(bool p, int* tmp, int* total) {
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const unsigned long long b = __ballot(p);
-  const int below = __popcll(b & ((1ull << lane) - 1ull));
-  if (lane == 0) tmp[wave] = __popcll(b);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < NT / kWave; ++w) {
-      const int t = tmp[w];
-      tmp[w] = run;
-      run += t;
-    }
-    tmp[NT / kWave] = run;
-  }
-  __syncthreads();
-  const int res = tmp[wave] + below;
-  *total = tmp[NT / kWave];
-  __syncthreads();
-  return res;
-}
-
-template <int NT>
-struct TopkSmem {
-  static constexpr int kBins = 2048;
-  uint32_t hist[kBins];
-  int tmp[2 * (NT / kWave) + 2];
-  int found[2];
-};
-
-// Workgroup top-k: calls emit(rank, position) for the k largest keys among
-// key(0..n-1), ties broken toward the lower position; ranks 0..k-1 follow
-// ascending position order.  Selected <=> #{i : key_i > key_j or (key_i == key_j and
-// i < j)} < k.  Radix select over 11/11/10-bit digits finds the exact k-th
-// key T and how many keys equal to T are taken; an ordered scan then writes
-// the selection.  0 <= k <= n.  All threads of the workgroup must call it.
+// Ordered emission of a top-k: with the threshold key T, every key above it
+// is taken and `need_eq` of the keys equal to it, lowest positions first.  Thread t owns the contiguous
+// positions [t*seg, (t+1)*seg): it counts its keys above and equal to T, one
+// workgroup scan gives the counts before it, then it emits its selected
+// positions in order.
 template <int NT, typename KeyFn, typename EmitFn>
-__device__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit, TopkSmem<NT>& sm) {
+__device__ __forceinline__ void wg_topk_emit(const KeyFn& key, int n, uint32_t T, int need_eq,
+                                             const EmitFn& emit, int* tmp) {
   const int t = threadIdx.x;
-  if (k <= 0) return;
-  if (k >= n) {
-    for (int i = t; i < n; i += NT) emit(i, i);
-    return;
-  }
-  uint32_t prefix = 0, mask = 0;
-  int need = k;  // keys still to take among those matching `prefix`
-  constexpr int kShift[3] = {21, 10, 0};
-  constexpr int kBits[3] = {11, 11, 10};
-  constexpr int kPer = TopkSmem<NT>::kBins / NT;  // bins owned by one thread
-  static_assert(kPer >= 1 && TopkSmem<NT>::kBins % NT == 0, "bins per thread");
-  // Histogram order: lane l of every wave walks the run [l*rows, (l+1)*rows)
-  // (rows odd), so the 64 lanes of one instruction touch keys far apart.
-  // Neighbouring keys are often nearly equal (pooled scores), and a wave whose
-  // lanes all hit one bin would serialise its LDS atomics.
-  const int rows = ((n + kWave - 1) / kWave) | 1;
-  const int lane = lane_id();
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = kShift[pass];
-    const uint32_t dmask = (1u << kBits[pass]) - 1u;
-    for (int b = t; b < TopkSmem<NT>::kBins; b += NT) sm.hist[b] = 0u;
-    __syncthreads();
-    for (int c = t / kWave; c < rows; c += NT / kWave) {
-      const int i = lane * rows + c;
-      if (i < n) {
-        const uint32_t kk = key(i);
-        if ((kk & mask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & dmask], 1u);
-      }
-    }
-    __syncthreads();
-    RK_PHASE(1 + pass);
-    // Thread t owns bins [top - (t+1)*kPer, top - t*kPer): thread 0 the highest.
-    const int hi = TopkSmem<NT>::kBins - t * kPer;
-    int own = 0;
-#pragma unroll
-    for (int j = 1; j <= kPer; ++j) own += int(sm.hist[hi - j]);
-    int total;
-    int above = wg_excl_scan<NT>(own, sm.tmp, &total);
-#pragma unroll
-    for (int j = 1; j <= kPer; ++j) {
-      const int c = int(sm.hist[hi - j]);
-      if (above < need && above + c >= need) {
-        sm.found[0] = hi - j;
-        sm.found[1] = need - above;
-      }
-      above += c;
-    }
-    __syncthreads();
-    prefix |= uint32_t(sm.found[0]) << shift;
-    mask |= dmask << shift;
-    need = sm.found[1];
-    __syncthreads();
-  }
-  // prefix == T (the k-th largest key); take `need` of the keys equal to T,
-  // lowest positions first, and every key above T.  Thread t owns the
-  // contiguous positions [t*seg, (t+1)*seg): it counts its keys above and
-  // equal to T, one workgroup scan gives the counts before it, then it emits
-  // its selected positions in order.
-  const uint32_t T = prefix;
-  const int need_eq = need;
   const int seg = ((n + NT - 1) / NT) | 1;  // odd: spreads LDS banks
   const int lo = min(t * seg, n);
   const int hi = min(lo + seg, n);
@@ -259,8 +184,8 @@ __device__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit, Topk
     n_gt += kk > T;
     n_eq += kk == T;
   }
-  RK_PHASE(4);
-  const int2 before = wg_excl_scan2<NT>(n_gt, n_eq, sm.tmp);
+  RK_PHASE(6);
+  const int2 before = wg_excl_scan2<NT>(n_gt, n_eq, tmp);
   int eq_seen = before.y;
   int pos = before.x + min(before.y, need_eq);
   for (int i = lo; i < hi; ++i) {
@@ -272,59 +197,271 @@ __device__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit, Topk
     }
     if (sel) emit(pos++, i);
   }
-  RK_PHASE(5);
+  RK_PHASE(7);
 }
 
-// Workgroup top-k for a small key set held in LDS (n up to a few thousand):
-// element j is selected iff #{i : key_i > key_j or (key_i == key_j and
-// i < j)} < k, counted directly (4 keys per LDS read, broadcast to the wave);
-// emit(rank, j) in ascending j order as wg_topk.  `keys` must be 16-byte
-// aligned with room for n rounded up to 4 (the padding is never counted).
-template <int NT, typename EmitFn>
-__device__ void wg_topk_rank(const uint32_t* keys, int n, int k, const EmitFn& emit, int* tmp) {
+// Workgroup top-k: calls emit(rank, position) for the k largest keys among
+// key(0..n-1), ties broken toward the lower position; ranks 0..k-1 follow
+// ascending position order.  Selected <=> #{i : key_i > key_j or (key_i ==
+// key_j and i < j)} < k.  0 <= k <= n; all threads of the workgroup call it,
+// and emitted results are complete after the caller's next barrier.
+//
+// Range-adaptive radix select.  A pass buckets the candidate keys, those in
+// [lo, hi], by (key - lo) >> shift, with shift chosen so the candidates' span
+// fills the BINS bins (the first pass takes lo, hi = min, max of all keys):
+// keys close in value still spread over many bins, so the LDS atomics rarely
+// collide and the boundary bin usually holds one or two keys.  Every wave
+// then finds the bin of the k-th largest key from the histogram by itself
+// (no barrier): keys above it are taken, keys below dropped.  It ends when the
+// boundary bin is one key value or is taken whole, after one pass in most
+// cases; each pass narrows the span by a factor BINS, so at most
+// ceil(32 / log2(BINS)) passes.  With NBUF = 2 histograms alternate between
+// two buffers so a pass needs two barriers; NBUF = 1 saves the LDS for a
+// third barrier per pass after the first.
+template <int NT, int BINS, int NBUF = 2>
+struct TopkSmem {
+  uint32_t hist[NBUF][BINS];
+  uint32_t red[2 * (NT / kWave)];
+  int tmp[2 * (NT / kWave) + 2];
+};
+
+// The bin holding the need-th largest key, counting from the top bin, and
+// how many keys it holds and are still needed from it.  Lane l reads bins
+// [BINS - (l+1)*BPL, BINS - l*BPL); a wave scan gives the count above each
+// lane, the lane that crosses `need` walks its bins.  Wave-uniform result.
+template <int BINS>
+__device__ __forceinline__ int3 wave_find_bin(const uint32_t* hist, int need) {
+  constexpr int BPL = BINS / kWave;
+  static_assert(BPL % 4 == 0, "bins per lane");
+  const int lane = lane_id();
+  const int base = BINS - (lane + 1) * BPL;
+  uint32_t c[BPL];
+#pragma unroll
+  for (int j = 0; j < BPL; j += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hist + base + j);
+    c[j] = v.x;
+    c[j + 1] = v.y;
+    c[j + 2] = v.z;
+    c[j + 3] = v.w;
+  }
+  int own = 0;
+#pragma unroll
+  for (int j = 0; j < BPL; ++j) own += int(c[j]);
+  const int incl = wave_incl_scan(own);
+  int above = incl - own;
+  const unsigned long long hit = __ballot(above < need && incl >= need);
+  const int L = __ffsll(static_cast<long long>(hit)) - 1;
+  int bin = 0, nin = 0, cnt = 0;
+#pragma unroll
+  for (int j = BPL - 1; j >= 0; --j) {
+    const int cj = int(c[j]);
+    if (above < need && above + cj >= need) {
+      bin = base + j;
+      nin = need - above;
+      cnt = cj;
+    }
+    above += cj;
+  }
+  return make_int3(__builtin_amdgcn_readlane(bin, L), __builtin_amdgcn_readlane(nin, L),
+                   __builtin_amdgcn_readlane(cnt, L));
+}
+
+// Ordered emission by one wave (n small): 64 positions per step, ballots give
+// each selected position its rank and each equal key its order among equals.
+template <typename KeyFn, typename EmitFn>
+__device__ __forceinline__ void wave_topk_emit(const KeyFn& key, int n, uint32_t T, int need_eq,
+                                               const EmitFn& emit) {
+  const int lane = lane_id();
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int base = 0, eq_seen = 0;
+#pragma unroll 2
+  for (int c0 = 0; c0 < n; c0 += kWave) {
+    const int i = c0 + lane;
+    const uint32_t kk = i < n ? key(i) : 0u;
+    const bool eq = i < n && kk == T;
+    const unsigned long long em = __ballot(eq);
+    const bool sel = (i < n && kk > T) || (eq && eq_seen + __popcll(em & below) < need_eq);
+    const unsigned long long sm = __ballot(sel);
+    if (sel) emit(base + __popcll(sm & below), i);
+    base += __popcll(sm);
+    eq_seen += __popcll(em);
+  }
+}
+
+// Top-k by one wave over n <= 64*R keys held in registers: lane l holds the
+// key of position l + 64 r in kr[r] (positions >= n are ignored).  Same
+// selection, emission order and range-adaptive passes as wg_topk, but the
+// histogram (BINS words of LDS) belongs to the wave alone and LDS operations
+// of one wave complete in order, so no barrier is needed anywhere: the
+// histogram is read right after its atomics.  Emission takes the 64-position
+// rows in order with ballots.
+template <int R, int BINS, typename EmitFn>
+__device__ void wave_topk(const uint32_t (&kr)[R], int n, int k, const EmitFn& emit,
+                          uint32_t* hist) {
+  constexpr int LOG_BINS = BINS == 256 ? 8 : BINS == 512 ? 9 : BINS == 1024 ? 10 : 11;
+  static_assert((1 << LOG_BINS) == BINS && BINS <= 2048 && BINS >= 256, "bins");
+  const int lane = lane_id();
+  if (k <= 0) return;
+  if (k >= n) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r * kWave + lane < n) emit(r * kWave + lane, r * kWave + lane);
+    return;
+  }
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r * kWave + lane < n) {
+      lo = min(lo, kr[r]);
+      hi = max(hi, kr[r]);
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  int need = k;
+  uint32_t T;
+  int need_eq;
+#pragma unroll 1
+  while (true) {
+    if (lo == hi) {
+      T = lo;
+      need_eq = need;
+      break;
+    }
+    const int span_bits = 32 - __clz(int(hi - lo));
+    const int shift = span_bits > LOG_BINS ? span_bits - LOG_BINS : 0;
+#pragma unroll
+    for (int j = 0; j < BINS / kWave; j += 4)
+      *reinterpret_cast<uint4*>(hist + lane * (BINS / kWave) + j) = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t kk = kr[r];
+      if (r * kWave + lane < n && kk >= lo && kk <= hi) atomicAdd(&hist[(kk - lo) >> shift], 1u);
+    }
+    const int3 f = wave_find_bin<BINS>(hist, need);
+    const uint32_t blo = lo + (uint32_t(f.x) << shift);
+    if (shift == 0) {
+      T = blo;
+      need_eq = f.y;
+      break;
+    }
+    if (f.y == f.z) {  // whole bin taken: every key >= blo (blo > 0 as in wg_topk)
+      T = blo - 1u;
+      need_eq = 0;
+      break;
+    }
+    const uint64_t bhi = uint64_t(blo) + ((uint64_t(1) << shift) - 1u);
+    hi = bhi < uint64_t(hi) ? uint32_t(bhi) : hi;
+    lo = blo;
+    need = f.y;
+  }
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = r * kWave + lane;
+    const uint32_t kk = kr[r];
+    const bool eq = i < n && kk == T;
+    const unsigned long long em = __ballot(eq);
+    const bool sel = (i < n && kk > T) || (eq && eq_seen + __popcll(em & below) < need_eq);
+    const unsigned long long sm = __ballot(sel);
+    if (sel) emit(base + __popcll(sm & below), i);
+    base += __popcll(sm);
+    eq_seen += __popcll(em);
+  }
+}
+
+// Most keys one wave emits; above it the workgroup emits (scan based).
+constexpr int kWaveEmitMax = 4096;
+
+template <int NT, int BINS, int NBUF, typename KeyFn, typename EmitFn>
+__device__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit,
+                        TopkSmem<NT, BINS, NBUF>& sm) {
+  constexpr int NW = NT / kWave;
+  constexpr int LOG_BINS = BINS == 256 ? 8 : BINS == 512 ? 9 : BINS == 1024 ? 10 : 11;
+  static_assert(BINS % NT == 0 || NT % BINS == 0, "bins");
+  static_assert((1 << LOG_BINS) == BINS && BINS <= 2048 && BINS >= 256, "bins");
   const int t = threadIdx.x;
+  const int wave = t / kWave;
+  const int lane = lane_id();
   if (k <= 0) return;
   if (k >= n) {
     for (int i = t; i < n; i += NT) emit(i, i);
     return;
   }
-  const int n4 = n & ~3;
-  int base = 0;
-  for (int c0 = 0; c0 < n; c0 += NT) {
-    const int j = c0 + t;
-    bool sel = false;
-    if (j < n) {
-      const uint32_t kj = keys[j];
-      int rank = 0;
-      const int n32 = n & ~31;
-      int i = 0;
-      for (; i < n32; i += 32) {  // eight 16-byte LDS reads in flight
-        uint4 kk[8];
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = t; i < n; i += NT) {
+    const uint32_t kk = key(i);
+    lo = min(lo, kk);
+    hi = max(hi, kk);
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) {
+    sm.red[wave] = lo;
+    sm.red[NW + wave] = hi;
+  }
+  for (int b = t; b < BINS; b += NT) sm.hist[0][b] = 0u;
+  __syncthreads();
 #pragma unroll
-        for (int x = 0; x < 8; ++x) kk[x] = *reinterpret_cast<const uint4*>(keys + i + 4 * x);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int b = i + 4 * x;
-          rank += int(kk[x].x > kj || (kk[x].x == kj && b < j));
-          rank += int(kk[x].y > kj || (kk[x].y == kj && b + 1 < j));
-          rank += int(kk[x].z > kj || (kk[x].z == kj && b + 2 < j));
-          rank += int(kk[x].w > kj || (kk[x].w == kj && b + 3 < j));
-        }
-      }
-      for (; i < n4; i += 4) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(keys + i);
-        rank += int(kk.x > kj || (kk.x == kj && i < j));
-        rank += int(kk.y > kj || (kk.y == kj && i + 1 < j));
-        rank += int(kk.z > kj || (kk.z == kj && i + 2 < j));
-        rank += int(kk.w > kj || (kk.w == kj && i + 3 < j));
-      }
-      for (; i < n; ++i) rank += int(keys[i] > kj || (keys[i] == kj && i < j));
-      sel = rank < k;
+  for (int w = 0; w < NW; ++w) {
+    lo = min(lo, sm.red[w]);
+    hi = max(hi, sm.red[NW + w]);
+  }
+  int need = k;  // keys still to take among the candidates [lo, hi]
+  uint32_t T;    // threshold: keys above are taken, need_eq of the keys equal to it
+  int need_eq;
+  // histogram order: lane l of a wave walks an odd-length run of positions,
+  // so one instruction's lanes touch keys far apart
+  const int rows = ((n + kWave - 1) / kWave) | 1;
+#pragma unroll 1
+  for (int pass = 0;; ++pass) {
+    if (lo == hi) {  // every candidate has one value
+      T = lo;
+      need_eq = need;
+      break;
     }
-    int tot;
-    const int pos = base + wg_excl_count<NT>(sel, tmp, &tot);
-    if (sel) emit(pos, j);
-    base += tot;
+    const int span_bits = 32 - __clz(int(hi - lo));
+    const int shift = span_bits > LOG_BINS ? span_bits - LOG_BINS : 0;
+    uint32_t* h = sm.hist[pass % NBUF];
+    if (pass > 0) {
+      if (NBUF == 1) __syncthreads();  // every wave has read the last histogram
+      for (int b = t; b < BINS; b += NT) h[b] = 0u;
+      __syncthreads();
+    }
+    for (int c = wave; c < rows; c += NW) {
+      const int i = lane * rows + c;
+      if (i < n) {
+        const uint32_t kk = key(i);
+        if (kk >= lo && kk <= hi) atomicAdd(&h[(kk - lo) >> shift], 1u);
+      }
+    }
+    __syncthreads();
+    RK_PHASE(12);
+    const int3 f = wave_find_bin<BINS>(h, need);
+    const uint32_t blo = lo + (uint32_t(f.x) << shift);
+    if (shift == 0) {  // the boundary bin is one key value
+      T = blo;
+      need_eq = f.y;
+      break;
+    }
+    if (f.y == f.z) {
+      // the whole bin is taken: the selection is every key >= blo (keys above
+      // the candidate interval were taken by earlier passes).  blo > 0 here,
+      // since blo == 0 would take all n keys while k < n.
+      T = blo - 1u;
+      need_eq = 0;
+      break;
+    }
+    const uint64_t bhi = uint64_t(blo) + ((uint64_t(1) << shift) - 1u);
+    hi = bhi < uint64_t(hi) ? uint32_t(bhi) : hi;
+    lo = blo;
+    need = f.y;
+  }
+  if (n <= kWaveEmitMax) {
+    if (wave == 0) wave_topk_emit(key, n, T, need_eq, emit);
+  } else {
+    wg_topk_emit<NT>(key, n, T, need_eq, emit, sm.tmp);
   }
 }
 

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
                                                       int W, int n_keep, int staged,
                                                       int32_t* __restrict__ kept) {
   extern __shared__ uint32_t skeys[];
-  __shared__ TopkSmem<1024> sm;
+  __shared__ TopkSmem<1024, 2048, 1> sm;
   const int u = blockIdx.x;
   const int P = S - W;
   const float* pu = pooled + size_t(u) * P;
@@ -252,9 +252,9 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
     }
     for (int i = 4 * P4 + threadIdx.x; i < P; i += 1024) skeys[i] = order_key(pu[i]);
     __syncthreads();
-    wg_topk<1024>([&](int i) { return skeys[i]; }, P, n_keep - W, emit, sm);
+    wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, P, n_keep - W, emit, sm);
   } else {
-    wg_topk<1024>([&](int i) { return order_key(pu[i]); }, P, n_keep - W, emit, sm);
+    wg_topk<1024, 2048>([&](int i) { return order_key(pu[i]); }, P, n_keep - W, emit, sm);
   }
   for (int r = threadIdx.x; r < W; r += 1024) ku[n_keep - W + r] = P + r;
 }

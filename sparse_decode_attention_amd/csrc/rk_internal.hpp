@@ -20,8 +20,17 @@ constexpr int kMaxSplits = 64;
 // Stage-1 selection keeps the order keys of up to this many bytes in LDS
 // (160 KB per workgroup on gfx950, minus the radix histogram and scan space).
 constexpr size_t kSelectKeysLds = 160 * 1024 - 10 * 1024;
-// LDS budget of the page-selection workgroup (gfx950: 160 KB per workgroup).
+// LDS budget of the page-scoring workgroup (gfx950: 160 KB per workgroup).
 constexpr size_t kSelectLdsBudget = 160 * 1024 - 16 * 1024;
+// Page scoring fetches every channel's Kmax and Kmin rows (not only the k1
+// chosen ones) when they total at most this many bytes over the launch.
+constexpr size_t kScoreAllBytes = size_t(8) << 20;
+// Up to this many pages the attention workgroup's page top-k runs in one
+// wave from registers (a multiple of 64).
+constexpr int kWaveTopkPages = 1024;
+// Dynamic LDS of an attention workgroup at most: the unit's page keys and the
+// pages of its split, kMaxPages 4-byte entries each.
+constexpr size_t kAttnDynLds = size_t(2 * kMaxPages) * 4;
 
 struct Dims {
   int B, Hq, Hkv, G, D;
@@ -54,17 +63,18 @@ inline EvictWs evict_ws_layout(const Dims& d, int64_t S, int W) {
 inline int partial_floats(int D) { return D + 4; }
 
 struct DecodeWs {
-  size_t sel, partials, total;
-  int n_split_max, nsel;
+  size_t keys, partials, total;
+  int n_split_max, nsel, keys_pitch;
 };
 inline DecodeWs decode_ws_layout(const Dims& d, int64_t nblk, int k2) {
   DecodeWs w{};
   w.nsel = int(nblk < k2 ? nblk : k2);
+  w.keys_pitch = int((nblk + 3) & ~int64_t(3));
   const int by_pages = (w.nsel + kMinPagesPerSplit - 1) / kMinPagesPerSplit;
   w.n_split_max = by_pages < kMaxSplits ? by_pages : kMaxSplits;
   const size_t u = size_t(d.units());
   size_t off = 0;
-  w.sel = off;      off += align256(u * w.nsel * sizeof(int32_t));
+  w.keys = off;     off += align256(u * size_t(w.keys_pitch) * sizeof(uint32_t));
   w.partials = off; off += align256(u * w.n_split_max * d.G * partial_floats(d.D) * sizeof(float));
   w.total = off;
   return w;

@@ -250,7 +250,7 @@ def test_kernel_timing_hooks(rk):
     rk.rk_hsa_decode(q, kc, vc, kmax, kmin, 512, 16, 16, 4, out)
     prof = rk.rk_profile_end()
     assert prof["aux_build"][0] == 3 and prof["aux_build"][1] > 0
-    assert set(prof) == {"aux_build", "hsa_select", "hsa_attn", "hsa_combine"}
+    assert set(prof) == {"aux_build", "hsa_score", "hsa_attn", "hsa_combine"}
     assert rk.rk_profile_end() == {}
 
 
