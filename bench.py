@@ -43,7 +43,24 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="issue every call eagerly instead of graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (scales the HBM byte "
+                         "counters FETCH_SIZE / WRITE_SIZE of a profiler run)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy kernel of known size: reads and writes mib MiB per launch."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}),
+          flush=True)
 
 
 def log(*a):
@@ -114,6 +131,10 @@ class Path:
             "hsa_attn": units * nsel * w.block * 2 * d * esize + B * Hq * d * esize,
             "hsa_attn_mt": units * nsel * w.block * (2 * d * esize + 4) + B * Hq * d * esize,
             "hsa_score": units * w.k1 * nb0 * esize + B * Hq * d * esize,
+            "hsa_fused": units * w.k1 * nb0 * esize + units * nsel * w.block * 2 * d * esize
+            + B * Hq * d * esize,
+            "hsa_fused_mt": units * w.k1 * nb0 * esize + units * nsel * w.block * (2 * d * esize + 4)
+            + B * Hq * d * esize,
             "aux_build": units * self.n_keep * d * esize + 2 * units * d * nb0 * esize,
             "gather_kv": 2 * 2 * units * self.n_keep * d * esize,
             "ws_pass1": units * self.S * d * esize + B * Hq * w.window * d * esize,
@@ -154,6 +175,9 @@ class Path:
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (the hot path shards over (batch, KV head) "
               f"units with no exchange; multi-GPU runs are not part of it); got --gpus {args.gpus}",
@@ -237,9 +261,11 @@ def main():
     if dominant in p.alg:
         achieved = p.alg[dominant] / (avg_ms * 1e-3) / 1e9
         roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dominant, w.name),
                 "bytes_per_launch": p.alg[dominant], "avg_launch_us": round(avg_ms * 1e3, 3)}
-    attn_name = "hsa_attn_mt" if p.mt else "hsa_attn"
+    attn_name = next((n for n in ("hsa_fused_mt", "hsa_fused", "hsa_attn_mt", "hsa_attn") if n in per_step),
+                     "hsa_attn")
     attn_avg = per_step.get(attn_name, (0, 0, float("nan")))[2]
     attn_gbps = p.alg[attn_name] / (attn_avg * 1e-3) / 1e9 if attn_avg == attn_avg else None
     ws1 = per_step.get("ws_pass1", (0, 0, float("nan")))[2]
@@ -277,6 +303,32 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter
+    summary (profiles/hbm_traffic_counters.md), or None when there is no row or
+    the kernel's sources have changed since the counters were taken."""
+    import hashlib
+    import os
+
+    # timing-hook names -> kernel function names (the MT variants share the function)
+    kernel = {"hsa_attn_mt": "hsa_attn", "hsa_fused_mt": "hsa_fused", "select_tokens": "select",
+              "gather_kv": "gather"}.get(kernel, kernel)
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "hbm_traffic_counters.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) != 8 or cells[0] != kernel or cells[1] != workload:
+            continue
+        h = hashlib.sha256()
+        for n in ("rk_device.hpp", "rk_internal.hpp", cells[6]):
+            with open(os.path.join(root, "sparse_decode_attention_amd", "csrc", n), "rb") as f:
+                h.update(f.read())
+        return round(float(cells[5]) * 1e6) if h.hexdigest()[:12] == cells[7] else None
+    return None
 
 
 def cpu_baseline(w, p, budget_s):

@@ -26,6 +26,123 @@
 namespace rk {
 namespace {
 
+// ---- step 2 building blocks --------------------------------------------------
+// Staging: thread (channel j, vector slot) of NT fetches 16-byte runs of the
+// sign-selected aux row of i1[j] (EPV consecutive pages; xu/nu point at the
+// first page of the range, a multiple of 8, and nblk_cap is a multiple of 8,
+// so runs stay aligned and inside the row) and scatters them transposed into
+// LDS as stage[page][channel] with row pitch k1p (16-channel blocks plus one
+// vector of padding).  All of a thread's loads are in flight together.
+template <typename T>
+__device__ __forceinline__ int staged_pitch(int k1) {
+  return (k1 + 15) / 16 * 16 + int(16 / sizeof(T));
+}
+template <typename T, int NT>
+__device__ __forceinline__ void stage_rows(const T* xu, const T* nu, int64_t nblk_cap, int np,
+                                           int k1, const int* i1_off, T* stage) {
+  constexpr int EPV = 16 / sizeof(T);
+  const int t = threadIdx.x;
+  const int k1p = staged_pitch<T>(k1);
+  const int groups = NT / k1;  // vector slots per channel (k1 <= 128 <= NT / 2)
+  const int nv = (np + EPV - 1) / EPV;
+  if (t >= groups * k1) return;
+  const int j = t % k1;
+  const int off = i1_off[j];
+  const T* row = off >= 0 ? xu + size_t(off) * nblk_cap : nu + size_t(-1 - off) * nblk_cap;
+  constexpr int NB = 4;
+  for (int v0 = t / k1; v0 < nv; v0 += groups * NB) {
+    Vec16<T> buf[NB];
+#pragma unroll
+    for (int x = 0; x < NB; ++x) {
+      const int vi = v0 + x * groups;
+      if (vi < nv) buf[x] = load16(row + vi * EPV);
+    }
+#pragma unroll
+    for (int x = 0; x < NB; ++x) {
+      const int vi = v0 + x * groups;
+      if (vi < nv) {
+        const T* src = reinterpret_cast<const T*>(&buf[x].raw);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) stage[size_t(vi * EPV + e) * k1p + j] = src[e];
+      }
+    }
+  }
+}
+
+// Scoring of staged pages: s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b],
+// thread t taking pages b = t, t + NT, ...  Channels go in blocks of 16: the
+// block's q_bar values come from LDS as float4 broadcasts and the page's 16
+// staged values as 16-byte reads, then the ordered terms, each one rounded
+// multiply and one rounded add (no fused multiply-add).  Writes order keys to
+// keys[b] and, when s1 is given, the scores to s1[b].
+template <typename T, int NT>
+__device__ __forceinline__ void score_staged(const T* stage, int np, int k1, const float* i1_q,
+                                             uint32_t* keys, float* s1) {
+#pragma clang fp contract(off)
+  constexpr int EPV = 16 / sizeof(T);
+  const int k1p = staged_pitch<T>(k1);
+  for (int b = threadIdx.x; b < np; b += NT) {
+    const T* sp = stage + size_t(b) * k1p;
+    float acc = 0.f;
+    for (int j0 = 0; j0 < k1; j0 += 16) {
+      float qv[16], sv[16];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float4 q4 = *reinterpret_cast<const float4*>(i1_q + j0 + 4 * x);
+        qv[4 * x] = q4.x;
+        qv[4 * x + 1] = q4.y;
+        qv[4 * x + 2] = q4.z;
+        qv[4 * x + 3] = q4.w;
+      }
+#pragma unroll
+      for (int x = 0; x < 16 / EPV; ++x) {
+        const Vec16<T> vv = load16(sp + j0 + x * EPV);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) sv[x * EPV + e] = vv.get(e);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (j0 + e < k1) acc = acc + qv[e] * sv[e];
+    }
+    keys[b] = order_key(acc);
+    if (s1) s1[b] = acc;
+  }
+}
+
+// Channel choice of HSA step 2 by one wave (wave 0 of the caller): group sums
+// of |q| and q per channel (g ascending, float32), top-k1 channels with ties
+// toward the lower channel, in ascending channel order.  Writes i1_q[rank] =
+// q_bar of the channel, i1_off[rank] = ch if q_bar >= 0 (Kmax row) else
+// -1 - ch (Kmin row), and chan_out[rank] = ch when chan_out is given.
+template <typename T, int D, int G>
+__device__ __forceinline__ void wave_choose_channels(const float (&qx)[D / kWave][G], int k1,
+                                                     float* i1_q, int* i1_off, int32_t* chan_out,
+                                                     uint32_t* hist) {
+  constexpr int R = D / kWave;
+  float qb[R];
+  uint32_t kr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float a = 0.f, s = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      a = __fadd_rn(a, fabsf(qx[r][g]));
+      s = __fadd_rn(s, qx[r][g]);
+    }
+    kr[r] = order_key(a);
+    qb[r] = s;
+  }
+  wave_topk<R, 1024>(kr, D, k1, [&](int rank, int ch) {
+    float qv = qb[0];  // the emitting lane holds the channel's q_bar
+#pragma unroll
+    for (int r = 1; r < R; ++r)
+      if ((ch >> 6) == r) qv = qb[r];
+    i1_q[rank] = qv;
+    i1_off[rank] = qv >= 0.f ? ch : -1 - ch;
+    if (chan_out) chan_out[rank] = ch;
+  }, hist);
+}
+
 // Step 2a: one workgroup per (page range, unit).  Every workgroup of a unit
 // makes the same channel choice (group sums of |q| in g order, top-k1 with
 // ties toward the lower channel), then stages its pages' sign-selected aux
@@ -78,32 +195,10 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
       }
     }
   }
-  if (wave == 0) {
-    // group sums of |q| and q per channel (g ascending, float32), then the
-    // top-k1 channels by one wave; the emitting lane holds the channel's q_bar
-    float qb[R];
-    uint32_t kr[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float a = 0.f, s = 0.f;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        a = __fadd_rn(a, fabsf(qx[r][g]));
-        s = __fadd_rn(s, qx[r][g]);
-      }
-      kr[r] = order_key(a);
-      qb[r] = s;
-    }
-    wave_topk<R, 1024>(kr, D, k1, [&](int rank, int ch) {
-      float qv = qb[0];
-#pragma unroll
-      for (int r = 1; r < R; ++r)
-        if ((ch >> 6) == r) qv = qb[r];
-      i1_q[rank] = qv;
-      i1_off[rank] = qv >= 0.f ? ch : -1 - ch;  // the sign picks the Kmax or the Kmin row
-      if (chan_opt && blockIdx.x == 0) chan_opt[size_t(u) * k1 + rank] = ch;
-    }, hist);
-  }
+  if (wave == 0)
+    wave_choose_channels<T, D, G>(qx, k1, i1_q, i1_off,
+                                  chan_opt && blockIdx.x == 0 ? chan_opt + size_t(u) * k1 : nullptr,
+                                  hist);
   if (ALL) {
 #pragma unroll
     for (int x = 0; x < NBA; ++x) {
@@ -146,152 +241,38 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
     return;
   }
 
-  // Staging: thread (channel j, vector slot) fetches 16-byte runs of row j
-  // (EPV consecutive pages; p0 and nblk_cap are multiples of 8, so runs stay
-  // aligned and inside the row) and scatters them transposed into LDS as
-  // stage[page][channel] (row pitch k1p: 16-channel blocks plus one vector of
-  // padding).  Scoring: s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b].
-  const int k1p = (k1 + 15) / 16 * 16 + EPV;
-  const int groups = 256 / k1;  // vector slots per channel (k1 <= 128)
-  if (t < groups * k1) {
-    const int j = t % k1;
-    const int off = i1_off[j];
-    const T* row = off >= 0 ? xu + size_t(off) * nblk_cap : nu + size_t(-1 - off) * nblk_cap;
-    constexpr int NB = 4;
-    for (int v0 = t / k1; v0 < nv; v0 += groups * NB) {
-      Vec16<T> buf[NB];
-#pragma unroll
-      for (int x = 0; x < NB; ++x) {
-        const int vi = v0 + x * groups;
-        if (vi < nv) buf[x] = load16(row + vi * EPV);
-      }
-#pragma unroll
-      for (int x = 0; x < NB; ++x) {
-        const int vi = v0 + x * groups;
-        if (vi < nv) {
-          const T* src = reinterpret_cast<const T*>(&buf[x].raw);
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) stage[size_t(vi * EPV + e) * k1p + j] = src[e];
-        }
-      }
-    }
-  }
+  stage_rows<T, 256>(xu, nu, nblk_cap, np, k1, i1_off, stage);
   __syncthreads();
-  {
-    // Thread t scores pages b = t, t + 256, ...  Channels go in blocks of 16:
-    // the block's q_bar values come from LDS as float4 broadcasts and the
-    // page's 16 staged values as 16-byte reads, then the ordered terms.
-    // One rounded multiply and one rounded add per term: no fused multiply-add.
-#pragma clang fp contract(off)
-    for (int b = t; b < np; b += 256) {
-      const T* sp = stage + size_t(b) * k1p;
-      float acc = 0.f;
-      for (int j0 = 0; j0 < k1; j0 += 16) {
-        float qv[16], sv[16];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float4 q4 = *reinterpret_cast<const float4*>(i1_q + j0 + 4 * x);
-          qv[4 * x] = q4.x;
-          qv[4 * x + 1] = q4.y;
-          qv[4 * x + 2] = q4.z;
-          qv[4 * x + 3] = q4.w;
-        }
-#pragma unroll
-        for (int x = 0; x < 16 / EPV; ++x) {
-          const Vec16<T> vv = load16(sp + j0 + x * EPV);
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) sv[x * EPV + e] = vv.get(e);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (j0 + e < k1) acc = acc + qv[e] * sv[e];
-      }
-      ku[b] = order_key(acc);
-      if (s1_opt) s1_opt[size_t(u) * nblk + p0 + b] = acc;
-    }
-  }
+  score_staged<T, 256>(stage, np, k1, i1_q, ku, s1_opt ? s1_opt + size_t(u) * nblk + p0 : nullptr);
 }
 
-// Step 2b + step 3.  Every workgroup of a unit first takes the top-k2 of the
-// unit's page scores itself (the same radix select in each, so all agree;
-// ties toward the lower page, pages in ascending order) and keeps the pages
-// of its own split: this saves a launch and a memory round trip between the
-// choice and the K/V fetch.  Then 4 waves stream whole pages.  Lanes split a
-// row into LPR 16-byte chunks, so SLOTS tokens are in flight per wave and each
-// slot takes TPS tokens per chunk before one softmax rescale.
-template <typename T, int D, int G, bool MT>
-__global__ __launch_bounds__(256) void hsa_attn_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
-    const int32_t* __restrict__ cand, int64_t cand_stride, const uint32_t* __restrict__ keys,
-    int keys_pitch, int nblk, int nsel, int pages_per_split, int n_split, int n_tokens,
-    int block, float scale_log2, float* __restrict__ partials, int32_t* __restrict__ sel_opt) {
-  constexpr int EPL = Vec16<T>::N;
-  constexpr int LPR = D / EPL;
-  constexpr int SLOTS = kWave / LPR;
-  constexpr int TPS = G >= 4 ? 2 : 4;  // fewer tokens per step for wide groups (registers)
-  constexpr int CHUNK = SLOTS * TPS;
-  constexpr int NW = 4;
-  constexpr int PF = D + 4;  // floats per head partial: m, l, pad, pad, o[D]
+// ---- step 3 building blocks -------------------------------------------------
+// A wave streams whole pages.  Lanes split a row into LPR 16-byte chunks, so
+// SLOTS tokens are in flight per wave and each slot takes TPS tokens per chunk
+// before one softmax rescale.  Per lane: running max m, sum l and o over its
+// channel chunk, per head of the group, in the exp2 domain.
+template <typename T, int D, int G, int TPS_ = (G >= 4 ? 2 : 4)>
+struct AttnShape {
+  static constexpr int EPL = Vec16<T>::N;
+  static constexpr int LPR = D / EPL;
+  static constexpr int SLOTS = kWave / LPR;
+  // tokens per slot per step; the split-K kernel takes fewer for wide groups
+  // (registers at four waves per SIMD)
+  static constexpr int TPS = TPS_;
+  static constexpr int CHUNK = SLOTS * TPS;
   static_assert(kWave % LPR == 0, "row chunks must tile a wave");
-  __shared__ float wm[NW][G], wl[NW][G];
-  __shared__ __align__(16) float wo[NW][G][D];
-  __shared__ TopkSmem<256, 1024, 1> tsm;
-  extern __shared__ __align__(16) uint32_t attn_lds[];  // the split's pages, then (many pages) the keys
+};
 
-  const int u = blockIdx.y;
-  const int split = blockIdx.x;
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const int slot = lane / LPR;
-  const int c = lane % LPR;
-
-  float qf[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) unpack16(load16(q + (size_t(u) * G + g) * D + c * EPL), qf[g]);
-
-  float m[G], l[G], o[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNegBig;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
-  }
-
-  const T* ku = k + size_t(u) * size_t(kv_cap) * D + c * EPL;
-  const T* vu = v + size_t(u) * size_t(kv_cap) * D + c * EPL;
-  const int32_t* cu = MT ? cand + size_t(u) * size_t(cand_stride) : nullptr;
-
-  RK_PHASE(8);
-  int* pages = reinterpret_cast<int*>(attn_lds);  // [pages_per_split]
-  const int e0 = split * pages_per_split;
-  const int np = min(e0 + pages_per_split, nsel) - e0;
-  int32_t* so = sel_opt && split == 0 ? sel_opt + size_t(u) * nsel : nullptr;
-  const uint32_t* kg = keys + size_t(u) * keys_pitch;
-  auto emit = [&](int r, int i) {
-    if (r >= e0 && r < e0 + np) pages[r - e0] = i;
-    if (so) so[r] = i;
-  };
-  if (nblk <= kWaveTopkPages) {
-    // one wave selects from keys held in registers; no barrier inside
-    if (wave == 0) {
-      constexpr int RK = kWaveTopkPages / kWave;
-      uint32_t kr[RK];
-#pragma unroll
-      for (int r = 0; r < RK; ++r) kr[r] = r * kWave + lane < nblk ? kg[r * kWave + lane] : 0u;
-      wave_topk<RK, 1024>(kr, nblk, nsel, emit, tsm.hist[0]);
-    }
-  } else {
-    uint32_t* kl = attn_lds + pages_per_split;  // [keys_pitch]
-    for (int i = threadIdx.x; i < keys_pitch / 4; i += 256)
-      reinterpret_cast<uint4*>(kl)[i] = reinterpret_cast<const uint4*>(kg)[i];
-    __syncthreads();
-    wg_topk<256, 1024>([&](int i) { return kl[i]; }, nblk, nsel, emit, tsm);
-  }
-  __syncthreads();
-  RK_PHASE(10);
-
-  for (int e = wave; e < np; e += NW) {
+template <typename T, int D, int G, bool MT, int TPS_ = AttnShape<T, D, G>::TPS>
+__device__ __forceinline__ void attend_pages(
+    const float (&qf)[G][Vec16<T>::N], const T* ku, const T* vu, const int32_t* cu,
+    int64_t kv_cap, const int* pages, int e_begin, int e_end, int e_step, int block,
+    int n_tokens, float scale_log2, float (&m)[G], float (&l)[G],
+    float (&o)[G][Vec16<T>::N]) {
+  using S = AttnShape<T, D, G, TPS_>;
+  constexpr int EPL = S::EPL, LPR = S::LPR, SLOTS = S::SLOTS, TPS = S::TPS, CHUNK = S::CHUNK;
+  const int slot = lane_id() / LPR;
+  for (int e = e_begin; e < e_end; e += e_step) {
     const int t0 = pages[e] * block;
     const int t1 = min(t0 + block, n_tokens);
     for (int tc = t0; tc < t1; tc += CHUNK) {
@@ -350,8 +331,17 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
       }
     }
   }
+}
 
-  // merge the SLOTS token slots of the wave (lanes that share a channel chunk)
+// Merge the SLOTS token slots of a wave (lanes sharing a channel chunk), then
+// slot 0 stores the wave's (m, l, o) at wm[wave*G + g], wl[..], wo[(wave*G + g)*D + ch].
+template <typename T, int D, int G>
+__device__ __forceinline__ void wave_state_to_lds(float (&m)[G], float (&l)[G],
+                                                  float (&o)[G][Vec16<T>::N],
+                                                  int wave, float* wm, float* wl, float* wo) {
+  using S = AttnShape<T, D, G>;
+  constexpr int EPL = S::EPL, LPR = S::LPR;
+  const int lane = lane_id();
 #pragma unroll
   for (int off = LPR; off < kWave; off <<= 1) {
 #pragma unroll
@@ -369,40 +359,247 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
       m[g] = mn;
     }
   }
-  if (slot == 0) {
+  if (lane < LPR) {
+    const int c = lane;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (c == 0) {
-        wm[wave][g] = m[g];
-        wl[wave][g] = l[g];
+        wm[wave * G + g] = m[g];
+        wl[wave * G + g] = l[g];
       }
 #pragma unroll
-      for (int ee = 0; ee < EPL; ++ee) wo[wave][g][c * EPL + ee] = o[g][ee];
+      for (int ee = 0; ee < EPL; ++ee) wo[size_t(wave * G + g) * D + c * EPL + ee] = o[g][ee];
     }
   }
+}
+
+// Merge NW waves' states (in wave order) for element idx = g*D + ch.
+template <int D, int G, int NW>
+__device__ __forceinline__ void merge_waves(int idx, const float* wm, const float* wl,
+                                            const float* wo, float* mm_out, float* ll_out,
+                                            float* oo_out) {
+  const int g = idx / D, ch = idx % D;
+  float mm = kNegBig;
+  for (int w = 0; w < NW; ++w) mm = fmaxf(mm, wm[w * G + g]);
+  float ll = 0.f, oo = 0.f;
+  for (int w = 0; w < NW; ++w) {
+    const float a = fast_exp2(wm[w * G + g] - mm);
+    ll += wl[w * G + g] * a;
+    oo += wo[size_t(w * G + g) * D + ch] * a;
+  }
+  *mm_out = mm;
+  *ll_out = ll;
+  *oo_out = oo;
+}
+
+// Step 2b + step 3, split-K form.  Every workgroup of a unit first takes the
+// top-k2 of the unit's page scores itself (the same radix select in each, so
+// all agree; ties toward the lower page, pages in ascending order) and keeps
+// the pages of its own split: this saves a launch and a memory round trip
+// between the choice and the K/V fetch.  Then 4 waves stream the pages and the
+// workgroup writes one partial (m, l, o[d]) per head.
+template <typename T, int D, int G, bool MT>
+__global__ __launch_bounds__(256) void hsa_attn_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
+    const int32_t* __restrict__ cand, int64_t cand_stride, const uint32_t* __restrict__ keys,
+    int keys_pitch, int nblk, int nsel, int pages_per_split, int n_split, int n_tokens,
+    int block, float scale_log2, float* __restrict__ partials, int32_t* __restrict__ sel_opt) {
+  using S = AttnShape<T, D, G>;
+  constexpr int EPL = S::EPL, LPR = S::LPR;
+  constexpr int NW = 4;
+  constexpr int PF = D + 4;  // floats per head partial: m, l, pad, pad, o[D]
+  __shared__ float wm[NW * G], wl[NW * G];
+  __shared__ __align__(16) float wo[NW * G * D];
+  __shared__ TopkSmem<256, 1024, 1> tsm;
+  extern __shared__ __align__(16) uint32_t attn_lds[];  // the split's pages, then (many pages) the keys
+
+  const int u = blockIdx.y;
+  const int split = blockIdx.x;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int c = lane % LPR;
+
+  float qf[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) unpack16(load16(q + (size_t(u) * G + g) * D + c * EPL), qf[g]);
+  float m[G], l[G], o[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegBig;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
+  }
+
+  RK_PHASE(8);
+  int* pages = reinterpret_cast<int*>(attn_lds);  // [pages_per_split]
+  const int e0 = split * pages_per_split;
+  const int np = min(e0 + pages_per_split, nsel) - e0;
+  int32_t* so = sel_opt && split == 0 ? sel_opt + size_t(u) * nsel : nullptr;
+  const uint32_t* kg = keys + size_t(u) * keys_pitch;
+  auto emit = [&](int r, int i) {
+    if (r >= e0 && r < e0 + np) pages[r - e0] = i;
+    if (so) so[r] = i;
+  };
+  if (nblk <= kWaveTopkPages) {
+    // one wave selects from keys held in registers; no barrier inside
+    if (wave == 0) {
+      constexpr int RK = kWaveTopkPages / kWave;
+      uint32_t kr[RK];
+#pragma unroll
+      for (int r = 0; r < RK; ++r) kr[r] = r * kWave + lane < nblk ? kg[r * kWave + lane] : 0u;
+      wave_topk<RK, 1024>(kr, nblk, nsel, emit, tsm.hist[0]);
+    }
+  } else {
+    uint32_t* kl = attn_lds + pages_per_split;  // [keys_pitch]
+    for (int i = threadIdx.x; i < keys_pitch / 4; i += 256)
+      reinterpret_cast<uint4*>(kl)[i] = reinterpret_cast<const uint4*>(kg)[i];
+    __syncthreads();
+    wg_topk<256, 1024>([&](int i) { return kl[i]; }, nblk, nsel, emit, tsm);
+  }
+  __syncthreads();
+  RK_PHASE(10);
+
+  const T* ku = k + size_t(u) * size_t(kv_cap) * D + c * EPL;
+  const T* vu = v + size_t(u) * size_t(kv_cap) * D + c * EPL;
+  const int32_t* cu = MT ? cand + size_t(u) * size_t(cand_stride) : nullptr;
+  attend_pages<T, D, G, MT>(qf, ku, vu, cu, kv_cap, pages, wave, np, NW, block, n_tokens,
+                            scale_log2, m, l, o);
+  wave_state_to_lds<T, D, G>(m, l, o, wave, wm, wl, wo);
   __syncthreads();
   RK_PHASE(11);
   // merge the 4 waves in order and write this split's partial per head
-  float* pu = partials + size_t(u) * n_split * G * PF;
-  float* pw = pu + size_t(split) * G * PF;
+  float* pw = partials + (size_t(u) * n_split + split) * G * PF;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int g = idx / D;
-    const int ch = idx % D;
-    float mm = kNegBig;
-    for (int w = 0; w < NW; ++w) mm = fmaxf(mm, wm[w][g]);
-    float ll = 0.f, oo = 0.f;
-    for (int w = 0; w < NW; ++w) {
-      const float a = fast_exp2(wm[w][g] - mm);
-      ll += wl[w][g] * a;
-      oo += wo[w][g][ch] * a;
-    }
-    float* pg = pw + size_t(g) * PF;
-    pg[4 + ch] = oo;
-    if (ch == 0) {
+    float mm, ll, oo;
+    merge_waves<D, G, NW>(idx, wm, wl, wo, &mm, &ll, &oo);
+    float* pg = pw + size_t(idx / D) * PF;
+    pg[4 + idx % D] = oo;
+    if (idx % D == 0) {
       pg[0] = mm;
       pg[1] = ll;
     }
   }
+}
+
+// Steps 2 and 3 in one workgroup per unit, for large batches (the units alone
+// fill the chip, so no split-K, no partials and no combine).  1024 threads:
+// wave 0 makes the channel choice; all threads stage and score the unit's
+// pages chunk by chunk (npc pages per chunk); one wave (or, for many pages,
+// the workgroup) takes the top-k2 pages; 16 waves stream them and the
+// workgroup writes the normalised output.  Gathers of scattered pages on
+// this chip gain bandwidth with resident waves per CU rather than with loads
+// in flight per wave, hence the full 1024-thread workgroup (4 waves per SIMD).
+//
+// Dynamic LDS: page keys [roundup4(nblk)] | chosen pages [roundup4(nsel)] |
+// a region holding first the staged chunk [npc][k1p], then the waves' merge
+// state (m, l per wave and head, o per wave, head and channel).
+template <typename T, int D, int G, bool MT>
+__global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
+    const int32_t* __restrict__ cand, int64_t cand_stride, const T* __restrict__ kmax,
+    const T* __restrict__ kmin, int64_t nblk_cap, int nblk, int k1, int nsel, int npc,
+    int n_tokens, int block, float scale_log2, float* __restrict__ out,
+    int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt) {
+  constexpr int TPS = AttnShape<T, D, G>::TPS;
+  using S = AttnShape<T, D, G, TPS>;
+  constexpr int EPL = S::EPL, LPR = S::LPR;
+  constexpr int NT = kFusedThreads, NW = NT / kWave;
+  constexpr int R = D / kWave;
+  extern __shared__ __align__(16) unsigned char dyn_lds[];
+  uint32_t* pkeys = reinterpret_cast<uint32_t*>(dyn_lds);
+  int* pages = reinterpret_cast<int*>(pkeys + ((nblk + 3) & ~3));
+  unsigned char* region = reinterpret_cast<unsigned char*>(pages + ((nsel + 3) & ~3));
+  T* stage = reinterpret_cast<T*>(region);
+  float* wm = reinterpret_cast<float*>(region);
+  float* wl = wm + NW * G;
+  float* wo = wl + NW * G;
+  __shared__ __align__(16) float i1_q[D + 16];
+  __shared__ __align__(16) int i1_off[D + 16];
+  __shared__ TopkSmem<NT, 1024, 1> tsm;
+
+  const int u = blockIdx.x;
+  const int t = threadIdx.x;
+  const int wave = t / kWave, lane = lane_id();
+  const int c = lane % LPR;
+
+  RK_PHASE(0);
+  float qf[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) unpack16(load16(q + (size_t(u) * G + g) * D + c * EPL), qf[g]);
+  if (wave == 0) {
+    float qx[R][G];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int g = 0; g < G; ++g) qx[r][g] = to_f32(q[(size_t(u) * G + g) * D + r * kWave + lane]);
+    wave_choose_channels<T, D, G>(qx, k1, i1_q, i1_off, chan_opt ? chan_opt + size_t(u) * k1 : nullptr,
+                                  tsm.hist[0]);
+  }
+  __syncthreads();
+  RK_PHASE(1);
+
+  const T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
+  const T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
+  for (int p0 = 0; p0 < nblk; p0 += npc) {
+    const int np = min(npc, nblk - p0);
+    stage_rows<T, NT>(xu + p0, nu + p0, nblk_cap, np, k1, i1_off, stage);
+    __syncthreads();
+    score_staged<T, NT>(stage, np, k1, i1_q, pkeys + p0,
+                        s1_opt ? s1_opt + size_t(u) * nblk + p0 : nullptr);
+    __syncthreads();
+  }
+
+  RK_PHASE(2);
+  int32_t* so = sel_opt ? sel_opt + size_t(u) * nsel : nullptr;
+  auto emit = [&](int r, int i) {
+    pages[r] = i;
+    if (so) so[r] = i;
+  };
+  if (nblk <= kWaveTopkPages) {
+    if (wave == 0) {
+      constexpr int RK = kWaveTopkPages / kWave;
+      uint32_t kr[RK];
+#pragma unroll
+      for (int r = 0; r < RK; ++r) kr[r] = r * kWave + lane < nblk ? pkeys[r * kWave + lane] : 0u;
+      wave_topk<RK, 1024>(kr, nblk, nsel, emit, tsm.hist[0]);
+    }
+  } else {
+    wg_topk<NT, 1024>([&](int i) { return pkeys[i]; }, nblk, nsel, emit, tsm);
+  }
+  __syncthreads();
+  RK_PHASE(3);
+
+  float m[G], l[G], o[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegBig;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
+  }
+  const T* ku = k + size_t(u) * size_t(kv_cap) * D + c * EPL;
+  const T* vu = v + size_t(u) * size_t(kv_cap) * D + c * EPL;
+  const int32_t* cu = MT ? cand + size_t(u) * size_t(cand_stride) : nullptr;
+  attend_pages<T, D, G, MT, TPS>(qf, ku, vu, cu, kv_cap, pages, wave, nsel, NW, block, n_tokens,
+                                 scale_log2, m, l, o);
+  RK_PHASE(4);
+  wave_state_to_lds<T, D, G>(m, l, o, wave, wm, wl, wo);  // the staged chunk is no longer read
+  __syncthreads();
+  RK_PHASE(5);
+  for (int idx = t; idx < G * D; idx += NT) {
+    float mm, ll, oo;
+    merge_waves<D, G, NW>(idx, wm, wl, wo, &mm, &ll, &oo);
+    out[size_t(u) * G * D + idx] = oo / ll;
+  }
+}
+
+// Dynamic LDS of the fused kernel for a chunk of npc pages.
+inline size_t fused_lds_bytes(int nblk, int nsel, int npc, int k1p, size_t esize, int D, int G) {
+  const size_t stage = size_t(npc) * k1p * esize;
+  constexpr int NW = kFusedThreads / kWave;
+  const size_t merge = (size_t(2) * NW * G + size_t(NW) * G * D) * sizeof(float);
+  return size_t((nblk + 3) & ~3) * 4 + size_t((nsel + 3) & ~3) * 4 + (stage > merge ? stage : merge);
 }
 
 // One wave per (unit, head) merges the split partials.  Lane s (< n_split)
@@ -476,6 +673,45 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   float* part = reinterpret_cast<float*>(wsb + lay.partials);
   const int units = d.units();
 
+  const float scale_log2 = float(1.4426950408889634 / sqrt(double(D)));
+  if constexpr (G <= 4) if (units >= kFusedMinUnits) {
+    // one workgroup per unit: chunk of npc pages within the LDS budget
+    const int k1pf = (k1 + 15) / 16 * 16 + int(16 / sizeof(T));
+    const size_t fixed = fused_lds_bytes(nblk, lay.nsel, 0, k1pf, sizeof(T), D, G);
+    const size_t keys_sel = size_t((nblk + 3) & ~3) * 4 + size_t((lay.nsel + 3) & ~3) * 4;
+    int npc = kFusedLdsBudget > keys_sel
+                  ? int((kFusedLdsBudget - keys_sel) / (size_t(k1pf) * sizeof(T))) / 8 * 8
+                  : 0;
+    const int nblk8 = (nblk + 7) / 8 * 8;
+    npc = npc > nblk8 ? nblk8 : npc;
+    if (npc >= 8 && fixed <= kFusedLdsBudget) {
+      const size_t lds = fused_lds_bytes(nblk, lay.nsel, npc, k1pf, sizeof(T), D, G);
+      static bool fattr = false;  // once per template instantiation
+      if (!fattr) {
+        for (const void* f : {reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, true>),
+                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false>)}) {
+          hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             int(kFusedLdsBudget));
+          if (e != hipSuccess) return e;
+        }
+        fattr = true;
+      }
+      if (cand)
+        RK_LAUNCH("hsa_fused_mt", (hsa_fused_kernel<T, D, G, true>), dim3(units), dim3(kFusedThreads), lds,
+                  s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                  kv_cap, cand, cand_stride, static_cast<const T*>(kmax),
+                  static_cast<const T*>(kmin), nblk_cap, nblk, k1, lay.nsel, npc, int(n_tokens),
+                  block, scale_log2, out, sel_opt, chan_opt, s1_opt);
+      else
+        RK_LAUNCH("hsa_fused", (hsa_fused_kernel<T, D, G, false>), dim3(units), dim3(kFusedThreads), lds,
+                  s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                  kv_cap, cand, cand_stride, static_cast<const T*>(kmax),
+                  static_cast<const T*>(kmin), nblk_cap, nblk, k1, lay.nsel, npc, int(n_tokens),
+                  block, scale_log2, out, sel_opt, chan_opt, s1_opt);
+      return hipGetLastError();
+    }
+  }
+
   // Step 2a grid: page ranges of ppw pages (a multiple of 8, the staged
   // slice within the LDS budget) so the launch has about 1024 workgroups, at
   // least 16 pages each.  Launches whose full aux slices come to at most
@@ -529,7 +765,6 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   const int nsel4 = (lay.nsel + 3) / 4 * 4;
   pps = pps > nsel4 ? nsel4 : pps;
   const int n_split = (lay.nsel + pps - 1) / pps;
-  const float scale_log2 = float(1.4426950408889634 / sqrt(double(D)));
   const size_t attn_lds =
       size_t(pps + (nblk > kWaveTopkPages ? lay.keys_pitch : 0)) * sizeof(uint32_t);  // <= 96 KB
   static bool attn_attr_set = false;  // once per template instantiation

@@ -302,15 +302,19 @@ __device__ void wave_topk(const uint32_t (&kr)[R], int n, int k, const EmitFn& e
   static_assert((1 << LOG_BINS) == BINS && BINS <= 2048 && BINS >= 256, "bins");
   const int lane = lane_id();
   if (k <= 0) return;
+  const int rows = (n + kWave - 1) / kWave;  // rows holding keys (wave-uniform)
   if (k >= n) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
+      if (r >= rows) break;
       if (r * kWave + lane < n) emit(r * kWave + lane, r * kWave + lane);
+    }
     return;
   }
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    if (r >= rows) break;
     if (r * kWave + lane < n) {
       lo = min(lo, kr[r]);
       hi = max(hi, kr[r]);
@@ -335,6 +339,7 @@ __device__ void wave_topk(const uint32_t (&kr)[R], int n, int k, const EmitFn& e
       *reinterpret_cast<uint4*>(hist + lane * (BINS / kWave) + j) = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
+      if (r >= rows) break;
       const uint32_t kk = kr[r];
       if (r * kWave + lane < n && kk >= lo && kk <= hi) atomicAdd(&hist[(kk - lo) >> shift], 1u);
     }
@@ -359,6 +364,7 @@ __device__ void wave_topk(const uint32_t (&kr)[R], int n, int k, const EmitFn& e
   int base = 0, eq_seen = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    if (r >= rows) break;
     const int i = r * kWave + lane;
     const uint32_t kk = kr[r];
     const bool eq = i < n && kk == T;

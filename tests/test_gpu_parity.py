@@ -275,3 +275,59 @@ def test_append_equals_rebuild(rk, dtype, d):
         torch.cuda.synchronize()
         assert torch.equal(kc[:, :, 200 + step], ka) and torch.equal(vc[:, :, 200 + step], va)
         U.check_aux_units(kmax, kmin, kc, 201 + step, 16, [(b, h) for b in range(3) for h in range(2)])
+
+
+def _decode_only(rk, w, n, k1, k2, units_to_check=None, cand_total=None, steps=2):
+    """Aux + decode over a synthetic cache (no stage 1), checked stage-wise."""
+    kc, vc, _ = WL.layer_kv(w, 0, device=DEV)
+    cand = None
+    if cand_total is not None:                       # MT: candidates = a strided subset of the cache
+        B, H = kc.shape[:2]
+        base = torch.arange(n, device=DEV, dtype=torch.int32) * (cand_total // n)
+        cand = base.repeat(B, H, 1).contiguous()
+        kmax, kmin = U.aux_and_check(rk, kc, n, w.block, w.n_q, idx=cand, units_to_check=units_to_check)
+    else:
+        kmax, kmin = U.aux_and_check(rk, kc, n, w.block, w.n_q, units_to_check=units_to_check)
+    for step in range(steps):
+        q = WL.decode_query(w, 0, step, device=DEV)
+        U.decode_and_check(rk, q, kc, vc, kmax, kmin, n, w.block, k1, k2, cand=cand,
+                           units_to_check=units_to_check)
+
+
+@pytest.mark.parametrize("dtype,d,G,B,Hkv,n,k1,k2", [
+    ("bf16", 128, 4, 20, 8, 997, 32, 16),      # 160 units: one fused workgroup per unit
+    ("f32", 64, 2, 40, 4, 500, 16, 8),
+    ("bf16", 128, 1, 6, 32, 1200, 32, 20),     # MHA group of one, 192 units
+])
+def test_fused_large_batch_decode(rk, dtype, d, G, B, Hkv, n, k1, k2):
+    say("fused decode", dtype, d, G, B, Hkv, n, k1, k2)
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=B, n_kv=Hkv, n_q=Hkv * G, d=d, dtype=dtype, seq=n + 40, n_plant=4)
+    _decode_only(rk, w, n, k1, k2)
+    kc, vc, _ = WL.layer_kv(w, 0, device=DEV)
+    kmax = torch.empty(B, Hkv, d, rk.aux_capacity(n, 16), dtype=kc.dtype, device=DEV)
+    kmin = torch.empty_like(kmax)
+    rk.rk_hsa_build_aux(kc, n, 0, 16, kmax, kmin)
+    out = torch.empty(B, Hkv * G, d, device=DEV)
+    rk.rk_profile_begin()
+    rk.rk_hsa_decode(WL.decode_query(w, 0, 0, device=DEV), kc, vc, kmax, kmin, n, 16, k1, k2, out)
+    assert set(rk.rk_profile_end()) == {"hsa_fused"}
+
+
+def test_fused_mt_decode(rk):
+    say("fused MT decode, 160 units")
+    base = WL.WORKLOADS["mt-mha-b8-s32k-c32"]
+    w = WL.scaled(base, batch=5, n_q=32, n_kv=32, seq=3000, n_plant=4)
+    _decode_only(rk, w, 700, 32, 12, cand_total=2900, units_to_check=[(0, 0), (2, 17), (4, 31)])
+
+
+@pytest.mark.parametrize("B,Hkv,n,k2", [
+    (1, 2, 20000, 200),      # 1250 pages: split path, workgroup page top-k
+    (20, 8, 17000, 64),      # 160 units with 1063 pages: fused path, workgroup page top-k
+])
+def test_many_pages_decode(rk, B, Hkv, n, k2):
+    say("many pages", B, Hkv, n, k2)
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=B, n_kv=Hkv, n_q=4 * Hkv, seq=n, n_plant=8)
+    units = [(0, 0), (B - 1, Hkv - 1)]
+    _decode_only(rk, w, n, 64, k2, units_to_check=units, steps=1)
