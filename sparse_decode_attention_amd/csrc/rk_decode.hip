@@ -8,7 +8,7 @@
 // one choice) and RocketKV-MT (pages over the stage-1 candidates of a full
 // cache).
 //
-// Three launches per call:
+// Small batches, three launches per call:
 //   hsa_score   one workgroup per (page range, unit): channel sums and top-k1;
 //               the range's k1 sign-selected aux rows are staged into LDS with
 //               16-byte loads (one memory round trip) and its pages scored
@@ -17,6 +17,9 @@
 //               whole pages with 16-byte K/V loads, online softmax in the exp2
 //               domain, one partial (m, l, o[d]) per head per workgroup
 //   hsa_combine one wave per (unit, head) merges the partials
+// Large batches (kFusedMinUnits units or more), one launch:
+//   hsa_fused   one 1024-thread workgroup per unit runs all of the above and
+//               writes the normalised output
 // HBM-bound: bytes per unit = q + k1*nblk aux elements + 2*d*|T| K/V elements.
 #include <math.h>
 
