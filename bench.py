@@ -305,10 +305,20 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def code_only(src):
+    """C/C++ source without comments and whitespace (edits to comments keep the hash)."""
+    import re
+
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return re.sub(r"\s+", "", src)
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from the committed counter
     summary (profiles/hbm_traffic_counters.md), or None when there is no row or
-    the kernel's sources have changed since the counters were taken."""
+    the kernel's sources (comments and whitespace aside) have changed since the
+    counters were taken."""
     import hashlib
     import os
 
@@ -325,8 +335,8 @@ def measured_traffic(kernel, workload):
             continue
         h = hashlib.sha256()
         for n in ("rk_device.hpp", "rk_internal.hpp", cells[6]):
-            with open(os.path.join(root, "sparse_decode_attention_amd", "csrc", n), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(root, "sparse_decode_attention_amd", "csrc", n)) as f:
+                h.update(code_only(f.read()).encode())
         return round(float(cells[5]) * 1e6) if h.hexdigest()[:12] == cells[7] else None
     return None
 
