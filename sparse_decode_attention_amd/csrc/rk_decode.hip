@@ -217,24 +217,37 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
   uint32_t* ku = keys + size_t(u) * keys_pitch + p0;
   if (ALL) {
     // s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b], P_i read from the
-    // Kmax or Kmin row the sign picked; four channels' reads in flight before
-    // their ordered terms; no fused multiply-add.
+    // Kmax or Kmin row the sign picked.  Blocks of 16 channels: the block's
+    // row choices and q_bar values come as 16-byte LDS reads, then its 16
+    // staged values, all in flight before the ordered terms (one rounded
+    // multiply and one rounded add each, no fused multiply-add).
 #pragma clang fp contract(off)
     for (int b = t; b < np; b += 256) {
       float acc = 0.f;
-      for (int j0 = 0; j0 < k1; j0 += 4) {
-        const int4 o4 = *reinterpret_cast<const int4*>(i1_off + j0);
-        const float4 q4 = *reinterpret_cast<const float4*>(i1_q + j0);
-        const int oo[4] = {o4.x, o4.y, o4.z, o4.w};
-        const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
-        float pv[4];
+      for (int j0 = 0; j0 < k1; j0 += 16) {
+        int oo[16];
+        float qq[16], pv[16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = oo[e] >= 0 ? oo[e] : D + (-1 - oo[e]);
-          pv[e] = j0 + e < k1 ? to_f32(stage[size_t(r) * ppw + b]) : 0.f;
+        for (int x = 0; x < 4; ++x) {
+          const int4 o4 = *reinterpret_cast<const int4*>(i1_off + j0 + 4 * x);
+          const float4 q4 = *reinterpret_cast<const float4*>(i1_q + j0 + 4 * x);
+          oo[4 * x] = o4.x;
+          oo[4 * x + 1] = o4.y;
+          oo[4 * x + 2] = o4.z;
+          oo[4 * x + 3] = o4.w;
+          qq[4 * x] = q4.x;
+          qq[4 * x + 1] = q4.y;
+          qq[4 * x + 2] = q4.z;
+          qq[4 * x + 3] = q4.w;
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 16; ++e) {
+          const int o = j0 + e < k1 ? oo[e] : 0;  // entries past k1 are not written
+          const int r = o >= 0 ? o : D + (-1 - o);
+          pv[e] = to_f32(stage[size_t(r) * ppw + b]);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
           if (j0 + e < k1) acc = acc + qq[e] * pv[e];
       }
       ku[b] = order_key(acc);

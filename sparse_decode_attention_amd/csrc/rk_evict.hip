@@ -192,6 +192,47 @@ __global__ __launch_bounds__(256) void ws_pass2_kernel(const T* __restrict__ q_w
   if (part == 0 && j0 + col < P) scores[size_t(u) * P + j0 + col] = total;
 }
 
+// Pooling for kernels up to 2*H+1 wide: a workgroup makes 1024 outputs, four
+// consecutive ones per thread, from a zero-padded LDS tile read back as
+// 16-byte vectors into registers; each output is summed left to right (the
+// first in-range term first: added zeros do not change a sum of
+// non-negative scores).
+template <int H>
+__global__ __launch_bounds__(256) void pool_sum_reg_kernel(const float* __restrict__ scores,
+                                                           int P, float* __restrict__ pooled) {
+  constexpr int OUT = 1024;
+  constexpr int TW = (OUT + 2 * H + 3) & ~3;
+  constexpr int NV = (4 + 2 * H + 3) / 4;  // 16-byte reads per thread
+  __shared__ __align__(16) float tile[TW];
+  const int u = blockIdx.y;
+  const int j0 = blockIdx.x * OUT;
+  const float* su = scores + size_t(u) * P;
+  for (int e = threadIdx.x; e < TW; e += 256) {
+    const int j = j0 - H + e;
+    tile[e] = (j >= 0 && j < P) ? su[j] : 0.f;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  float v[NV * 4];
+#pragma unroll
+  for (int x = 0; x < NV; ++x) {
+    const float4 f = *reinterpret_cast<const float4*>(tile + 4 * t + 4 * x);
+    v[4 * x] = f.x;
+    v[4 * x + 1] = f.y;
+    v[4 * x + 2] = f.z;
+    v[4 * x + 3] = f.w;
+  }
+  float* pu = pooled + size_t(u) * P;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float acc = v[e];
+#pragma unroll
+    for (int i = 1; i <= 2 * H; ++i) acc = __fadd_rn(acc, v[e + i]);
+    const int j = j0 + 4 * t + e;
+    if (j < P) pu[j] = acc;
+  }
+}
+
 // pooled[j] = sum_{i=j-h}^{j+h} score[i] (zero outside [0, P)), left to right.
 __global__ __launch_bounds__(256) void pool_sum_kernel(const float* __restrict__ scores, int P, int h,
                                                    float* __restrict__ pooled) {
@@ -512,6 +553,9 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   const int RG = (M + 31) / 32;
   const int CS = RG >= 4 ? 1 : 4 / RG;
   // keys per workgroup: about 2048 workgroups per pass, in whole 128-key tiles
+  // (splitting the passes over unit chunks small enough for the second pass to
+  // re-read K from the MALL measured slower: the smaller launches lose more
+  // than the re-read gains)
   auto range = [&](int keys) {
     const int wpu = (2048 + units - 1) / units;
     int kpw = (keys + wpu - 1) / wpu;
@@ -547,9 +591,15 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
                 s, qw, kk, kv_cap, S, W, d.G, scale_log2, stats, scores);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (P > 0) {
     const int h = (pool_kernel - 1) / 2;
-    RK_LAUNCH("pool_sum", pool_sum_kernel, dim3((P + 255) / 256, units), dim3(256),
-                       size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
+    if (h == 31)
+      RK_LAUNCH("pool_sum", pool_sum_reg_kernel<31>, dim3((P + 1023) / 1024, units), dim3(256), 0,
+                s, scores, P, pooled);
+    else
+      RK_LAUNCH("pool_sum", pool_sum_kernel, dim3((P + 255) / 256, units), dim3(256),
+                size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int staged = size_t(P) * 4 <= kSelectKeysLds ? 1 : 0;
