@@ -77,7 +77,7 @@ class Path:
         self.mt = w.mt_turns > 0
         self.S = w.seq + (w.mt_turns * w.mt_append if self.mt else 0)   # MT: the last turn
         sp = rk.rk_split(w.c, self.S, w.window, w.block, w.d)
-        self.n_keep, self.k2 = sp["n_keep"], sp["k2_blocks"]
+        self.n_keep, self.k2 = sp["n_keep"], WL.stage2_pages(w, sp)
         self.steps = w.decode_steps
         B, Hq, Hkv, d = w.batch, w.n_q, w.n_kv, w.d
         cap_c = self.n_keep + (self.steps if w.appends else 0)

@@ -72,14 +72,20 @@ typedef struct {
   int32_t k2_blocks; /* stage-2 pages: ceil(t / block)                        */
   int32_t paper_page;/* the notes' own page size ceil(c^((1-r)/2))            */
   double paper_k1;   /* the notes' own head-dim share: d / (c^(1-r)/page)     */
+  int32_t paper_k1_channels; /* paper_k1 rounded to nearest, within [1, d]    */
+  int32_t paper_k2_blocks;   /* the notes' step-3 half of the budget in their
+                                own pages: ceil((t / 2) / paper_page)         */
 } rk_split_out;
 
 /*
  * rk_split -- the adaptive compression split.
  * [RKV] method details: adaptive split equation r = min(0.2 + 0.06 log2 c,
  * 0.8) with r restricted to [0.2, 0.8]; stage 1 takes c^r, stage 2 c^(1-r);
- * token budget paragraph: t = S / c per GQA group; split inside HSA: page =
- * ceil(c^((1-r)/2)), the head-dim axis gets c^(1-r)/page.
+ * token budget paragraph: t = S / c per GQA group, shared evenly between
+ * HSA steps 2 and 3; split inside HSA: page = ceil(c^((1-r)/2)), the head-dim
+ * axis gets c^(1-r)/page.  k2_blocks gives step 3 the whole budget in pages
+ * of `block` tokens (the workloads' sizing); the paper_* fields give the
+ * notes' own decomposition (their page, k1 and the step-3 half of t).
  * c >= 1, 1 <= window <= seq_len, block >= 1, head_dim >= 1.  Pure host math
  * in double; touches no device.  RK_EINVAL on bad arguments or out == NULL.
  */

@@ -72,7 +72,11 @@ def split(c: float, seq_len: int, window: int, block: int, head_dim: int) -> dic
 
     Returns float64 scalars r, c1, c2, t and the integer sizes n_keep (stage-1
     kept tokens, reading R2), k2_blocks (reading R3), paper_page and the
-    paper's (real-valued) k1.
+    paper's (real-valued) k1.  The notes' own decomposition also shares the
+    budget t evenly between HSA steps 2 and 3 ([RKV] token budget paragraph):
+    paper_k2_blocks = ceil((t/2) / paper_page) pages for step 3 and
+    paper_k1_channels = paper_k1 rounded to the nearest integer in [1, d]
+    (reading R22).
     """
     if not (c >= 1.0):
         raise ValueError("compression ratio must be >= 1")
@@ -86,8 +90,11 @@ def split(c: float, seq_len: int, window: int, block: int, head_dim: int) -> dic
     k2 = max(1, math.ceil(t / block))
     page = math.ceil(c ** ((1.0 - r) / 2.0))
     paper_k1 = head_dim / (c2 / page)
+    paper_k1_channels = min(head_dim, max(1, math.floor(paper_k1 + 0.5)))
+    paper_k2 = max(1, math.ceil(t / 2.0 / page))
     return dict(r=r, c1=c1, c2=c2, budget_t=t, n_keep=n_keep, k2_blocks=k2,
-                paper_page=page, paper_k1=paper_k1)
+                paper_page=page, paper_k1=paper_k1, paper_k1_channels=paper_k1_channels,
+                paper_k2_blocks=paper_k2)
 
 
 def table1_storage_traffic(c: float) -> dict:

@@ -147,6 +147,12 @@ rk_status rk_split(double c, int64_t seq_len, int32_t window, int32_t block, int
   out->k2_blocks = int32_t(k2 > INT32_MAX ? INT32_MAX : k2);
   out->paper_page = page;
   out->paper_k1 = double(head_dim) / (c2 / double(page));
+  int64_t k1p = int64_t(floor(out->paper_k1 + 0.5));
+  k1p = k1p < 1 ? 1 : (k1p > head_dim ? head_dim : k1p);
+  out->paper_k1_channels = int32_t(k1p);
+  int64_t k2p = int64_t(ceil(t / 2.0 / double(page)));
+  k2p = k2p < 1 ? 1 : k2p;
+  out->paper_k2_blocks = int32_t(k2p > INT32_MAX ? INT32_MAX : k2p);
   return RK_OK;
 }
 

@@ -288,64 +288,77 @@ __device__ __forceinline__ void attend_pages(
   using S = AttnShape<T, D, G, TPS_>;
   constexpr int EPL = S::EPL, LPR = S::LPR, SLOTS = S::SLOTS, TPS = S::TPS, CHUNK = S::CHUNK;
   const int slot = lane_id() / LPR;
-  for (int e = e_begin; e < e_end; e += e_step) {
-    const int t0 = pages[e] * block;
-    const int t1 = min(t0 + block, n_tokens);
-    for (int tc = t0; tc < t1; tc += CHUNK) {
-      Vec16<T> kr[TPS], vr[TPS];
-      bool ok[TPS];
+  // One step: TPS tokens per slot (rows[i], valid when ok[i]): K and V rows
+  // with 16-byte loads, scores, one online-softmax rescale, V accumulation.
+  auto step = [&](const int (&rows)[TPS], const bool (&ok)[TPS]) {
+    Vec16<T> kr[TPS], vr[TPS];
 #pragma unroll
-      for (int i = 0; i < TPS; ++i) {
-        const int tok = tc + slot + SLOTS * i;
-        ok[i] = tok < t1;
-        const int row = ok[i] ? (MT ? clamp_row(cu[tok], kv_cap) : tok) : 0;
-        if (ok[i]) {
-          kr[i] = load16(ku + size_t(row) * D);
-          vr[i] = load16(vu + size_t(row) * D);
-        } else {
-          kr[i].raw = {};
-          vr[i].raw = {};
-        }
-      }
-      float x[G][TPS];
-#pragma unroll
-      for (int i = 0; i < TPS; ++i) {
-        float kf[EPL];
-        unpack16(kr[i], kf);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float s = 0.f;
-#pragma unroll
-          for (int ee = 0; ee < EPL; ++ee) s += qf[g][ee] * kf[ee];
-          x[g][i] = group_sum<LPR>(s) * scale_log2;
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float cm = kNegBig;
-#pragma unroll
-        for (int i = 0; i < TPS; ++i)
-          if (ok[i]) cm = fmaxf(cm, x[g][i]);
-        const float mn = fmaxf(m[g], cm);
-        const float corr = fast_exp2(m[g] - mn);
-        float p[TPS];
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < TPS; ++i) {
-          p[i] = ok[i] ? fast_exp2(x[g][i] - mn) : 0.f;
-          ps += p[i];
-        }
-        l[g] = l[g] * corr + ps;
-        m[g] = mn;
-#pragma unroll
-        for (int ee = 0; ee < EPL; ++ee) {
-          float acc = o[g][ee] * corr;
-#pragma unroll
-          for (int i = 0; i < TPS; ++i) acc += p[i] * vr[i].get(ee);
-          o[g][ee] = acc;
-        }
+    for (int i = 0; i < TPS; ++i) {
+      if (ok[i]) {
+        kr[i] = load16(ku + size_t(rows[i]) * D);
+        vr[i] = load16(vu + size_t(rows[i]) * D);
+      } else {
+        kr[i].raw = {};
+        vr[i].raw = {};
       }
     }
+    float x[G][TPS];
+#pragma unroll
+    for (int i = 0; i < TPS; ++i) {
+      float kf[EPL];
+      unpack16(kr[i], kf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float s = 0.f;
+#pragma unroll
+        for (int ee = 0; ee < EPL; ++ee) s += qf[g][ee] * kf[ee];
+        x[g][i] = group_sum<LPR>(s) * scale_log2;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float cm = kNegBig;
+#pragma unroll
+      for (int i = 0; i < TPS; ++i)
+        if (ok[i]) cm = fmaxf(cm, x[g][i]);
+      const float mn = fmaxf(m[g], cm);
+      const float corr = fast_exp2(m[g] - mn);
+      float p[TPS];
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < TPS; ++i) {
+        p[i] = ok[i] ? fast_exp2(x[g][i] - mn) : 0.f;
+        ps += p[i];
+      }
+      l[g] = l[g] * corr + ps;
+      m[g] = mn;
+#pragma unroll
+      for (int ee = 0; ee < EPL; ++ee) {
+        float acc = o[g][ee] * corr;
+#pragma unroll
+        for (int i = 0; i < TPS; ++i) acc += p[i] * vr[i].get(ee);
+        o[g][ee] = acc;
+      }
+    }
+  };
+  // The wave's pages (e_begin, e_begin + e_step, ... < e_end) are taken as one
+  // token sequence, tau = (page rank) * block + offset, so pages shorter than
+  // a step still fill every slot; tokens past n_tokens (a ragged last page)
+  // are skipped.
+  const int npw = e_end > e_begin ? (e_end - e_begin + e_step - 1) / e_step : 0;
+  const int ntok = npw * block;
+  for (int tc = 0; tc < ntok; tc += CHUNK) {
+    int rows[TPS];
+    bool ok[TPS];
+#pragma unroll
+    for (int i = 0; i < TPS; ++i) {
+      const int tau = tc + slot + SLOTS * i;
+      const int pr = tau / block;
+      const int tok = tau < ntok ? pages[e_begin + pr * e_step] * block + (tau - pr * block) : n_tokens;
+      ok[i] = tok < n_tokens;
+      rows[i] = ok[i] ? (MT ? clamp_row(cu[tok], kv_cap) : tok) : 0;
+    }
+    step(rows, ok);
   }
 }
 

@@ -378,7 +378,7 @@ __device__ void wave_topk(const uint32_t (&kr)[R], int n, int k, const EmitFn& e
 }
 
 // Most keys one wave emits; above it the workgroup emits (scan based).
-constexpr int kWaveEmitMax = 4096;
+constexpr int kWaveEmitMax = 1024;
 
 template <int NT, int BINS, int NBUF, typename KeyFn, typename EmitFn>
 __device__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit,

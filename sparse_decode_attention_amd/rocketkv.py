@@ -33,7 +33,8 @@ class RkSplitOut(ctypes.Structure):
     _fields_ = [("r", ctypes.c_double), ("c1", ctypes.c_double), ("c2", ctypes.c_double),
                 ("budget_t", ctypes.c_double), ("n_keep", ctypes.c_int64),
                 ("k2_blocks", ctypes.c_int32), ("paper_page", ctypes.c_int32),
-                ("paper_k1", ctypes.c_double)]
+                ("paper_k1", ctypes.c_double), ("paper_k1_channels", ctypes.c_int32),
+                ("paper_k2_blocks", ctypes.c_int32)]
 
 
 _i32, _i64, _f64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t

@@ -55,6 +55,7 @@ class Workload:
     mt_turns: int = 0       # RocketKV-MT turns (0: plain RocketKV)
     mt_append: int = 0      # tokens appended to the full cache per turn
     qhat_scale: str = "sqrt_d"
+    paper_split: bool = False  # page, k1 and k2 from the notes' own decomposition
 
     @property
     def group(self) -> int:
@@ -78,6 +79,10 @@ WORKLOADS = {
         # Llama-3.1-8B-shaped single layer, 32K prompt, budget 2048
         Workload("llama8b-layer-s32k-c16", 1, 1, 32768, 32, 8, 128, "bf16", 32, 63, 16.0, 16, 64, 64,
                  256, 3.0, 0.3, 8, 6.0),
+        # the same layer with the notes' own decomposition: pages of ceil(c^((1-r)/2)) = 3
+        # tokens, k1 = round(d * page / c^(1-r)) = 81, half the budget (342 pages) to step 3
+        Workload("llama8b-layer-s32k-c16-paper", 1, 1, 32768, 32, 8, 128, "bf16", 32, 63, 16.0, 3, 81,
+                 64, 256, 3.0, 0.3, 8, 6.0, paper_split=True),
         # Llama-3.1-8B-shaped full stack, batch 32, budget 512, per-step appends
         Workload("llama8b-stack-b32-s32k-c64", 32, 32, 32768, 32, 8, 128, "bf16", 32, 63, 64.0, 16, 32,
                  32, 256, 3.0, 0.3, 8, 6.0, appends=True),
@@ -89,6 +94,12 @@ WORKLOADS = {
                  64, 256, 3.0, 0.3, 8, 6.0, mt_turns=4, mt_append=1024),
     ]
 }
+
+def stage2_pages(w: Workload, split: dict) -> int:
+    """k2 of the workload, taken from a split result: the whole budget in pages
+    of w.block tokens, or the notes' step-3 half when w.paper_split."""
+    return split["paper_k2_blocks"] if w.paper_split else split["k2_blocks"]
+
 
 _TENSOR_IDS = {"qhat": 1, "outliers": 2, "k": 3, "v": 4, "plant_pos": 5, "plant_noise": 6,
                "q_win": 7, "q_dec": 8, "k_app": 9, "v_app": 10, "k_turn": 11, "v_turn": 12,

@@ -53,9 +53,8 @@ def test_split_matches_oracle(rk, c, S, W, B, d):
     want = O.split(c, S, W, B, d)
     for key in ("r", "c1", "c2", "budget_t", "paper_k1"):
         assert got[key] == pytest.approx(want[key], rel=1e-12), key
-    assert got["n_keep"] == want["n_keep"]
-    assert got["k2_blocks"] == want["k2_blocks"]
-    assert got["paper_page"] == want["paper_page"]
+    for key in ("n_keep", "k2_blocks", "paper_page", "paper_k1_channels", "paper_k2_blocks"):
+        assert got[key] == want[key], key
 
 
 def test_split_config_values(rk):

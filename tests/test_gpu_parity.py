@@ -37,7 +37,7 @@ def _pipeline(rk, w, layer=0, steps=None, seed=0):
     s = rk.rk_split(w.c, w.seq, w.window, w.block, w.d)
     k, v, pos = WL.layer_kv(w, layer, device=DEV, seed=seed)
     qw = WL.window_queries(w, layer, device=DEV, seed=seed)
-    n_keep, k2 = s["n_keep"], s["k2_blocks"]
+    n_keep, k2 = s["n_keep"], WL.stage2_pages(w, s)
     kept, kc, vc, pooled, sw1 = U.evict_and_check(rk, qw, k, v, w.seq, w.window, w.pool, n_keep)
     kmax, kmin = U.aux_and_check(rk, kc, n_keep, w.block, w.n_q)
     swaps = 0
@@ -64,6 +64,29 @@ def test_llama8b_layer_full_pipeline(rk):
     say(w.name, "64 decode steps")
     res = _pipeline(rk, w)
     say("swaps", res["swaps_evict"], res["swaps_decode"])
+
+
+def test_paper_decomposition_pipeline(rk):
+    """The notes' own HSA decomposition: 3-token pages, k1 = 81, 342 pages."""
+    w = WL.scaled(WL.WORKLOADS["llama8b-layer-s32k-c16-paper"], decode_steps=8)
+    s = rk.rk_split(w.c, w.seq, w.window, w.block, w.d)
+    assert (w.block, w.k1, WL.stage2_pages(w, s)) == (s["paper_page"], s["paper_k1_channels"], 342)
+    say(w.name, "8 decode steps")
+    res = _pipeline(rk, w)
+    say("swaps", res["swaps_evict"], res["swaps_decode"])
+
+
+@pytest.mark.parametrize("block", [1, 3, 5, 24])
+def test_short_and_odd_pages(rk, block):
+    """Pages of 1, 3, 5 and 24 tokens on both decode paths (the attention takes
+    a wave's pages as one token sequence when they are shorter than a step)."""
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    say("pages of", block, "split path")
+    w = WL.scaled(base, batch=2, seq=900, n_plant=8, block=block)
+    _decode_only(rk, w, 877, 32, max(1, 200 // block))
+    say("pages of", block, "fused path")
+    w = WL.scaled(base, batch=20, seq=500, n_plant=4, block=block)
+    _decode_only(rk, w, 487, 32, max(1, 120 // block), units_to_check=[(0, 0), (7, 3), (19, 7)], steps=1)
 
 
 @pytest.mark.parametrize("dtype,d,G,S,W,pool", [

@@ -37,6 +37,26 @@ def test_split_worked_example():
     assert math.isclose(s["c1"] * s["c2"], want["c"], rel_tol=1e-12)
 
 
+def test_split_paper_decomposition_halves_budget():
+    """[RKV] token budget paragraph: the budget t is shared evenly between HSA
+    steps 2 and 3; split inside HSA: pages of ceil(c^((1-r)/2)) tokens and
+    k1 = d / (c^(1-r)/page) channels.  Step 3 then fetches about t/2 KV
+    pairs, and step 2 (k1 sign-selected aux values for each of the N1/page
+    pages, d-element KV rows counted in pairs of two) about t/2 as well."""
+    # the printed c = 64 example: page 3, head-dim share 6.2 / 3 ~ 2.1, so about 62 of 128 channels
+    s = O.split(64.0, 65536, 32, 16, 128)
+    assert s["paper_page"] == 3 and s["paper_k1_channels"] == 62
+    for c, S, d in [(16, 32768, 128), (64, 32768, 128), (428, 109568, 128), (32, 36864, 128), (8, 2048, 64)]:
+        s = O.split(c, S, 32, 16, d)
+        page, t = s["paper_page"], s["budget_t"]
+        # step 3: the smallest page count covering half the budget
+        assert s["paper_k2_blocks"] * page >= t / 2 > (s["paper_k2_blocks"] - 1) * page
+        # step 2: k1 aux values per page over the stage-1 pages, in KV-pair units
+        step2_pairs = s["paper_k1"] * (S / s["c1"] / page) / (2 * d)
+        assert step2_pairs == pytest.approx(t / 2, rel=1e-9)
+        assert abs(s["paper_k1_channels"] - s["paper_k1"]) <= 0.5
+
+
 def test_split_clamp_bounds():
     """[RKV] prose after the r equation: r is restricted to [0.2, 0.8]."""
     assert O.split(1.0, 4096, 16, 16, 64)["r"] == pytest.approx(0.2)
