@@ -19,6 +19,8 @@
 //   gather     compaction of K and V rows (skipped for the RocketKV-MT form)
 #include <math.h>
 
+#include <algorithm>
+
 #include "rk_device.hpp"
 #include "rk_internal.hpp"
 
@@ -298,6 +300,59 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
     wg_topk<1024, 2048>([&](int i) { return order_key(pu[i]); }, P, n_keep - W, emit, sm);
   }
   for (int r = threadIdx.x; r < W; r += 1024) ku[n_keep - W + r] = P + r;
+}
+
+// Top-k over more keys than LDS holds, in two launches.  select_chunk: one
+// workgroup per (chunk of C keys, unit) takes the chunk's own top-min(k, len)
+// and writes their positions, ascending, over the chunk's (spent) score
+// entries.  select_final: one workgroup per unit takes the top-k of the union
+// of the candidates, which are in ascending position order.  Exact: a key in
+// the overall top-k has fewer than k keys ahead of it (greater, or equal at a
+// lower position) overall, so also within its chunk.
+__global__ __launch_bounds__(1024) void select_chunk_kernel(const float* __restrict__ pooled,
+                                                            int P, int C, int k,
+                                                            int32_t* __restrict__ cand) {
+  extern __shared__ uint32_t skeys[];
+  __shared__ TopkSmem<1024, 2048, 1> sm;
+  const int u = blockIdx.y;
+  const int j0 = blockIdx.x * C;
+  const int len = min(C, P - j0);
+  const float* pu = pooled + size_t(u) * P + j0;
+  for (int i = threadIdx.x; i < len; i += 1024) skeys[i] = order_key(pu[i]);
+  __syncthreads();
+  int32_t* cu = cand + size_t(u) * P + j0;
+  wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, len, min(k, len),
+                      [&](int r, int i) { cu[r] = j0 + i; }, sm);
+}
+
+__global__ __launch_bounds__(1024) void select_final_kernel(const float* __restrict__ pooled, int S,
+                                                            int W, int C, int n_keep,
+                                                            const int32_t* __restrict__ cand,
+                                                            int32_t* __restrict__ kept) {
+  extern __shared__ uint32_t fl[];  // keys [n_cand], then positions [n_cand]
+  __shared__ TopkSmem<1024, 2048, 1> sm;
+  const int u = blockIdx.x;
+  const int P = S - W;
+  const int k = n_keep - W;
+  const int n_chunks = (P + C - 1) / C;
+  const int kc = min(k, C);
+  int n_cand = 0;
+  for (int c = 0; c < n_chunks; ++c) n_cand += min(kc, P - c * C);
+  uint32_t* keys = fl;
+  int32_t* pos = reinterpret_cast<int32_t*>(fl + n_cand);
+  const float* pu = pooled + size_t(u) * P;
+  const int32_t* cu = cand + size_t(u) * P;
+  for (int i = threadIdx.x; i < n_cand; i += 1024) {
+    const int c = min(i / kc, n_chunks - 1);  // every chunk but the last holds kc candidates
+    const int p = cu[c * C + (i - c * kc)];
+    pos[i] = p;
+    keys[i] = order_key(pu[p]);
+  }
+  __syncthreads();
+  int32_t* ku = kept + size_t(u) * n_keep;
+  wg_topk<1024, 2048>([&](int i) { return keys[i]; }, n_cand, k,
+                      [&](int r, int i) { ku[r] = pos[i]; }, sm);
+  for (int r = threadIdx.x; r < W; r += 1024) ku[k + r] = P + r;
 }
 
 // Compact cache rows: out[n] = in[kept[n]] for K and V.
@@ -605,14 +660,33 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   const int staged = size_t(P) * 4 <= kSelectKeysLds ? 1 : 0;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       int(kSelectKeysLds));
-    if (e != hipSuccess) return e;
+    for (const void* f : {reinterpret_cast<const void*>(&select_kernel),
+                          reinterpret_cast<const void*>(&select_chunk_kernel),
+                          reinterpret_cast<const void*>(&select_final_kernel)}) {
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         int(kSelectKeysLds));
+      if (e != hipSuccess) return e;
+    }
     attr_set = true;
   }
-  RK_LAUNCH("select_tokens", select_kernel, dim3(units), dim3(1024),
-            staged ? size_t(P) * 4 : size_t(0), s, pooled, S, W, int(n_keep), staged, kept);
+  // more keys than LDS holds: chunked select when the candidates of all
+  // chunks (positions and keys) fit in LDS, else the global-key path
+  const int C = int(kSelectKeysLds / 4) / 64 * 64;
+  const int k_sel = int(n_keep) - W;
+  const int n_chunks = (P + C - 1) / C;
+  int n_cand = 0;
+  for (int c = 0; c < n_chunks; ++c) n_cand += std::min(std::min(k_sel, C), P - c * C);
+  if (!staged && size_t(n_cand) * 8 <= kSelectKeysLds) {
+    int32_t* cand = reinterpret_cast<int32_t*>(scores);  // the scores are spent once pooled
+    RK_LAUNCH("select_chunk", select_chunk_kernel, dim3(n_chunks, units), dim3(1024),
+              size_t(C) * 4, s, pooled, P, C, k_sel, cand);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    RK_LAUNCH("select_tokens", select_final_kernel, dim3(units), dim3(1024), size_t(n_cand) * 8,
+              s, pooled, S, W, C, int(n_keep), cand, kept);
+  } else {
+    RK_LAUNCH("select_tokens", select_kernel, dim3(units), dim3(1024),
+              staged ? size_t(P) * 4 : size_t(0), s, pooled, S, W, int(n_keep), staged, kept);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (k_out) {
     RK_LAUNCH("gather_kv", (gather_kernel<T, D>), dim3(unsigned((n_keep + 63) / 64), units),

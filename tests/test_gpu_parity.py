@@ -354,3 +354,15 @@ def test_many_pages_decode(rk, B, Hkv, n, k2):
     w = WL.scaled(base, batch=B, n_kv=Hkv, n_q=4 * Hkv, seq=n, n_plant=8)
     units = [(0, 0), (B - 1, Hkv - 1)]
     _decode_only(rk, w, n, 64, k2, units_to_check=units, steps=1)
+
+
+@pytest.mark.parametrize("n_keep", [3000, 15000])
+def test_long_prompt_select(rk, n_keep):
+    """More prompt keys than LDS holds (80000): the chunked two-launch select
+    (3000 kept) and the global-key select (15000 kept, too many candidates)."""
+    say("long prompt select, keep", n_keep)
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=1, n_kv=2, n_q=4, seq=80000, n_plant=16)
+    k, v, _ = WL.layer_kv(w, 0, device=DEV)
+    qw = WL.window_queries(w, 0, device=DEV)
+    U.evict_and_check(rk, qw, k, v, w.seq, w.window, w.pool, n_keep)
