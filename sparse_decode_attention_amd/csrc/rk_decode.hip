@@ -217,38 +217,36 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
   uint32_t* ku = keys + size_t(u) * keys_pitch + p0;
   if (ALL) {
     // s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b], P_i read from the
-    // Kmax or Kmin row the sign picked.  Blocks of 16 channels: the block's
-    // row choices and q_bar values come as 16-byte LDS reads, then its 16
-    // staged values, all in flight before the ordered terms (one rounded
-    // multiply and one rounded add each, no fused multiply-add).
+    // Kmax or Kmin row the sign picked.  All threads first form the rounded
+    // products q_bar_i * P_i[b] (np * k1 of them) into LDS; then the thread
+    // of page b adds its row of products in channel order (one rounded
+    // multiply and one rounded add per term, as in a sequential sum).
 #pragma clang fp contract(off)
+    float* prod = reinterpret_cast<float*>(stage + size_t(2) * D * ppw);  // [np][pp]
+    const int pp = (k1 + 15) / 16 * 16 + 4;  // whole 16-channel blocks, padded row
+    for (int idx = t; idx < np * k1; idx += 256) {
+      const int b = idx / k1, j = idx - b * k1;
+      const int o = i1_off[j];
+      const int r = o >= 0 ? o : D + (-1 - o);
+      prod[b * pp + j] = i1_q[j] * to_f32(stage[size_t(r) * ppw + b]);
+    }
+    __syncthreads();
     for (int b = t; b < np; b += 256) {
+      const float* pb = prod + b * pp;
       float acc = 0.f;
       for (int j0 = 0; j0 < k1; j0 += 16) {
-        int oo[16];
-        float qq[16], pv[16];
+        float pv[16];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const int4 o4 = *reinterpret_cast<const int4*>(i1_off + j0 + 4 * x);
-          const float4 q4 = *reinterpret_cast<const float4*>(i1_q + j0 + 4 * x);
-          oo[4 * x] = o4.x;
-          oo[4 * x + 1] = o4.y;
-          oo[4 * x + 2] = o4.z;
-          oo[4 * x + 3] = o4.w;
-          qq[4 * x] = q4.x;
-          qq[4 * x + 1] = q4.y;
-          qq[4 * x + 2] = q4.z;
-          qq[4 * x + 3] = q4.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int o = j0 + e < k1 ? oo[e] : 0;  // entries past k1 are not written
-          const int r = o >= 0 ? o : D + (-1 - o);
-          pv[e] = to_f32(stage[size_t(r) * ppw + b]);
+          const float4 f = *reinterpret_cast<const float4*>(pb + j0 + 4 * x);
+          pv[4 * x] = f.x;
+          pv[4 * x + 1] = f.y;
+          pv[4 * x + 2] = f.z;
+          pv[4 * x + 3] = f.w;
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (j0 + e < k1) acc = acc + qq[e] * pv[e];
+          if (j0 + e < k1) acc = acc + pv[e];
       }
       ku[b] = order_key(acc);
       if (s1_opt) s1_opt[size_t(u) * nblk + p0 + b] = acc;
@@ -757,7 +755,9 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   const bool all = size_t(2) * D * nblk * units * sizeof(T) <= kScoreAllBytes &&
                    2 * D * (ppw / EPV) <= 256 * 8;
   const int n_ranges = (nblk + ppw - 1) / ppw;
-  const size_t lds = (all ? size_t(2) * D : size_t(k1p)) * sizeof(T) * ppw;
+  // ALL: every channel's two rows, then the products [ppw][roundup16(k1) + 4] fp32
+  const size_t lds = all ? size_t(2) * D * sizeof(T) * ppw + size_t(ppw) * ((k1 + 15) / 16 * 16 + 4) * 4
+                         : size_t(k1p) * sizeof(T) * ppw;
   static bool attr_set = false;  // once per template instantiation
   if (!attr_set) {
     for (const void* f : {reinterpret_cast<const void*>(&hsa_score_kernel<T, D, G, true>),
