@@ -158,8 +158,8 @@ __device__ __forceinline__ void wave_choose_channels(const float (&qx)[D / kWave
 template <typename T, int D, int G, bool ALL>
 __global__ __launch_bounds__(256) void hsa_score_kernel(
     const T* __restrict__ q, const T* __restrict__ kmax, const T* __restrict__ kmin,
-    int64_t nblk_cap, int nblk, int k1, int ppw, uint32_t* __restrict__ keys, int keys_pitch,
-    int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt) {
+    int64_t nblk_cap, int nblk, int k1, int ppw, int units, uint32_t* __restrict__ keys,
+    int keys_pitch, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt) {
   constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   T* stage = reinterpret_cast<T*>(dyn_lds);  // [ppw][k1p]
@@ -169,8 +169,13 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
 
   constexpr int R = D / kWave;  // channels per lane of wave 0
   constexpr int NBA = 8;        // 16-byte vectors per thread in ALL mode (one round)
-  const int u = blockIdx.y;
-  const int p0 = blockIdx.x * ppw;
+  // work items (unit, page range), unit-major, XCD-local: the ranges of a unit
+  // read neighbouring 16-byte runs of the same aux rows
+  const int n_ranges = (nblk + ppw - 1) / ppw;
+  const int item = xcd_local_item(n_ranges * units);
+  if (item >= n_ranges * units) return;
+  const int u = item / n_ranges;
+  const int p0 = (item % n_ranges) * ppw;
   const int np = min(ppw, nblk - p0);
   const int t = threadIdx.x;
   const int wave = t / kWave, lane = lane_id();
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
   }
   if (wave == 0)
     wave_choose_channels<T, D, G>(qx, k1, i1_q, i1_off,
-                                  chan_opt && blockIdx.x == 0 ? chan_opt + size_t(u) * k1 : nullptr,
+                                  chan_opt && p0 == 0 ? chan_opt + size_t(u) * k1 : nullptr,
                                   hist);
   if (ALL) {
 #pragma unroll
@@ -429,7 +434,7 @@ template <typename T, int D, int G, bool MT>
 __global__ __launch_bounds__(256) void hsa_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
     const int32_t* __restrict__ cand, int64_t cand_stride, const uint32_t* __restrict__ keys,
-    int keys_pitch, int nblk, int nsel, int pages_per_split, int n_split, int n_tokens,
+    int keys_pitch, int nblk, int nsel, int pages_per_split, int n_split, int units, int n_tokens,
     int block, float scale_log2, float* __restrict__ partials, int32_t* __restrict__ sel_opt) {
   using S = AttnShape<T, D, G>;
   constexpr int EPL = S::EPL, LPR = S::LPR;
@@ -440,8 +445,12 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   __shared__ TopkSmem<256, 1024, 1> tsm;
   extern __shared__ __align__(16) uint32_t attn_lds[];  // the split's pages, then (many pages) the keys
 
-  const int u = blockIdx.y;
-  const int split = blockIdx.x;
+  // work items (unit, split), unit-major, XCD-local: the splits of a unit read
+  // the same page keys
+  const int item = xcd_local_item(n_split * units);
+  if (item >= n_split * units) return;
+  const int u = item / n_split;
+  const int split = item % n_split;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int c = lane % LPR;
@@ -755,6 +764,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   const bool all = size_t(2) * D * nblk * units * sizeof(T) <= kScoreAllBytes &&
                    2 * D * (ppw / EPV) <= 256 * 8;
   const int n_ranges = (nblk + ppw - 1) / ppw;
+  const int score_wgs = (n_ranges * units + kXcds - 1) / kXcds * kXcds;
   // ALL: every channel's two rows, then the products [ppw][roundup16(k1) + 4] fp32
   const size_t lds = all ? size_t(2) * D * sizeof(T) * ppw + size_t(ppw) * ((k1 + 15) / 16 * 16 + 4) * 4
                          : size_t(k1p) * sizeof(T) * ppw;
@@ -770,15 +780,13 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   }
   uint32_t* keys = reinterpret_cast<uint32_t*>(wsb + lay.keys);
   if (all)
-    RK_LAUNCH("hsa_score", (hsa_score_kernel<T, D, G, true>), dim3(n_ranges, units), dim3(256),
-              lds, s, static_cast<const T*>(q), static_cast<const T*>(kmax),
-              static_cast<const T*>(kmin), nblk_cap, nblk, k1, ppw, keys, lay.keys_pitch,
-              chan_opt, s1_opt);
+    RK_LAUNCH("hsa_score", (hsa_score_kernel<T, D, G, true>), dim3(score_wgs), dim3(256), lds, s,
+              static_cast<const T*>(q), static_cast<const T*>(kmax), static_cast<const T*>(kmin),
+              nblk_cap, nblk, k1, ppw, units, keys, lay.keys_pitch, chan_opt, s1_opt);
   else
-    RK_LAUNCH("hsa_score", (hsa_score_kernel<T, D, G, false>), dim3(n_ranges, units), dim3(256),
-              lds, s, static_cast<const T*>(q), static_cast<const T*>(kmax),
-              static_cast<const T*>(kmin), nblk_cap, nblk, k1, ppw, keys, lay.keys_pitch,
-              chan_opt, s1_opt);
+    RK_LAUNCH("hsa_score", (hsa_score_kernel<T, D, G, false>), dim3(score_wgs), dim3(256), lds, s,
+              static_cast<const T*>(q), static_cast<const T*>(kmax), static_cast<const T*>(kmin),
+              nblk_cap, nblk, k1, ppw, units, keys, lay.keys_pitch, chan_opt, s1_opt);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -807,16 +815,17 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
     attn_attr_set = true;
   }
   if (attn_lds > kAttnDynLds) return hipErrorInvalidValue;
+  const int attn_wgs = (n_split * units + kXcds - 1) / kXcds * kXcds;
   if (cand)
-    RK_LAUNCH("hsa_attn_mt", (hsa_attn_kernel<T, D, G, true>), dim3(n_split, units), dim3(256),
+    RK_LAUNCH("hsa_attn_mt", (hsa_attn_kernel<T, D, G, true>), dim3(attn_wgs), dim3(256),
               attn_lds, s, static_cast<const T*>(q), static_cast<const T*>(k),
               static_cast<const T*>(v), kv_cap, cand, cand_stride, keys, lay.keys_pitch, nblk,
-              lay.nsel, pps, n_split, int(n_tokens), block, scale_log2, part, sel_opt);
+              lay.nsel, pps, n_split, units, int(n_tokens), block, scale_log2, part, sel_opt);
   else
-    RK_LAUNCH("hsa_attn", (hsa_attn_kernel<T, D, G, false>), dim3(n_split, units), dim3(256),
+    RK_LAUNCH("hsa_attn", (hsa_attn_kernel<T, D, G, false>), dim3(attn_wgs), dim3(256),
               attn_lds, s, static_cast<const T*>(q), static_cast<const T*>(k),
               static_cast<const T*>(v), kv_cap, cand, cand_stride, keys, lay.keys_pitch, nblk,
-              lay.nsel, pps, n_split, int(n_tokens), block, scale_log2, part, sel_opt);
+              lay.nsel, pps, n_split, units, int(n_tokens), block, scale_log2, part, sel_opt);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   RK_LAUNCH("hsa_combine", (hsa_combine_kernel<D, G>), dim3((units * G + 3) / 4), dim3(256), 0, s,
             part, n_split, units, out);

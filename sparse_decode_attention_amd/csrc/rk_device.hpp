@@ -80,6 +80,19 @@ __device__ __forceinline__ int clamp_row(int32_t row, int64_t cap) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// XCD-aware work mapping.  MI355X deals the workgroups of a launch out to its
+// 8 XCDs round robin (workgroup L to XCD L mod 8), and each XCD has its own
+// L2.  With a 1-D grid of 8 * ceil(n/8) workgroups, XCD x here takes the
+// contiguous work items [x * per, (x + 1) * per), so neighbouring items
+// (pages of one unit, splits of one unit) share an L2.  Returns the item of
+// this workgroup; items >= n are padding and do nothing.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_local_item(int n_items) {
+  const int per = (n_items + kXcds - 1) / kXcds;
+  const int L = blockIdx.x;
+  return (L % kXcds) * per + L / kXcds;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts build the
 // sums inside each 16-lane row (zero fill at the row edge), then the totals of
 // the earlier rows come in through lane reads.  No LDS traffic.
