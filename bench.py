@@ -136,7 +136,7 @@ class Path:
             "hsa_fused_mt": units * w.k1 * nb0 * esize + units * nsel * w.block * (2 * d * esize + 4)
             + B * Hq * d * esize,
             "aux_build": units * self.n_keep * d * esize + 2 * units * d * nb0 * esize,
-            "gather_kv": 2 * 2 * units * self.n_keep * d * esize,
+            "gather_kv": 2 * 2 * units * self.n_keep * d * esize + 2 * units * d * nb0 * esize,
             "ws_pass1": units * self.S * d * esize + B * Hq * w.window * d * esize,
             "ws_pass2": units * (self.S - w.window) * d * esize + B * Hq * w.window * d * esize,
             "append_kv": units * d * esize * 5,
@@ -152,9 +152,9 @@ class Path:
                                ws=self.ws_e)
             rk.rk_hsa_build_aux(k, self.n_keep, 0, w.block, self.kmax, self.kmin, n_q_heads=w.n_q, idx=self.kept)
         else:
+            # the compaction builds Kmax/Kmin of the compact cache on the way
             rk.rk_snapkv_evict(qw, k, v, self.S, w.window, w.pool, self.n_keep, self.kept, self.kc, self.vc,
-                               None, ws=self.ws_e)
-            rk.rk_hsa_build_aux(self.kc, self.n_keep, 0, w.block, self.kmax, self.kmin, n_q_heads=w.n_q)
+                               None, ws=self.ws_e, kmax=self.kmax, kmin=self.kmin, block=w.block)
 
     def decode_part(self, r):
         rk, w = self.rk, self.w

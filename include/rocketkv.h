@@ -121,13 +121,24 @@ size_t rk_snapkv_workspace_bytes(const rk_shape* shape, int64_t seq_len, int32_t
  *                                   (row n = k[kept_idx[n]]).  Both NULL for
  *                                   the RocketKV-MT form (indices only).
  *   pooled_opt [B, Hkv, seq_len-W]  out (optional, float32): pooled scores
+ *   kmax_opt, kmin_opt [B, Hkv, d, nblk_cap]  out (optional, with k_out): the
+ *                                   HSA step-1 Kmax/Kmin of the compact cache
+ *                                   in pages of `block` tokens, exactly what
+ *                                   rk_hsa_build_aux(k_out, n_keep, 0, block,
+ *                                   ...) writes; built while the rows are
+ *                                   compacted, so the compact K is not read
+ *                                   again.  Both NULL: no aux (block and
+ *                                   nblk_cap are then ignored).
  * Requires 1 <= W <= seq_len <= kv_cap, W <= n_keep <= seq_len, odd
- * pool_kernel >= 1, out_cap >= n_keep when k_out is given, seq_len < 2^31.
+ * pool_kernel >= 1, out_cap >= n_keep when k_out is given, seq_len < 2^31;
+ * with the aux outputs also k_out, block >= 1, ceil(n_keep/block) <=
+ * nblk_cap, nblk_cap a multiple of 8.
  */
 rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* k,
                           const void* v, int64_t kv_cap, int64_t seq_len, int32_t window,
                           int32_t pool_kernel, int64_t n_keep, int32_t* kept_idx,
                           void* k_out, void* v_out, int64_t out_cap, float* pooled_opt,
+                          void* kmax_opt, void* kmin_opt, int64_t nblk_cap, int32_t block,
                           void* ws, size_t ws_bytes, rk_stream stream);
 
 /*

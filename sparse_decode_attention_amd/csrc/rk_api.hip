@@ -165,7 +165,8 @@ size_t rk_snapkv_workspace_bytes(const rk_shape* shape, int64_t seq_len, int32_t
 rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* k,
                           const void* v, int64_t kv_cap, int64_t seq_len, int32_t window,
                           int32_t pool_kernel, int64_t n_keep, int32_t* kept_idx, void* k_out,
-                          void* v_out, int64_t out_cap, float* pooled_opt, void* ws,
+                          void* v_out, int64_t out_cap, float* pooled_opt, void* kmax_opt,
+                          void* kmin_opt, int64_t nblk_cap, int32_t block, void* ws,
                           size_t ws_bytes, rk_stream stream) {
   rk::Dims d;
   rk_status st = check_shape(shape, &d);
@@ -184,14 +185,25 @@ rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* 
   if (pool_kernel < 1 || (pool_kernel % 2) == 0 || pool_kernel > 4097)
     return fail(RK_EINVAL, "pool_kernel must be odd, in [1, 4097]");
   if (k_out && out_cap < n_keep) return fail(RK_EINVAL, "out_cap below n_keep");
+  if ((kmax_opt == nullptr) != (kmin_opt == nullptr))
+    return fail(RK_EINVAL, "kmax_opt and kmin_opt must both be given or both be NULL");
+  if (kmax_opt) {
+    if (!k_out) return fail(RK_EINVAL, "the aux outputs need the compact cache (k_out)");
+    if (!aligned16(kmax_opt) || !aligned16(kmin_opt))
+      return fail(RK_EINVAL, "kmax and kmin must be 16-byte aligned");
+    if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
+    if ((n_keep + block - 1) / block > nblk_cap)
+      return fail(RK_EINVAL, "nblk_cap below the page count of n_keep tokens");
+    if (nblk_cap % 8 != 0) return fail(RK_EINVAL, "nblk_cap must be a multiple of 8");
+  }
   if (int64_t(d.G) * window > 1024)
     return fail(RK_EUNSUPPORTED, "group * window above 1024 rows");
   const rk::EvictWs lay = rk::evict_ws_layout(d, seq_len, window);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != RK_OK) return st;
   return device_status(
       rk::launch_snapkv_evict(d, q_win, k, v, kv_cap, seq_len, window, pool_kernel, n_keep,
-                              kept_idx, k_out, v_out, out_cap, pooled_opt, ws,
-                              static_cast<hipStream_t>(stream)),
+                              kept_idx, k_out, v_out, out_cap, pooled_opt, kmax_opt, kmin_opt,
+                              nblk_cap, block, ws, static_cast<hipStream_t>(stream)),
       "rk_snapkv_evict launch");
 }
 

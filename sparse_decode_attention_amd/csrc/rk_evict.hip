@@ -582,11 +582,94 @@ __global__ __launch_bounds__(256) void ws_mfma_kernel(
   }
 }
 
+// Compaction with the HSA step-1 aux built on the way (the compact K is not
+// read again).  One workgroup per (PPW pages, unit): a page's rows are split
+// over RG row groups of CPR threads (one 16-byte chunk of a row each), which
+// copy their rows of K and V and keep running max/min; the groups merge
+// through LDS and the workgroup writes its pages' Kmax/Kmin channel-major.
+// Exact: max/min only.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather_aux_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
+    const int32_t* __restrict__ kept, int n_keep, T* __restrict__ k_out, T* __restrict__ v_out,
+    int64_t out_cap, int block, T* __restrict__ kmax, T* __restrict__ kmin, int64_t nblk_cap) {
+  constexpr int EPL = Vec16<T>::N;
+  constexpr int CPR = D / EPL;
+  constexpr int RG = 4;
+  constexpr int PPW = 256 / (CPR * RG);
+  static_assert(PPW >= 1 && 256 % (CPR * RG) == 0, "workgroup shape");
+  __shared__ float smx[PPW][RG][D];
+  __shared__ float smn[PPW][RG][D];
+  const int t = threadIdx.x;
+  const int c = t % CPR;
+  const int g = (t / CPR) % RG;
+  const int j = t / (CPR * RG);
+  const int u = blockIdx.y;
+  const int nblk = (n_keep + block - 1) / block;
+  const int p0 = blockIdx.x * PPW;
+  const int p = p0 + j;
+  float mx[EPL], mn[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    mx[e] = -INFINITY;
+    mn[e] = INFINITY;
+  }
+  if (p < nblk) {
+    const int n1 = min((p + 1) * block, n_keep);
+    const int* ku = kept + size_t(u) * n_keep;
+    using Rw = decltype(Vec16<T>::raw);
+    for (int n = p * block + g; n < n1; n += RG) {
+      const size_t src = (size_t(u) * size_t(kv_cap) + size_t(ku[n])) * D + c * EPL;
+      const size_t dst = (size_t(u) * size_t(out_cap) + size_t(n)) * D + c * EPL;
+      const Vec16<T> kr = load16(k + src);
+      *reinterpret_cast<Rw*>(v_out + dst) = *reinterpret_cast<const Rw*>(v + src);
+      *reinterpret_cast<Rw*>(k_out + dst) = kr.raw;
+      float x[EPL];
+      unpack16(kr, x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        mx[e] = x[e] > mx[e] ? x[e] : mx[e];
+        mn[e] = x[e] < mn[e] ? x[e] : mn[e];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    smx[j][g][c * EPL + e] = mx[e];
+    smn[j][g][c * EPL + e] = mn[e];
+  }
+  __syncthreads();
+  T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
+  T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
+  for (int e = t; e < D * PPW; e += 256) {
+    const int ch = e / PPW;
+    const int jj = e % PPW;
+    if (p0 + jj < nblk) {
+      float a = smx[jj][0][ch], b = smn[jj][0][ch];
+#pragma unroll
+      for (int gg = 1; gg < RG; ++gg) {
+        const float x = smx[jj][gg][ch], y = smn[jj][gg][ch];
+        a = x > a ? x : a;
+        b = y < b ? y : b;
+      }
+      if constexpr (sizeof(T) == 2) {
+        // the values came from bf16, so dropping the low half is exact
+        xu[size_t(ch) * nblk_cap + p0 + jj].bits = uint16_t(__float_as_uint(a) >> 16);
+        nu[size_t(ch) * nblk_cap + p0 + jj].bits = uint16_t(__float_as_uint(b) >> 16);
+      } else {
+        xu[size_t(ch) * nblk_cap + p0 + jj] = a;
+        nu[size_t(ch) * nblk_cap + p0 + jj] = b;
+      }
+    }
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const void* v,
                           int64_t kv_cap, int64_t S64, int W, int pool_kernel, int64_t n_keep,
                           int32_t* kept, void* k_out, void* v_out, int64_t out_cap,
-                          float* pooled_opt, void* ws, hipStream_t s) {
+                          float* pooled_opt, void* kmax, void* kmin, int64_t nblk_cap, int block,
+                          void* ws, hipStream_t s) {
   const int S = int(S64);
   const int P = S - W;
   const EvictWs lay = evict_ws_layout(d, S64, W);
@@ -688,7 +771,15 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
               staged ? size_t(P) * 4 : size_t(0), s, pooled, S, W, int(n_keep), staged, kept);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (k_out) {
+  if (k_out && kmax) {
+    constexpr int PPW = 256 / ((D / Vec16<T>::N) * 4);
+    const int64_t nblk = (n_keep + block - 1) / block;
+    RK_LAUNCH("gather_kv", (gather_aux_kernel<T, D>), dim3(unsigned((nblk + PPW - 1) / PPW), units),
+              dim3(256), 0, s, kk, static_cast<const T*>(v), kv_cap, kept, int(n_keep),
+              static_cast<T*>(k_out), static_cast<T*>(v_out), out_cap, block,
+              static_cast<T*>(kmax), static_cast<T*>(kmin), nblk_cap);
+    err = hipGetLastError();
+  } else if (k_out) {
     RK_LAUNCH("gather_kv", (gather_kernel<T, D>), dim3(unsigned((n_keep + 63) / 64), units),
                        dim3(256), 0, s, kk, static_cast<const T*>(v), kv_cap, kept, int(n_keep),
                        static_cast<T*>(k_out), static_cast<T*>(v_out), out_cap);
@@ -702,19 +793,18 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
 hipError_t launch_snapkv_evict(const Dims& d, const void* q_win, const void* k, const void* v,
                                int64_t kv_cap, int64_t S, int W, int pool_kernel,
                                int64_t n_keep, int32_t* kept, void* k_out, void* v_out,
-                               int64_t out_cap, float* pooled_opt, void* ws, hipStream_t s) {
+                               int64_t out_cap, float* pooled_opt, void* kmax, void* kmin,
+                               int64_t nblk_cap, int block, void* ws, hipStream_t s) {
+#define RK_EVICT(TT, DD)                                                                      \
+  return launch_evict_t<TT, DD>(d, q_win, k, v, kv_cap, S, W, pool_kernel, n_keep, kept, k_out, \
+                                v_out, out_cap, pooled_opt, kmax, kmin, nblk_cap, block, ws, s)
   if (d.bf16) {
-    if (d.D == 128)
-      return launch_evict_t<bf16_t, 128>(d, q_win, k, v, kv_cap, S, W, pool_kernel, n_keep,
-                                         kept, k_out, v_out, out_cap, pooled_opt, ws, s);
-    return launch_evict_t<bf16_t, 64>(d, q_win, k, v, kv_cap, S, W, pool_kernel, n_keep, kept,
-                                      k_out, v_out, out_cap, pooled_opt, ws, s);
+    if (d.D == 128) RK_EVICT(bf16_t, 128);
+    RK_EVICT(bf16_t, 64);
   }
-  if (d.D == 128)
-    return launch_evict_t<float, 128>(d, q_win, k, v, kv_cap, S, W, pool_kernel, n_keep, kept,
-                                      k_out, v_out, out_cap, pooled_opt, ws, s);
-  return launch_evict_t<float, 64>(d, q_win, k, v, kv_cap, S, W, pool_kernel, n_keep, kept,
-                                   k_out, v_out, out_cap, pooled_opt, ws, s);
+  if (d.D == 128) RK_EVICT(float, 128);
+  RK_EVICT(float, 64);
+#undef RK_EVICT
 }
 
 }  // namespace rk

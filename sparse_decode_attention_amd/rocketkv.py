@@ -44,7 +44,7 @@ _lib.rk_split.argtypes = [_f64, _i64, _i32, _i32, _i32, ctypes.POINTER(RkSplitOu
 _lib.rk_snapkv_workspace_bytes.argtypes = [_SP, _i64, _i32]
 _lib.rk_snapkv_workspace_bytes.restype = _sz
 _lib.rk_snapkv_evict.argtypes = [_SP, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i64, _vp, _vp, _vp,
-                                 _i64, _vp, _vp, _sz, _vp]
+                                 _i64, _vp, _vp, _vp, _i64, _i32, _vp, _sz, _vp]
 _lib.rk_hsa_build_aux.argtypes = [_SP, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _i64, _vp]
 _lib.rk_hsa_workspace_bytes.argtypes = [_SP, _i64, _i32, _i32, _i32]
 _lib.rk_hsa_workspace_bytes.restype = _sz
@@ -118,19 +118,23 @@ def rk_snapkv_workspace_bytes(shape: RkShape, seq_len: int, window: int) -> int:
 
 
 def rk_snapkv_evict(q_win, k, v, seq_len, window, pool_kernel, n_keep, kept_idx,
-                    k_out=None, v_out=None, pooled=None, ws=None, stream=None):
+                    k_out=None, v_out=None, pooled=None, ws=None, stream=None,
+                    kmax=None, kmin=None, block=16):
     """Stage 1.  q_win [B,Hq,W,d]; k, v [B,Hkv,cap,d]; kept_idx [B,Hkv,n_keep] int32;
-    k_out, v_out [B,Hkv,out_cap,d] or None (RocketKV-MT); pooled [B,Hkv,S-W] fp32 or None."""
-    _need_contig(q_win, k, v, kept_idx, k_out, v_out, pooled)
+    k_out, v_out [B,Hkv,out_cap,d] or None (RocketKV-MT); pooled [B,Hkv,S-W] fp32 or None;
+    kmax, kmin [B,Hkv,d,nblk_cap] or None: also build the compact cache's Kmax/Kmin in
+    pages of `block` tokens."""
+    _need_contig(q_win, k, v, kept_idx, k_out, v_out, pooled, kmax, kmin)
     B, Hq, W, d = q_win.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     nbytes = rk_snapkv_workspace_bytes(shape, seq_len, window)
     ws = _ws(nbytes, k, ws)
     out_cap = k_out.shape[2] if k_out is not None else 0
+    nblk_cap = kmax.shape[3] if kmax is not None else 0
     _check(_lib.rk_snapkv_evict(ctypes.byref(shape), _ptr(q_win), _ptr(k), _ptr(v), k.shape[2],
                                 seq_len, window, pool_kernel, n_keep, _ptr(kept_idx), _ptr(k_out),
-                                _ptr(v_out), out_cap, _ptr(pooled), _ptr(ws), ws.numel(),
-                                _stream(stream)), "rk_snapkv_evict")
+                                _ptr(v_out), out_cap, _ptr(pooled), _ptr(kmax), _ptr(kmin), nblk_cap,
+                                block, _ptr(ws), ws.numel(), _stream(stream)), "rk_snapkv_evict")
     return ws
 
 

@@ -61,9 +61,12 @@ def ascending(x) -> bool:
 
 
 # --------------------------------------------------------------------------
-def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compact=True, out_cap=None):
-    """Run rk_snapkv_evict and check every (or the given) unit against the oracle.
-    Returns (kept, k_out, v_out, pooled, swaps)."""
+def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compact=True, out_cap=None,
+                    aux_block=None):
+    """Run rk_snapkv_evict and check every (or the given) unit against the oracle;
+    with aux_block, the call also builds Kmax/Kmin of the compact cache, checked
+    bit-exactly.  Returns (kept, k_out, v_out, pooled, swaps), plus (kmax, kmin)
+    with aux_block."""
     B, Hq, _, d = qw.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
@@ -71,10 +74,16 @@ def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compa
     kept = torch.full((B, Hkv, n_keep), -1, dtype=torch.int32, device=dev)
     pooled = torch.empty(B, Hkv, S - W, dtype=torch.float32, device=dev)
     ko = vo = None
+    kmax = kmin = None
     if compact:
         ko = torch.empty(B, Hkv, out_cap or n_keep, d, dtype=k.dtype, device=dev)
         vo = torch.empty_like(ko)
-    rk.rk_snapkv_evict(qw, k, v, S, W, pool, n_keep, kept, ko, vo, pooled)
+        if aux_block:
+            kmax = torch.full((B, Hkv, d, rk.aux_capacity(out_cap or n_keep, aux_block)), 7.0,
+                              dtype=k.dtype, device=dev)
+            kmin = torch.full_like(kmax, 7.0)
+    rk.rk_snapkv_evict(qw, k, v, S, W, pool, n_keep, kept, ko, vo, pooled, kmax=kmax, kmin=kmin,
+                       block=aux_block or 16)
     torch.cuda.synchronize()
     swaps = 0
     units = units_to_check or [(b, h) for b in range(B) for h in range(Hkv)]
@@ -96,6 +105,15 @@ def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compa
         if compact:
             idx = torch.as_tensor(got, dtype=torch.long, device=dev)
             assert torch.equal(ko[b, h, :n_keep], k[b, h, idx]) and torch.equal(vo[b, h, :n_keep], v[b, h, idx])
+        if kmax is not None:
+            nblk = -(-n_keep // aux_block)
+            wmax, wmin = O.build_aux(np32(ko[b, h, :n_keep]), n_keep, aux_block)
+            assert np.array_equal(np32(kmax[b, h, :, :nblk]), wmax), (b, h)
+            assert np.array_equal(np32(kmin[b, h, :, :nblk]), wmin), (b, h)
+            # pages beyond the compact cache are left untouched
+            assert bool((kmax[b, h, :, nblk:] == 7.0).all()) and bool((kmin[b, h, :, nblk:] == 7.0).all())
+    if aux_block:
+        return kept, ko, vo, pooled, swaps, kmax, kmin
     return kept, ko, vo, pooled, swaps
 
 

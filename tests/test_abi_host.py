@@ -126,11 +126,13 @@ def test_error_codes_before_any_launch(rk):
 
     def evict(**kw):
         a = dict(q=_vp(FAKE), k=_vp(FAKE), v=_vp(FAKE), cap=2048, S=2048, W=16, pool=7, keep=930,
-                 kept=_vp(FAKE), ko=_vp(FAKE), vo=_vp(FAKE), out_cap=930, ws=_vp(FAKE), wsb=1 << 30)
+                 kept=_vp(FAKE), ko=_vp(FAKE), vo=_vp(FAKE), out_cap=930, ws=_vp(FAKE), wsb=1 << 30,
+                 kmax=None, kmin=None, nblk_cap=0, block=16)
         a.update(kw)
         return lib.rk_snapkv_evict(byref(sh), a["q"], a["k"], a["v"], a["cap"], a["S"], a["W"],
                                    a["pool"], a["keep"], a["kept"], a["ko"], a["vo"], a["out_cap"],
-                                   None, a["ws"], a["wsb"], None)
+                                   None, a["kmax"], a["kmin"], a["nblk_cap"], a["block"], a["ws"],
+                                   a["wsb"], None)
 
     assert evict(pool=8) == rk.RK_EINVAL and evict(pool=0) == rk.RK_EINVAL
     assert evict(keep=15) == rk.RK_EINVAL and evict(keep=2049) == rk.RK_EINVAL
@@ -138,6 +140,12 @@ def test_error_codes_before_any_launch(rk):
     assert evict(S=4096) == rk.RK_EINVAL                                # above kv_cap
     assert evict(out_cap=929) == rk.RK_EINVAL
     assert evict(vo=None) == rk.RK_EINVAL                               # k_out without v_out
+    assert evict(kmax=_vp(FAKE)) == rk.RK_EINVAL                        # kmax without kmin
+    aux = dict(kmax=_vp(FAKE), kmin=_vp(FAKE), nblk_cap=64)
+    assert evict(**aux, block=0) == rk.RK_EINVAL
+    assert evict(**dict(aux, nblk_cap=56)) == rk.RK_EINVAL               # 930 tokens need 59 pages
+    assert evict(**dict(aux, nblk_cap=60)) == rk.RK_EINVAL               # not a multiple of 8
+    assert evict(**aux, ko=None, vo=None) == rk.RK_EINVAL                # aux needs the compact cache
     assert evict(wsb=100) == rk.RK_EWORKSPACE
     need = lib.rk_snapkv_workspace_bytes(byref(sh), 2048, 16)
     assert need > 0 and evict(wsb=need - 1) == rk.RK_EWORKSPACE

@@ -32,14 +32,18 @@ def say(*a):
     print("[case]", *a, file=sys.stderr, flush=True)
 
 
-def _pipeline(rk, w, layer=0, steps=None, seed=0):
+def _pipeline(rk, w, layer=0, steps=None, seed=0, fused_aux=True):
     """Stage 1 + aux + decode steps of one layer of workload w, checked stage-wise."""
     s = rk.rk_split(w.c, w.seq, w.window, w.block, w.d)
     k, v, pos = WL.layer_kv(w, layer, device=DEV, seed=seed)
     qw = WL.window_queries(w, layer, device=DEV, seed=seed)
     n_keep, k2 = s["n_keep"], WL.stage2_pages(w, s)
-    kept, kc, vc, pooled, sw1 = U.evict_and_check(rk, qw, k, v, w.seq, w.window, w.pool, n_keep)
-    kmax, kmin = U.aux_and_check(rk, kc, n_keep, w.block, w.n_q)
+    if fused_aux:   # the compaction builds Kmax/Kmin on the way
+        kept, kc, vc, pooled, sw1, kmax, kmin = U.evict_and_check(rk, qw, k, v, w.seq, w.window, w.pool,
+                                                                  n_keep, aux_block=w.block)
+    else:
+        kept, kc, vc, pooled, sw1 = U.evict_and_check(rk, qw, k, v, w.seq, w.window, w.pool, n_keep)
+        kmax, kmin = U.aux_and_check(rk, kc, n_keep, w.block, w.n_q)
     swaps = 0
     for step in range(w.decode_steps if steps is None else steps):
         q = WL.decode_query(w, layer, step, device=DEV, seed=seed)
@@ -51,7 +55,7 @@ def _pipeline(rk, w, layer=0, steps=None, seed=0):
 def test_tiny_gqa_fp32_full_pipeline(rk):
     w = WL.WORKLOADS["tiny-gqa-s2048-d64-fp32"]
     say(w.name, "all 8 decode steps")
-    res = _pipeline(rk, w)
+    res = _pipeline(rk, w, fused_aux=False)     # separate aux build
     # the planted keys survive stage 1
     kept = res["kept"].cpu().numpy()
     for h in range(w.n_kv):
