@@ -135,7 +135,7 @@ __device__ __forceinline__ void wave_choose_channels(const float (&qx)[D / kWave
     kr[r] = order_key(a);
     qb[r] = s;
   }
-  wave_topk<R, 1024>(kr, D, k1, [&](int rank, int ch) {
+  wave_topk<R>(kr, D, k1, [&](int rank, int ch) {
     float qv = qb[0];  // the emitting lane holds the channel's q_bar
 #pragma unroll
     for (int r = 1; r < R; ++r)
@@ -207,6 +207,7 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
     wave_choose_channels<T, D, G>(qx, k1, i1_q, i1_off,
                                   chan_opt && p0 == 0 ? chan_opt + size_t(u) * k1 : nullptr,
                                   hist);
+  RK_PHASE(17);
   if (ALL) {
 #pragma unroll
     for (int x = 0; x < NBA; ++x) {
@@ -236,6 +237,7 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
       prod[b * pp + j] = i1_q[j] * to_f32(stage[size_t(r) * ppw + b]);
     }
     __syncthreads();
+    RK_PHASE(19);
     for (int b = t; b < np; b += 256) {
       const float* pb = prod + b * pp;
       float acc = 0.f;
@@ -473,19 +475,17 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   const int np = min(e0 + pages_per_split, nsel) - e0;
   int32_t* so = sel_opt && split == 0 ? sel_opt + size_t(u) * nsel : nullptr;
   const uint32_t* kg = keys + size_t(u) * keys_pitch;
-  auto emit = [&](int r, int i) {
+  auto emit = [=](int r, int i) {  // by value: no local needs an address
     if (r >= e0 && r < e0 + np) pages[r - e0] = i;
     if (so) so[r] = i;
   };
+  static_assert(kWaveTopkPages <= 16 * kWave, "one-wave top-k holds at most 16 rows");
   if (nblk <= kWaveTopkPages) {
-    // one wave selects from keys held in registers; no barrier inside
-    if (wave == 0) {
-      constexpr int RK = kWaveTopkPages / kWave;
-      uint32_t kr[RK];
-#pragma unroll
-      for (int r = 0; r < RK; ++r) kr[r] = r * kWave + lane < nblk ? kg[r * kWave + lane] : 0u;
-      wave_topk<RK, 1024>(kr, nblk, nsel, emit, tsm.hist[0]);
-    }
+    // one wave selects from keys held in registers (no barrier inside) and
+    // emits only the ranks this split needs (all of them for the sel output)
+    if (wave == 0)
+      wave_topk_rows([=](int i) { return kg[i]; }, nblk, nsel, emit, tsm.hist[0], so ? 0 : e0,
+                     so ? nsel : e0 + np);
   } else {
     uint32_t* kl = attn_lds + pages_per_split;  // [keys_pitch]
     for (int i = threadIdx.x; i < keys_pitch / 4; i += 256)
@@ -588,18 +588,13 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
 
   RK_PHASE(2);
   int32_t* so = sel_opt ? sel_opt + size_t(u) * nsel : nullptr;
-  auto emit = [&](int r, int i) {
+  auto emit = [=](int r, int i) {
     pages[r] = i;
     if (so) so[r] = i;
   };
   if (nblk <= kWaveTopkPages) {
-    if (wave == 0) {
-      constexpr int RK = kWaveTopkPages / kWave;
-      uint32_t kr[RK];
-#pragma unroll
-      for (int r = 0; r < RK; ++r) kr[r] = r * kWave + lane < nblk ? pkeys[r * kWave + lane] : 0u;
-      wave_topk<RK, 1024>(kr, nblk, nsel, emit, tsm.hist[0]);
-    }
+    if (wave == 0)
+      wave_topk_rows([=](int i) { return pkeys[i]; }, nblk, nsel, emit, tsm.hist[0], 0, nsel);
   } else {
     wg_topk<NT, 1024>([&](int i) { return pkeys[i]; }, nblk, nsel, emit, tsm);
   }

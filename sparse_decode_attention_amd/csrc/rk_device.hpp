@@ -233,7 +233,7 @@ __device__ __forceinline__ void wg_topk_emit(const KeyFn& key, int n, uint32_t T
 // third barrier per pass after the first.
 template <int NT, int BINS, int NBUF = 2>
 struct TopkSmem {
-  uint32_t hist[NBUF][BINS];
+  alignas(16) uint32_t hist[NBUF][BINS];
   uint32_t red[2 * (NT / kWave)];
   int tmp[2 * (NT / kWave) + 2];
 };
@@ -301,49 +301,115 @@ __device__ __forceinline__ void wave_topk_emit(const KeyFn& key, int n, uint32_t
   }
 }
 
-// Top-k by one wave over n <= 64*R keys held in registers: lane l holds the
-// key of position l + 64 r in kr[r] (positions >= n are ignored).  Same
-// selection, emission order and range-adaptive passes as wg_topk, but the
-// histogram (BINS words of LDS) belongs to the wave alone and LDS operations
-// of one wave complete in order, so no barrier is needed anywhere: the
-// histogram is read right after its atomics.  Emission takes the 64-position
-// rows in order with ballots.
-template <int R, int BINS, typename EmitFn>
-__device__ void wave_topk(const uint32_t (&kr)[R], int n, int k, const EmitFn& emit,
-                          uint32_t* hist) {
-  constexpr int LOG_BINS = BINS == 256 ? 8 : BINS == 512 ? 9 : BINS == 1024 ? 10 : 11;
-  static_assert((1 << LOG_BINS) == BINS && BINS <= 2048 && BINS >= 256, "bins");
+// Keys ranked against each other once the radix bin holding the cut has at
+// most this many keys (one wave's passes stop there).
+constexpr int kWaveRankMax = 16;
+
+// Exact cut among the c <= kWaveRankMax keys of [lo, hi]: the keys are packed
+// into LDS slots (position order), lane l takes slot l and counts the slots
+// above it (gt) and at or above it (ge) with broadcast reads; the lane with
+// gt < need <= ge holds T, the need-th largest of the range.  Returns T, the
+// keys still needed at T (need - gt) and how many keys equal T (ge - gt).
+template <int R>
+__device__ __forceinline__ uint3 wave_rank_range(const uint32_t (&kz)[R], int n, uint32_t lo,
+                                                 uint32_t hi, int need, uint32_t* slots) {
   const int lane = lane_id();
-  if (k <= 0) return;
-  const int rows = (n + kWave - 1) / kWave;  // rows holding keys (wave-uniform)
-  if (k >= n) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (r >= rows) break;
-      if (r * kWave + lane < n) emit(r * kWave + lane, r * kWave + lane);
-    }
-    return;
-  }
-  uint32_t lo = 0xffffffffu, hi = 0u;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int cnt = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r >= rows) break;
-    if (r * kWave + lane < n) {
+    const bool in = r * kWave + lane < n && kz[r] >= lo && kz[r] <= hi;
+    const unsigned long long m = __ballot(in);
+    if (m) {
+      if (in) slots[cnt + __popcll(m & below)] = kz[r];
+      cnt += __popcll(m);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  const uint32_t mine = lane < cnt ? slots[lane] : 0u;
+  int gt = 0, ge = 0;
+#pragma unroll
+  for (int j = 0; j < kWaveRankMax; j += 4) {
+    const uint4 s4 = *reinterpret_cast<const uint4*>(slots + j);
+    const uint32_t sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool live = j + e < cnt;
+      gt += live && sv[e] > mine ? 1 : 0;
+      ge += live && sv[e] >= mine ? 1 : 0;
+    }
+  }
+  const unsigned long long hit = __ballot(lane < cnt && gt < need && ge >= need);
+  const int L = __ffsll(static_cast<long long>(hit)) - 1;
+  const int gtL = __builtin_amdgcn_readlane(gt, L), geL = __builtin_amdgcn_readlane(ge, L);
+  return make_uint3(uint32_t(__builtin_amdgcn_readlane(int(mine), L)), uint32_t(need - gtL),
+                    uint32_t(geL - gtL));
+}
+
+// Where a top-k cuts: every key > T, then the first need_eq keys equal to T
+// (position order); when `fast`, exactly the keys >= thr.
+struct TopkCut {
+  uint32_t T, thr;
+  int need_eq;
+  bool fast;
+};
+
+// Keys of one lane's rows with 0 at positions >= n (counts only ask for
+// keys >= 1), and the wave's key range.
+template <int R>
+__device__ __forceinline__ void topk_prepare(const uint32_t (&kr)[R], int n, uint32_t (&kz)[R],
+                                             uint32_t& lo, uint32_t& hi) {
+  const int lane = lane_id();
+  lo = 0xffffffffu;
+  hi = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool valid = r * kWave + lane < n;
+    kz[r] = valid ? kr[r] : 0u;
+    if (valid) {
       lo = min(lo, kr[r]);
       hi = max(hi, kr[r]);
     }
   }
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
-  int need = k;
-  uint32_t T;
-  int need_eq;
+}
+
+// The cut of a top-k (0 < k < n) over keys held by one wave: range-adaptive
+// radix passes, each a histogram of the live key range [lo, hi] over BINS
+// bins of LDS (hist: BINS words, 16-byte aligned, the wave's own; LDS
+// operations of one wave complete in order, so it is read right after its
+// atomics with no barrier), narrowing to the bin that holds the cut; once
+// that bin holds at most kWaveRankMax keys they are ranked against each
+// other instead.  Rows at or beyond `rows` hold no keys and are skipped.
+template <int R, int BINS>
+__device__ __forceinline__ TopkCut wave_topk_cut(const uint32_t (&kz)[R], int n, int rows, int k,
+                                                 uint32_t lo, uint32_t hi, uint32_t* hist) {
+  constexpr int LOG_BINS = BINS == 256 ? 8 : BINS == 512 ? 9 : BINS == 1024 ? 10 : 11;
+  static_assert((1 << LOG_BINS) == BINS && BINS <= 2048 && BINS >= 256, "bins");
+  const int lane = lane_id();
+  // state: [lo, hi] holds the cut, `need` more keys come from it, and it
+  // holds in_range keys (need <= in_range)
+  int need = k, in_range = n;
+  TopkCut cut{0u, 0u, 0, false};
 #pragma unroll 1
   while (true) {
+    if (need == in_range) {  // the whole range is taken
+      cut.thr = lo;
+      cut.fast = true;
+      return cut;
+    }
     if (lo == hi) {
-      T = lo;
-      need_eq = need;
-      break;
+      cut.T = lo;
+      cut.need_eq = need;
+      return cut;
+    }
+    if (in_range <= kWaveRankMax) {
+      const uint3 c = wave_rank_range(kz, n, lo, hi, need, hist);
+      cut.T = cut.thr = c.x;
+      cut.need_eq = int(c.y);
+      cut.fast = c.y == c.z;
+      return cut;
     }
     const int span_bits = 32 - __clz(int(hi - lo));
     const int shift = span_bits > LOG_BINS ? span_bits - LOG_BINS : 0;
@@ -352,50 +418,121 @@ __device__ void wave_topk(const uint32_t (&kr)[R], int n, int k, const EmitFn& e
       *reinterpret_cast<uint4*>(hist + lane * (BINS / kWave) + j) = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (r >= rows) break;
-      const uint32_t kk = kr[r];
-      if (r * kWave + lane < n && kk >= lo && kk <= hi) atomicAdd(&hist[(kk - lo) >> shift], 1u);
+      if (r < rows) {
+        const uint32_t kk = kz[r];
+        if (r * kWave + lane < n && kk >= lo && kk <= hi) atomicAdd(&hist[(kk - lo) >> shift], 1u);
+      }
     }
     const int3 f = wave_find_bin<BINS>(hist, need);
     const uint32_t blo = lo + (uint32_t(f.x) << shift);
-    if (shift == 0) {
-      T = blo;
-      need_eq = f.y;
-      break;
-    }
-    if (f.y == f.z) {  // whole bin taken: every key >= blo (blo > 0 as in wg_topk)
-      T = blo - 1u;
-      need_eq = 0;
-      break;
-    }
     const uint64_t bhi = uint64_t(blo) + ((uint64_t(1) << shift) - 1u);
     hi = bhi < uint64_t(hi) ? uint32_t(bhi) : hi;
     lo = blo;
     need = f.y;
+    in_range = f.z;
   }
+}
+
+// Emission of a cut by one wave: calls emit(rank, position) for the selected
+// keys whose rank lies in [rank_lo, rank_hi); the rows' selection masks come
+// first, so rows outside that rank window are skipped whole.
+template <int R, typename EmitFn>
+__device__ __forceinline__ void wave_emit_cut(const uint32_t (&kz)[R], int n, const TopkCut& cut,
+                                              const EmitFn& emit, int rank_lo, int rank_hi) {
+  const int lane = lane_id();
   const unsigned long long below = (1ull << lane) - 1ull;
+  if (cut.fast) {
+    unsigned long long sm[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) sm[r] = __ballot(kz[r] >= cut.thr && r * kWave + lane < n);
+    int base = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int cnt = __popcll(sm[r]);
+      if (cnt > 0 && base < rank_hi && base + cnt > rank_lo) {
+        const int rank = base + __popcll(sm[r] & below);
+        if (((sm[r] >> lane) & 1ull) && rank >= rank_lo && rank < rank_hi)
+          emit(rank, r * kWave + lane);
+      }
+      base += cnt;
+    }
+    return;
+  }
   int base = 0, eq_seen = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    if (r >= rows) break;
     const int i = r * kWave + lane;
-    const uint32_t kk = kr[r];
-    const bool eq = i < n && kk == T;
+    const bool eq = i < n && kz[r] == cut.T;
     const unsigned long long em = __ballot(eq);
-    const bool sel = (i < n && kk > T) || (eq && eq_seen + __popcll(em & below) < need_eq);
+    const bool sel =
+        (i < n && kz[r] > cut.T) || (eq && eq_seen + __popcll(em & below) < cut.need_eq);
     const unsigned long long sm = __ballot(sel);
-    if (sel) emit(base + __popcll(sm & below), i);
+    const int rank = base + __popcll(sm & below);
+    if (sel && rank >= rank_lo && rank < rank_hi) emit(rank, i);
     base += __popcll(sm);
     eq_seen += __popcll(em);
   }
+}
+
+// Top-k by one wave over n <= 64*R keys held in registers: lane l holds the
+// key of position l + 64 r in kr[r] (positions >= n are ignored).  Same
+// selection and emission order as wg_topk (every key above the threshold,
+// then the keys equal to it in position order); emit(rank, position) is
+// called for ranks in [rank_lo, rank_hi) only.  hist: 256 words of LDS,
+// 16-byte aligned, the wave's own.
+template <int R, typename EmitFn>
+__device__ __forceinline__ void wave_topk(const uint32_t (&kr)[R], int n, int k, const EmitFn& emit,
+                                          uint32_t* hist, int rank_lo = 0, int rank_hi = 1 << 30) {
+  if (k <= 0) return;
+  if (k >= n) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = r * kWave + lane;
+      if (i < n && i >= rank_lo && i < rank_hi) emit(i, i);
+    }
+    return;
+  }
+  uint32_t kz[R], lo, hi;
+  topk_prepare(kr, n, kz, lo, hi);
+  RK_PHASE(9);
+  const TopkCut cut = wave_topk_cut<R, 256>(kz, n, (n + kWave - 1) / kWave, k, lo, hi, hist);
+  RK_PHASE(23);
+  wave_emit_cut(kz, n, cut, emit, rank_lo, rank_hi);
+}
+
+// One wave's top-k over n <= 16*64 keys read through key(i), with the
+// register rows sized to n (4, 8, 12 or 16 rows of 64 keys), since the
+// passes and the emission cost per row.
+template <int R, typename KeyFn, typename EmitFn>
+__device__ __forceinline__ void wave_topk_load(const KeyFn& key, int n, int k, const EmitFn& emit,
+                                               uint32_t* hist, int rank_lo, int rank_hi) {
+  const int lane = lane_id();
+  uint32_t kr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) kr[r] = r * kWave + lane < n ? key(r * kWave + lane) : 0u;
+  wave_topk<R>(kr, n, k, emit, hist, rank_lo, rank_hi);
+}
+template <typename KeyFn, typename EmitFn>
+__device__ __forceinline__ void wave_topk_rows(const KeyFn& key, int n, int k, const EmitFn& emit,
+                                               uint32_t* hist, int rank_lo, int rank_hi) {
+  const int rows = (n + kWave - 1) / kWave;
+  if (rows <= 4)
+    wave_topk_load<4>(key, n, k, emit, hist, rank_lo, rank_hi);
+  else if (rows <= 8)
+    wave_topk_load<8>(key, n, k, emit, hist, rank_lo, rank_hi);
+  else if (rows <= 12)
+    wave_topk_load<12>(key, n, k, emit, hist, rank_lo, rank_hi);
+  else
+    wave_topk_load<16>(key, n, k, emit, hist, rank_lo, rank_hi);
 }
 
 // Most keys one wave emits; above it the workgroup emits (scan based).
 constexpr int kWaveEmitMax = 1024;
 
 template <int NT, int BINS, int NBUF, typename KeyFn, typename EmitFn>
-__device__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit,
-                        TopkSmem<NT, BINS, NBUF>& sm) {
+__device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit,
+                                        TopkSmem<NT, BINS, NBUF>& sm) {
   constexpr int NW = NT / kWave;
   constexpr int LOG_BINS = BINS == 256 ? 8 : BINS == 512 ? 9 : BINS == 1024 ? 10 : 11;
   static_assert(BINS % NT == 0 || NT % BINS == 0, "bins");

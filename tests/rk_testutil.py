@@ -163,7 +163,8 @@ def decode_and_check(rk, q, kc, vc, kmax, kmin, n_tokens, block, k1, k2, cand=No
         assert np.array_equal(np32(s1[b, h]), ws1), (b, h)           # same float32 ops, same order
         gsel = sel[b, h].cpu().numpy()
         assert ascending(gsel) or nsel == 1
-        swaps += compare_sets(gsel, O.block_select(ws1, k2), ws1)
+        # the scores are bit-exact, so the page choice (ties to the lower page) is too
+        assert np.array_equal(gsel, O.block_select(ws1, k2)), (b, h)
         toks = O.selected_tokens(gsel, n_tokens, block)
         if cand is None:
             rows = toks

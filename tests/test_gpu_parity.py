@@ -360,6 +360,27 @@ def test_many_pages_decode(rk, B, Hkv, n, k2):
     _decode_only(rk, w, n, 64, k2, units_to_check=units, steps=1)
 
 
+@pytest.mark.parametrize("B,spread", [(1, 2), (1, 200), (20, 2), (20, 200)])
+def test_page_topk_exact_ties(rk, B, spread):
+    """Integer-valued q and Kmax/Kmin make many channel sums and page scores
+    exactly equal (spread 2: a few distinct scores; 200: scattered ties): the
+    channel and page choices must follow the lower-index tie rule exactly, on
+    the split path (8 units) and the fused path (160 units)."""
+    say("exact ties", B, spread)
+    Hkv, G, d, n, block, k1, k2 = 8, 4, 128, 605 * 16 - 7, 16, 64, 128
+    g = torch.Generator().manual_seed(1000 + spread + B)
+    q = torch.randint(-2, 3, (B, Hkv * G, d), generator=g).to(torch.bfloat16).to(DEV)
+    cap = rk.aux_capacity(n, block)
+    kmax = torch.randint(0, spread + 1, (B, Hkv, d, cap), generator=g)
+    kmin = kmax - torch.randint(0, spread + 1, (B, Hkv, d, cap), generator=g)
+    kmax = kmax.to(torch.bfloat16).to(DEV)
+    kmin = kmin.to(torch.bfloat16).to(DEV)
+    kc = torch.randn(B, Hkv, n, d, generator=g).to(torch.bfloat16).to(DEV)
+    vc = torch.randn(B, Hkv, n, d, generator=g).to(torch.bfloat16).to(DEV)
+    units = None if B == 1 else [(0, 0), (7, 3), (13, 5), (B - 1, Hkv - 1)]
+    U.decode_and_check(rk, q, kc, vc, kmax, kmin, n, block, k1, k2, units_to_check=units)
+
+
 @pytest.mark.parametrize("n_keep", [3000, 15000])
 def test_long_prompt_select(rk, n_keep):
     """More prompt keys than LDS holds (80000): the chunked two-launch select
