@@ -87,7 +87,8 @@ __device__ __forceinline__ void score_staged(const T* stage, int np, int k1, con
   for (int b = threadIdx.x; b < np; b += NT) {
     const T* sp = stage + size_t(b) * k1p;
     float acc = 0.f;
-    for (int j0 = 0; j0 < k1; j0 += 16) {
+    // whole 16-channel blocks unmasked, then the masked tail block
+    auto block16 = [&](int j0, int lim) {
       float qv[16], sv[16];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
@@ -105,8 +106,12 @@ __device__ __forceinline__ void score_staged(const T* stage, int np, int k1, con
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        if (j0 + e < k1) acc = acc + qv[e] * sv[e];
-    }
+        if (e < lim) acc = acc + qv[e] * sv[e];
+    };
+    const int kfull = k1 & ~15;
+#pragma unroll 2
+    for (int j0 = 0; j0 < kfull; j0 += 16) block16(j0, 16);
+    if (kfull < k1) block16(kfull, k1 - kfull);
     keys[b] = order_key(acc);
     if (s1) s1[b] = acc;
   }
@@ -241,7 +246,9 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
     for (int b = t; b < np; b += 256) {
       const float* pb = prod + b * pp;
       float acc = 0.f;
-      for (int j0 = 0; j0 < k1; j0 += 16) {
+      // whole 16-channel blocks unmasked, then the masked tail block
+      const int kfull = k1 & ~15;
+      auto block16 = [&](int j0, int lim) {
         float pv[16];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -253,8 +260,11 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (j0 + e < k1) acc = acc + pv[e];
-      }
+          if (e < lim) acc = acc + pv[e];
+      };
+#pragma unroll 4
+      for (int j0 = 0; j0 < kfull; j0 += 16) block16(j0, 16);
+      if (kfull < k1) block16(kfull, k1 - kfull);
       ku[b] = order_key(acc);
       if (s1_opt) s1_opt[size_t(u) * nblk + p0 + b] = acc;
     }
