@@ -141,6 +141,8 @@ class Path:
             "ws_pass2": units * (self.S - w.window) * d * esize + B * Hq * w.window * d * esize,
             "append_kv": units * d * esize * 5,
         }
+        # the one-launch decode step with its append: the fused bytes plus the append's
+        self.alg["hsa_fused_append"] = self.alg["hsa_fused"] + self.alg["append_kv"]
         self.flops_ws = 2.0 * units * G * w.window * self.S * d
         self.dec_bytes = self.alg["hsa_attn_mt" if self.mt else "hsa_attn"] + self.alg["hsa_score"]
 
@@ -164,13 +166,13 @@ class Path:
                 rk.rk_hsa_decode_mt(qs[s], k, v, self.kept, self.n_keep, self.kmax, self.kmin, w.block, w.k1,
                                     self.k2, self.out[s], ws=self.ws_d)
             else:
-                n = self.n_keep
-                if app is not None:
-                    rk.rk_append_kv(app[s][0], app[s][1], self.kc, self.vc, n + s, self.kmax, self.kmin, w.block,
-                                    n_q_heads=w.n_q)
-                    n = n + s + 1
-                rk.rk_hsa_decode(qs[s], self.kc, self.vc, self.kmax, self.kmin, n, w.block, w.k1, self.k2,
-                                 self.out[s], ws=self.ws_d)
+                if app is not None:   # the step appends its token, then decodes (one call)
+                    rk.rk_hsa_append_decode(qs[s], app[s][0], app[s][1], self.kc, self.vc, self.n_keep + s,
+                                            self.kmax, self.kmin, w.block, w.k1, self.k2, self.out[s],
+                                            ws=self.ws_d)
+                else:
+                    rk.rk_hsa_decode(qs[s], self.kc, self.vc, self.kmax, self.kmin, self.n_keep, w.block, w.k1,
+                                     self.k2, self.out[s], ws=self.ws_d)
 
 
 def main():
@@ -264,7 +266,8 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(dominant, w.name),
                 "bytes_per_launch": p.alg[dominant], "avg_launch_us": round(avg_ms * 1e3, 3)}
-    attn_name = next((n for n in ("hsa_fused_mt", "hsa_fused", "hsa_attn_mt", "hsa_attn") if n in per_step),
+    attn_name = next((n for n in ("hsa_fused_mt", "hsa_fused_append", "hsa_fused", "hsa_attn_mt", "hsa_attn")
+                      if n in per_step),
                      "hsa_attn")
     attn_avg = per_step.get(attn_name, (0, 0, float("nan")))[2]
     attn_gbps = p.alg[attn_name] / (attn_avg * 1e-3) / 1e9 if attn_avg == attn_avg else None
@@ -323,7 +326,8 @@ def measured_traffic(kernel, workload):
     import os
 
     # timing-hook names -> kernel function names (the MT variants share the function)
-    kernel = {"hsa_attn_mt": "hsa_attn", "hsa_fused_mt": "hsa_fused", "select_tokens": "select",
+    kernel = {"hsa_attn_mt": "hsa_attn", "hsa_fused_mt": "hsa_fused", "hsa_fused_append": "hsa_fused",
+              "select_tokens": "select",
               "gather_kv": "gather"}.get(kernel, kernel)
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", "hbm_traffic_counters.md")

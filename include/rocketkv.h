@@ -223,6 +223,35 @@ rk_status rk_hsa_decode(const rk_shape* shape, const void* q, const void* k, con
                         float* block_scores_opt, void* ws, size_t ws_bytes, rk_stream stream);
 
 /*
+ * rk_hsa_append_decode -- one decode step that appends its token first:
+ * rk_append_kv(k_new, v_new at pos) followed by rk_hsa_decode over
+ * n_tokens = pos + 1, in one call.  [RKV] method details, HSA step 1 (the
+ * aux data follows every generated key) and steps 2-3.
+ *
+ *   q        [B, Hq, d]             decode queries
+ *   k_new, v_new [B, Hkv, d]        the step's new key / value rows
+ *   k, v     [B, Hkv, kv_cap, d]    compact cache, tokens 0..pos-1 valid;
+ *                                   row pos is written
+ *   kmax, kmin [B, Hkv, d, nblk_cap]  valid for tokens 0..pos-1; page
+ *                                   pos/block is refreshed as rk_append_kv does
+ *   out, sel_blocks_opt, sel_channels_opt, block_scores_opt, ws: as for
+ *   rk_hsa_decode with n_tokens = pos + 1 (workspace from
+ *   rk_hsa_workspace_bytes(shape, pos + 1, ...)).
+ * Afterwards k, v, kmax, kmin equal the state rk_append_kv leaves, bit for
+ * bit; the selections equal rk_hsa_decode's on that state, and out equals
+ * it to float32 rounding.  Large batches run both in one launch (the new
+ * token enters the attention from registers); small ones append with a
+ * launch of its own first.  Requires 0 <= pos < kv_cap, k_new and v_new
+ * 16-byte aligned, and everything rk_hsa_decode requires.
+ */
+rk_status rk_hsa_append_decode(const rk_shape* shape, const void* q, const void* k_new,
+                               const void* v_new, void* k, void* v, int64_t kv_cap, int64_t pos,
+                               void* kmax, void* kmin, int64_t nblk_cap, int32_t block, int32_t k1,
+                               int32_t k2, float* out, int32_t* sel_blocks_opt,
+                               int32_t* sel_channels_opt, float* block_scores_opt, void* ws,
+                               size_t ws_bytes, rk_stream stream);
+
+/*
  * rk_hsa_decode_mt -- RocketKV-MT decode: HSA over a candidate subset of a
  * full, never-evicted cache.
  * [RKV] method details, RocketKV-MT: every token stays in memory, but stage 2

@@ -67,7 +67,7 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
                         const void* kmax, const void* kmin, int64_t nblk_cap, int64_t n_tokens,
                         int32_t block, int32_t k1, int32_t k2, float* out, int32_t* sel_opt,
                         int32_t* chan_opt, float* s1_opt, void* ws, size_t ws_bytes,
-                        rk_stream stream, bool mt) {
+                        rk_stream stream, bool mt, const rk::AppendArgs* app = nullptr) {
   rk::Dims d;
   rk_status st = check_shape(shape, &d);
   if (st != RK_OK) return st;
@@ -101,8 +101,8 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
   return device_status(
       rk::launch_hsa_decode(d, q, k, v, kv_cap, mt ? cand : nullptr, cand_stride, kmax, kmin,
                             nblk_cap, n_tokens, block, k1, k2, out, sel_opt, chan_opt, s1_opt,
-                            ws, static_cast<hipStream_t>(stream)),
-      mt ? "rk_hsa_decode_mt launch" : "rk_hsa_decode launch");
+                            ws, static_cast<hipStream_t>(stream), app),
+      mt ? "rk_hsa_decode_mt launch" : app ? "rk_hsa_append_decode launch" : "rk_hsa_decode launch");
 }
 
 }  // namespace
@@ -264,6 +264,22 @@ rk_status rk_hsa_decode(const rk_shape* shape, const void* q, const void* k, con
   return decode_common(shape, q, k, v, kv_cap, nullptr, 0, kmax, kmin, nblk_cap, n_tokens, block,
                        k1, k2, out, sel_blocks_opt, sel_channels_opt, block_scores_opt, ws,
                        ws_bytes, stream, false);
+}
+
+rk_status rk_hsa_append_decode(const rk_shape* shape, const void* q, const void* k_new,
+                               const void* v_new, void* k, void* v, int64_t kv_cap, int64_t pos,
+                               void* kmax, void* kmin, int64_t nblk_cap, int32_t block, int32_t k1,
+                               int32_t k2, float* out, int32_t* sel_blocks_opt,
+                               int32_t* sel_channels_opt, float* block_scores_opt, void* ws,
+                               size_t ws_bytes, rk_stream stream) {
+  if (!k_new || !v_new) return fail(RK_EINVAL, "null tensor argument");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(RK_EINVAL, "k_new and v_new must be 16-byte aligned");
+  if (pos < 0 || pos >= kv_cap) return fail(RK_EINVAL, "pos outside [0, kv_cap)");
+  const rk::AppendArgs app{k_new, v_new, k, v, kmax, kmin};
+  return decode_common(shape, q, k, v, kv_cap, nullptr, 0, kmax, kmin, nblk_cap, pos + 1, block,
+                       k1, k2, out, sel_blocks_opt, sel_channels_opt, block_scores_opt, ws,
+                       ws_bytes, stream, false, &app);
 }
 
 rk_status rk_hsa_decode_mt(const rk_shape* shape, const void* q, const void* k, const void* v,

@@ -528,6 +528,17 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   }
 }
 
+// Typed form of AppendArgs for the fused kernel.
+template <typename T>
+struct AppendPtrs {
+  const T* k_new;
+  const T* v_new;
+  T* k;
+  T* v;
+  T* kmax;
+  T* kmin;
+};
+
 // Steps 2 and 3 in one workgroup per unit, for large batches (the units alone
 // fill the chip, so no split-K, no partials and no combine).  1024 threads:
 // wave 0 makes the channel choice; all threads stage and score the unit's
@@ -537,16 +548,23 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
 // this chip gain bandwidth with resident waves per CU rather than with loads
 // in flight per wave, hence the full 1024-thread workgroup (4 waves per SIMD).
 //
+// APP (a decode step that first appends token n_tokens - 1, as rk_append_kv
+// would): the workgroup writes the unit's new K/V row and the refreshed
+// Kmax/Kmin column of the last page up front, patches that column into its
+// own staged scores, and lets the new token into the attention from
+// registers rather than reading back what it wrote.
+//
 // Dynamic LDS: page keys [roundup4(nblk)] | chosen pages [roundup4(nsel)] |
 // a region holding first the staged chunk [npc][k1p], then the waves' merge
 // state (m, l per wave and head, o per wave, head and channel).
-template <typename T, int D, int G, bool MT>
+template <typename T, int D, int G, bool MT, bool APP = false>
 __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
     const int32_t* __restrict__ cand, int64_t cand_stride, const T* __restrict__ kmax,
     const T* __restrict__ kmin, int64_t nblk_cap, int nblk, int k1, int nsel, int npc,
     int n_tokens, int block, float scale_log2, float* __restrict__ out,
-    int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt) {
+    int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt,
+    AppendPtrs<T> app) {
   constexpr int TPS = AttnShape<T, D, G>::TPS;
   using S = AttnShape<T, D, G, TPS>;
   constexpr int EPL = S::EPL, LPR = S::LPR;
@@ -573,6 +591,31 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   float qf[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) unpack16(load16(q + (size_t(u) * G + g) * D + c * EPL), qf[g]);
+  const int n_cached = APP ? n_tokens - 1 : n_tokens;  // tokens read from the cache
+  const int app_page = (n_tokens - 1) / block;
+  // APP: the new key (as T, for the patch) and the new K/V rows (as float,
+  // for the attention) go to LDS; the page's old Kmax/Kmin column is fetched
+  // now and folded and written back at the end, off every critical path.
+  // The last waves do this work: wave 0's loads for the channel choice must
+  // not queue behind the scattered column reads.
+  __shared__ T app_knt[APP ? D : 1];
+  __shared__ float app_kf[APP ? D : 1], app_vf[APP ? D : 1];
+  T app_kn{}, app_vn{}, app_ox{}, app_on{};
+  const bool app_fold = n_cached % block != 0;  // the page already holds tokens
+  const int ta = t - (NT - D);                   // channel of this thread in the append work
+  if constexpr (APP) {
+    if (ta >= 0) {
+      const size_t a = (size_t(u) * D + ta) * size_t(nblk_cap) + app_page;
+      app_kn = app.k_new[size_t(u) * D + ta];
+      app_vn = app.v_new[size_t(u) * D + ta];
+      if (app_fold) {
+        app_ox = app.kmax[a];
+        app_on = app.kmin[a];
+      }
+      app.k[(size_t(u) * size_t(kv_cap) + size_t(n_cached)) * D + ta] = app_kn;
+      app.v[(size_t(u) * size_t(kv_cap) + size_t(n_cached)) * D + ta] = app_vn;
+    }
+  }
   if (wave == 0) {
     float qx[R][G];
 #pragma unroll
@@ -590,7 +633,25 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   for (int p0 = 0; p0 < nblk; p0 += npc) {
     const int np = min(npc, nblk - p0);
     stage_rows<T, NT>(xu + p0, nu + p0, nblk_cap, np, k1, i1_off, stage);
+    if (APP && p0 == 0 && ta >= 0) {
+      app_knt[ta] = app_kn;
+      app_kf[ta] = to_f32(app_kn);
+      app_vf[ta] = to_f32(app_vn);
+    }
     __syncthreads();
+    if (APP && app_page >= p0 && app_page < p0 + np) {
+      // the staged (old) value of each chosen row of the last page takes the
+      // new key in: max for a Kmax row, min for a Kmin row, the key itself
+      // when the page starts with it
+      if (t < k1) {
+        const int o = i1_off[t];
+        T* sv = stage + size_t(app_page - p0) * staged_pitch<T>(k1) + t;
+        const T kn = app_knt[o >= 0 ? o : -1 - o];
+        const float x = to_f32(kn), old = to_f32(*sv);
+        if (!app_fold || (o >= 0 ? x > old : x < old)) *sv = kn;
+      }
+      __syncthreads();
+    }
     score_staged<T, NT>(stage, np, k1, i1_q, pkeys + p0,
                         s1_opt ? s1_opt + size_t(u) * nblk + p0 : nullptr);
     __syncthreads();
@@ -622,8 +683,29 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   const T* ku = k + size_t(u) * size_t(kv_cap) * D + c * EPL;
   const T* vu = v + size_t(u) * size_t(kv_cap) * D + c * EPL;
   const int32_t* cu = MT ? cand + size_t(u) * size_t(cand_stride) : nullptr;
-  attend_pages<T, D, G, MT, TPS>(qf, ku, vu, cu, kv_cap, pages, wave, nsel, NW, block, n_tokens,
+  attend_pages<T, D, G, MT, TPS>(qf, ku, vu, cu, kv_cap, pages, wave, nsel, NW, block, n_cached,
                                  scale_log2, m, l, o);
+  if constexpr (APP) {
+    // the new token, when its page was chosen (the last page, so the last
+    // entry of the ascending list), goes to wave 0's token slot 0
+    if (wave == 0 && pages[nsel - 1] == app_page) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float sdot = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sdot += qf[g][e] * app_kf[c * EPL + e];
+        const float x = group_sum<LPR>(sdot) * scale_log2;
+        if (lane < LPR) {
+          const float mn = fmaxf(m[g], x);
+          const float corr = fast_exp2(m[g] - mn), pn = fast_exp2(x - mn);
+          l[g] = l[g] * corr + pn;
+          m[g] = mn;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[g][e] = o[g][e] * corr + pn * app_vf[c * EPL + e];
+        }
+      }
+    }
+  }
   RK_PHASE(4);
   wave_state_to_lds<T, D, G>(m, l, o, wave, wm, wl, wo);  // the staged chunk is no longer read
   __syncthreads();
@@ -632,6 +714,17 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
     float mm, ll, oo;
     merge_waves<D, G, NW>(idx, wm, wl, wo, &mm, &ll, &oo);
     out[size_t(u) * G * D + idx] = oo / ll;
+  }
+  if (APP && ta >= 0) {  // the refreshed column of the last page, for later steps
+    T mx = app_kn, mn = app_kn;
+    if (app_fold) {
+      const float x = to_f32(app_kn);
+      mx = x > to_f32(app_ox) ? app_kn : app_ox;
+      mn = x < to_f32(app_on) ? app_kn : app_on;
+    }
+    const size_t a = (size_t(u) * D + ta) * size_t(nblk_cap) + app_page;
+    app.kmax[a] = mx;
+    app.kmin[a] = mn;
   }
 }
 
@@ -707,7 +800,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
                            const void* kmax, const void* kmin, int64_t nblk_cap,
                            int64_t n_tokens, int block, int k1, int k2, float* out,
                            int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                           hipStream_t s) {
+                           hipStream_t s, const AppendArgs* app) {
   const int nblk = int((n_tokens + block - 1) / block);
   const DecodeWs lay = decode_ws_layout(d, nblk, k2);
   char* wsb = static_cast<char*>(ws);
@@ -730,27 +823,46 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
       static bool fattr = false;  // once per template instantiation
       if (!fattr) {
         for (const void* f : {reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, true>),
-                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false>)}) {
+                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false>),
+                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, true>)}) {
           hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                              int(kFusedLdsBudget));
           if (e != hipSuccess) return e;
         }
         fattr = true;
       }
+      const AppendPtrs<T> ap =
+          app ? AppendPtrs<T>{static_cast<const T*>(app->k_new), static_cast<const T*>(app->v_new),
+                              static_cast<T*>(app->k), static_cast<T*>(app->v),
+                              static_cast<T*>(app->kmax), static_cast<T*>(app->kmin)}
+              : AppendPtrs<T>{};
       if (cand)
         RK_LAUNCH("hsa_fused_mt", (hsa_fused_kernel<T, D, G, true>), dim3(units), dim3(kFusedThreads), lds,
                   s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                   kv_cap, cand, cand_stride, static_cast<const T*>(kmax),
                   static_cast<const T*>(kmin), nblk_cap, nblk, k1, lay.nsel, npc, int(n_tokens),
-                  block, scale_log2, out, sel_opt, chan_opt, s1_opt);
+                  block, scale_log2, out, sel_opt, chan_opt, s1_opt, ap);
+      else if (app)
+        RK_LAUNCH("hsa_fused_append", (hsa_fused_kernel<T, D, G, false, true>), dim3(units),
+                  dim3(kFusedThreads), lds, s, static_cast<const T*>(q), static_cast<const T*>(k),
+                  static_cast<const T*>(v), kv_cap, cand, cand_stride, static_cast<const T*>(kmax),
+                  static_cast<const T*>(kmin), nblk_cap, nblk, k1, lay.nsel, npc, int(n_tokens),
+                  block, scale_log2, out, sel_opt, chan_opt, s1_opt, ap);
       else
         RK_LAUNCH("hsa_fused", (hsa_fused_kernel<T, D, G, false>), dim3(units), dim3(kFusedThreads), lds,
                   s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                   kv_cap, cand, cand_stride, static_cast<const T*>(kmax),
                   static_cast<const T*>(kmin), nblk_cap, nblk, k1, lay.nsel, npc, int(n_tokens),
-                  block, scale_log2, out, sel_opt, chan_opt, s1_opt);
+                  block, scale_log2, out, sel_opt, chan_opt, s1_opt, ap);
       return hipGetLastError();
     }
+  }
+
+  // the split-K path appends with its own launch first
+  if (app) {
+    const hipError_t e = launch_append_kv(d, app->k_new, app->v_new, app->k, app->v, kv_cap,
+                                          n_tokens - 1, app->kmax, app->kmin, nblk_cap, block, s);
+    if (e != hipSuccess) return e;
   }
 
   // Step 2a grid: page ranges of ppw pages (a multiple of 8, the staged
@@ -843,12 +955,12 @@ hipError_t launch_decode_d(const Dims& d, const void* q, const void* k, const vo
                            const void* kmax, const void* kmin, int64_t nblk_cap,
                            int64_t n_tokens, int block, int k1, int k2, float* out,
                            int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                           hipStream_t s) {
+                           hipStream_t s, const AppendArgs* app) {
 #define RK_DECODE_G(GG)                                                                        \
   case GG:                                                                                     \
     return launch_decode_t<T, D, GG>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,       \
                                      nblk_cap, n_tokens, block, k1, k2, out, sel_opt,         \
-                                     chan_opt, s1_opt, ws, s);
+                                     chan_opt, s1_opt, ws, s, app);
   switch (d.G) {
     RK_DECODE_G(1)
     RK_DECODE_G(2)
@@ -867,23 +979,23 @@ hipError_t launch_hsa_decode(const Dims& d, const void* q, const void* k, const 
                              const void* kmax, const void* kmin, int64_t nblk_cap,
                              int64_t n_tokens, int block, int k1, int k2, float* out,
                              int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                             hipStream_t s) {
+                             hipStream_t s, const AppendArgs* app) {
   if (d.bf16) {
     if (d.D == 128)
       return launch_decode_d<bf16_t, 128>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                           nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                          chan_opt, s1_opt, ws, s);
+                                          chan_opt, s1_opt, ws, s, app);
     return launch_decode_d<bf16_t, 64>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                        nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                       chan_opt, s1_opt, ws, s);
+                                       chan_opt, s1_opt, ws, s, app);
   }
   if (d.D == 128)
     return launch_decode_d<float, 128>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                        nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                       chan_opt, s1_opt, ws, s);
+                                       chan_opt, s1_opt, ws, s, app);
   return launch_decode_d<float, 64>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                     nblk_cap, n_tokens, block, k1, k2, out, sel_opt, chan_opt,
-                                    s1_opt, ws, s);
+                                    s1_opt, ws, s, app);
 }
 
 }  // namespace rk

@@ -111,12 +111,23 @@ hipError_t launch_append_kv(const Dims& d, const void* k_new, const void* v_new,
                             int64_t kv_cap, int64_t pos, void* kmax, void* kmin,
                             int64_t nblk_cap, int block, hipStream_t s);
 
+// A decode step that first appends token n_tokens - 1 (rk_append_kv's
+// effect): the new rows and the buffers it writes.
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k;
+  void* v;
+  void* kmax;
+  void* kmin;
+};
+
 hipError_t launch_hsa_decode(const Dims& d, const void* q, const void* k, const void* v,
                              int64_t kv_cap, const int32_t* cand, int64_t cand_stride,
                              const void* kmax, const void* kmin, int64_t nblk_cap,
                              int64_t n_tokens, int block, int k1, int k2, float* out,
                              int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                             hipStream_t s);
+                             hipStream_t s, const AppendArgs* app = nullptr);
 
 hipError_t launch_snapkv_evict(const Dims& d, const void* q_win, const void* k, const void* v,
                                int64_t kv_cap, int64_t S, int W, int pool_kernel,

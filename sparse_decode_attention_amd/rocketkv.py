@@ -153,6 +153,9 @@ def rk_hsa_build_aux(k, n_tokens, first_token, block, kmax, kmin, n_q_heads=None
 
 _lib.rk_append_kv.argtypes = [_SP, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _i32, _vp]
 _lib.rk_append_kv.restype = ctypes.c_int
+_lib.rk_hsa_append_decode.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _i32,
+                                      _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.rk_hsa_append_decode.restype = ctypes.c_int
 
 
 def rk_append_kv(k_new, v_new, k, v, pos, kmax, kmin, block, n_q_heads=None, stream=None):
@@ -182,6 +185,22 @@ def rk_hsa_decode(q, k, v, kmax, kmin, n_tokens, block, k1, k2, out, sel_blocks=
                               _ptr(kmax), _ptr(kmin), kmax.shape[3], n_tokens, block, k1, k2,
                               _ptr(out), _ptr(sel_blocks), _ptr(sel_channels), _ptr(block_scores),
                               _ptr(ws), ws.numel(), _stream(stream)), "rk_hsa_decode")
+    return ws
+
+
+def rk_hsa_append_decode(q, k_new, v_new, k, v, pos, kmax, kmin, block, k1, k2, out,
+                         sel_blocks=None, sel_channels=None, block_scores=None, ws=None,
+                         stream=None):
+    """rk_append_kv at pos followed by rk_hsa_decode over pos + 1 tokens, in one call."""
+    _need_contig(q, k_new, v_new, k, v, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    B, Hq, d = q.shape
+    shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
+    ws = _ws(rk_hsa_workspace_bytes(shape, pos + 1, block, k1, k2), k, ws)
+    _check(_lib.rk_hsa_append_decode(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                     _ptr(k), _ptr(v), k.shape[2], pos, _ptr(kmax), _ptr(kmin),
+                                     kmax.shape[3], block, k1, k2, _ptr(out), _ptr(sel_blocks),
+                                     _ptr(sel_channels), _ptr(block_scores), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "rk_hsa_append_decode")
     return ws
 
 

@@ -29,7 +29,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     names = _declared()
     assert {"rk_split", "rk_snapkv_evict", "rk_hsa_build_aux", "rk_hsa_decode",
-            "rk_hsa_decode_mt"} <= set(names)
+            "rk_hsa_decode_mt", "rk_append_kv", "rk_hsa_append_decode"} <= set(names)
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -172,6 +172,20 @@ def test_error_codes_before_any_launch(rk):
     assert app(pos=1024) == rk.RK_EINVAL and app(pos=-1) == rk.RK_EINVAL
     assert app(nblk_cap=62) == rk.RK_EINVAL and app(nblk_cap=63) == rk.RK_EINVAL
     assert app(kn=None) == rk.RK_EINVAL and app(block=0) == rk.RK_EINVAL
+
+    def appdec(**kw):
+        a = dict(kn=_vp(FAKE), vn=_vp(FAKE), cap=1024, pos=999, nblk_cap=64, block=16)
+        a.update(kw)
+        return lib.rk_hsa_append_decode(byref(sh), _vp(FAKE), a["kn"], a["vn"], _vp(FAKE), _vp(FAKE),
+                                        a["cap"], a["pos"], _vp(FAKE), _vp(FAKE), a["nblk_cap"],
+                                        a["block"], 16, 16, _vp(FAKE), None, None, None, _vp(FAKE),
+                                        1 << 30, None)
+
+    assert appdec(pos=-1) == rk.RK_EINVAL and appdec(pos=1024) == rk.RK_EINVAL
+    assert appdec(kn=None) == rk.RK_EINVAL and appdec(vn=None) == rk.RK_EINVAL
+    assert appdec(kn=_vp(FAKE + 2)) == rk.RK_EINVAL                    # misaligned
+    assert appdec(nblk_cap=56) == rk.RK_EINVAL                          # 1000 tokens need 63 pages
+    assert appdec(block=0) == rk.RK_EINVAL
 
     assert lib.rk_hsa_decode_mt(byref(sh), _vp(FAKE), _vp(FAKE), _vp(FAKE), 4096, None, 1000, 1000,
                                 _vp(FAKE), _vp(FAKE), 63, 16, 16, 16, _vp(FAKE), None, None, None,

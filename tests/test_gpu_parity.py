@@ -304,6 +304,74 @@ def test_append_equals_rebuild(rk, dtype, d):
         U.check_aux_units(kmax, kmin, kc, 201 + step, 16, [(b, h) for b in range(3) for h in range(2)])
 
 
+@pytest.mark.parametrize("dtype,d,G,B,Hkv,n0,k2,big", [
+    ("bf16", 128, 4, 20, 8, 997, 16, False),   # 160 units: one launch; new token mid-page
+    ("bf16", 128, 4, 20, 8, 992, 16, True),    # new token opens a page that gets chosen
+    ("bf16", 128, 4, 20, 8, 1001, 64, True),   # mid-page, its page chosen
+    ("f32", 64, 2, 40, 4, 500, 8, True),
+    ("bf16", 128, 4, 1, 8, 997, 16, True),     # 8 units: the split path appends first
+    ("bf16", 128, 4, 1, 8, 992, 16, False),
+])
+def test_append_decode_equals_append_then_decode(rk, dtype, d, G, B, Hkv, n0, k2, big):
+    """rk_hsa_append_decode leaves the cache and Kmax/Kmin exactly as rk_append_kv
+    does, selects exactly what rk_hsa_decode selects on that state, and its output
+    agrees with it to float32 rounding and with the oracle over the chosen pages."""
+    say("append+decode", dtype, d, G, B, Hkv, n0, k2, big)
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=B, n_kv=Hkv, n_q=Hkv * G, d=d, dtype=dtype, seq=n0, n_plant=4)
+    kc0, vc0, _ = WL.layer_kv(w, 0, device=DEV)
+    cap, k1, block = n0 + 24, 32 if d == 128 else 16, 16
+    kc = torch.zeros(B, Hkv, cap, d, dtype=kc0.dtype, device=DEV)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :n0] = kc0
+    vc[:, :, :n0] = vc0
+    kmax = torch.empty(B, Hkv, d, rk.aux_capacity(cap, block), dtype=kc.dtype, device=DEV)
+    kmin = torch.empty_like(kmax)
+    rk.rk_hsa_build_aux(kc, n0, 0, block, kmax, kmin)
+    ka, va = WL.append_kv(w, 0, 0, device=DEV)
+    if big:   # a strong new key makes its page a likely pick
+        ka = (ka.float() * 6).to(ka.dtype).contiguous()
+    q = WL.decode_query(w, 0, 0, device=DEV)
+    n = n0 + 1
+    nsel = min(k2, -(-n // block))
+    outs = []
+    for fused in (False, True):
+        kcx, vcx, kxx, knx = kc.clone(), vc.clone(), kmax.clone(), kmin.clone()
+        out = torch.empty(B, Hkv * G, d, device=DEV)
+        sel = torch.empty(B, Hkv, nsel, dtype=torch.int32, device=DEV)
+        chan = torch.empty(B, Hkv, k1, dtype=torch.int32, device=DEV)
+        s1 = torch.empty(B, Hkv, -(-n // block), device=DEV)
+        if fused:
+            rk.rk_hsa_append_decode(q, ka, va, kcx, vcx, n0, kxx, knx, block, k1, k2, out, sel, chan, s1)
+        else:
+            rk.rk_append_kv(ka, va, kcx, vcx, n0, kxx, knx, block)
+            rk.rk_hsa_decode(q, kcx, vcx, kxx, knx, n, block, k1, k2, out, sel, chan, s1)
+        torch.cuda.synchronize()
+        outs.append((kcx, vcx, kxx, knx, out, sel, chan, s1))
+    a, b = outs
+    for x, y in zip(a[:4], b[:4]):
+        assert torch.equal(x, y)
+    for x, y in zip(a[5:], b[5:]):
+        assert torch.equal(x, y)
+    assert (a[4] - b[4]).abs().max().item() <= 1e-5
+    last = (n - 1) // block
+    picked = int((b[5][..., -1] == last).sum())
+    say("  last page chosen in", picked, "of", B * Hkv, "units")
+    if big:
+        assert picked > 0
+    for bb, h in [(0, 0), (B - 1, Hkv - 1), (B // 2, Hkv // 2)]:
+        toks = O.selected_tokens(b[5][bb, h].cpu().numpy(), n, block)
+        ridx = torch.as_tensor(toks, dtype=torch.long, device=DEV)
+        want = O.attention(U.np32(q[bb, h * G:(h + 1) * G]), U.np32(b[0][bb, h, ridx]),
+                           U.np32(b[1][bb, h, ridx]))
+        U.check_output(U.np32(b[4][bb, h * G:(h + 1) * G]), want)
+    if B * Hkv >= 160:
+        rk.rk_profile_begin()
+        rk.rk_hsa_append_decode(q, ka, va, kc, vc, n0, kmax, kmin, block, k1, k2,
+                                torch.empty(B, Hkv * G, d, device=DEV))
+        assert set(rk.rk_profile_end()) == {"hsa_fused_append"}
+
+
 def _decode_only(rk, w, n, k1, k2, units_to_check=None, cand_total=None, steps=2):
     """Aux + decode over a synthetic cache (no stage 1), checked stage-wise."""
     kc, vc, _ = WL.layer_kv(w, 0, device=DEV)
