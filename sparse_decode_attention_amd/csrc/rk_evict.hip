@@ -365,18 +365,37 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k,
   constexpr int EPL = Vec16<T>::N;
   constexpr int CPR = D / EPL;
   constexpr int RPP = 256 / CPR;  // rows per pass
+  static_assert(64 % RPP == 0, "rows per workgroup");
   const int u = blockIdx.y;
   const int n0 = blockIdx.x * 64;
   const int ch = threadIdx.x % CPR;
   const int* ku = kept + size_t(u) * n_keep;
-  for (int rr = threadIdx.x / CPR; rr < 64; rr += RPP) {
-    const int n = n0 + rr;
-    if (n >= n_keep) break;
-    const size_t src = (size_t(u) * size_t(kv_cap) + size_t(ku[n])) * D + ch * EPL;
-    const size_t dst = (size_t(u) * size_t(out_cap) + size_t(n)) * D + ch * EPL;
-    using R = decltype(Vec16<T>::raw);
-    *reinterpret_cast<R*>(k_out + dst) = *reinterpret_cast<const R*>(k + src);
-    *reinterpret_cast<R*>(v_out + dst) = *reinterpret_cast<const R*>(v + src);
+  // the workgroup's 64 rows: every index, then every K and V load, in flight
+  // before any is used
+  constexpr int NI = 64 / RPP;
+  using R = decltype(Vec16<T>::raw);
+  int src_row[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int n = n0 + threadIdx.x / CPR + i * RPP;
+    src_row[i] = n < n_keep ? ku[n] : 0;
+  }
+  // rows past n_keep read the unit's row 0 (in bounds) and are dropped
+  Vec16<T> kr[NI], vr[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const size_t src = (size_t(u) * size_t(kv_cap) + size_t(src_row[i])) * D + ch * EPL;
+    kr[i] = load16(k + src);
+    vr[i] = load16(v + src);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int n = n0 + threadIdx.x / CPR + i * RPP;
+    if (n < n_keep) {
+      const size_t dst = (size_t(u) * size_t(out_cap) + size_t(n)) * D + ch * EPL;
+      *reinterpret_cast<R*>(k_out + dst) = kr[i].raw;
+      *reinterpret_cast<R*>(v_out + dst) = vr[i].raw;
+    }
   }
 }
 
@@ -618,18 +637,36 @@ __global__ __launch_bounds__(256) void gather_aux_kernel(
     const int n1 = min((p + 1) * block, n_keep);
     const int* ku = kept + size_t(u) * n_keep;
     using Rw = decltype(Vec16<T>::raw);
-    for (int n = p * block + g; n < n1; n += RG) {
-      const size_t src = (size_t(u) * size_t(kv_cap) + size_t(ku[n])) * D + c * EPL;
-      const size_t dst = (size_t(u) * size_t(out_cap) + size_t(n)) * D + c * EPL;
-      const Vec16<T> kr = load16(k + src);
-      *reinterpret_cast<Rw*>(v_out + dst) = *reinterpret_cast<const Rw*>(v + src);
-      *reinterpret_cast<Rw*>(k_out + dst) = kr.raw;
-      float x[EPL];
-      unpack16(kr, x);
+    // NI rows per round: all their indices, then all their K and V loads,
+    // are in flight before any is used (the index -> row chain is the latency)
+    constexpr int NI = 4;
+    for (int n0 = p * block + g; n0 < n1; n0 += NI * RG) {
+      int src_row[NI];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        mx[e] = x[e] > mx[e] ? x[e] : mx[e];
-        mn[e] = x[e] < mn[e] ? x[e] : mn[e];
+      for (int i = 0; i < NI; ++i) src_row[i] = n0 + i * RG < n1 ? ku[n0 + i * RG] : 0;
+      // rows past the page read the unit's row 0 (in bounds) and are dropped
+      Vec16<T> kr[NI], vr[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const size_t src = (size_t(u) * size_t(kv_cap) + size_t(src_row[i])) * D + c * EPL;
+        kr[i] = load16(k + src);
+        vr[i] = load16(v + src);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int n = n0 + i * RG;
+        if (n < n1) {
+          const size_t dst = (size_t(u) * size_t(out_cap) + size_t(n)) * D + c * EPL;
+          *reinterpret_cast<Rw*>(k_out + dst) = kr[i].raw;
+          *reinterpret_cast<Rw*>(v_out + dst) = vr[i].raw;
+          float x[EPL];
+          unpack16(kr[i], x);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            mx[e] = x[e] > mx[e] ? x[e] : mx[e];
+            mn[e] = x[e] < mn[e] ? x[e] : mn[e];
+          }
+        }
       }
     }
   }
