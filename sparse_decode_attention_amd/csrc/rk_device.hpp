@@ -80,6 +80,10 @@ __device__ __forceinline__ int clamp_row(int32_t row, int64_t cap) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Lanes of the wave where b holds, straight from the compare (no bool -> int
+// round trip, which costs two extra instructions per call).
+__device__ __forceinline__ unsigned long long ballot(bool b) { return __builtin_amdgcn_ballot_w64(b); }
+
 // XCD-aware work mapping.  MI355X deals the workgroups of a launch out to its
 // 8 XCDs round robin (workgroup L to XCD L mod 8), and each XCD has its own
 // L2.  With a 1-D grid of 8 * ceil(n/8) workgroups, XCD x here takes the
@@ -262,7 +266,7 @@ __device__ __forceinline__ int3 wave_find_bin(const uint32_t* hist, int need) {
   for (int j = 0; j < BPL; ++j) own += int(c[j]);
   const int incl = wave_incl_scan(own);
   int above = incl - own;
-  const unsigned long long hit = __ballot(above < need && incl >= need);
+  const unsigned long long hit = ballot(above < need && incl >= need);
   const int L = __ffsll(static_cast<long long>(hit)) - 1;
   int bin = 0, nin = 0, cnt = 0;
 #pragma unroll
@@ -292,9 +296,9 @@ __device__ __forceinline__ void wave_topk_emit(const KeyFn& key, int n, uint32_t
     const int i = c0 + lane;
     const uint32_t kk = i < n ? key(i) : 0u;
     const bool eq = i < n && kk == T;
-    const unsigned long long em = __ballot(eq);
+    const unsigned long long em = ballot(eq);
     const bool sel = (i < n && kk > T) || (eq && eq_seen + __popcll(em & below) < need_eq);
-    const unsigned long long sm = __ballot(sel);
+    const unsigned long long sm = ballot(sel);
     if (sel) emit(base + __popcll(sm & below), i);
     base += __popcll(sm);
     eq_seen += __popcll(em);
@@ -305,7 +309,7 @@ __device__ __forceinline__ void wave_topk_emit(const KeyFn& key, int n, uint32_t
 // most this many keys (one wave's passes stop there).
 constexpr int kWaveRankMax = 16;
 
-// Exact cut among the c <= kWaveRankMax keys of [lo, hi]: the keys are packed
+// Exact cut among the c <= kWaveRankMax keys of [lo, hi] (lo >= 1): the keys are packed
 // into LDS slots (position order), lane l takes slot l and counts the slots
 // above it (gt) and at or above it (ge) with broadcast reads; the lane with
 // gt < need <= ge holds T, the need-th largest of the range.  Returns T, the
@@ -315,17 +319,24 @@ __device__ __forceinline__ uint3 wave_rank_range(const uint32_t (&kz)[R], int n,
                                                  uint32_t hi, int need, uint32_t* slots) {
   const int lane = lane_id();
   const unsigned long long below = (1ull << lane) - 1ull;
+  // every row's candidate mask first (independent compares), then the
+  // packing of the rows that hold any
+  const uint32_t span = hi - lo;
+  // unused slots read as 0, below every candidate (lo >= 1 here)
+  if (lane < kWaveRankMax / 4) reinterpret_cast<uint4*>(slots)[lane] = make_uint4(0u, 0u, 0u, 0u);
+  unsigned long long m[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) m[r] = ballot(kz[r] - lo <= span);  // padding 0 < lo falls out
   int cnt = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const bool in = r * kWave + lane < n && kz[r] >= lo && kz[r] <= hi;
-    const unsigned long long m = __ballot(in);
-    if (m) {
-      if (in) slots[cnt + __popcll(m & below)] = kz[r];
-      cnt += __popcll(m);
+    if (m[r]) {
+      if ((m[r] >> lane) & 1ull) slots[cnt + __popcll(m[r] & below)] = kz[r];
+      cnt += __popcll(m[r]);
     }
   }
   __builtin_amdgcn_wave_barrier();
+  RK_PHASE(25);
   const uint32_t mine = lane < cnt ? slots[lane] : 0u;
   int gt = 0, ge = 0;
 #pragma unroll
@@ -334,12 +345,12 @@ __device__ __forceinline__ uint3 wave_rank_range(const uint32_t (&kz)[R], int n,
     const uint32_t sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool live = j + e < cnt;
-      gt += live && sv[e] > mine ? 1 : 0;
-      ge += live && sv[e] >= mine ? 1 : 0;
+      gt += sv[e] > mine ? 1 : 0;
+      ge += sv[e] >= mine ? 1 : 0;
     }
   }
-  const unsigned long long hit = __ballot(lane < cnt && gt < need && ge >= need);
+  RK_PHASE(26);
+  const unsigned long long hit = ballot(lane < cnt && gt < need && ge >= need);
   const int L = __ffsll(static_cast<long long>(hit)) - 1;
   const int gtL = __builtin_amdgcn_readlane(gt, L), geL = __builtin_amdgcn_readlane(ge, L);
   return make_uint3(uint32_t(__builtin_amdgcn_readlane(int(mine), L)), uint32_t(need - gtL),
@@ -404,8 +415,10 @@ __device__ __forceinline__ TopkCut wave_topk_cut(const uint32_t (&kz)[R], int n,
       cut.need_eq = need;
       return cut;
     }
-    if (in_range <= kWaveRankMax) {
+    if (in_range <= kWaveRankMax && lo != 0u) {
+      RK_PHASE(24);
       const uint3 c = wave_rank_range(kz, n, lo, hi, need, hist);
+      RK_PHASE(27);
       cut.T = cut.thr = c.x;
       cut.need_eq = int(c.y);
       cut.fast = c.y == c.z;
@@ -416,11 +429,14 @@ __device__ __forceinline__ TopkCut wave_topk_cut(const uint32_t (&kz)[R], int n,
 #pragma unroll
     for (int j = 0; j < BINS / kWave; j += 4)
       *reinterpret_cast<uint4*>(hist + lane * (BINS / kWave) + j) = make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t span = hi - lo;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (r < rows) {
-        const uint32_t kk = kz[r];
-        if (r * kWave + lane < n && kk >= lo && kk <= hi) atomicAdd(&hist[(kk - lo) >> shift], 1u);
+        // one unsigned compare tests lo <= key <= hi; padding zeros fall out
+        // unless lo is 0 (only a NaN pattern orders there)
+        const uint32_t off = kz[r] - lo;
+        if (off <= span && (lo != 0u || r * kWave + lane < n)) atomicAdd(&hist[off >> shift], 1u);
       }
     }
     const int3 f = wave_find_bin<BINS>(hist, need);
@@ -443,8 +459,13 @@ __device__ __forceinline__ void wave_emit_cut(const uint32_t (&kz)[R], int n, co
   const unsigned long long below = (1ull << lane) - 1ull;
   if (cut.fast) {
     unsigned long long sm[R];
+    if (cut.thr != 0u) {  // padding zeros fall below the threshold by themselves
 #pragma unroll
-    for (int r = 0; r < R; ++r) sm[r] = __ballot(kz[r] >= cut.thr && r * kWave + lane < n);
+      for (int r = 0; r < R; ++r) sm[r] = ballot(kz[r] >= cut.thr);
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) sm[r] = ballot(r * kWave + lane < n);
+    }
     int base = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -463,10 +484,10 @@ __device__ __forceinline__ void wave_emit_cut(const uint32_t (&kz)[R], int n, co
   for (int r = 0; r < R; ++r) {
     const int i = r * kWave + lane;
     const bool eq = i < n && kz[r] == cut.T;
-    const unsigned long long em = __ballot(eq);
+    const unsigned long long em = ballot(eq);
     const bool sel =
         (i < n && kz[r] > cut.T) || (eq && eq_seen + __popcll(em & below) < cut.need_eq);
-    const unsigned long long sm = __ballot(sel);
+    const unsigned long long sm = ballot(sel);
     const int rank = base + __popcll(sm & below);
     if (sel && rank >= rank_lo && rank < rank_hi) emit(rank, i);
     base += __popcll(sm);
