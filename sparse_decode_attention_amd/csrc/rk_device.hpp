@@ -585,6 +585,7 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
     lo = min(lo, sm.red[w]);
     hi = max(hi, sm.red[NW + w]);
   }
+  RK_PHASE(13);
   int need = k;  // keys still to take among the candidates [lo, hi]
   uint32_t T;    // threshold: keys above are taken, need_eq of the keys equal to it
   int need_eq;
@@ -615,6 +616,7 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
     }
     __syncthreads();
     RK_PHASE(12);
+    if (pass == 0) RK_PHASE(14);
     const int3 f = wave_find_bin<BINS>(h, need);
     const uint32_t blo = lo + (uint32_t(f.x) << shift);
     if (shift == 0) {  // the boundary bin is one key value
@@ -635,11 +637,13 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
     lo = blo;
     need = f.y;
   }
+  RK_PHASE(15);
   if (n <= kWaveEmitMax) {
     if (wave == 0) wave_topk_emit(key, n, T, need_eq, emit);
   } else {
     wg_topk_emit<NT>(key, n, T, need_eq, emit, sm.tmp);
   }
+  RK_PHASE(16);
 }
 
 // Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32), result in every

@@ -295,6 +295,7 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
     }
     for (int i = 4 * P4 + threadIdx.x; i < P; i += 1024) skeys[i] = order_key(pu[i]);
     __syncthreads();
+    RK_PHASE(1);
     wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, P, n_keep - W, emit, sm);
   } else {
     wg_topk<1024, 2048>([&](int i) { return order_key(pu[i]); }, P, n_keep - W, emit, sm);
@@ -727,15 +728,17 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   const bool mfma = kBf16 && M <= 128;
   const int RG = (M + 31) / 32;
   const int CS = RG >= 4 ? 1 : 4 / RG;
-  // keys per workgroup: about 2048 workgroups per pass, in whole 128-key tiles
-  // (splitting the passes over unit chunks small enough for the second pass to
-  // re-read K from the MALL measured slower: the smaller launches lose more
-  // than the re-read gains)
+  // keys per workgroup: about 2048 workgroups per pass, in whole 128-key tiles,
+  // but at least 4 tiles, so each workgroup's window-row fetch is spread over
+  // a streamed run of K (at batch 1 one-tile workgroups measured 4 % slower
+  // for the whole eviction).  Splitting the passes over unit chunks small
+  // enough for the second pass to re-read K from the MALL measured slower:
+  // the smaller launches lose more than the re-read gains.
   auto range = [&](int keys) {
     const int wpu = (2048 + units - 1) / units;
     int kpw = (keys + wpu - 1) / wpu;
     kpw = (kpw + TK - 1) / TK * TK;
-    return kpw < TK ? TK : kpw;
+    return kpw < 4 * TK ? 4 * TK : kpw;
   };
   const int kpw1 = range(S);
   const int n_wg1 = mfma ? (S + kpw1 - 1) / kpw1 : lay.n_tiles;
