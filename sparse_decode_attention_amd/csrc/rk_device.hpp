@@ -184,17 +184,30 @@ __device__ __forceinline__ int2 wg_excl_scan2(int a, int b, int* tmp) {
 }
 
 // Ordered emission of a top-k: with the threshold key T, every key above it
-// is taken and `need_eq` of the keys equal to it, lowest positions first.  Thread t owns the contiguous
-// positions [t*seg, (t+1)*seg): it counts its keys above and equal to T, one
+// is taken and `need_eq` of the keys equal to it, lowest positions first (or,
+// when all_eq, every key >= T: one comparison per key).  Thread t owns the
+// contiguous positions [t*seg, (t+1)*seg): it counts its selected keys, one
 // workgroup scan gives the counts before it, then it emits its selected
-// positions in order.
+// positions in order.  (Per-thread runs beat per-row ballots here: a row of
+// 64 positions costs a dozen wave-wide instructions, a thread's key two.)
 template <int NT, typename KeyFn, typename EmitFn>
 __device__ __forceinline__ void wg_topk_emit(const KeyFn& key, int n, uint32_t T, int need_eq,
-                                             const EmitFn& emit, int* tmp) {
+                                             bool all_eq, const EmitFn& emit, int* tmp) {
   const int t = threadIdx.x;
   const int seg = ((n + NT - 1) / NT) | 1;  // odd: spreads LDS banks
   const int lo = min(t * seg, n);
   const int hi = min(lo + seg, n);
+  if (all_eq) {
+    int n_ge = 0;
+    for (int i = lo; i < hi; ++i) n_ge += key(i) >= T ? 1 : 0;
+    RK_PHASE(6);
+    int total;
+    int pos = wg_excl_scan<NT>(n_ge, tmp, &total);
+    for (int i = lo; i < hi; ++i)
+      if (key(i) >= T) emit(pos++, i);
+    RK_PHASE(7);
+    return;
+  }
   int n_gt = 0, n_eq = 0;
   for (int i = lo; i < hi; ++i) {
     const uint32_t kk = key(i);
@@ -553,7 +566,8 @@ constexpr int kWaveEmitMax = 1024;
 
 template <int NT, int BINS, int NBUF, typename KeyFn, typename EmitFn>
 __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit,
-                                        TopkSmem<NT, BINS, NBUF>& sm) {
+                                        TopkSmem<NT, BINS, NBUF>& sm, bool have_range = false,
+                                        uint32_t lo_in = 0xffffffffu, uint32_t hi_in = 0u) {
   constexpr int NW = NT / kWave;
   constexpr int LOG_BINS = BINS == 256 ? 8 : BINS == 512 ? 9 : BINS == 1024 ? 10 : 11;
   static_assert(BINS % NT == 0 || NT % BINS == 0, "bins");
@@ -566,11 +580,15 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
     for (int i = t; i < n; i += NT) emit(i, i);
     return;
   }
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int i = t; i < n; i += NT) {
-    const uint32_t kk = key(i);
-    lo = min(lo, kk);
-    hi = max(hi, kk);
+  // key range: this thread's share of it from the caller (have_range) or
+  // from a pass over the keys
+  uint32_t lo = lo_in, hi = hi_in;
+  if (!have_range) {
+    for (int i = t; i < n; i += NT) {
+      const uint32_t kk = key(i);
+      lo = min(lo, kk);
+      hi = max(hi, kk);
+    }
   }
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
@@ -586,9 +604,11 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
     hi = max(hi, sm.red[NW + w]);
   }
   RK_PHASE(13);
-  int need = k;  // keys still to take among the candidates [lo, hi]
-  uint32_t T;    // threshold: keys above are taken, need_eq of the keys equal to it
+  int need = k;      // keys still to take among the candidates [lo, hi]
+  int in_range = n;  // candidates in [lo, hi]
+  uint32_t T;        // threshold: keys above are taken, need_eq of the keys equal to it
   int need_eq;
+  bool all_eq;       // every key equal to T is taken: the choice is key >= T
   // histogram order: lane l of a wave walks an odd-length run of positions,
   // so one instruction's lanes touch keys far apart
   const int rows = ((n + kWave - 1) / kWave) | 1;
@@ -597,6 +617,7 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
     if (lo == hi) {  // every candidate has one value
       T = lo;
       need_eq = need;
+      all_eq = need == in_range;
       break;
     }
     const int span_bits = 32 - __clz(int(hi - lo));
@@ -622,26 +643,33 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
     if (shift == 0) {  // the boundary bin is one key value
       T = blo;
       need_eq = f.y;
+      all_eq = f.y == f.z;
       break;
     }
     if (f.y == f.z) {
       // the whole bin is taken: the selection is every key >= blo (keys above
-      // the candidate interval were taken by earlier passes).  blo > 0 here,
-      // since blo == 0 would take all n keys while k < n.
-      T = blo - 1u;
-      need_eq = 0;
+      // the candidate interval were taken by earlier passes)
+      T = blo;
+      need_eq = f.y;
+      all_eq = true;
       break;
     }
     const uint64_t bhi = uint64_t(blo) + ((uint64_t(1) << shift) - 1u);
     hi = bhi < uint64_t(hi) ? uint32_t(bhi) : hi;
     lo = blo;
     need = f.y;
+    in_range = f.z;
   }
   RK_PHASE(15);
   if (n <= kWaveEmitMax) {
-    if (wave == 0) wave_topk_emit(key, n, T, need_eq, emit);
+    if (wave == 0) {
+      if (all_eq)  // keys >= T: keys above T - 1 (T >= 1 here, else all n keys would be taken)
+        wave_topk_emit(key, n, T - 1u, 0, emit);
+      else
+        wave_topk_emit(key, n, T, need_eq, emit);
+    }
   } else {
-    wg_topk_emit<NT>(key, n, T, need_eq, emit, sm.tmp);
+    wg_topk_emit<NT>(key, n, T, need_eq, all_eq, emit, sm.tmp);
   }
   RK_PHASE(16);
 }

@@ -273,8 +273,16 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
   RK_PHASE(0);
   if (staged) {
     // 16-byte loads where the row allows it, all of a thread's loads in flight
+    // (the key range comes along: no separate pass for it)
     const bool vec = (reinterpret_cast<uintptr_t>(pu) & 15u) == 0;
     const int P4 = vec ? P / 4 : 0;
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    auto put = [&](int i, float x) {
+      const uint32_t kk = order_key(x);
+      skeys[i] = kk;
+      lo = min(lo, kk);
+      hi = max(hi, kk);
+    };
     for (int i0 = threadIdx.x; i0 < P4; i0 += 1024 * 16) {
       float4 buf[16];
 #pragma unroll
@@ -286,17 +294,17 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
       for (int x = 0; x < 16; ++x) {
         const int i = i0 + x * 1024;
         if (i < P4) {
-          skeys[4 * i] = order_key(buf[x].x);
-          skeys[4 * i + 1] = order_key(buf[x].y);
-          skeys[4 * i + 2] = order_key(buf[x].z);
-          skeys[4 * i + 3] = order_key(buf[x].w);
+          put(4 * i, buf[x].x);
+          put(4 * i + 1, buf[x].y);
+          put(4 * i + 2, buf[x].z);
+          put(4 * i + 3, buf[x].w);
         }
       }
     }
-    for (int i = 4 * P4 + threadIdx.x; i < P; i += 1024) skeys[i] = order_key(pu[i]);
+    for (int i = 4 * P4 + threadIdx.x; i < P; i += 1024) put(i, pu[i]);
     __syncthreads();
     RK_PHASE(1);
-    wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, P, n_keep - W, emit, sm);
+    wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, P, n_keep - W, emit, sm, true, lo, hi);
   } else {
     wg_topk<1024, 2048>([&](int i) { return order_key(pu[i]); }, P, n_keep - W, emit, sm);
   }

@@ -102,6 +102,8 @@ def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compa
         assert (got[n_keep - W:] == np.arange(S - W, S)).all()
         assert got.min() >= 0 and got[: n_keep - W].max(initial=-1) < S - W
         swaps += compare_sets(got[: n_keep - W], want[: n_keep - W], pl)
+        if S > W:   # on the GPU's own pooled scores the choice is exact (ties to the lower position)
+            assert np.array_equal(got, O.snapkv_select(g_pl, S, W, n_keep)), (b, h)
         if compact:
             idx = torch.as_tensor(got, dtype=torch.long, device=dev)
             assert torch.equal(ko[b, h, :n_keep], k[b, h, idx]) and torch.equal(vo[b, h, :n_keep], v[b, h, idx])
