@@ -441,8 +441,9 @@ __device__ __forceinline__ void merge_waves(int idx, const float* wm, const floa
 // all agree; ties toward the lower page, pages in ascending order) and keeps
 // the pages of its own split: this saves a launch and a memory round trip
 // between the choice and the K/V fetch.  Then 4 waves stream the pages and the
-// workgroup writes one partial (m, l, o[d]) per head.
-template <typename T, int D, int G, bool MT>
+// workgroup writes one partial (m, l, o[d]) per head.  TPS_: tokens per slot
+// per step (more loads in flight per wave, more registers).
+template <typename T, int D, int G, bool MT, int TPS_ = AttnShape<T, D, G>::TPS>
 __global__ __launch_bounds__(256) void hsa_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
     const int32_t* __restrict__ cand, int64_t cand_stride, const uint32_t* __restrict__ keys,
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   const T* ku = k + size_t(u) * size_t(kv_cap) * D + c * EPL;
   const T* vu = v + size_t(u) * size_t(kv_cap) * D + c * EPL;
   const int32_t* cu = MT ? cand + size_t(u) * size_t(cand_stride) : nullptr;
-  attend_pages<T, D, G, MT>(qf, ku, vu, cu, kv_cap, pages, wave, np, NW, block, n_tokens,
+  attend_pages<T, D, G, MT, TPS_>(qf, ku, vu, cu, kv_cap, pages, wave, np, NW, block, n_tokens,
                             scale_log2, m, l, o);
   wave_state_to_lds<T, D, G>(m, l, o, wave, wm, wl, wo);
   __syncthreads();
@@ -924,7 +925,9 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   static bool attn_attr_set = false;  // once per template instantiation
   if (!attn_attr_set) {
     for (const void* f : {reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, true>),
-                          reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, false>)}) {
+                          reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, false>),
+                          reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, true, 4>),
+                          reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, false, 4>)}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          int(kAttnDynLds));
       if (e != hipSuccess) return e;
@@ -933,16 +936,26 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   }
   if (attn_lds > kAttnDynLds) return hipErrorInvalidValue;
   const int attn_wgs = (n_split * units + kXcds - 1) / kXcds * kXcds;
-  if (cand)
-    RK_LAUNCH("hsa_attn_mt", (hsa_attn_kernel<T, D, G, true>), dim3(attn_wgs), dim3(256),
-              attn_lds, s, static_cast<const T*>(q), static_cast<const T*>(k),
-              static_cast<const T*>(v), kv_cap, cand, cand_stride, keys, lay.keys_pitch, nblk,
-              lay.nsel, pps, n_split, units, int(n_tokens), block, scale_log2, part, sel_opt);
-  else
-    RK_LAUNCH("hsa_attn", (hsa_attn_kernel<T, D, G, false>), dim3(attn_wgs), dim3(256),
-              attn_lds, s, static_cast<const T*>(q), static_cast<const T*>(k),
-              static_cast<const T*>(v), kv_cap, cand, cand_stride, keys, lay.keys_pitch, nblk,
-              lay.nsel, pps, n_split, units, int(n_tokens), block, scale_log2, part, sel_opt);
+  // at most one workgroup per CU: registers cannot limit occupancy, so each
+  // wave takes 4 tokens per slot per step (fewer dependent load rounds)
+  const bool one_per_cu = attn_wgs <= kComputeUnits;
+#define RK_ATTN(NAME, MTV, TPSV)                                                                  \
+  RK_LAUNCH(NAME, (hsa_attn_kernel<T, D, G, MTV, TPSV>), dim3(attn_wgs), dim3(256), attn_lds, s, \
+            static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), kv_cap, \
+            cand, cand_stride, keys, lay.keys_pitch, nblk, lay.nsel, pps, n_split, units,        \
+            int(n_tokens), block, scale_log2, part, sel_opt)
+  if (cand) {
+    if (one_per_cu)
+      RK_ATTN("hsa_attn_mt", true, 4);
+    else
+      RK_ATTN("hsa_attn_mt", true, (AttnShape<T, D, G>::TPS));
+  } else {
+    if (one_per_cu)
+      RK_ATTN("hsa_attn", false, 4);
+    else
+      RK_ATTN("hsa_attn", false, (AttnShape<T, D, G>::TPS));
+  }
+#undef RK_ATTN
   if ((err = hipGetLastError()) != hipSuccess) return err;
   RK_LAUNCH("hsa_combine", (hsa_combine_kernel<D, G>), dim3((units * G + 3) / 4), dim3(256), 0, s,
             part, n_split, units, out);

@@ -15,6 +15,7 @@ constexpr int64_t kMaxPages = 12288;
 constexpr int kWsTile = 64;
 // Pages handled by one attention workgroup at least (split-K granularity),
 // and the most workgroups one unit's attention is split over.
+constexpr int kComputeUnits = 256;  // MI355X
 constexpr int kMinPagesPerSplit = 4;
 constexpr int kMaxSplits = 64;
 // Stage-1 selection keeps the order keys of up to this many bytes in LDS

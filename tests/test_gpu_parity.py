@@ -416,6 +416,24 @@ def test_fused_mt_decode(rk):
     _decode_only(rk, w, 700, 32, 12, cand_total=2900, units_to_check=[(0, 0), (2, 17), (4, 31)])
 
 
+def test_split_decode_many_workgroups(rk):
+    """96 units on the split-K path with 768 attention workgroups (more than one
+    per CU: the two-tokens-per-slot variant), next to the batch-1 tests that run
+    the one-workgroup-per-CU variant."""
+    say("split decode, 96 units")
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=12, n_kv=8, n_q=32, seq=1040, n_plant=4)
+    _decode_only(rk, w, 997, 32, 32, units_to_check=[(0, 0), (5, 3), (11, 7)])
+    kc, vc, _ = WL.layer_kv(w, 0, device=DEV)
+    kmax = torch.empty(12, 8, 128, rk.aux_capacity(997, 16), dtype=kc.dtype, device=DEV)
+    kmin = torch.empty_like(kmax)
+    rk.rk_hsa_build_aux(kc, 997, 0, 16, kmax, kmin)
+    rk.rk_profile_begin()
+    rk.rk_hsa_decode(WL.decode_query(w, 0, 0, device=DEV), kc, vc, kmax, kmin, 997, 16, 32, 32,
+                     torch.empty(12, 32, 128, device=DEV))
+    assert set(rk.rk_profile_end()) == {"hsa_score", "hsa_attn", "hsa_combine"}
+
+
 @pytest.mark.parametrize("B,Hkv,n,k2", [
     (1, 2, 20000, 200),      # 1250 pages: split path, workgroup page top-k
     (20, 8, 17000, 64),      # 160 units with 1063 pages: fused path, workgroup page top-k
