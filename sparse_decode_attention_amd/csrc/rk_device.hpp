@@ -253,6 +253,7 @@ struct TopkSmem {
   alignas(16) uint32_t hist[NBUF][BINS];
   uint32_t red[2 * (NT / kWave)];
   int tmp[2 * (NT / kWave) + 2];
+  int n_cand;  // keys gathered into the caller's candidate buffer
 };
 
 // The bin holding the need-th largest key, counting from the top bin, and
@@ -567,7 +568,8 @@ constexpr int kWaveEmitMax = 1024;
 template <int NT, int BINS, int NBUF, typename KeyFn, typename EmitFn>
 __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const EmitFn& emit,
                                         TopkSmem<NT, BINS, NBUF>& sm, bool have_range = false,
-                                        uint32_t lo_in = 0xffffffffu, uint32_t hi_in = 0u) {
+                                        uint32_t lo_in = 0xffffffffu, uint32_t hi_in = 0u,
+                                        uint32_t* cand = nullptr, int cand_cap = 0) {
   constexpr int NW = NT / kWave;
   constexpr int LOG_BINS = BINS == 256 ? 8 : BINS == 512 ? 9 : BINS == 1024 ? 10 : 11;
   static_assert(BINS % NT == 0 || NT % BINS == 0, "bins");
@@ -612,6 +614,11 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
   // histogram order: lane l of a wave walks an odd-length run of positions,
   // so one instruction's lanes touch keys far apart
   const int rows = ((n + kWave - 1) / kWave) | 1;
+  // with a candidate buffer (cand_cap words of LDS), the second pass also
+  // gathers its candidates there when they fit, and later passes read only
+  // them instead of all n keys
+  bool from_cand = false;
+  if (t == 0) sm.n_cand = 0;
 #pragma unroll 1
   for (int pass = 0;; ++pass) {
     if (lo == hi) {  // every candidate has one value
@@ -628,17 +635,57 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
       for (int b = t; b < BINS; b += NT) h[b] = 0u;
       __syncthreads();
     }
-    for (int c = wave; c < rows; c += NW) {
-      const int i = lane * rows + c;
-      if (i < n) {
-        const uint32_t kk = key(i);
+    const bool gather = cand && pass == 1 && in_range <= cand_cap;
+    if (from_cand) {  // the gathered keys of the second pass's range hold this one's
+      const int nc = sm.n_cand;
+      for (int i = t; i < nc; i += NT) {
+        const uint32_t kk = cand[i];
         if (kk >= lo && kk <= hi) atomicAdd(&h[(kk - lo) >> shift], 1u);
       }
+    } else {
+      // UR keys of a lane read before any is used (one LDS round trip per UR)
+      constexpr int UR = 8;
+      for (int c0 = wave; c0 < rows; c0 += NW * UR) {
+        uint32_t kr[UR];
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          const int i = lane * rows + c0 + u * NW;
+          kr[u] = c0 + u * NW < rows && i < n ? key(i) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < UR; ++u) {
+          const int i = lane * rows + c0 + u * NW;
+          const uint32_t kk = kr[u];
+          if (c0 + u * NW < rows && i < n && kk >= lo && kk <= hi) {
+            atomicAdd(&h[(kk - lo) >> shift], 1u);
+            if (gather) cand[atomicAdd(&sm.n_cand, 1)] = kk;  // order is irrelevant to counts
+          }
+        }
+      }
     }
+    from_cand = from_cand || gather;
     __syncthreads();
     RK_PHASE(12);
     if (pass == 0) RK_PHASE(14);
-    const int3 f = wave_find_bin<BINS>(h, need);
+    if (pass == 1) RK_PHASE(17);
+    int3 f;
+    if constexpr (NW > 4) {
+      // one wave walks the histogram and shares the result: with several
+      // waves per SIMD, redundant walks would queue behind each other
+      if (wave == 0) {
+        f = wave_find_bin<BINS>(h, need);
+        if (lane == 0) {
+          sm.tmp[0] = f.x;
+          sm.tmp[1] = f.y;
+          sm.tmp[2] = f.z;
+        }
+      }
+      __syncthreads();
+      f = make_int3(sm.tmp[0], sm.tmp[1], sm.tmp[2]);
+      if (pass == 0) RK_PHASE(18);
+    } else {
+      f = wave_find_bin<BINS>(h, need);
+    }
     const uint32_t blo = lo + (uint32_t(f.x) << shift);
     if (shift == 0) {  // the boundary bin is one key value
       T = blo;

@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256) void pool_sum_kernel(const float* __restrict__
 // When the P = S - W keys fit, they are converted to order keys once and held
 // in LDS (dynamic, P words) for all radix passes and the compaction.
 __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ pooled, int S,
-                                                      int W, int n_keep, int staged,
+                                                      int W, int n_keep, int staged, int cand_cap,
                                                       int32_t* __restrict__ kept) {
   extern __shared__ uint32_t skeys[];
   __shared__ TopkSmem<1024, 2048, 1> sm;
@@ -304,7 +304,9 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
     for (int i = 4 * P4 + threadIdx.x; i < P; i += 1024) put(i, pu[i]);
     __syncthreads();
     RK_PHASE(1);
-    wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, P, n_keep - W, emit, sm, true, lo, hi);
+    // the LDS after the keys (cand_cap words) takes the later passes' candidates
+    wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, P, n_keep - W, emit, sm, true, lo, hi,
+                        skeys + P, cand_cap);
   } else {
     wg_topk<1024, 2048>([&](int i) { return order_key(pu[i]); }, P, n_keep - W, emit, sm);
   }
@@ -815,8 +817,12 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
     RK_LAUNCH("select_tokens", select_final_kernel, dim3(units), dim3(1024), size_t(n_cand) * 8,
               s, pooled, S, W, C, int(n_keep), cand, kept);
   } else {
+    // staged keys, then up to 4096 words of radix candidates in what LDS is left
+    const int cand_cap =
+        staged ? int(std::min<size_t>(4096, (kSelectKeysLds - size_t(P) * 4) / 4)) : 0;
     RK_LAUNCH("select_tokens", select_kernel, dim3(units), dim3(1024),
-              staged ? size_t(P) * 4 : size_t(0), s, pooled, S, W, int(n_keep), staged, kept);
+              staged ? size_t(P + cand_cap) * 4 : size_t(0), s, pooled, S, W, int(n_keep), staged,
+              cand_cap, kept);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (k_out && kmax) {
