@@ -379,8 +379,10 @@ struct TopkCut {
   bool fast;
 };
 
-// Keys of one lane's rows with 0 at positions >= n (counts only ask for
-// keys >= 1), and the wave's key range.
+// Keys of one lane's rows with 0 at positions >= n and every real key >= 1
+// (key 0 is a NaN pattern; merging it with key 1, another NaN, changes no
+// order that matters), so padding never falls in a key range [lo, hi]; and
+// the wave's key range.
 template <int R>
 __device__ __forceinline__ void topk_prepare(const uint32_t (&kr)[R], int n, uint32_t (&kz)[R],
                                              uint32_t& lo, uint32_t& hi) {
@@ -390,10 +392,10 @@ __device__ __forceinline__ void topk_prepare(const uint32_t (&kr)[R], int n, uin
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const bool valid = r * kWave + lane < n;
-    kz[r] = valid ? kr[r] : 0u;
+    kz[r] = valid ? max(kr[r], 1u) : 0u;
     if (valid) {
-      lo = min(lo, kr[r]);
-      hi = max(hi, kr[r]);
+      lo = min(lo, kz[r]);
+      hi = max(hi, kz[r]);
     }
   }
   lo = wave_min_u32(lo);
@@ -406,9 +408,9 @@ __device__ __forceinline__ void topk_prepare(const uint32_t (&kr)[R], int n, uin
 // operations of one wave complete in order, so it is read right after its
 // atomics with no barrier), narrowing to the bin that holds the cut; once
 // that bin holds at most kWaveRankMax keys they are ranked against each
-// other instead.  Rows at or beyond `rows` hold no keys and are skipped.
+// other instead.  Padding keys (0) never fall in the range.
 template <int R, int BINS>
-__device__ __forceinline__ TopkCut wave_topk_cut(const uint32_t (&kz)[R], int n, int rows, int k,
+__device__ __forceinline__ TopkCut wave_topk_cut(const uint32_t (&kz)[R], int n, int k,
                                                  uint32_t lo, uint32_t hi, uint32_t* hist) {
   constexpr int LOG_BINS = BINS == 256 ? 8 : BINS == 512 ? 9 : BINS == 1024 ? 10 : 11;
   static_assert((1 << LOG_BINS) == BINS && BINS <= 2048 && BINS >= 256, "bins");
@@ -429,7 +431,7 @@ __device__ __forceinline__ TopkCut wave_topk_cut(const uint32_t (&kz)[R], int n,
       cut.need_eq = need;
       return cut;
     }
-    if (in_range <= kWaveRankMax && lo != 0u) {
+    if (in_range <= kWaveRankMax) {
       RK_PHASE(24);
       const uint3 c = wave_rank_range(kz, n, lo, hi, need, hist);
       RK_PHASE(27);
@@ -446,12 +448,9 @@ __device__ __forceinline__ TopkCut wave_topk_cut(const uint32_t (&kz)[R], int n,
     const uint32_t span = hi - lo;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (r < rows) {
-        // one unsigned compare tests lo <= key <= hi; padding zeros fall out
-        // unless lo is 0 (only a NaN pattern orders there)
-        const uint32_t off = kz[r] - lo;
-        if (off <= span && (lo != 0u || r * kWave + lane < n)) atomicAdd(&hist[off >> shift], 1u);
-      }
+      // one unsigned compare tests lo <= key <= hi; padding zeros fall out
+      const uint32_t off = kz[r] - lo;
+      if (off <= span) atomicAdd(&hist[off >> shift], 1u);
     }
     const int3 f = wave_find_bin<BINS>(hist, need);
     const uint32_t blo = lo + (uint32_t(f.x) << shift);
@@ -472,14 +471,9 @@ __device__ __forceinline__ void wave_emit_cut(const uint32_t (&kz)[R], int n, co
   const int lane = lane_id();
   const unsigned long long below = (1ull << lane) - 1ull;
   if (cut.fast) {
-    unsigned long long sm[R];
-    if (cut.thr != 0u) {  // padding zeros fall below the threshold by themselves
+    unsigned long long sm[R];  // padding zeros fall below the threshold (>= 1)
 #pragma unroll
-      for (int r = 0; r < R; ++r) sm[r] = ballot(kz[r] >= cut.thr);
-    } else {
-#pragma unroll
-      for (int r = 0; r < R; ++r) sm[r] = ballot(r * kWave + lane < n);
-    }
+    for (int r = 0; r < R; ++r) sm[r] = ballot(kz[r] >= cut.thr);
     int base = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -531,7 +525,7 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&kr)[R], int n, int k,
   uint32_t kz[R], lo, hi;
   topk_prepare(kr, n, kz, lo, hi);
   RK_PHASE(9);
-  const TopkCut cut = wave_topk_cut<R, 256>(kz, n, (n + kWave - 1) / kWave, k, lo, hi, hist);
+  const TopkCut cut = wave_topk_cut<R, 256>(kz, n, k, lo, hi, hist);
   RK_PHASE(23);
   wave_emit_cut(kz, n, cut, emit, rank_lo, rank_hi);
 }
@@ -543,9 +537,11 @@ template <int R, typename KeyFn, typename EmitFn>
 __device__ __forceinline__ void wave_topk_load(const KeyFn& key, int n, int k, const EmitFn& emit,
                                                uint32_t* hist, int rank_lo, int rank_hi) {
   const int lane = lane_id();
+  // every read unconditional (positions past n re-read key n-1 and are masked
+  // later), so all R are in flight together rather than each behind a branch
   uint32_t kr[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) kr[r] = r * kWave + lane < n ? key(r * kWave + lane) : 0u;
+  for (int r = 0; r < R; ++r) kr[r] = key(min(r * kWave + lane, n - 1));
   wave_topk<R>(kr, n, k, emit, hist, rank_lo, rank_hi);
 }
 template <typename KeyFn, typename EmitFn>
