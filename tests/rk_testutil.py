@@ -150,10 +150,19 @@ def decode_and_check(rk, q, kc, vc, kmax, kmin, n_tokens, block, k1, k2, cand=No
     sel = torch.empty(B, Hkv, nsel, dtype=torch.int32, device=dev)
     chan = torch.empty(B, Hkv, k1, dtype=torch.int32, device=dev)
     s1 = torch.empty(B, Hkv, nblk, dtype=torch.float32, device=dev)
-    if cand is None:
-        rk.rk_hsa_decode(q, kc, vc, kmax, kmin, n_tokens, block, k1, k2, out, sel, chan, s1)
-    else:
-        rk.rk_hsa_decode_mt(q, kc, vc, cand, n_tokens, kmax, kmin, block, k1, k2, out, sel, chan, s1)
+    # twice: the checked call gets a workspace holding all-ones bytes (the
+    # result must not depend on what the workspace held before the call)
+    ws = None
+    for _ in range(2):
+        if ws is not None:
+            ws.fill_(255)
+            out.fill_(float("nan"))
+        if cand is None:
+            ws = rk.rk_hsa_decode(q, kc, vc, kmax, kmin, n_tokens, block, k1, k2, out, sel, chan,
+                                  s1, ws=ws)
+        else:
+            ws = rk.rk_hsa_decode_mt(q, kc, vc, cand, n_tokens, kmax, kmin, block, k1, k2, out,
+                                     sel, chan, s1, ws=ws)
     torch.cuda.synchronize()
     swaps = 0
     units = units_to_check or [(b, h) for b in range(B) for h in range(Hkv)]
