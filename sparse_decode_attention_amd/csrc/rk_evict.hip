@@ -426,8 +426,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k,
 //   pass 1: product K_chunk * Q^T, so lane l owns window row l%32 of its group
 //           and keeps that row's running (max, sum of exp2) in two registers
 //   pass 2: product Q * K_chunk^T, so lane l owns key l%32 and sums
-//           exp2(x - m_row) / Z_row over its 16 rows; row groups are then
-//           added in order -> score
+//           exp2(x - m_row - log2 Z_row) (= exp2(x - m_row) / Z_row, one
+//           multiply and 16 registers fewer) over its 16 rows; row groups
+//           are then added in order -> score
+// Registers are held to 128 per lane so four workgroups share a CU (16
+// waves): streaming K gains more from the extra resident waves than it
+// loses to operand fragments being fetched closer to their use.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -441,7 +445,7 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p, bool ok) {
 }
 
 template <int D, int PASS>
-__global__ __launch_bounds__(256) void ws_mfma_kernel(
+__global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
     const bf16_t* __restrict__ q_win, const bf16_t* __restrict__ k, int64_t kv_cap, int S, int W,
     int G, int n_wg, int keys_per_wg, float scale_log2, float2* __restrict__ partials,
     const float2* __restrict__ stats, float* __restrict__ scores) {
@@ -478,16 +482,16 @@ __global__ __launch_bounds__(256) void ws_mfma_kernel(
     for (int ks = 0; ks < KS; ++ks)
       a[ks] = load_bf16x8(qg + size_t(arow) * D + ks * 16 + half * 8, active && arow < M);
   }
-  // pass 1: (max, sum) of this lane's row; pass 2: (m, 1/Z) of its 16 rows
+  // pass 1: (max, sum) of this lane's row; pass 2: m + log2 Z of its 16 rows
+  // (rows past M get a huge offset, so they add zeros)
   float m1 = kNegBig, z1 = 0.f;
-  float m2[16], z2[16];
+  float m2[16];
   if (PASS == 2 && active) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = rg * 32 + 8 * (i / 4) + 4 * half + (i & 3);
-      const float2 st = row < M ? stats[size_t(u) * M + row] : make_float2(1.0e30f, 0.f);
-      m2[i] = st.x;
-      z2[i] = st.y;
+      const float2 st = row < M ? stats[size_t(u) * M + row] : make_float2(1.0e30f, 1.f);
+      m2[i] = st.x - __builtin_amdgcn_logf(st.y);  // stats hold (m, 1/Z); logf is log2
     }
   }
 
@@ -566,13 +570,16 @@ __global__ __launch_bounds__(256) void ws_mfma_kernel(
           for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b[ks], acc, 0, 0, 0);
           float cs_sum = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) cs_sum += fast_exp2(fmaf(acc[i], scale_log2, -m2[i])) * z2[i];
+          for (int i = 0; i < 16; ++i) cs_sum += fast_exp2(fmaf(acc[i], scale_log2, -m2[i]));
           cs_sum += __shfl_xor(cs_sum, 32);
           if (lane < 32) smem[rg * TK + c * 32 + lane] = cs_sum;
         }
       }
     }
     __syncthreads();
+    // the next tile goes to LDS first: the score stores below must not sit
+    // in front of the wait for its loads
+    if (next) stash();
     if (PASS == 2) {
       for (int cidx = threadIdx.x; cidx < TK; cidx += 256) {
         const int j = t0 + cidx;
@@ -582,7 +589,6 @@ __global__ __launch_bounds__(256) void ws_mfma_kernel(
         scores[size_t(u) * P + j] = sacc;
       }
     }
-    if (next) stash();
     __syncthreads();
   }
   if (PASS == 1) {
@@ -738,14 +744,15 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   const bool mfma = kBf16 && M <= 128;
   const int RG = (M + 31) / 32;
   const int CS = RG >= 4 ? 1 : 4 / RG;
-  // keys per workgroup: about 2048 workgroups per pass, in whole 128-key tiles,
-  // but at least 4 tiles, so each workgroup's window-row fetch is spread over
-  // a streamed run of K (at batch 1 one-tile workgroups measured 4 % slower
-  // for the whole eviction).  Splitting the passes over unit chunks small
-  // enough for the second pass to re-read K from the MALL measured slower:
-  // the smaller launches lose more than the re-read gains.
+  // keys per workgroup: about 8192 workgroups per pass (8 per CU slot; at
+  // batch 32, 2048 measured 8 % slower and 16384 slower again), in whole
+  // 128-key tiles, but at least 4 tiles, so each workgroup's window-row fetch
+  // is spread over a streamed run of K (at batch 1 one-tile workgroups
+  // measured 4 % slower for the whole eviction).  Splitting the passes over
+  // unit chunks small enough for the second pass to re-read K from the MALL
+  // measured slower: the smaller launches lose more than the re-read gains.
   auto range = [&](int keys) {
-    const int wpu = (2048 + units - 1) / units;
+    const int wpu = (8192 + units - 1) / units;
     int kpw = (keys + wpu - 1) / wpu;
     kpw = (kpw + TK - 1) / TK * TK;
     return kpw < 4 * TK ? 4 * TK : kpw;
