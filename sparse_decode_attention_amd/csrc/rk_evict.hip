@@ -460,7 +460,9 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
   const int RG = (M + 31) / 32;
   const int CS = RG >= 4 ? 1 : 4 / RG;  // waves sharing one row group
   const int items = RG * CS;
-  const int u = blockIdx.y;
+  // pass 2 walks the units in reverse: workgroups start in launch order, so
+  // it begins with the K that pass 1 read last, still in the MALL
+  const int u = PASS == 1 ? blockIdx.y : gridDim.y - 1 - blockIdx.y;
   const int wgi = blockIdx.x;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
