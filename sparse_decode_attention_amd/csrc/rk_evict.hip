@@ -194,18 +194,27 @@ __global__ __launch_bounds__(256) void ws_pass2_kernel(const T* __restrict__ q_w
   if (part == 0 && j0 + col < P) scores[size_t(u) * P + j0 + col] = total;
 }
 
-// Pooling for kernels up to 2*H+1 wide: a workgroup makes 1024 outputs, four
-// consecutive ones per thread, from a zero-padded LDS tile read back as
-// 16-byte vectors into registers; each output is summed left to right (the
-// first in-range term first: added zeros do not change a sum of
-// non-negative scores).
+// Pooling for a kernel 2*H+1 wide (H >= 4): a workgroup makes 2048 outputs,
+// PT = 8 consecutive ones per thread, from a zero-padded LDS tile read back as
+// 16-byte vectors.  The thread's outputs j0..j0+7 share the 2H-6 terms
+// j0+7-H .. j0+H; that middle is summed once (left to right) and each output
+// adds its own left run (summed right to left, so the runs nest) and right
+// run (left to right): about 10 adds per output instead of 2H, which made
+// the old one-sum-per-output form arithmetic-bound.  All terms are
+// non-negative, so the regrouping changes a sum by a few ulp at most; zeros
+// past either end add nothing.  Results go through LDS so the stores are
+// coalesced whatever the row alignment.
 template <int H>
 __global__ __launch_bounds__(256) void pool_sum_reg_kernel(const float* __restrict__ scores,
                                                            int P, float* __restrict__ pooled) {
-  constexpr int OUT = 1024;
-  constexpr int TW = (OUT + 2 * H + 3) & ~3;
-  constexpr int NV = (4 + 2 * H + 3) / 4;  // 16-byte reads per thread
+  constexpr int PT = 8;
+  constexpr int OUT = 256 * PT;
+  constexpr int NVAL = PT + 2 * H;        // scores a thread reads
+  constexpr int NV = (NVAL + 3) / 4;      // as 16-byte vectors
+  constexpr int TW = OUT - PT + 4 * NV;   // tile width (a multiple of 4)
+  static_assert(2 * H + 1 >= PT, "the outputs of a thread must share a middle");
   __shared__ __align__(16) float tile[TW];
+  __shared__ float res[OUT];
   const int u = blockIdx.y;
   const int j0 = blockIdx.x * OUT;
   const float* su = scores + size_t(u) * P;
@@ -218,20 +227,34 @@ __global__ __launch_bounds__(256) void pool_sum_reg_kernel(const float* __restri
   float v[NV * 4];
 #pragma unroll
   for (int x = 0; x < NV; ++x) {
-    const float4 f = *reinterpret_cast<const float4*>(tile + 4 * t + 4 * x);
+    const float4 f = *reinterpret_cast<const float4*>(tile + PT * t + 4 * x);
     v[4 * x] = f.x;
     v[4 * x + 1] = f.y;
     v[4 * x + 2] = f.z;
     v[4 * x + 3] = f.w;
   }
+  // output e (0 <= e < PT) sums v[e .. e + 2H]
+  float mid = v[PT - 1];
+#pragma unroll
+  for (int i = PT; i <= 2 * H; ++i) mid = __fadd_rn(mid, v[i]);
+  float left[PT];  // left[e] = v[e] + ... + v[PT - 2]
+  left[PT - 1] = 0.f;
+#pragma unroll
+  for (int e = PT - 2; e >= 0; --e) left[e] = e == PT - 2 ? v[e] : __fadd_rn(v[e], left[e + 1]);
+  float right = 0.f;  // v[2H + 1] + ... + v[2H + e]
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    if (e > 0) right = e == 1 ? v[2 * H + 1] : __fadd_rn(right, v[2 * H + e]);
+    float acc = e < PT - 1 ? __fadd_rn(left[e], mid) : mid;
+    if (e > 0) acc = __fadd_rn(acc, right);
+    res[PT * t + e] = acc;
+  }
+  __syncthreads();
   float* pu = pooled + size_t(u) * P;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float acc = v[e];
-#pragma unroll
-    for (int i = 1; i <= 2 * H; ++i) acc = __fadd_rn(acc, v[e + i]);
-    const int j = j0 + 4 * t + e;
-    if (j < P) pu[j] = acc;
+  for (int i = 0; i < PT; ++i) {
+    const int j = j0 + i * 256 + t;
+    if (j < P) pu[j] = res[i * 256 + t];
   }
 }
 
@@ -792,7 +815,7 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   if (P > 0) {
     const int h = (pool_kernel - 1) / 2;
     if (h == 31)
-      RK_LAUNCH("pool_sum", pool_sum_reg_kernel<31>, dim3((P + 1023) / 1024, units), dim3(256), 0,
+      RK_LAUNCH("pool_sum", pool_sum_reg_kernel<31>, dim3((P + 2047) / 2048, units), dim3(256), 0,
                 s, scores, P, pooled);
     else
       RK_LAUNCH("pool_sum", pool_sum_kernel, dim3((P + 255) / 256, units), dim3(256),
