@@ -27,6 +27,13 @@ struct bf16_t {
 // are negligible next to the sums of >= 1 they are added to.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait until this wave's vector memory loads have all returned (s_waitcnt
+// vmcnt(0); expcnt and lgkmcnt left at their maxima).  Placed after loads
+// made once before a loop whose body also issues loads, it lets the
+// compiler's wait counting see those registers as ready inside the loop;
+// otherwise it may wait for every load in flight at the loop head.
+__device__ __forceinline__ void wait_vector_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x.bits) << 16); }
 

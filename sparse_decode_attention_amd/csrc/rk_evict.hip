@@ -519,6 +519,9 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
       m2[i] = st.x - __builtin_amdgcn_logf(st.y);  // stats hold (m, 1/Z); logf is log2
     }
   }
+  // the Q fragments and row statistics are ready before the tile loop, so its
+  // first chunk need not wait for the next tile's loads
+  wait_vector_loads();
 
   uint4 pre[LPT];
   auto fetch = [&](int t0) {
