@@ -500,6 +500,7 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
   // guarantees at most 4 items.  Its Q fragments stay in registers.
   const bool active = wave < items;
   const int rg = wave / CS, cs = wave % CS;
+  RK_PHASE(PASS == 1 ? 18 : 21);
   bf16x8_t a[KS];
   {
     const int arow = rg * 32 + (lane & 31);
@@ -545,6 +546,7 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
     stash();
   }
   __syncthreads();
+  RK_PHASE(PASS == 1 ? 19 : 22);
   for (int t0 = kb; t0 < ke; t0 += TK) {
     const bool next = t0 + TK < ke;
     if (next) fetch(t0 + TK);             // in flight while this tile is multiplied
@@ -619,6 +621,7 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
     }
     __syncthreads();
   }
+  RK_PHASE(PASS == 1 ? 20 : 23);
   if (PASS == 1) {
     if (wave < items) {
       // the two half-waves hold disjoint keys of the same 32 rows
@@ -774,16 +777,17 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   const int CS = RG >= 4 ? 1 : 4 / RG;
   // keys per workgroup: about 8192 workgroups per pass (8 per CU slot; at
   // batch 32, 2048 measured 8 % slower and 16384 slower again), in whole
-  // 128-key tiles, but at least 4 tiles, so each workgroup's window-row fetch
+  // 128-key tiles, but at least 2 tiles, so each workgroup's window-row fetch
   // is spread over a streamed run of K (at batch 1 one-tile workgroups
-  // measured 4 % slower for the whole eviction).  Splitting the passes over
+  // measured 4 % slower for the whole eviction, two-tile ones 6 % faster
+  // than four-tile ones on the 109K prompt).  Splitting the passes over
   // unit chunks small enough for the second pass to re-read K from the MALL
   // measured slower: the smaller launches lose more than the re-read gains.
   auto range = [&](int keys) {
     const int wpu = (8192 + units - 1) / units;
     int kpw = (keys + wpu - 1) / wpu;
     kpw = (kpw + TK - 1) / TK * TK;
-    return kpw < 4 * TK ? 4 * TK : kpw;
+    return kpw < 2 * TK ? 2 * TK : kpw;
   };
   const int kpw1 = range(S);
   const int n_wg1 = mfma ? (S + kpw1 - 1) / kpw1 : lay.n_tiles;
