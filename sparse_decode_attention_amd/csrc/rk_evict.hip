@@ -126,30 +126,56 @@ __global__ __launch_bounds__(256) void ws_pass1_kernel(const T* __restrict__ q_w
     }
 #pragma unroll
     for (int off = 1; off < 8; off <<= 1) z += __shfl_xor(z, off);
-    if (part == 0 && r_all < M) partials[(size_t(u) * M + r_all) * n_tiles + tile] = make_float2(mx, z);
+    if (part == 0 && r_all < M) partials[(size_t(u) * n_tiles + tile) * M + r_all] = make_float2(mx, z);
     __syncthreads();
   }
 }
 
-// Merge the tile partials of every row: (m, 1/Z).  One wave per (unit, row);
-// lane l takes tiles l, l+64, ... in order, then a fixed butterfly merges lanes.
-__global__ __launch_bounds__(256) void ws_stats_kernel(const float2* __restrict__ partials,
-                                                       int M, int n_tiles, int units,
-                                                       float2* __restrict__ stats) {
-  const int wi = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (wi >= units * M) return;
-  const int lane = lane_id();
-  const float2* pr = partials + size_t(wi) * n_tiles;
-  float mm = kNegBig;
-  for (int t = lane; t < n_tiles; t += kWave) mm = fmaxf(mm, pr[t].x);
-  mm = wave_max(mm);
-  float z = 0.f;
-  for (int t = lane; t < n_tiles; t += kWave) {
-    const float2 p = pr[t];
-    z += p.y * fast_exp2(p.x - mm);
+// Merge the tile partials of every row: (m, 1/Z).  Partials are laid out
+// [unit][tile][row] (each pass-1 workgroup writes one contiguous run, no
+// partial-line writes).  A workgroup takes 64 rows; its 16 waves split the
+// tiles in groups of 8 consecutive ones (wave s: groups s, s+16, ...), each
+// thread one row, so a wave's reads of one tile are consecutive and a
+// group's loads are in flight together.  The 16 split results are then
+// merged in split order.
+__global__ __launch_bounds__(1024) void ws_stats_kernel(const float2* __restrict__ partials,
+                                                        int M, int n_tiles, int units,
+                                                        float2* __restrict__ stats) {
+  constexpr int RPW = 64, SPL = 16, GRP = 8;
+  __shared__ float2 part[SPL][RPW];
+  const int rl = threadIdx.x % RPW, sp = threadIdx.x / RPW;
+  const int i = blockIdx.x * RPW + rl;  // row of all units: u * M + r
+  float mm = kNegBig, z = 0.f;
+  if (i < units * M) {
+    const int u = i / M, r = i % M;
+    const float2* pr = partials + size_t(u) * n_tiles * M + r;
+    for (int t0 = sp * GRP; t0 < n_tiles; t0 += SPL * GRP) {
+      float2 p[GRP];
+#pragma unroll
+      for (int g = 0; g < GRP; ++g)
+        p[g] = t0 + g < n_tiles ? pr[size_t(t0 + g) * M] : make_float2(kNegBig, 0.f);
+      float mn = mm;
+#pragma unroll
+      for (int g = 0; g < GRP; ++g) mn = fmaxf(mn, p[g].x);
+      float zz = z * fast_exp2(mm - mn);
+#pragma unroll
+      for (int g = 0; g < GRP; ++g) zz += p[g].y * fast_exp2(p[g].x - mn);
+      z = zz;
+      mm = mn;
+    }
   }
-  z = wave_sum(z);
-  if (lane == 0) stats[wi] = make_float2(mm, 1.0f / z);
+  part[sp][rl] = make_float2(mm, z);
+  __syncthreads();
+  if (sp == 0 && i < units * M) {
+#pragma unroll
+    for (int s2 = 1; s2 < SPL; ++s2) {
+      const float2 q = part[s2][rl];
+      const float mn = fmaxf(mm, q.x);
+      z = z * fast_exp2(mm - mn) + q.y * fast_exp2(q.x - mn);
+      mm = mn;
+    }
+    stats[i] = make_float2(mm, 1.0f / z);
+  }
 }
 
 // Pass 2: score[j] = sum over the G*W rows of exp2(x - m) / Z, prefix keys only.
@@ -644,7 +670,7 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
         zz = zz * fast_exp2(mm - mn) + pz.y * fast_exp2(pz.x - mn);
         mm = mn;
       }
-      partials[(size_t(u) * M + r) * n_wg + wgi] = make_float2(mm, zz);
+      partials[(size_t(u) * n_wg + wgi) * M + r] = make_float2(mm, zz);
     }
   }
 }
@@ -804,7 +830,7 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  RK_LAUNCH("ws_stats", ws_stats_kernel, dim3((units * M + 3) / 4), dim3(256), 0, s, partials, M,
+  RK_LAUNCH("ws_stats", ws_stats_kernel, dim3((units * M + 63) / 64), dim3(1024), 0, s, partials, M,
             n_tiles, units, stats);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (P > 0) {
