@@ -7,27 +7,32 @@
 // (pages over the stage-1 candidate list of the full cache).  Also the
 // decode-time append: one new row per unit folded into its page.
 //
-// One workgroup covers kPagesPerWg consecutive pages of one unit.  Each thread
-// owns one 16-byte channel chunk of one page: it streams the page's rows
-// (coalesced 16-byte loads, a whole 256-byte row per 16 lanes), keeps the
-// running max/min in registers, then the tile is transposed through LDS so
-// the channel-major output is written in contiguous page runs.  Bandwidth
-// bound: bytes = rows read + 2 * d * pages * sizeof(T) written.
+// One 512-thread workgroup covers PPW consecutive pages of one unit (32 for
+// 256-byte rows, so each channel's output run is a whole 64-byte line).  Each
+// thread owns one 16-byte channel chunk of one page: it reads the page's rows
+// eight at a time (their indices, then all eight coalesced 16-byte loads in
+// flight; a short page repeats its last row, which max/min ignore), keeps
+// the running max/min in registers, then the tile is transposed through LDS
+// so the channel-major output is written in contiguous page runs.
+// Bandwidth bound: bytes = rows read + 2 * d * pages * sizeof(T) written.
 #include "rk_device.hpp"
 #include "rk_internal.hpp"
 
 namespace rk {
 namespace {
 
+constexpr int kAuxThreads = 512;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void aux_build_kernel(
+__global__ __launch_bounds__(kAuxThreads) void aux_build_kernel(
     const T* __restrict__ k, int64_t k_cap, const int32_t* __restrict__ idx, int64_t idx_stride,
     int n_tokens, int first_block, int nblk, int block, T* __restrict__ kmax,
     T* __restrict__ kmin, int64_t nblk_cap) {
   constexpr int EPL = Vec16<T>::N;   // elements per 16-byte chunk
   constexpr int CPR = D / EPL;       // chunks per row
-  constexpr int PPW = 256 / CPR;     // pages per workgroup
-  static_assert(D % EPL == 0 && 256 % CPR == 0, "row must split into 16-byte chunks");
+  constexpr int PPW = kAuxThreads / CPR;  // pages per workgroup
+  constexpr int RB = 8;              // rows in flight per thread
+  static_assert(D % EPL == 0 && kAuxThreads % CPR == 0, "row must split into 16-byte chunks");
   __shared__ T smax[D][PPW + 1];
   __shared__ T smin[D][PPW + 1];
 
@@ -44,20 +49,30 @@ __global__ __launch_bounds__(256) void aux_build_kernel(
     const int n0 = p * block;
     const int n1 = min(n0 + block, n_tokens);
     float mx[EPL], mn[EPL];
-    {
-      const int row = iu ? clamp_row(iu[n0], k_cap) : n0;
-      unpack16(load16(ku + size_t(row) * D), mx);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) mn[e] = mx[e];
+    for (int e = 0; e < EPL; ++e) {
+      mx[e] = -INFINITY;
+      mn[e] = INFINITY;
     }
-    for (int n = n0 + 1; n < n1; ++n) {
-      const int row = iu ? clamp_row(iu[n], k_cap) : n;
-      float x[EPL];
-      unpack16(load16(ku + size_t(row) * D), x);
+    for (int b0 = n0; b0 < n1; b0 += RB) {
+      int row[RB];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        mx[e] = x[e] > mx[e] ? x[e] : mx[e];
-        mn[e] = x[e] < mn[e] ? x[e] : mn[e];
+      for (int i = 0; i < RB; ++i) {
+        const int n = min(b0 + i, n1 - 1);
+        row[i] = iu ? clamp_row(iu[n], k_cap) : n;
+      }
+      Vec16<T> xr[RB];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) xr[i] = load16(ku + size_t(row[i]) * D);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        float x[EPL];
+        unpack16(xr[i], x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          mx[e] = x[e] > mx[e] ? x[e] : mx[e];
+          mn[e] = x[e] < mn[e] ? x[e] : mn[e];
+        }
       }
     }
 #pragma unroll
@@ -75,7 +90,7 @@ __global__ __launch_bounds__(256) void aux_build_kernel(
   __syncthreads();
   T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
   T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
-  for (int e = t; e < D * PPW; e += 256) {
+  for (int e = t; e < D * PPW; e += kAuxThreads) {
     const int ch = e / PPW;
     const int jj = e % PPW;
     const int pp = p0 + jj;
@@ -90,11 +105,11 @@ template <typename T, int D>
 hipError_t launch_aux_t(const Dims& d, const void* k, int64_t k_cap, const int32_t* idx,
                         int64_t idx_stride, int64_t n_tokens, int64_t first_block, int block,
                         void* kmax, void* kmin, int64_t nblk_cap, hipStream_t s) {
-  constexpr int PPW = 256 / (D / Vec16<T>::N);
+  constexpr int PPW = kAuxThreads / (D / Vec16<T>::N);
   const int64_t nblk = (n_tokens + block - 1) / block;
   const int64_t npages = nblk - first_block;
   dim3 grid(unsigned((npages + PPW - 1) / PPW), unsigned(d.units()));
-  RK_LAUNCH("aux_build", (aux_build_kernel<T, D>), grid, dim3(256), 0, s,
+  RK_LAUNCH("aux_build", (aux_build_kernel<T, D>), grid, dim3(kAuxThreads), 0, s,
                      static_cast<const T*>(k), k_cap, idx, idx_stride, int(n_tokens),
                      int(first_block), int(nblk), block, static_cast<T*>(kmax),
                      static_cast<T*>(kmin), nblk_cap);

@@ -459,6 +459,96 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k,
   }
 }
 
+// The same compaction + aux for launches with many pages: one 512-thread
+// workgroup per 32 pages (256-byte rows), each thread one 16-byte chunk of one
+// page for all of the page's rows, read eight at a time (indices, then all
+// K and V loads in flight; a short page repeats its last row for max/min and
+// skips its store).  No row-group merge is needed, and each channel's aux run
+// is a whole 64-byte line instead of 8 bytes (short runs are written back as
+// partial lines, which the counters showed as ~20 % extra write traffic).
+constexpr int kGatherWideThreads = 512;
+template <typename T, int D>
+__global__ __launch_bounds__(kGatherWideThreads, 4) void gather_aux_wide_kernel(
+    const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
+    const int32_t* __restrict__ kept, int n_keep, T* __restrict__ k_out, T* __restrict__ v_out,
+    int64_t out_cap, int block, T* __restrict__ kmax, T* __restrict__ kmin, int64_t nblk_cap) {
+  constexpr int EPL = Vec16<T>::N;
+  constexpr int CPR = D / EPL;
+  constexpr int PPW = kGatherWideThreads / CPR;
+  constexpr int RB = 8;
+  static_assert(kGatherWideThreads % CPR == 0, "workgroup shape");
+  __shared__ T smax[D][PPW + 1];
+  __shared__ T smin[D][PPW + 1];
+  using Rw = decltype(Vec16<T>::raw);
+  const int t = threadIdx.x;
+  const int c = t % CPR;
+  const int j = t / CPR;
+  const int u = blockIdx.y;
+  const int nblk = (n_keep + block - 1) / block;
+  const int p0 = blockIdx.x * PPW;
+  const int p = p0 + j;
+  if (p < nblk) {
+    const int n0 = p * block;
+    const int n1 = min(n0 + block, n_keep);
+    const int* ku = kept + size_t(u) * n_keep;
+    float mx[EPL], mn[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      mx[e] = -INFINITY;
+      mn[e] = INFINITY;
+    }
+    for (int b0 = n0; b0 < n1; b0 += RB) {
+      int src[RB];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) src[i] = ku[min(b0 + i, n1 - 1)];
+      Vec16<T> kr[RB], vr[RB];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const size_t a = (size_t(u) * size_t(kv_cap) + size_t(src[i])) * D + c * EPL;
+        kr[i] = load16(k + a);
+        vr[i] = load16(v + a);
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (b0 + i < n1) {
+          const size_t dst = (size_t(u) * size_t(out_cap) + size_t(b0 + i)) * D + c * EPL;
+          *reinterpret_cast<Rw*>(k_out + dst) = kr[i].raw;
+          *reinterpret_cast<Rw*>(v_out + dst) = vr[i].raw;
+        }
+        float x[EPL];
+        unpack16(kr[i], x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          mx[e] = x[e] > mx[e] ? x[e] : mx[e];
+          mn[e] = x[e] < mn[e] ? x[e] : mn[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      if constexpr (sizeof(T) == 2) {
+        // the values came from bf16, so dropping the low half is exact
+        smax[c * EPL + e][j].bits = uint16_t(__float_as_uint(mx[e]) >> 16);
+        smin[c * EPL + e][j].bits = uint16_t(__float_as_uint(mn[e]) >> 16);
+      } else {
+        smax[c * EPL + e][j] = mx[e];
+        smin[c * EPL + e][j] = mn[e];
+      }
+    }
+  }
+  __syncthreads();
+  T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
+  T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
+  for (int e = t; e < D * PPW; e += kGatherWideThreads) {
+    const int ch = e / PPW;
+    const int jj = e % PPW;
+    if (p0 + jj < nblk) {
+      xu[size_t(ch) * nblk_cap + p0 + jj] = smax[ch][jj];
+      nu[size_t(ch) * nblk_cap + p0 + jj] = smin[ch][jj];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 window scoring on the matrix cores (v_mfma_f32_32x32x16_bf16).
 //
@@ -891,12 +981,23 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (k_out && kmax) {
+    // wide workgroups (whole-line aux runs) once they still make >= 2 per CU;
+    // small launches keep 4-page workgroups, which spread the copy over more CUs
     constexpr int PPW = 256 / ((D / Vec16<T>::N) * 4);
+    constexpr int PPW_WIDE = kGatherWideThreads / (D / Vec16<T>::N);
     const int64_t nblk = (n_keep + block - 1) / block;
-    RK_LAUNCH("gather_kv", (gather_aux_kernel<T, D>), dim3(unsigned((nblk + PPW - 1) / PPW), units),
-              dim3(256), 0, s, kk, static_cast<const T*>(v), kv_cap, kept, int(n_keep),
-              static_cast<T*>(k_out), static_cast<T*>(v_out), out_cap, block,
-              static_cast<T*>(kmax), static_cast<T*>(kmin), nblk_cap);
+    const int64_t wide_wgs = (nblk + PPW_WIDE - 1) / PPW_WIDE * units;
+    if (wide_wgs >= 2 * kComputeUnits)
+      RK_LAUNCH("gather_kv", (gather_aux_wide_kernel<T, D>),
+                dim3(unsigned((nblk + PPW_WIDE - 1) / PPW_WIDE), units), dim3(kGatherWideThreads),
+                0, s, kk, static_cast<const T*>(v), kv_cap, kept, int(n_keep),
+                static_cast<T*>(k_out), static_cast<T*>(v_out), out_cap, block,
+                static_cast<T*>(kmax), static_cast<T*>(kmin), nblk_cap);
+    else
+      RK_LAUNCH("gather_kv", (gather_aux_kernel<T, D>), dim3(unsigned((nblk + PPW - 1) / PPW), units),
+                dim3(256), 0, s, kk, static_cast<const T*>(v), kv_cap, kept, int(n_keep),
+                static_cast<T*>(k_out), static_cast<T*>(v_out), out_cap, block,
+                static_cast<T*>(kmax), static_cast<T*>(kmin), nblk_cap);
     err = hipGetLastError();
   } else if (k_out) {
     RK_LAUNCH("gather_kv", (gather_kernel<T, D>), dim3(unsigned((n_keep + 63) / 64), units),

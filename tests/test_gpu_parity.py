@@ -109,6 +109,19 @@ def test_shapes_and_ragged_tails(rk, dtype, d, G, S, W, pool):
     say("swaps", res["swaps_evict"], res["swaps_decode"])
 
 
+@pytest.mark.parametrize("n_keep,out_cap", [(700, 700), (705, 760)])
+def test_compaction_aux_many_pages(rk, n_keep, out_cap):
+    """Batch 32 x 8 KV heads: the compaction with Kmax/Kmin takes its wide
+    (32 pages per workgroup) form; ragged last page, spare capacity."""
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=32, seq=1500, n_plant=8)
+    say("compaction + aux", w.batch, "x", w.n_kv, "units, n_keep", n_keep, "cap", out_cap)
+    k, v, _ = WL.layer_kv(w, 0, device=DEV)
+    qw = WL.window_queries(w, 0, device=DEV)
+    U.evict_and_check(rk, qw, k, v, w.seq, w.window, w.pool, n_keep, out_cap=out_cap,
+                      aux_block=w.block, units_to_check=[(0, 0), (13, 5), (31, 7)])
+
+
 def test_keep_all_and_window_only(rk):
     base = WL.WORKLOADS["tiny-gqa-s2048-d64-fp32"]
     w = WL.scaled(base, seq=600, batch=2)
