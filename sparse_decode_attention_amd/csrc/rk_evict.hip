@@ -981,13 +981,15 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (k_out && kmax) {
-    // wide workgroups (whole-line aux runs) once they still make >= 2 per CU;
-    // small launches keep 4-page workgroups, which spread the copy over more CUs
+    // wide workgroups (whole-line aux runs) unless they would leave most CUs
+    // idle: at batch 1 with 32K keys (152 of them) they measured as fast as
+    // the 4-page form, and twice as fast with 3-token pages; the 109K needle
+    // (8 of them) keeps 4-page workgroups, which spread its copy over more CUs
     constexpr int PPW = 256 / ((D / Vec16<T>::N) * 4);
     constexpr int PPW_WIDE = kGatherWideThreads / (D / Vec16<T>::N);
     const int64_t nblk = (n_keep + block - 1) / block;
     const int64_t wide_wgs = (nblk + PPW_WIDE - 1) / PPW_WIDE * units;
-    if (wide_wgs >= 2 * kComputeUnits)
+    if (wide_wgs >= kComputeUnits / 4)
       RK_LAUNCH("gather_kv", (gather_aux_wide_kernel<T, D>),
                 dim3(unsigned((nblk + PPW_WIDE - 1) / PPW_WIDE), units), dim3(kGatherWideThreads),
                 0, s, kk, static_cast<const T*>(v), kv_cap, kept, int(n_keep),
