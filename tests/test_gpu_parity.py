@@ -459,6 +459,17 @@ def test_many_pages_decode(rk, B, Hkv, n, k2):
     _decode_only(rk, w, n, 64, k2, units_to_check=units, steps=1)
 
 
+@pytest.mark.parametrize("n", [12288 * 16, 12288 * 16 - 5])
+def test_max_pages_decode(rk, n):
+    """The largest page count a decode call takes (12288 pages of 16; the
+    second case with a ragged last page): workgroup page top-k over every
+    page key held in LDS at its full size."""
+    say("max pages", n)
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=1, n_kv=2, n_q=8, seq=n, n_plant=8)
+    _decode_only(rk, w, n, 64, 256, steps=1)
+
+
 @pytest.mark.parametrize("B,spread", [(1, 2), (1, 200), (20, 2), (20, 200)])
 def test_page_topk_exact_ties(rk, B, spread):
     """Integer-valued q and Kmax/Kmin make many channel sums and page scores
