@@ -809,7 +809,10 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   const int units = d.units();
 
   const float scale_log2 = float(1.4426950408889634 / sqrt(double(D)));
-  if constexpr (G <= 4) if (units >= kFusedMinUnits) {
+  // one workgroup per unit when the units fill the chip, or when each of its
+  // 16 waves streams at most one page (the 109K needle: 16 pages per unit),
+  // where the split path's three launches cost more than one CU per unit
+  if constexpr (G <= 4) if (units >= kFusedMinUnits || lay.nsel <= kFusedThreads / kWave) {
     // one workgroup per unit: chunk of npc pages within the LDS budget
     const int k1pf = (k1 + 15) / 16 * 16 + int(16 / sizeof(T));
     const size_t fixed = fused_lds_bytes(nblk, lay.nsel, 0, k1pf, sizeof(T), D, G);

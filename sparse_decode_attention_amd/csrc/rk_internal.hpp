@@ -29,9 +29,9 @@ constexpr size_t kScoreAllBytes = size_t(8) << 20;
 // Up to this many pages the attention workgroup's page top-k runs in one
 // wave from registers (a multiple of 64).
 constexpr int kWaveTopkPages = 1024;
-// Decode calls with at least this many units run steps 2 and 3 in one
-// workgroup per unit (the units alone fill the 256 CUs), with at most this
-// much dynamic LDS per workgroup.
+// Decode calls with at least this many units (the units alone fill the 256
+// CUs), or with at most one chosen page per wave, run steps 2 and 3 in one
+// workgroup per unit, with at most this much dynamic LDS per workgroup.
 constexpr int kFusedMinUnits = 160;
 constexpr int kFusedThreads = 1024;
 constexpr size_t kFusedLdsBudget = 144 * 1024;

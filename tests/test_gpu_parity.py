@@ -87,7 +87,7 @@ def test_short_and_odd_pages(rk, block):
     base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
     say("pages of", block, "split path")
     w = WL.scaled(base, batch=2, seq=900, n_plant=8, block=block)
-    _decode_only(rk, w, 877, 32, max(1, 200 // block))
+    _decode_only(rk, w, 877, 32, max(17, 200 // block))     # > 16 pages: split path
     say("pages of", block, "fused path")
     w = WL.scaled(base, batch=20, seq=500, n_plant=4, block=block)
     _decode_only(rk, w, 487, 32, max(1, 120 // block), units_to_check=[(0, 0), (7, 3), (19, 7)], steps=1)
@@ -287,7 +287,7 @@ def test_kernel_timing_hooks(rk):
         rk.rk_hsa_build_aux(kc, 512, 0, 16, kmax, kmin, n_q_heads=8)
     q = WL.decode_query(w, 0, 0, device=DEV)
     out = torch.empty(1, 8, 64, device=DEV)
-    rk.rk_hsa_decode(q, kc, vc, kmax, kmin, 512, 16, 16, 4, out)
+    rk.rk_hsa_decode(q, kc, vc, kmax, kmin, 512, 16, 16, 20, out)   # > 16 pages: split path
     prof = rk.rk_profile_end()
     assert prof["aux_build"][0] == 3 and prof["aux_build"][1] > 0
     assert set(prof) == {"aux_build", "hsa_score", "hsa_attn", "hsa_combine"}
@@ -419,6 +419,24 @@ def test_fused_large_batch_decode(rk, dtype, d, G, B, Hkv, n, k1, k2):
     out = torch.empty(B, Hkv * G, d, device=DEV)
     rk.rk_profile_begin()
     rk.rk_hsa_decode(WL.decode_query(w, 0, 0, device=DEV), kc, vc, kmax, kmin, n, 16, k1, k2, out)
+    assert set(rk.rk_profile_end()) == {"hsa_fused"}
+
+
+@pytest.mark.parametrize("k2", [16, 5])
+def test_fused_few_pages_batch1(rk, k2):
+    """Batch 1 with at most 16 chosen pages (one per wave): one workgroup per
+    unit, checked against the oracle, and the launch is the fused kernel."""
+    say("fused decode, batch 1, k2", k2)
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=1, seq=1040, n_plant=4)
+    _decode_only(rk, w, 997, 32, k2)
+    kc, vc, _ = WL.layer_kv(w, 0, device=DEV)
+    kmax = torch.empty(1, 8, 128, rk.aux_capacity(997, 16), dtype=kc.dtype, device=DEV)
+    kmin = torch.empty_like(kmax)
+    rk.rk_hsa_build_aux(kc, 997, 0, 16, kmax, kmin)
+    rk.rk_profile_begin()
+    rk.rk_hsa_decode(WL.decode_query(w, 0, 0, device=DEV), kc, vc, kmax, kmin, 997, 16, 32, k2,
+                     torch.empty(1, 32, 128, device=DEV))
     assert set(rk.rk_profile_end()) == {"hsa_fused"}
 
 
