@@ -362,6 +362,117 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
   for (int r = threadIdx.x; r < W; r += 1024) ku[n_keep - W + r] = P + r;
 }
 
+// Pooling and selection in one launch (pool kernel 2H+1, the prefix keys
+// held in LDS): the workgroup stages the unit's window scores with a zero
+// halo of H on either side, pools them eight outputs per thread at a time as
+// pool_sum_reg_kernel does (same grouping, so the same values), turns them
+// into order keys in place once every thread has read its window, and selects
+// as select_kernel does.  Saves the pooled scores' round trip through memory
+// and a launch; the pooled scores are still written when asked for.
+template <int H>
+__global__ __launch_bounds__(1024) void select_pool_kernel(const float* __restrict__ scores,
+                                                           int S, int W, int n_keep, int cand_cap,
+                                                           float* __restrict__ pooled_opt,
+                                                           int32_t* __restrict__ kept) {
+  constexpr int PT = 8;                       // outputs per thread chunk
+  constexpr int NVAL = PT + 2 * H;            // window of a chunk
+  constexpr int NV = (NVAL + 3) / 4;          // as 16-byte vectors
+  constexpr int MAXC = 5;                     // chunks per thread: P <= 5 * 8 * 1024
+  static_assert(2 * H + 1 >= PT, "the outputs of a chunk must share a middle");
+  extern __shared__ __align__(16) uint32_t skeys[];  // raw scores (haloed), then keys
+  __shared__ TopkSmem<1024, 2048, 1> sm;
+  float* raw = reinterpret_cast<float*>(skeys);   // raw[H + i] = score[i]
+  const int u = blockIdx.x;
+  const int t = threadIdx.x;
+  const int P = S - W;
+  const float* su = scores + size_t(u) * P;
+  int32_t* ku = kept + size_t(u) * n_keep;
+  auto emit = [&](int r, int i) { ku[r] = i; };
+  const int nchunk = (P + PT - 1) / PT;
+  const int tw = nchunk * PT + 4 * NV - PT;       // raw words any chunk reads
+  for (int e = t; e < H; e += 1024) raw[e] = 0.f;
+  for (int e = H + P + t; e < tw; e += 1024) raw[e] = 0.f;
+  {
+    // 16-byte loads where the row allows it, all of a thread's loads in flight
+    const bool vec = (reinterpret_cast<uintptr_t>(su) & 15u) == 0;
+    const int P4 = vec ? P / 4 : 0;
+    for (int i0 = t; i0 < P4; i0 += 1024 * 16) {
+      float4 buf[16];
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int i = i0 + x * 1024;
+        if (i < P4) buf[x] = reinterpret_cast<const float4*>(su)[i];
+      }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int i = i0 + x * 1024;
+        if (i < P4) {
+          raw[H + 4 * i] = buf[x].x;
+          raw[H + 4 * i + 1] = buf[x].y;
+          raw[H + 4 * i + 2] = buf[x].z;
+          raw[H + 4 * i + 3] = buf[x].w;
+        }
+      }
+    }
+    for (int i = 4 * P4 + t; i < P; i += 1024) raw[H + i] = su[i];
+  }
+  __syncthreads();
+  float out[MAXC][PT];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int ch = t + c * 1024;
+    if (ch < nchunk) {
+      float v[NV * 4];
+#pragma unroll
+      for (int x = 0; x < NV; ++x) {
+        const float4 f = *reinterpret_cast<const float4*>(raw + PT * ch + 4 * x);
+        v[4 * x] = f.x;
+        v[4 * x + 1] = f.y;
+        v[4 * x + 2] = f.z;
+        v[4 * x + 3] = f.w;
+      }
+      float mid = v[PT - 1];
+#pragma unroll
+      for (int i = PT; i <= 2 * H; ++i) mid = __fadd_rn(mid, v[i]);
+      float left[PT];
+      left[PT - 1] = 0.f;
+#pragma unroll
+      for (int e = PT - 2; e >= 0; --e) left[e] = e == PT - 2 ? v[e] : __fadd_rn(v[e], left[e + 1]);
+      float right = 0.f;
+#pragma unroll
+      for (int e = 0; e < PT; ++e) {
+        if (e > 0) right = e == 1 ? v[2 * H + 1] : __fadd_rn(right, v[2 * H + e]);
+        float acc = e < PT - 1 ? __fadd_rn(left[e], mid) : mid;
+        if (e > 0) acc = __fadd_rn(acc, right);
+        out[c][e] = acc;
+      }
+    }
+  }
+  __syncthreads();  // every window is read: the keys go over the raw scores
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int ch = t + c * 1024;
+    if (ch < nchunk) {
+#pragma unroll
+      for (int e = 0; e < PT; ++e) {
+        const int i = PT * ch + e;
+        if (i < P) {
+          const uint32_t kk = order_key(out[c][e]);
+          skeys[i] = kk;
+          lo = min(lo, kk);
+          hi = max(hi, kk);
+          if (pooled_opt) pooled_opt[size_t(u) * P + i] = out[c][e];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, P, n_keep - W, emit, sm, true, lo, hi,
+                      skeys + P, cand_cap);
+  for (int r = t; r < W; r += 1024) ku[n_keep - W + r] = P + r;
+}
+
 // Top-k over more keys than LDS holds, in two launches.  select_chunk: one
 // workgroup per (chunk of C keys, unit) takes the chunk's own top-min(k, len)
 // and writes their positions, ascending, over the chunk's (spent) score
@@ -935,20 +1046,10 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (P > 0) {
-    const int h = (pool_kernel - 1) / 2;
-    if (h == 31)
-      RK_LAUNCH("pool_sum", pool_sum_reg_kernel<31>, dim3((P + 2047) / 2048, units), dim3(256), 0,
-                s, scores, P, pooled);
-    else
-      RK_LAUNCH("pool_sum", pool_sum_kernel, dim3((P + 255) / 256, units), dim3(256),
-                size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  const int staged = size_t(P) * 4 <= kSelectKeysLds ? 1 : 0;
   static bool attr_set = false;
   if (!attr_set) {
     for (const void* f : {reinterpret_cast<const void*>(&select_kernel),
+                          reinterpret_cast<const void*>(&select_pool_kernel<31>),
                           reinterpret_cast<const void*>(&select_chunk_kernel),
                           reinterpret_cast<const void*>(&select_final_kernel)}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -957,27 +1058,52 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
     }
     attr_set = true;
   }
-  // more keys than LDS holds: chunked select when the candidates of all
-  // chunks (positions and keys) fit in LDS, else the global-key path
-  const int C = int(kSelectKeysLds / 4) / 64 * 64;
-  const int k_sel = int(n_keep) - W;
-  const int n_chunks = (P + C - 1) / C;
-  int n_cand = 0;
-  for (int c = 0; c < n_chunks; ++c) n_cand += std::min(std::min(k_sel, C), P - c * C);
-  if (!staged && size_t(n_cand) * 8 <= kSelectKeysLds) {
-    int32_t* cand = reinterpret_cast<int32_t*>(scores);  // the scores are spent once pooled
-    RK_LAUNCH("select_chunk", select_chunk_kernel, dim3(n_chunks, units), dim3(1024),
-              size_t(C) * 4, s, pooled, P, C, k_sel, cand);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    RK_LAUNCH("select_tokens", select_final_kernel, dim3(units), dim3(1024), size_t(n_cand) * 8,
-              s, pooled, S, W, C, int(n_keep), cand, kept);
+  const int h = (pool_kernel - 1) / 2;
+  // kernel 63 with the haloed scores in LDS and enough units to spread the
+  // pooling over the CUs: pooling inside the select launch (at batch 32,
+  // 49 -> 41 us for both; at batch 1 the 8 workgroups' LDS reads of the
+  // pooling windows cost more than the separate launch, 30 -> 36 us)
+  constexpr int kPoolH = 31;
+  const size_t pool_words = size_t((P + 7) / 8 * 8 + 2 * kPoolH + 8);
+  if (P > 0 && h == kPoolH && pool_words * 4 <= kSelectKeysLds && units >= kComputeUnits / 4) {
+    const size_t words = std::max(pool_words, size_t(P) + 4096);
+    const int cand_cap = int(std::min<size_t>(4096, kSelectKeysLds / 4 - size_t(P)));
+    RK_LAUNCH("select_tokens", select_pool_kernel<kPoolH>, dim3(units), dim3(1024),
+              std::min(words, kSelectKeysLds / 4) * 4, s, scores, S, W, int(n_keep), cand_cap,
+              pooled_opt, kept);
   } else {
-    // staged keys, then up to 4096 words of radix candidates in what LDS is left
-    const int cand_cap =
-        staged ? int(std::min<size_t>(4096, (kSelectKeysLds - size_t(P) * 4) / 4)) : 0;
-    RK_LAUNCH("select_tokens", select_kernel, dim3(units), dim3(1024),
-              staged ? size_t(P + cand_cap) * 4 : size_t(0), s, pooled, S, W, int(n_keep), staged,
-              cand_cap, kept);
+    if (P > 0) {
+      if (h == 31)
+        RK_LAUNCH("pool_sum", pool_sum_reg_kernel<31>, dim3((P + 2047) / 2048, units), dim3(256),
+                  0, s, scores, P, pooled);
+      else
+        RK_LAUNCH("pool_sum", pool_sum_kernel, dim3((P + 255) / 256, units), dim3(256),
+                  size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    const int staged = size_t(P) * 4 <= kSelectKeysLds ? 1 : 0;
+    // more keys than LDS holds: chunked select when the candidates of all
+    // chunks (positions and keys) fit in LDS, else the global-key path
+    const int C = int(kSelectKeysLds / 4) / 64 * 64;
+    const int k_sel = int(n_keep) - W;
+    const int n_chunks = (P + C - 1) / C;
+    int n_cand = 0;
+    for (int c = 0; c < n_chunks; ++c) n_cand += std::min(std::min(k_sel, C), P - c * C);
+    if (!staged && size_t(n_cand) * 8 <= kSelectKeysLds) {
+      int32_t* cand = reinterpret_cast<int32_t*>(scores);  // the scores are spent once pooled
+      RK_LAUNCH("select_chunk", select_chunk_kernel, dim3(n_chunks, units), dim3(1024),
+                size_t(C) * 4, s, pooled, P, C, k_sel, cand);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      RK_LAUNCH("select_tokens", select_final_kernel, dim3(units), dim3(1024), size_t(n_cand) * 8,
+                s, pooled, S, W, C, int(n_keep), cand, kept);
+    } else {
+      // staged keys, then up to 4096 words of radix candidates in what LDS is left
+      const int cand_cap =
+          staged ? int(std::min<size_t>(4096, (kSelectKeysLds - size_t(P) * 4) / 4)) : 0;
+      RK_LAUNCH("select_tokens", select_kernel, dim3(units), dim3(1024),
+                staged ? size_t(P + cand_cap) * 4 : size_t(0), s, pooled, S, W, int(n_keep), staged,
+                cand_cap, kept);
+    }
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (k_out && kmax) {
