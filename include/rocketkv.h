@@ -108,10 +108,11 @@ size_t rk_snapkv_workspace_bytes(const rk_shape* shape, int64_t seq_len, int32_t
  * row r sits at position S-W+r) over the S prompt keys with scale 1/sqrt(d);
  * each row is softmax-normalised; score[j] = sum over the G heads and W rows
  * of the probability of key j, for the prefix j < S-W; pooled[j] = the sum of
- * score over [j-h, j+h] (h = (pool_kernel-1)/2, zero outside the prefix,
- * added left to right); the n_keep - W prefix positions with the largest
- * pooled score (ties to the lower position) are kept, ascending, followed by
- * the W window positions S-W .. S-1.
+ * score over [j-h, j+h] (h = (pool_kernel-1)/2, zero outside the prefix; for
+ * kernel 63 the terms are grouped so neighbouring outputs share their common
+ * middle, which moves a sum by a few ulp at most); the n_keep - W prefix
+ * positions with the largest pooled score (ties to the lower position) are
+ * kept, ascending, followed by the W window positions S-W .. S-1.
  *
  *   q_win    [B, Hq, W, d]          window queries (rows in position order)
  *   k, v     [B, Hkv, kv_cap, d]    prompt keys/values, first seq_len valid;

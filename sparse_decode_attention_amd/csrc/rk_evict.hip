@@ -8,15 +8,17 @@
 // softmax(Q K^T / sqrt(D)) summed over the window).
 //
 // Launch sequence per call (one stream, no host synchronisation):
-//   ws_pass1   logits of the group's G*W window rows against a 64-key tile,
-//              causal on the window keys; per row, the tile's max and sum of
-//              exp2 (log2 domain) -> partials
-//   ws_stats   merge the tile partials of each row in tile order -> (m, 1/Z)
+//   ws_pass1   logits of the group's G*W window rows against K tiles (bf16 on
+//              the matrix cores), causal on the window keys; per row, each
+//              workgroup's max and sum of exp2 (log2 domain) -> partials
+//   ws_stats   merge the partials of each row in tile order -> (m, 1/Z)
 //   ws_pass2   recompute the prefix logits, p = exp2(x - m) / Z, sum over the
 //              G*W rows in a fixed order -> score[j], j < S-W
-//   pool       windowed sum of width pool_kernel, left to right -> pooled
+//   pool       windowed sum of width pool_kernel -> pooled (for kernel 63 with
+//              many units, done inside the select launch instead)
 //   select     workgroup radix top-k (ties to the lower position) + window
-//   gather     compaction of K and V rows (skipped for the RocketKV-MT form)
+//   gather     compaction of K and V rows, with the compact cache's Kmax/Kmin
+//              when asked for (skipped for the RocketKV-MT form)
 #include <math.h>
 
 #include <algorithm>
