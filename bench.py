@@ -181,8 +181,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (the hot path shards over (batch, KV head) "
-              f"units with no exchange; multi-GPU runs are not part of it); got --gpus {args.gpus}",
+        print(f"bench.py: measures one GPU only (the hot path shards over (batch, KV head) units "
+              f"with no exchange; multi-GPU runs are not measured here); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
 

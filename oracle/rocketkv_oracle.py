@@ -27,8 +27,7 @@ explicit order (stated per function).  The attention output, which decides
 nothing, is computed in float64.  bf16 inputs are up-cast exactly by the
 caller (every bf16 value is an exact float32).
 
-Readings where the pages are silent or ambiguous (each is listed again in
-DESIGN.md):
+Readings where the pages are silent or ambiguous:
   R1  r is clamped to [0.2, 0.8] (the prose bound), c >= 1 is required.
   R2  the stage-1 keep count is ceil(S / c^r), at least the window W and at
       most S.
