@@ -122,6 +122,25 @@ def test_compaction_aux_many_pages(rk, n_keep, out_cap):
                       aux_block=w.block, units_to_check=[(0, 0), (13, 5), (31, 7)])
 
 
+def test_keep_all_and_window_only_many_units(rk):
+    """64 units with kernel 63 (pooling inside the select launch): keep all,
+    window only, and one prefix key."""
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=8, seq=600, n_plant=4)
+    k, v, _ = WL.layer_kv(w, 0, device=DEV)
+    qw = WL.window_queries(w, 0, device=DEV)
+    units = [(0, 0), (3, 5), (7, 7)]
+    say("64 units, keep all")
+    kept, kc, vc, _, _ = U.evict_and_check(rk, qw, k, v, 600, w.window, w.pool, 600, units_to_check=units)
+    assert (kept.cpu().numpy() == np.arange(600)).all()
+    assert torch.equal(kc, k) and torch.equal(vc, v)
+    say("64 units, window only")
+    kept, _, _, _, _ = U.evict_and_check(rk, qw, k, v, 600, w.window, w.pool, w.window, units_to_check=units)
+    assert (kept.cpu().numpy() == np.arange(600 - w.window, 600)).all()
+    say("64 units, one prefix key")
+    U.evict_and_check(rk, qw, k, v, 600, w.window, w.pool, w.window + 1, units_to_check=units)
+
+
 def test_keep_all_and_window_only(rk):
     base = WL.WORKLOADS["tiny-gqa-s2048-d64-fp32"]
     w = WL.scaled(base, seq=600, batch=2)
