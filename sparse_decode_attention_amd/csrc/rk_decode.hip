@@ -769,11 +769,18 @@ __global__ __launch_bounds__(256) void hsa_combine_kernel(const float* __restric
   const float mm = wave_max(ml.x);
   const float a = lane < n_split ? fast_exp2(ml.x - mm) : 0.f;
   const float ll = wave_sum(ml.y * a);
+  // every split's weight first (the lane permutes issue together), then the sums
+  float wv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = cls + i * CLASSES;
+    wv[i] = __shfl(a, s < kWave ? s : 0);
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int s = cls + i * CLASSES;
-    const float w = __shfl(a, s < kWave ? s : 0);
+    const float w = wv[i];
     if (s < n_split) {
       acc.x += ov[i].x * w;
       acc.y += ov[i].y * w;
