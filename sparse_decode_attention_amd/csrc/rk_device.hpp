@@ -739,16 +739,27 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Wave-wide reductions (all 64 lanes take part).
+// Wave-wide reductions (all 64 lanes take part, every lane gets the result):
+// within each 16-lane row by DPP (the ALU's own lane moves), then the four
+// row results read as scalars, in row order; no LDS permutes in the chain.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false)));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
-  return x;
+  x = group_sum<16>(x);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (a + b) + (c + d);
 }
 
 }  // namespace rk
