@@ -318,7 +318,7 @@ __device__ __forceinline__ void wave_topk_emit(const KeyFn& key, int n, uint32_t
     const uint32_t kk = i < n ? key(i) : 0u;
     const bool eq = i < n && kk == T;
     const unsigned long long em = ballot(eq);
-    const bool sel = (i < n && kk > T) || (eq && eq_seen + __popcll(em & below) < need_eq);
+    const bool sel = (i < n && kk > T) || (eq && eq_seen + int(__popcll(em & below)) < need_eq);
     const unsigned long long sm = ballot(sel);
     if (sel) emit(base + __popcll(sm & below), i);
     base += __popcll(sm);
@@ -336,7 +336,7 @@ constexpr int kWaveRankMax = 16;
 // gt < need <= ge holds T, the need-th largest of the range.  Returns T, the
 // keys still needed at T (need - gt) and how many keys equal T (ge - gt).
 template <int R>
-__device__ __forceinline__ uint3 wave_rank_range(const uint32_t (&kz)[R], int n, uint32_t lo,
+__device__ __forceinline__ uint3 wave_rank_range(const uint32_t (&kz)[R], int /*n*/, uint32_t lo,
                                                  uint32_t hi, int need, uint32_t* slots) {
   const int lane = lane_id();
   const unsigned long long below = (1ull << lane) - 1ull;
@@ -501,7 +501,7 @@ __device__ __forceinline__ void wave_emit_cut(const uint32_t (&kz)[R], int n, co
     const bool eq = i < n && kz[r] == cut.T;
     const unsigned long long em = ballot(eq);
     const bool sel =
-        (i < n && kz[r] > cut.T) || (eq && eq_seen + __popcll(em & below) < cut.need_eq);
+        (i < n && kz[r] > cut.T) || (eq && eq_seen + int(__popcll(em & below)) < cut.need_eq);
     const unsigned long long sm = ballot(sel);
     const int rank = base + __popcll(sm & below);
     if (sel && rank >= rank_lo && rank < rank_hi) emit(rank, i);

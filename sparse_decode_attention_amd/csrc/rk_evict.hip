@@ -689,7 +689,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int TK = 128;              // keys per LDS tile
-constexpr int TCH = TK / 32;         // 32-key chunks per tile
 
 __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p, bool ok) {
   uint4 r = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0u, 0u, 0u, 0u);
