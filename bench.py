@@ -1,23 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the RocketKV hot path on one MI355X.
 
-Default workload: the Llama-3.1-8B-shaped single layer (batch 1, 32K prompt,
-32 query / 8 KV heads, d 128, bf16, c = 16).  A step is one pass of the whole
-hot path over one batch of synthetic input: the adaptive split, SnapKV
-eviction of the layer (window scoring, pooling, top-k, compaction), the
-Kmax/Kmin build and the workload's HSA decode steps.  `--workload` runs one
-layer of another workload instead (the batch-32 stack: append + decode per
-step; the 109K needle; the last RocketKV-MT turn: index-only eviction of the
-resident full cache, aux over the candidates, MT decode).
+Default workload: RocketKV-MT on the MHA shape (batch 8, 32 heads, d 128,
+bf16, c 32), its last turn: a 32K prompt plus 4 x 1024 appended tokens kept
+whole in HBM, index-only SnapKV eviction over all 36864 tokens, Kmax/Kmin
+over the candidates and 64 MT decode steps.  It is the largest workload that
+fits one GPU and one of the two whose decode is HBM-bound.  The other
+HBM-bound workload, one layer of the batch-32 Llama-8B stack (c 64, per-step
+appends), is measured in the same run and reported under "also".
 
-Inputs are resident in HBM before timing; steps rotate over enough prompt
-replicas that eviction does not re-read a cache-resident K.  Each step is
-replayed from two HIP graphs (eviction + aux, then the decode calls) with HIP
-events between them.  Reported: `value` = HSA decode time per decode step
-(us), `ms_per_step` = one whole pass, SnapKV eviction ms/layer, decode HBM
-GB/s, the roofline of the dominant kernel (per-kernel durations from the
-library's HIP-event timing over an eager pass of the same steps) and the CPU
-oracle timed on a bounded sample on the host.
+A step is one pass of the whole hot path over R layers of the workload (each
+layer its own synthetic inputs and caches): per layer the adaptive split,
+SnapKV eviction and the Kmax/Kmin build; then the decode steps, interleaved
+across the layers (step s of layer 0, of layer 1, ..., then step s + 1), as a
+stack of layers runs them.  R is chosen so that the decode traffic of the
+other layers between two visits to one layer exceeds twice the 256 MB MALL:
+every decode step then reads its pages from HBM, as it would between the
+other layers (and weights) of a real model.  Per-layer figures are the step's
+totals divided by R.
+
+Inputs are resident in HBM before timing.  Each step replays two HIP graphs
+(eviction + aux of the R layers; the interleaved decode calls) with HIP
+events between them.  Reported: `value` = HSA decode time per layer per
+decode step (median over steps, us), `ms_per_step` = one whole step (wall
+clock, mean over the K timed steps), SnapKV eviction ms/layer, decode HBM
+GB/s, window-scoring TFLOP/s (the once-counted 2*G*W*S*d over pass 1 +
+statistics + pass 2), the roofline of the dominant kernel (per-kernel
+durations from the library's HIP-event timing over an eager step) and the
+CPU oracle timed on a bounded sample on the host.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -27,10 +37,15 @@ from __future__ import annotations
 import argparse
 import json
 import math
+import os
+import statistics
 import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256e6
+MODEL_LAYERS = 32            # the stacks the large workloads stand for
 
 
 def parse():
@@ -38,8 +53,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama8b-layer-s32k-c16")
-    ap.add_argument("--replicas", type=int, default=0, help="prompt replicas (0: enough to exceed 512 MB)")
+    ap.add_argument("--workload", default="mt-mha-b8-s32k-c32")
+    ap.add_argument("--also", default="llama8b-stack-b32-s32k-c64",
+                    help="a second workload measured in the same run ('' for none)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layers per step (0: enough that other layers' decode traffic exceeds 2x MALL)")
     ap.add_argument("--no-graph", action="store_true", help="issue every call eagerly instead of graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -67,10 +85,14 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-class Path:
-    """Buffers and calls of one layer of a workload (one replica per prompt)."""
+class Layer:
+    """Inputs, caches and outputs of one layer of a workload."""
 
-    def __init__(self, rk, WL, w, dev, replicas):
+
+class Path:
+    """Buffers and calls of R layers of a workload."""
+
+    def __init__(self, rk, WL, w, dev, n_layers):
         import torch
 
         self.rk, self.w = rk, w
@@ -80,14 +102,50 @@ class Path:
         self.n_keep, self.k2 = sp["n_keep"], WL.stage2_pages(w, sp)
         self.steps = w.decode_steps
         B, Hq, Hkv, d = w.batch, w.n_q, w.n_kv, w.d
-        cap_c = self.n_keep + (self.steps if w.appends else 0)
-        self.nblk = -(-cap_c // w.block)
+        G = w.group
+        self.cap_c = self.n_keep + (self.steps if w.appends else 0)
+        self.nblk = -(-self.cap_c // w.block)
         esize = 2 if w.dtype == "bf16" else 4
+        units = B * Hkv
+        nb0 = -(-self.n_keep // w.block)
+        nsel = min(self.k2, self.nblk)
+        # algorithmic bytes per launch (what the method must move), per kernel
+        self.alg = {
+            "hsa_attn": units * nsel * w.block * 2 * d * esize + B * Hq * d * esize,
+            "hsa_attn_mt": units * nsel * w.block * (2 * d * esize + 4) + B * Hq * d * esize,
+            "hsa_score": units * w.k1 * nb0 * esize + B * Hq * d * esize,
+            "hsa_fused": units * w.k1 * nb0 * esize + units * nsel * w.block * 2 * d * esize
+            + B * Hq * d * esize,
+            "hsa_fused_mt": units * w.k1 * nb0 * esize + units * nsel * w.block * (2 * d * esize + 4)
+            + B * Hq * d * esize,
+            "aux_build": units * self.n_keep * d * esize + 2 * units * d * nb0 * esize
+            + (units * self.n_keep * 4 if self.mt else 0),
+            "gather_kv": 2 * 2 * units * self.n_keep * d * esize + 2 * units * d * nb0 * esize,
+            "ws_pass1": units * self.S * d * esize + B * Hq * w.window * d * esize,
+            "ws_pass2": units * (self.S - w.window) * d * esize + B * Hq * w.window * d * esize,
+            "append_kv": units * d * esize * 5,
+        }
+        # the one-launch decode step with its append: the fused bytes plus the append's
+        self.alg["hsa_fused_append"] = self.alg["hsa_fused"] + self.alg["append_kv"]
+        self.flops_ws = 2.0 * units * G * w.window * self.S * d
+        if self.mt:
+            self.dec_bytes = self.alg["hsa_fused_mt"]
+        elif w.appends:
+            self.dec_bytes = self.alg["hsa_fused"] + self.alg["append_kv"]
+        else:
+            self.dec_bytes = self.alg["hsa_fused"]
+        # layers: enough that the other layers' decode traffic between two
+        # visits of one layer's data exceeds twice the MALL
+        aux_bytes = 2 * units * d * nb0 * esize
+        self.R = n_layers or max(2, math.ceil(2 * MALL_BYTES / (self.dec_bytes + aux_bytes)) + 1)
+        self.R = min(self.R, 16)
+        # prompt K/V of the plain workloads is only read by the eviction
+        # (> MALL on its own for the large ones): two copies rotate; MT keeps
+        # each layer's full cache
         kv_bytes = 2 * B * Hkv * self.S * d * esize
-        R = replicas or max(1, min(4, math.ceil(512e6 / kv_bytes)))
-        self.R = R
-        self.reps = []
-        for r in range(R):
+        n_prompts = self.R if self.mt else max(1, min(self.R, math.ceil(2 * MALL_BYTES / kv_bytes)))
+        prompts = []
+        for r in range(n_prompts):
             if self.mt:
                 k = torch.empty(B, Hkv, self.S, d, dtype=w.torch_dtype, device=dev)
                 v = torch.empty_like(k)
@@ -99,80 +157,182 @@ class Path:
                     kt, vt = WL.turn_kv(w, r, t, device=dev)
                     k[:, :, s0:s0 + w.mt_append], v[:, :, s0:s0 + w.mt_append] = kt, vt
                     s0 += w.mt_append
-                qw = WL.window_queries(w, r, device=dev, turn=w.mt_turns - 1)
-                qs = torch.stack([WL.decode_query(w, r, (w.mt_turns - 1) * self.steps + s, device=dev)
-                                  for s in range(self.steps)])
             else:
                 k, v, _ = WL.layer_kv(w, r, device=dev)
-                qw = WL.window_queries(w, r, device=dev)
-                qs = torch.stack([WL.decode_query(w, r, s, device=dev) for s in range(self.steps)])
-            app = None
-            if w.appends:
-                app = [WL.append_kv(w, r, s, device=dev) for s in range(self.steps)]
-            self.reps.append((k, v, qw, qs, app))
-        self.kept = torch.empty(B, Hkv, self.n_keep, dtype=torch.int32, device=dev)
-        self.kc = self.vc = None
-        if not self.mt:
-            self.kc = torch.empty(B, Hkv, cap_c, d, dtype=w.torch_dtype, device=dev)
-            self.vc = torch.empty_like(self.kc)
-        self.kmax = torch.empty(B, Hkv, d, rk.aux_capacity(cap_c, w.block), dtype=w.torch_dtype, device=dev)
-        self.kmin = torch.empty_like(self.kmax)
-        self.out = torch.empty(self.steps, B, Hq, d, dtype=torch.float32, device=dev)
+            prompts.append((k, v))
         shape = rk.shape_of(B, Hq, Hkv, d, w.torch_dtype)
-        self.ws_e = torch.empty(rk.rk_snapkv_workspace_bytes(shape, self.S, w.window), dtype=torch.uint8, device=dev)
-        self.ws_d = torch.empty(rk.rk_hsa_workspace_bytes(shape, cap_c, w.block, w.k1, self.k2),
+        self.ws_e = torch.empty(rk.rk_snapkv_workspace_bytes(shape, self.S, w.window), dtype=torch.uint8,
+                                device=dev)
+        self.ws_d = torch.empty(rk.rk_hsa_workspace_bytes(shape, self.cap_c, w.block, w.k1, self.k2),
                                 dtype=torch.uint8, device=dev)
-        # algorithmic bytes per launch (what the method must move)
-        units = B * Hkv
-        nb0 = -(-self.n_keep // w.block)
-        nsel = min(self.k2, self.nblk)
-        G = w.group
-        self.alg = {
-            "hsa_attn": units * nsel * w.block * 2 * d * esize + B * Hq * d * esize,
-            "hsa_attn_mt": units * nsel * w.block * (2 * d * esize + 4) + B * Hq * d * esize,
-            "hsa_score": units * w.k1 * nb0 * esize + B * Hq * d * esize,
-            "hsa_fused": units * w.k1 * nb0 * esize + units * nsel * w.block * 2 * d * esize
-            + B * Hq * d * esize,
-            "hsa_fused_mt": units * w.k1 * nb0 * esize + units * nsel * w.block * (2 * d * esize + 4)
-            + B * Hq * d * esize,
-            "aux_build": units * self.n_keep * d * esize + 2 * units * d * nb0 * esize,
-            "gather_kv": 2 * 2 * units * self.n_keep * d * esize + 2 * units * d * nb0 * esize,
-            "ws_pass1": units * self.S * d * esize + B * Hq * w.window * d * esize,
-            "ws_pass2": units * (self.S - w.window) * d * esize + B * Hq * w.window * d * esize,
-            "append_kv": units * d * esize * 5,
-        }
-        # the one-launch decode step with its append: the fused bytes plus the append's
-        self.alg["hsa_fused_append"] = self.alg["hsa_fused"] + self.alg["append_kv"]
-        self.flops_ws = 2.0 * units * G * w.window * self.S * d
-        self.dec_bytes = self.alg["hsa_attn_mt" if self.mt else "hsa_attn"] + self.alg["hsa_score"]
+        self.layers = []
+        for r in range(self.R):
+            L = Layer()
+            L.k, L.v = prompts[r % n_prompts]
+            turn = w.mt_turns - 1 if self.mt else -1
+            L.qw = WL.window_queries(w, r, device=dev, turn=turn)
+            s_off = (w.mt_turns - 1) * self.steps if self.mt else 0
+            L.qs = torch.stack([WL.decode_query(w, r, s_off + s, device=dev) for s in range(self.steps)])
+            L.app = [WL.append_kv(w, r, s, device=dev) for s in range(self.steps)] if w.appends else None
+            L.kept = torch.empty(B, Hkv, self.n_keep, dtype=torch.int32, device=dev)
+            L.kc = L.vc = None
+            if not self.mt:
+                L.kc = torch.empty(B, Hkv, self.cap_c, d, dtype=w.torch_dtype, device=dev)
+                L.vc = torch.empty_like(L.kc)
+            L.kmax = torch.empty(B, Hkv, d, rk.aux_capacity(self.cap_c, w.block), dtype=w.torch_dtype, device=dev)
+            L.kmin = torch.empty_like(L.kmax)
+            L.out = torch.empty(self.steps, B, Hq, d, dtype=torch.float32, device=dev)
+            self.layers.append(L)
 
-    def evict_part(self, r):
+    def evict_part(self):
         rk, w = self.rk, self.w
-        k, v, qw = self.reps[r][:3]
-        if self.mt:
-            rk.rk_snapkv_evict(qw, k, v, self.S, w.window, w.pool, self.n_keep, self.kept, None, None, None,
-                               ws=self.ws_e)
-            rk.rk_hsa_build_aux(k, self.n_keep, 0, w.block, self.kmax, self.kmin, n_q_heads=w.n_q, idx=self.kept)
-        else:
-            # the compaction builds Kmax/Kmin of the compact cache on the way
-            rk.rk_snapkv_evict(qw, k, v, self.S, w.window, w.pool, self.n_keep, self.kept, self.kc, self.vc,
-                               None, ws=self.ws_e, kmax=self.kmax, kmin=self.kmin, block=w.block)
-
-    def decode_part(self, r):
-        rk, w = self.rk, self.w
-        k, v, _, qs, app = self.reps[r]
-        for s in range(self.steps):
+        for L in self.layers:
             if self.mt:
-                rk.rk_hsa_decode_mt(qs[s], k, v, self.kept, self.n_keep, self.kmax, self.kmin, w.block, w.k1,
-                                    self.k2, self.out[s], ws=self.ws_d)
+                rk.rk_snapkv_evict(L.qw, L.k, L.v, self.S, w.window, w.pool, self.n_keep, L.kept, None, None,
+                                   None, ws=self.ws_e)
+                rk.rk_hsa_build_aux(L.k, self.n_keep, 0, w.block, L.kmax, L.kmin, n_q_heads=w.n_q, idx=L.kept)
             else:
-                if app is not None:   # the step appends its token, then decodes (one call)
-                    rk.rk_hsa_append_decode(qs[s], app[s][0], app[s][1], self.kc, self.vc, self.n_keep + s,
-                                            self.kmax, self.kmin, w.block, w.k1, self.k2, self.out[s],
-                                            ws=self.ws_d)
+                # the compaction builds Kmax/Kmin of the compact cache on the way
+                rk.rk_snapkv_evict(L.qw, L.k, L.v, self.S, w.window, w.pool, self.n_keep, L.kept, L.kc, L.vc,
+                                   None, ws=self.ws_e, kmax=L.kmax, kmin=L.kmin, block=w.block)
+
+    def decode_part(self):
+        rk, w = self.rk, self.w
+        for s in range(self.steps):
+            for L in self.layers:
+                if self.mt:
+                    rk.rk_hsa_decode_mt(L.qs[s], L.k, L.v, L.kept, self.n_keep, L.kmax, L.kmin, w.block, w.k1,
+                                        self.k2, L.out[s], ws=self.ws_d)
+                elif L.app is not None:   # the step appends its token, then decodes (one call)
+                    rk.rk_hsa_append_decode(L.qs[s], L.app[s][0], L.app[s][1], L.kc, L.vc, self.n_keep + s,
+                                            L.kmax, L.kmin, w.block, w.k1, self.k2, L.out[s], ws=self.ws_d)
                 else:
-                    rk.rk_hsa_decode(qs[s], self.kc, self.vc, self.kmax, self.kmin, self.n_keep, w.block, w.k1,
-                                     self.k2, self.out[s], ws=self.ws_d)
+                    rk.rk_hsa_decode(L.qs[s], L.kc, L.vc, L.kmax, L.kmin, self.n_keep, w.block, w.k1,
+                                     self.k2, L.out[s], ws=self.ws_d)
+
+
+def measure(rk, WL, name, args, dev, with_cpu):
+    """Time `args.steps` steps of R layers of workload `name`; returns the
+    figures of the JSON line (and the per-kernel table)."""
+    import torch
+
+    w = WL.WORKLOADS[name]
+    p = Path(rk, WL, w, dev, args.layers)
+    R = p.R
+    log(f"workload {w.name}: {R} layers per step, S={p.S} n_keep={p.n_keep} k1={w.k1} k2={p.k2} "
+        f"decode steps={p.steps}")
+    torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup)):           # eager warm-up (also before capture)
+        p.evict_part()
+        p.decode_part()
+    torch.cuda.synchronize()
+
+    use_graph = not args.no_graph
+    if use_graph:
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            ge, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(ge, stream=stream):
+                p.evict_part()
+            with torch.cuda.graph(gd, stream=stream):
+                p.decode_part()
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+
+    def run_step(ev):
+        ev[0].record()
+        ge.replay() if use_graph else p.evict_part()
+        ev[1].record()
+        gd.replay() if use_graph else p.decode_part()
+        ev[2].record()
+
+    for _ in range(args.warmup):
+        run_step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    torch.cuda.synchronize()
+
+    # ---- timed region ----
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    evict_ms = [e[0].elapsed_time(e[1]) / R for e in evs]                       # per layer
+    dec_us = [e[1].elapsed_time(e[2]) * 1e3 / (R * p.steps) for e in evs]      # per layer-step
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    evict_ms_layer = statistics.median(evict_ms)
+    dec_us_step = statistics.median(dec_us)
+    log(f"wall {ms_per_step:.3f} ms/step ({R} layers); evict+aux {evict_ms_layer:.3f} ms/layer; "
+        f"decode {dec_us_step:.2f} us per layer-step (medians)")
+
+    # ---- per-kernel durations: library HIP-event timing over eager steps ----
+    prof_steps = min(args.steps, 3)
+    rk.rk_profile_begin()
+    for _ in range(prof_steps):
+        p.evict_part()
+        p.decode_part()
+    prof = rk.rk_profile_end()
+    torch.cuda.synchronize()
+    # per layer (launches and ms), and the average launch (ms)
+    per_layer = {n: (c / (prof_steps * R), t / (prof_steps * R), t / c) for n, (c, t) in prof.items()}
+    for n, (cpl, tpl, avg) in per_layer.items():
+        log(f"kernel {n:16s} {cpl:6.1f} launches/layer {tpl:8.4f} ms/layer avg {avg * 1e3:8.2f} us")
+
+    dominant = max(per_layer, key=lambda n: per_layer[n][1])
+    roof = None
+    if dominant in p.alg:
+        avg_ms = per_layer[dominant][2]
+        achieved = p.alg[dominant] / (avg_ms * 1e-3) / 1e9
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dominant, w.name),
+                "bytes_per_launch": p.alg[dominant], "avg_launch_us": round(avg_ms * 1e3, 3)}
+    attn_name = next((n for n in ("hsa_fused_mt", "hsa_fused_append", "hsa_fused", "hsa_attn_mt", "hsa_attn")
+                      if n in per_layer), "hsa_attn")
+    attn_avg = per_layer.get(attn_name, (0, 0, float("nan")))[2]
+    attn_gbps = p.alg[attn_name] / (attn_avg * 1e-3) / 1e9 if attn_avg == attn_avg else None
+    ws_ms = sum(per_layer.get(n, (0, 0, 0))[1] for n in ("ws_pass1", "ws_stats", "ws_pass2"))
+    ws1 = per_layer.get("ws_pass1", (0, 0, float("nan")))[2]
+    dec_gbps = p.dec_bytes / (dec_us_step * 1e-6) / 1e9
+    ws_tflops = p.flops_ws / (ws_ms * 1e-3) / 1e12 if ws_ms > 0 else None
+
+    res = {
+        "workload": w.name,
+        "layers_per_step": R,
+        "evict_ms_per_layer": round(evict_ms_layer, 4),
+        "decode_us_per_layer_step": round(dec_us_step, 3),
+        "decode_us_per_32_layer_step": round(dec_us_step * MODEL_LAYERS, 1),
+        "evict_ms_per_32_layers": round(evict_ms_layer * MODEL_LAYERS, 2),
+        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median_events": round(statistics.median(step_ms), 4),
+        "hsa_decode_GBps": round(dec_gbps, 1),
+        "hsa_decode_hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "hsa_decode_bytes_per_layer_step": p.dec_bytes,
+        "hsa_attn_kernel": attn_name,
+        "hsa_attn_avg_us": round(attn_avg * 1e3, 3),
+        "hsa_attn_GBps": round(attn_gbps, 1) if attn_gbps else None,
+        "hsa_attn_hbm_frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
+        "window_scoring_us_per_layer": round(ws_ms * 1e3, 2),
+        "window_scoring_TFLOPs": round(ws_tflops, 2) if ws_tflops else None,
+        "window_scoring_bf16_frac": round(ws_tflops / BF16_PEAK_TFLOPS, 4) if ws_tflops else None,
+        "ws_pass1_TFLOPs": round(p.flops_ws / (ws1 * 1e-3) / 1e12, 2) if ws1 == ws1 else None,
+        "kernels_ms_per_layer": {n: round(v[1], 5) for n, v in per_layer.items()},
+        "kernels_avg_us": {n: round(v[2] * 1e3, 3) for n, v in per_layer.items()},
+        "roofline": roof,
+        "config": {"workload": w.name, "layers_timed": R, "batch": w.batch, "seq_len": p.S, "n_q_heads": w.n_q,
+                   "n_kv_heads": w.n_kv, "head_dim": w.d, "kv_dtype": w.dtype, "compression": round(w.c, 3),
+                   "n_keep": p.n_keep, "k1": w.k1, "k2_pages": p.k2, "page": w.block, "decode_steps": p.steps,
+                   "appends": w.appends, "rocketkv_mt": p.mt, "graph_replay": use_graph},
+    }
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, p, args.cpu_seconds)
+    del p
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -193,118 +353,36 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = WL.WORKLOADS[args.workload]
-    p = Path(rk, WL, w, dev, args.replicas)
-    R = p.R
-    log(f"workload {w.name} (one layer): S={p.S} n_keep={p.n_keep} k1={w.k1} k2={p.k2} "
-        f"decode steps={p.steps} replicas={R}")
-    torch.cuda.synchronize()
-
-    for i in range(max(1, args.warmup)):           # eager warm-up (also before capture)
-        p.evict_part(i % R)
-        p.decode_part(i % R)
-    torch.cuda.synchronize()
-
-    use_graph = not args.no_graph
-    graphs = []
-    if use_graph:
-        stream = torch.cuda.Stream()
-        stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(stream):
-            for r in range(R):
-                ge, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-                with torch.cuda.graph(ge, stream=stream):
-                    p.evict_part(r)
-                with torch.cuda.graph(gd, stream=stream):
-                    p.decode_part(r)
-                graphs.append((ge, gd))
-        torch.cuda.current_stream().wait_stream(stream)
-        torch.cuda.synchronize()
-
-    def run_step(i, ev):
-        r = i % R
-        ev[0].record()
-        graphs[r][0].replay() if use_graph else p.evict_part(r)
-        ev[1].record()
-        graphs[r][1].replay() if use_graph else p.decode_part(r)
-        ev[2].record()
-
-    for i in range(args.warmup):
-        run_step(i, [torch.cuda.Event(enable_timing=True) for _ in range(3)])
-    torch.cuda.synchronize()
-
-    # ---- timed region ----
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        run_step(i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    evict_ms_layer = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    dec_us_step = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e3 / p.steps
-    log(f"wall {ms_per_step:.3f} ms/step; evict+aux {evict_ms_layer:.3f} ms/layer; decode {dec_us_step:.2f} us/step")
-
-    # ---- per-kernel durations: library HIP-event timing over an eager pass ----
-    rk.rk_profile_begin()
-    for i in range(args.steps):
-        p.evict_part(i % R)
-        p.decode_part(i % R)
-    prof = rk.rk_profile_end()
-    torch.cuda.synchronize()
-    per_step = {n: (c / args.steps, t / args.steps, t / c) for n, (c, t) in prof.items()}
-    for n, (cps, tps, avg) in per_step.items():
-        log(f"kernel {n:14s} {cps:6.1f} launches/step {tps:8.4f} ms/step avg {avg * 1e3:8.2f} us")
-
-    dominant = max(per_step, key=lambda n: per_step[n][1])
-    avg_ms = per_step[dominant][2]
-    roof = None
-    if dominant in p.alg:
-        achieved = p.alg[dominant] / (avg_ms * 1e-3) / 1e9
-        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(dominant, w.name),
-                "bytes_per_launch": p.alg[dominant], "avg_launch_us": round(avg_ms * 1e3, 3)}
-    attn_name = next((n for n in ("hsa_fused_mt", "hsa_fused_append", "hsa_fused", "hsa_attn_mt", "hsa_attn")
-                      if n in per_step),
-                     "hsa_attn")
-    attn_avg = per_step.get(attn_name, (0, 0, float("nan")))[2]
-    attn_gbps = p.alg[attn_name] / (attn_avg * 1e-3) / 1e9 if attn_avg == attn_avg else None
-    ws1 = per_step.get("ws_pass1", (0, 0, float("nan")))[2]
-    dec_gbps = p.dec_bytes / (dec_us_step * 1e-6) / 1e9
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, p, args.cpu_seconds)
+    main_res = measure(rk, WL, args.workload, args, dev, not args.no_cpu_baseline)
+    also = None
+    if args.also and args.also != args.workload:
+        a = measure(rk, WL, args.also, args, dev, False)
+        also = {k: a[k] for k in ("workload", "layers_per_step", "decode_us_per_layer_step",
+                                  "decode_us_per_32_layer_step", "evict_ms_per_layer", "evict_ms_per_32_layers",
+                                  "hsa_decode_GBps", "hsa_decode_hbm_frac", "hsa_attn_kernel", "hsa_attn_avg_us",
+                                  "hsa_attn_GBps", "hsa_attn_hbm_frac", "window_scoring_us_per_layer",
+                                  "window_scoring_TFLOPs", "window_scoring_bf16_frac", "kernels_avg_us",
+                                  "roofline", "config")}
 
     line = {
         "metric": "HSA decode us/step + HBM GB/s (% peak); SnapKV evict ms/layer",
-        "value": round(dec_us_step, 3),
-        "unit": "us/step",
+        "value": main_res["decode_us_per_layer_step"],
+        "unit": "us/step (one layer)",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "layers_timed": 1, "batch": w.batch, "seq_len": p.S, "n_q_heads": w.n_q,
-                   "n_kv_heads": w.n_kv, "head_dim": w.d, "kv_dtype": w.dtype, "compression": round(w.c, 3),
-                   "n_keep": p.n_keep, "k1": w.k1, "k2_pages": p.k2, "page": w.block, "decode_steps": p.steps,
-                   "appends": w.appends, "rocketkv_mt": p.mt, "replicas": R, "graph_replay": use_graph},
-        "snapkv_evict_ms_per_layer": round(evict_ms_layer, 4),
-        "hsa_decode_GBps": round(dec_gbps, 1),
-        "hsa_decode_hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-        "hsa_attn_avg_us": round(attn_avg * 1e3, 3),
-        "hsa_attn_GBps": round(attn_gbps, 1) if attn_gbps else None,
-        "window_scoring_TFLOPs": round(p.flops_ws / (ws1 * 1e-3) / 1e12, 2) if ws1 == ws1 else None,
-        "kernels_ms_per_step": {n: round(v[1], 5) for n, v in per_step.items()},
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "config": main_res["config"],
     }
+    for k, v in main_res.items():
+        if k not in ("config", "ms_per_step", "workload"):
+            line[k] = v
+    line["also"] = also
     print(json.dumps(line), flush=True)
 
 
@@ -323,7 +401,6 @@ def measured_traffic(kernel, workload):
     the kernel's sources (comments and whitespace aside) have changed since the
     counters were taken."""
     import hashlib
-    import os
 
     # timing-hook names -> kernel function names (the MT variants share the function)
     kernel = {"hsa_attn_mt": "hsa_attn", "hsa_fused_mt": "hsa_fused", "hsa_fused_append": "hsa_fused",
@@ -351,10 +428,12 @@ def cpu_baseline(w, p, budget_s):
 
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
-        threads = 1
-    k, v, qw, qs, _ = p.reps[0]
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    L = p.layers[0]
+    k, v, qw, qs = L.k, L.v, L.qw, L.qs
     G = w.group
     S, W = p.S, w.window
     units_all = [(b, h) for b in range(w.batch) for h in range(w.n_kv)]
@@ -384,10 +463,13 @@ def cpu_baseline(w, p, budget_s):
             O.hsa_unit(qn[done, b, h * G:(h + 1) * G], c[0], c[1], c[2], c[3], p.n_keep, w.block, w.k1, p.k2)
         done += 1
     per_step_us = (time.perf_counter() - t0) * 1e6 / max(done, 1) * (len(units_all) / len(units))
-    return {"value": round(per_step_us, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
-            "sample": f"HSA decode of {len(units)} of {len(units_all)} units for {done} of {p.steps} steps, "
-                      f"scaled to all units (aux built once); stage 1 of one unit {evict_unit_ms:.0f} ms, "
-                      f"x{len(units_all)} units = {evict_unit_ms * len(units_all):.0f} ms/layer (extrapolated)",
+    return {"value": round(per_step_us, 1), "unit": "us/step (one layer)", "cores": cores,
+            "blas_threads": blas_threads, "kind": "oracle",
+            "sample": f"HSA decode of {len(units)} of {len(units_all)} units for {done} of {p.steps} steps "
+                      f"of one layer, scaled to all units (aux built once; for RocketKV-MT over the "
+                      f"compacted candidate rows, which is the same arithmetic); stage 1 of one unit "
+                      f"{evict_unit_ms:.0f} ms, x{len(units_all)} units = "
+                      f"{evict_unit_ms * len(units_all):.0f} ms/layer (extrapolated)",
             "evict_ms_per_layer_extrapolated": round(evict_unit_ms * len(units_all), 1)}
 
 

@@ -1,6 +1,7 @@
 """Build librocketkv.so (hand-written HIP for gfx950) in-tree.
 
     python -m sparse_decode_attention_amd.build      # or build() from Python
+    python -m sparse_decode_attention_amd.build --incremental   # changed sources only
 
 Every .hip file under csrc/ is compiled to an object with hipcc (in parallel)
 and linked into sparse_decode_attention_amd/librocketkv.so.  Packed-FP32
@@ -37,8 +38,18 @@ def _hipcc() -> str:
     return exe
 
 
-def _compile(src: str) -> str:
+def _stale(src: str, obj: str) -> bool:
+    """True when obj is missing or older than src or any header it may include."""
+    if not os.path.exists(obj):
+        return True
+    deps = [src, *glob.glob(os.path.join(CSRC, "*.hpp")), *glob.glob(os.path.join(INCLUDE, "*.h")), __file__]
+    return os.path.getmtime(obj) < max(os.path.getmtime(x) for x in deps)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+    if incremental and not _stale(src, obj):
+        return obj
     cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -46,14 +57,16 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every csrc/*.hip and link librocketkv.so; returns its path."""
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every csrc/*.hip and link librocketkv.so; returns its path.
+    incremental: recompile only sources newer than their objects (or whose
+    headers changed); the default compiles everything."""
     os.makedirs(OBJ_DIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources found")
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda x: _compile(x, incremental), srcs))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,7 +80,7 @@ def build(verbose: bool = True) -> str:
 
 if __name__ == "__main__":
     try:
-        build()
+        build(incremental="--incremental" in sys.argv[1:])
     except RuntimeError as e:
         print(e, file=sys.stderr)
         sys.exit(1)

@@ -23,6 +23,8 @@
 // HBM-bound: bytes per unit = q + k1*nblk aux elements + 2*d*|T| K/V elements.
 #include <math.h>
 
+#include <type_traits>
+
 #include "rk_device.hpp"
 #include "rk_internal.hpp"
 
@@ -558,11 +560,16 @@ struct AppendPtrs {
 // Dynamic LDS: page keys [roundup4(nblk)] | chosen pages [roundup4(nsel)] |
 // a region holding first the staged chunk [npc][k1p], then the waves' merge
 // state (m, l per wave and head, o per wave, head and channel).
+// The cache and aux inputs are not restrict-qualified in the append form,
+// which writes them through the AppendPtrs (same buffers) in the same launch.
+template <typename T, bool APP>
+using CacheIn = std::conditional_t<APP, const T*, const T* __restrict__>;
+
 template <typename T, int D, int G, bool MT, bool APP = false>
 __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
-    const int32_t* __restrict__ cand, int64_t cand_stride, const T* __restrict__ kmax,
-    const T* __restrict__ kmin, int64_t nblk_cap, int nblk, int k1, int nsel, int npc,
+    const T* __restrict__ q, CacheIn<T, APP> k, CacheIn<T, APP> v, int64_t kv_cap,
+    const int32_t* __restrict__ cand, int64_t cand_stride, CacheIn<T, APP> kmax,
+    CacheIn<T, APP> kmin, int64_t nblk_cap, int nblk, int k1, int nsel, int npc,
     int n_tokens, int block, float scale_log2, float* __restrict__ out,
     int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt,
     AppendPtrs<T> app) {

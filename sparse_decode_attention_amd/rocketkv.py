@@ -100,10 +100,17 @@ def _need_contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
-def _ws(nbytes: int, like: torch.Tensor, ws):
+def _ws(nbytes: int, like: torch.Tensor, ws, stream=None):
+    """The caller's workspace, or a new one.  A new one is allocated on the
+    current stream; when the call runs on another stream it is recorded there
+    too, so the caching allocator does not hand its memory out again while
+    that stream may still use it."""
     if ws is not None:
         return ws
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+    if stream is not None and stream != torch.cuda.current_stream(like.device):
+        ws.record_stream(stream)
+    return ws
 
 
 # --------------------------------------------------------------------------
@@ -128,7 +135,7 @@ def rk_snapkv_evict(q_win, k, v, seq_len, window, pool_kernel, n_keep, kept_idx,
     B, Hq, W, d = q_win.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     nbytes = rk_snapkv_workspace_bytes(shape, seq_len, window)
-    ws = _ws(nbytes, k, ws)
+    ws = _ws(nbytes, k, ws, stream)
     out_cap = k_out.shape[2] if k_out is not None else 0
     nblk_cap = kmax.shape[3] if kmax is not None else 0
     _check(_lib.rk_snapkv_evict(ctypes.byref(shape), _ptr(q_win), _ptr(k), _ptr(v), k.shape[2],
@@ -180,7 +187,7 @@ def rk_hsa_decode(q, k, v, kmax, kmin, n_tokens, block, k1, k2, out, sel_blocks=
     _need_contig(q, k, v, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
-    ws = _ws(rk_hsa_workspace_bytes(shape, n_tokens, block, k1, k2), k, ws)
+    ws = _ws(rk_hsa_workspace_bytes(shape, n_tokens, block, k1, k2), k, ws, stream)
     _check(_lib.rk_hsa_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), k.shape[2],
                               _ptr(kmax), _ptr(kmin), kmax.shape[3], n_tokens, block, k1, k2,
                               _ptr(out), _ptr(sel_blocks), _ptr(sel_channels), _ptr(block_scores),
@@ -195,7 +202,7 @@ def rk_hsa_append_decode(q, k_new, v_new, k, v, pos, kmax, kmin, block, k1, k2, 
     _need_contig(q, k_new, v_new, k, v, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
-    ws = _ws(rk_hsa_workspace_bytes(shape, pos + 1, block, k1, k2), k, ws)
+    ws = _ws(rk_hsa_workspace_bytes(shape, pos + 1, block, k1, k2), k, ws, stream)
     _check(_lib.rk_hsa_append_decode(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new),
                                      _ptr(k), _ptr(v), k.shape[2], pos, _ptr(kmax), _ptr(kmin),
                                      kmax.shape[3], block, k1, k2, _ptr(out), _ptr(sel_blocks),
@@ -210,7 +217,7 @@ def rk_hsa_decode_mt(q, k, v, cand_idx, n_cand, kmax, kmin, block, k1, k2, out, 
     _need_contig(q, k, v, cand_idx, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
-    ws = _ws(rk_hsa_workspace_bytes(shape, n_cand, block, k1, k2), k, ws)
+    ws = _ws(rk_hsa_workspace_bytes(shape, n_cand, block, k1, k2), k, ws, stream)
     _check(_lib.rk_hsa_decode_mt(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), k.shape[2],
                                  _ptr(cand_idx), cand_idx.shape[2], n_cand, _ptr(kmax), _ptr(kmin),
                                  kmax.shape[3], block, k1, k2, _ptr(out), _ptr(sel_blocks),

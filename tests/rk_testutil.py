@@ -195,3 +195,42 @@ def check_aux_units(kmax, kmin, kc, n_tokens, block, units, idx=None):
         wmax, wmin = O.build_aux(rows.cpu().float().numpy(), n_tokens, block)
         assert np.array_equal(np32(kmax[b, h, :, :nblk]), wmax), (b, h)
         assert np.array_equal(np32(kmin[b, h, :, :nblk]), wmin), (b, h)
+
+
+def append_decode_and_check(rk, q, ka, va, kc, vc, kmax, kmin, pos, block, k1, k2, units_to_check,
+                            ws=None):
+    """One rk_hsa_append_decode step (append row `pos`, then decode over pos + 1
+    tokens), checked on the given units: the appended rows, Kmax/Kmin against a
+    rebuild from the cache rows (bit-exact), the channel set and page scores
+    against the oracle on the post-append state (bit-exact), the page choice
+    (exact on those scores) and the output against the oracle's attention over
+    the chosen pages.  Returns (out, sel, ws)."""
+    B, Hq, d = q.shape
+    Hkv = kc.shape[1]
+    G = Hq // Hkv
+    dev = q.device
+    n = pos + 1
+    nblk = -(-n // block)
+    nsel = min(k2, nblk)
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    sel = torch.empty(B, Hkv, nsel, dtype=torch.int32, device=dev)
+    chan = torch.empty(B, Hkv, k1, dtype=torch.int32, device=dev)
+    s1 = torch.empty(B, Hkv, nblk, dtype=torch.float32, device=dev)
+    ws = rk.rk_hsa_append_decode(q, ka, va, kc, vc, pos, kmax, kmin, block, k1, k2, out, sel, chan, s1,
+                                 ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[:, :, pos], ka) and torch.equal(vc[:, :, pos], va)
+    check_aux_units(kmax, kmin, kc, n, block, units_to_check)
+    for b, h in units_to_check:
+        qg = np32(q[b, h * G:(h + 1) * G])
+        i1, qbar = O.channel_select(qg, k1)
+        assert np.array_equal(chan[b, h].cpu().numpy(), i1), (b, h)
+        ws1 = O.block_scores(qbar, i1, np32(kmax[b, h, :, :nblk]), np32(kmin[b, h, :, :nblk]))
+        assert np.array_equal(np32(s1[b, h]), ws1), (b, h)
+        gsel = sel[b, h].cpu().numpy()
+        assert np.array_equal(gsel, O.block_select(ws1, k2)), (b, h)
+        toks = O.selected_tokens(gsel, n, block)
+        ridx = torch.as_tensor(toks, dtype=torch.long, device=dev)
+        want = O.attention(qg, np32(kc[b, h, ridx]), np32(vc[b, h, ridx]))
+        check_output(np32(out[b, h * G:(h + 1) * G]), want)
+    return out, sel, ws

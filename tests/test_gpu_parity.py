@@ -99,6 +99,11 @@ def test_short_and_odd_pages(rk, block):
     ("f32", 128, 1, 513, 8, 3),
     ("f32", 64, 8, 300, 4, 1),
     ("bf16", 128, 8, 2100, 32, 63),
+    # pool 1: the pooled output is the per-key window score itself, so the
+    # matrix-core scorer is compared with the oracle key by key (G*W = 128, 32, 32)
+    ("bf16", 128, 4, 1000, 32, 1),
+    ("bf16", 128, 1, 1000, 32, 1),
+    ("bf16", 64, 2, 777, 16, 1),
 ])
 def test_shapes_and_ragged_tails(rk, dtype, d, G, S, W, pool):
     say("shape", dtype, d, G, S, W, pool)
@@ -341,8 +346,12 @@ def test_append_equals_rebuild(rk, dtype, d):
     ("bf16", 128, 4, 20, 8, 992, 16, True),    # new token opens a page that gets chosen
     ("bf16", 128, 4, 20, 8, 1001, 64, True),   # mid-page, its page chosen
     ("f32", 64, 2, 40, 4, 500, 8, True),
-    ("bf16", 128, 4, 1, 8, 997, 16, True),     # 8 units: the split path appends first
-    ("bf16", 128, 4, 1, 8, 992, 16, False),
+    # 8 units choosing more pages than the fused kernel's 16 waves: the split
+    # path, which appends with a launch of its own first
+    ("bf16", 128, 4, 1, 8, 997, 32, True),
+    ("bf16", 128, 4, 1, 8, 992, 32, False),
+    ("bf16", 128, 8, 1, 4, 1001, 32, True),    # group of 8 (always the split path)
+    ("f32", 64, 2, 2, 4, 500, 24, True),
 ])
 def test_append_decode_equals_append_then_decode(rk, dtype, d, G, B, Hkv, n0, k2, big):
     """rk_hsa_append_decode leaves the cache and Kmax/Kmin exactly as rk_append_kv
@@ -397,11 +406,14 @@ def test_append_decode_equals_append_then_decode(rk, dtype, d, G, B, Hkv, n0, k2
         want = O.attention(U.np32(q[bb, h * G:(h + 1) * G]), U.np32(b[0][bb, h, ridx]),
                            U.np32(b[1][bb, h, ridx]))
         U.check_output(U.np32(b[4][bb, h * G:(h + 1) * G]), want)
+    rk.rk_profile_begin()
+    rk.rk_hsa_append_decode(q, ka, va, kc, vc, n0, kmax, kmin, block, k1, k2,
+                            torch.empty(B, Hkv * G, d, device=DEV))
+    launched = set(rk.rk_profile_end())
     if B * Hkv >= 160:
-        rk.rk_profile_begin()
-        rk.rk_hsa_append_decode(q, ka, va, kc, vc, n0, kmax, kmin, block, k1, k2,
-                                torch.empty(B, Hkv * G, d, device=DEV))
-        assert set(rk.rk_profile_end()) == {"hsa_fused_append"}
+        assert launched == {"hsa_fused_append"}
+    else:
+        assert launched == {"append_kv", "hsa_score", "hsa_attn", "hsa_combine"}, launched
 
 
 def _decode_only(rk, w, n, k1, k2, units_to_check=None, cand_total=None, steps=2):

@@ -363,3 +363,49 @@ def test_mt_ignores_non_candidates():
     c = O.hsa_decode_mt_unit(q, kf, vf, cand, B, 8, 10 ** 6)
     want = softmax(q.astype(np.float64) @ kf[cand].T.astype(np.float64) / math.sqrt(d), axis=1) @ vf[cand]
     np.testing.assert_allclose(c["out"], want, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- attention (closed forms)
+def test_attention_zero_query_is_mean_of_values():
+    """[RKV] HSA step 3 / Algorithm 1, y = attn(q, K[i2], V[i2]): with q = 0
+    every logit is 0, so each weight is 1/n and the output is the plain mean
+    of the value rows (worked by hand, no softmax call)."""
+    rng = np.random.default_rng(21)
+    for n, d, G in [(1, 8, 1), (5, 16, 2), (37, 32, 4)]:
+        k = rng.standard_normal((n, d))
+        v = rng.standard_normal((n, d))
+        out = O.attention(np.zeros((G, d)), k, v)
+        want = v.sum(axis=0) / n
+        for g in range(G):
+            np.testing.assert_allclose(out[g], want, rtol=0, atol=1e-14)
+
+
+def test_attention_two_keys_log3_apart_weigh_three_to_one():
+    """Two keys whose scaled logits differ by ln 3 get weights exactly 3/4 and
+    1/4: e^(ln 3) / (e^(ln 3) + 1) = 3/4.  d = 4, so the 1/sqrt(d) scale is
+    1/2 and q carries 2 ln 3 on channel 0; a transposed operand, a missing or
+    doubled scale, or a swapped K/V each move the result."""
+    d = 4
+    q = np.array([[2.0 * math.log(3.0), 0.0, 0.0, 0.0]])
+    k = np.array([[1.0, 0.0, 0.0, 0.0], [0.0, 1.0, 0.0, 0.0]])   # logits ln 3 and 0
+    v = np.array([[4.0, 0.0, -8.0, 1.0], [0.0, 8.0, 4.0, 1.0]])
+    out = O.attention(q, k, v)
+    np.testing.assert_allclose(out[0], [3.0, 2.0, -5.0, 1.0], rtol=0, atol=1e-13)
+    # a second head with the logits swapped (ln 3 on the second key) takes the mirror weights
+    q2 = np.array([[2.0 * math.log(3.0), 0.0, 0.0, 0.0], [0.0, 2.0 * math.log(3.0), 0.0, 0.0]])
+    out2 = O.attention(q2, k, v)
+    np.testing.assert_allclose(out2[1], [1.0, 6.0, 1.0, 1.0], rtol=0, atol=1e-13)
+    # a shift common to every logit changes nothing (softmax is shift invariant):
+    # a third key with logit ln 3 as well splits the weight 3/7, 1/7, 3/7
+    k3 = np.vstack([k, [[1.0, 0.0, 0.0, 0.0]]])
+    v3 = np.vstack([v, [[0.0, 0.0, 0.0, 8.0]]])
+    out3 = O.attention(q, k3, v3)
+    np.testing.assert_allclose(out3[0], [12.0 / 7, 8.0 / 7, -20.0 / 7, 4.0], rtol=0, atol=1e-13)
+
+
+def test_attention_single_key_returns_its_value():
+    """With one key the softmax weight is 1 whatever the logit (here a large
+    one, which a missing max subtraction would overflow)."""
+    v = np.array([[0.5, -2.0, 3.25]])
+    out = O.attention(np.array([[900.0, 0.0, 0.0]]), np.array([[1.0, 0.0, 0.0]]), v)
+    np.testing.assert_allclose(out[0], v[0], rtol=0, atol=0)
