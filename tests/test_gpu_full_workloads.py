@@ -71,7 +71,10 @@ def test_llama8b_stack_batch32_appends(rk):
             rk.rk_hsa_build_aux(kc, n_keep, 0, w.block, kmax, kmin, n_q_heads=w.n_q)
         U.check_aux_units(kmax, kmin, kc, n_keep, w.block, units)
         swaps = 0
-        ws = None
+        # one workspace for every step, sized for the full capacity (as the benchmark does)
+        shape = rk.shape_of(w.batch, w.n_q, w.n_kv, w.d, kc.dtype)
+        ws = torch.empty(rk.rk_hsa_workspace_bytes(shape, cap, w.block, w.k1, k2), dtype=torch.uint8,
+                         device=DEV)
         for step in range(w.decode_steps):
             n = n_keep + step
             ka, va = WL.append_kv(w, layer, step, device=DEV)

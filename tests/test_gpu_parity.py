@@ -390,8 +390,9 @@ def test_append_decode_equals_append_then_decode(rk, dtype, d, G, B, Hkv, n0, k2
         torch.cuda.synchronize()
         outs.append((kcx, vcx, kxx, knx, out, sel, chan, s1))
     a, b = outs
-    for x, y in zip(a[:4], b[:4]):
-        assert torch.equal(x, y)
+    for x, y in zip(a[:4], b[:4]):   # bitwise: spare aux pages hold whatever torch.empty left (NaN included)
+        assert torch.equal(x.view(torch.int16 if x.element_size() == 2 else torch.int32),
+                           y.view(torch.int16 if y.element_size() == 2 else torch.int32))
     for x, y in zip(a[5:], b[5:]):
         assert torch.equal(x, y)
     assert (a[4] - b[4]).abs().max().item() <= 1e-5
