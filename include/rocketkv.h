@@ -22,7 +22,8 @@
  *   - Ownership: the caller owns every buffer.  The library allocates no
  *     device memory and keeps no pointer after a call returns; scratch space
  *     is the caller's workspace `ws` of at least *_workspace_bytes() bytes
- *     (256-byte aligned).
+ *     (256-byte aligned), except for rk_hsa_decode_noalloc, which uses a
+ *     static device array of the library instead.
  *   - Calls that take a stream enqueue asynchronously on it (NULL = the null
  *     stream).  Outputs are valid after the stream reaches that point; inputs
  *     must stay alive until then.  Calls on one workspace must not overlap.
@@ -251,6 +252,32 @@ rk_status rk_hsa_append_decode(const rk_shape* shape, const void* q, const void*
                                int32_t k2, float* out, int32_t* sel_blocks_opt,
                                int32_t* sel_channels_opt, float* block_scores_opt, void* ws,
                                size_t ws_bytes, rk_stream stream);
+
+/*
+ * rk_hsa_decode_noalloc -- rk_hsa_decode without a caller workspace and
+ * without any allocation.  For callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as rk_hsa_decode (minus
+ * ws / ws_bytes); the scratch space is a static device array of the library
+ * (rk_hsa_decode_noalloc_max_bytes() bytes, 16 MiB, one copy per GPU, held
+ * until the process ends).  A call whose workspace
+ * (rk_hsa_workspace_bytes of the same arguments) exceeds that returns
+ * RK_EWORKSPACE before touching the device.  Every call on one GPU shares
+ * that GPU's scratch: calls that overlap on one GPU (two streams, two host
+ * threads) race and give undefined results; serialise them.  Nothing in the
+ * scratch needs to start at zero (every value a call reads it has written
+ * earlier in the same call).  Calls no hipMalloc, hipFree or other
+ * allocating routine.
+ */
+rk_status rk_hsa_decode_noalloc(const rk_shape* shape, const void* q, const void* k,
+                                const void* v, int64_t kv_cap, const void* kmax, const void* kmin,
+                                int64_t nblk_cap, int64_t n_tokens, int32_t block, int32_t k1,
+                                int32_t k2, float* out, int32_t* sel_blocks_opt,
+                                int32_t* sel_channels_opt, float* block_scores_opt,
+                                rk_stream stream);
+
+/* Size of rk_hsa_decode_noalloc's static scratch in bytes (16 MiB). */
+size_t rk_hsa_decode_noalloc_max_bytes(void);
 
 /*
  * rk_hsa_decode_mt -- RocketKV-MT decode: HSA over a candidate subset of a

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/rocketkv.h"
@@ -103,6 +104,41 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
                             nblk_cap, n_tokens, block, k1, k2, out, sel_opt, chan_opt, s1_opt,
                             ws, static_cast<hipStream_t>(stream), app),
       mt ? "rk_hsa_decode_mt launch" : app ? "rk_hsa_append_decode launch" : "rk_hsa_decode launch");
+}
+
+// ---- static scratch of rk_hsa_decode_noalloc -----------------------------
+// Device memory that the library owns for callers that cannot allocate: the
+// split-K decode's workspace (page keys and partials) lives here instead of a
+// caller workspace.  Each GPU the library runs on holds its own copy until
+// the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is ever handed to kernels.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch`, per device
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with it current).
+rk_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return device_status(err, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(RK_EUNSUPPORTED, "device %d beyond the %d the static scratch tracks", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return device_status(err, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(RK_EDEVICE, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RK_OK;
 }
 
 }  // namespace
@@ -281,6 +317,32 @@ rk_status rk_hsa_append_decode(const rk_shape* shape, const void* q, const void*
                        k1, k2, out, sel_blocks_opt, sel_channels_opt, block_scores_opt, ws,
                        ws_bytes, stream, false, &app);
 }
+
+rk_status rk_hsa_decode_noalloc(const rk_shape* shape, const void* q, const void* k,
+                                const void* v, int64_t kv_cap, const void* kmax, const void* kmin,
+                                int64_t nblk_cap, int64_t n_tokens, int32_t block, int32_t k1,
+                                int32_t k2, float* out, int32_t* sel_blocks_opt,
+                                int32_t* sel_channels_opt, float* block_scores_opt,
+                                rk_stream stream) {
+  // the size check comes first: a call the scratch cannot hold touches no device
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  if (block < 1 || k2 < 1 || n_tokens < 1) return fail(RK_EINVAL, "block, k2 and n_tokens must be >= 1");
+  const size_t need = rk::decode_ws_layout(d, (n_tokens + block - 1) / block, k2).total;
+  if (need > kScratchBytes)
+    return fail(RK_EWORKSPACE,
+                "rk_hsa_decode_noalloc: the call needs %zu bytes of scratch, the static scratch "
+                "holds %zu; use rk_hsa_decode with a workspace",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != RK_OK) return st;
+  return decode_common(shape, q, k, v, kv_cap, nullptr, 0, kmax, kmin, nblk_cap, n_tokens, block,
+                       k1, k2, out, sel_blocks_opt, sel_channels_opt, block_scores_opt, ws,
+                       kScratchBytes, stream, false);
+}
+
+size_t rk_hsa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
 rk_status rk_hsa_decode_mt(const rk_shape* shape, const void* q, const void* k, const void* v,
                            int64_t kv_cap, const int32_t* cand_idx, int64_t cand_stride,

@@ -211,6 +211,30 @@ def rk_hsa_append_decode(q, k_new, v_new, k, v, pos, kmax, kmin, block, k1, k2, 
     return ws
 
 
+_lib.rk_hsa_decode_noalloc.argtypes = [_SP, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32, _i32, _i32,
+                                       _vp, _vp, _vp, _vp, _vp]
+_lib.rk_hsa_decode_noalloc.restype = ctypes.c_int
+_lib.rk_hsa_decode_noalloc_max_bytes.argtypes = []
+_lib.rk_hsa_decode_noalloc_max_bytes.restype = _sz
+
+
+def rk_hsa_decode_noalloc(q, k, v, kmax, kmin, n_tokens, block, k1, k2, out, sel_blocks=None,
+                          sel_channels=None, block_scores=None, stream=None):
+    """rk_hsa_decode with the library's static scratch instead of a workspace:
+    allocates nothing (every tensor, out included, comes from the caller)."""
+    _need_contig(q, k, v, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    B, Hq, d = q.shape
+    shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
+    _check(_lib.rk_hsa_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), k.shape[2],
+                                      _ptr(kmax), _ptr(kmin), kmax.shape[3], n_tokens, block, k1, k2,
+                                      _ptr(out), _ptr(sel_blocks), _ptr(sel_channels), _ptr(block_scores),
+                                      _stream(stream)), "rk_hsa_decode_noalloc")
+
+
+def rk_hsa_decode_noalloc_max_bytes() -> int:
+    return _lib.rk_hsa_decode_noalloc_max_bytes()
+
+
 def rk_hsa_decode_mt(q, k, v, cand_idx, n_cand, kmax, kmin, block, k1, k2, out, sel_blocks=None,
                      sel_channels=None, block_scores=None, ws=None, stream=None):
     """RocketKV-MT decode over the candidate rows cand_idx [B,Hkv,stride] of the full k, v."""

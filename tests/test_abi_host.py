@@ -205,3 +205,19 @@ def test_workspace_sizes_monotone(rk):
     assert 0 < c < e
     assert lib.rk_hsa_workspace_bytes(ctypes.byref(sh), 0, 16, 32, 32) == 0
     assert lib.rk_snapkv_workspace_bytes(None, 4096, 32) == 0
+
+
+def test_noalloc_refuses_oversized_call_before_the_device(rk):
+    """rk_hsa_decode_noalloc checks its scratch need first: a call larger than
+    the static scratch returns RK_EWORKSPACE without touching a device (this
+    runs where there is none)."""
+    lib = rk.raw_library()
+    assert lib.rk_hsa_decode_noalloc_max_bytes() == 16 << 20
+    shape = rk.shape_of(64, 32, 8, 128, rk.RK_BF16)
+    n = 12000 * 16
+    assert rk.rk_hsa_workspace_bytes(shape, n, 16, 32, 256) > 16 << 20
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.rk_hsa_decode_noalloc(ctypes.byref(shape), fake, fake, fake, n, fake, fake, 12000, n, 16, 32,
+                                   256, fake, None, None, None, None)
+    assert st == rk.RK_EWORKSPACE
+    assert b"static scratch" in lib.rk_last_error()
