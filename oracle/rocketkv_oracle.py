@@ -45,6 +45,8 @@ Readings where the pages are silent or ambiguous:
   R15 the approximate block score is sum over i in i1 of q_bar_i * P_i[b].
   R16 no block is forced into the selection.
   R17 RocketKV-MT builds blocks over the sorted candidate list.
+  R23-R26 (the Exact-TopK, Quest and SparQ baselines and their budgets) are
+      stated with their functions at the end of this module.
 """
 
 from __future__ import annotations
@@ -393,3 +395,167 @@ def hsa_decode_mt_unit(q_group, k_full, v_full, cand, block, k1, k2, sel_overrid
     vc = np.asarray(v_full)[cand]
     kmax, kmin = build_aux(kc, len(cand), block)
     return hsa_unit(q_group, kc, vc, kmax, kmin, len(cand), block, k1, k2, sel_override)
+
+
+# --------------------------------------------------------------------------
+# Dynamic-selection baselines compared with HSA: Exact-TopK, Quest, SparQ
+# --------------------------------------------------------------------------
+# [RKV] background (Exact-TopK as the ideal top-k attention, Figs. 1-2),
+# method details ("limits of existing dynamic selection": Quest keeps per-page
+# element-wise min/max along the sequence, SparQ uses head-dimension
+# sparsity), appendix A.3 (for Quest and SparQ the token budget is shared
+# evenly between the approximate scoring that finds the top-k indices and the
+# sparse attention; Quest is made GQA-aware by choosing per attention group
+# on the accumulated scores) and B.1.1 (standalone HSA against Quest and
+# SparQ, Fig. 8).  Table 1: Quest stores 1 + 1/c, SparQ 2.
+#
+# Readings (R23-R26):
+#   R23 the "attention score" a group accumulates for token n is the sum over
+#       its heads of the logits, sum_g q_g . k_n = q_bar . k_n, the quantity
+#       HSA step 2 approximates; Exact-TopK takes the top-k tokens by it (for
+#       one head this is the top-k by attention weight, softmax being
+#       monotone).  Float32, q_bar summed over g ascending, then channels in
+#       ascending order, one rounded multiply and one rounded add per term.
+#   R24 Quest: pages of `page` tokens with element-wise Kmax/Kmin; the page
+#       score is the per-channel bound max(q_bar_i Kmax_i, q_bar_i Kmin_i)
+#       summed over all d channels (the bound of the accumulated score
+#       q_bar . k of every token in the page); it reads one of the two values
+#       per channel (the sign of q_bar picks it), d values per page.
+#   R25 SparQ: the r channels of largest sum_g |q_g| (ties to the lower
+#       channel), token score q_bar[i1] . k[i1] over those channels only, the
+#       top tokens by it; attention is then exact over the chosen tokens (the
+#       pages do not describe SparQ's value-mean correction; every method is
+#       compared by the tokens it attends).
+#   R26 budgets at total compression c, t = S / c KV pairs, estimation and
+#       attention t/2 each: Quest page = ceil(c) (d of 2d values per page of
+#       c tokens), SparQ r = d / c channels (rounded, in [1, d]), standalone
+#       HSA page = ceil(sqrt(c)) and k1 = d * page / c (the split inside HSA
+#       with all of c in stage 2); each attends ceil((t/2) / page) pages.
+#       Exact-TopK spends nothing on estimation in this accounting (it is the
+#       ideal) and attends ceil(t) tokens.
+SELECT_METHODS = ("hsa", "quest", "sparq", "exact")
+
+
+def select_plan(method: str, c: float, seq_len: int, head_dim: int) -> dict:
+    """Page size, channels per page and attended pages of a selection method
+    at total compression c (readings R24-R26), plus its estimation traffic
+    in KV pairs (channels values per page over ceil(S/page) pages, 2d values
+    per pair)."""
+    if not (c >= 1.0) or seq_len < 1 or head_dim < 1:
+        raise ValueError("bad plan arguments")
+    t = seq_len / c
+    d = head_dim
+    if method == "hsa":
+        page = math.ceil(math.sqrt(c))
+        channels = min(d, max(1, math.floor(d * page / c + 0.5)))
+        k2 = max(1, math.ceil(t / 2 / page))
+    elif method == "quest":
+        page = math.ceil(c)
+        channels = d
+        k2 = max(1, math.ceil(t / 2 / page))
+    elif method == "sparq":
+        page = 1
+        channels = min(d, max(1, math.floor(d / c + 0.5)))
+        k2 = max(1, math.ceil(t / 2))
+    elif method == "exact":
+        page = 1
+        channels = d
+        k2 = max(1, math.ceil(t))
+    else:
+        raise ValueError(f"unknown method {method}")
+    n_pages = -(-seq_len // page)
+    return dict(page=page, channels=channels, k2=k2, attn_tokens=min(seq_len, k2 * page), budget_t=t,
+                est_pairs=channels * n_pages / (2.0 * d))
+
+
+def _group_sums(q_group):
+    """(sum_g |q_g|, q_bar = sum_g q_g) in float32, g ascending."""
+    q = np.asarray(q_group, dtype=F32)
+    a = np.zeros(q.shape[1], F32)
+    qbar = np.zeros(q.shape[1], F32)
+    for g in range(q.shape[0]):
+        a = (a + np.abs(q[g])).astype(F32)
+        qbar = (qbar + q[g]).astype(F32)
+    return a, qbar
+
+
+def exact_topk_scores(q_group: np.ndarray, k_rows: np.ndarray) -> np.ndarray:
+    """Accumulated group logit of every token (reading R23): score[n] =
+    q_bar . k_n, float32, channels ascending, one rounded product and one
+    rounded add per term.  q_group [G, d], k_rows [N, d]."""
+    _, qbar = _group_sums(q_group)
+    k = np.asarray(k_rows, dtype=F32)
+    s = np.zeros(k.shape[0], F32)
+    for i in range(k.shape[1]):
+        s = (s + (qbar[i] * k[:, i]).astype(F32)).astype(F32)
+    return s
+
+
+def quest_page_scores(q_group: np.ndarray, kmax: np.ndarray, kmin: np.ndarray) -> np.ndarray:
+    """Quest's page bound of the accumulated score (reading R24): s[b] = sum
+    over channels i ascending of max(q_bar_i Kmax_i[b], q_bar_i Kmin_i[b]),
+    float32, each term the larger of two rounded products, one rounded add.
+    kmax, kmin [d, nblk]."""
+    _, qbar = _group_sums(q_group)
+    kmax = np.asarray(kmax, F32)
+    kmin = np.asarray(kmin, F32)
+    s = np.zeros(kmax.shape[1], F32)
+    for i in range(kmax.shape[0]):
+        hi = (qbar[i] * kmax[i]).astype(F32)
+        lo = (qbar[i] * kmin[i]).astype(F32)
+        s = (s + np.maximum(hi, lo)).astype(F32)
+    return s
+
+
+def sparq_channels(q_group: np.ndarray, r: int) -> np.ndarray:
+    """SparQ's r channels of largest sum_g |q_g| (ties to the lower channel),
+    ascending (reading R25)."""
+    a, _ = _group_sums(q_group)
+    return topk_lower_index(a, r)
+
+
+def sparq_scores(q_group: np.ndarray, k_rows: np.ndarray, r: int) -> np.ndarray:
+    """SparQ's approximate accumulated logit (reading R25): score[n] = sum over
+    the r chosen channels, ascending, of q_bar_i k_n,i (float32, rounded
+    product then rounded add)."""
+    _, qbar = _group_sums(q_group)
+    k = np.asarray(k_rows, dtype=F32)
+    s = np.zeros(k.shape[0], F32)
+    for i in sparq_channels(q_group, r):
+        s = (s + (qbar[i] * k[:, i]).astype(F32)).astype(F32)
+    return s
+
+
+def select_decode_unit(method: str, q_group, kc, vc, n_tokens: int, page: int, channels: int,
+                       k2: int, sel_override=None) -> dict:
+    """One decode step of a selection method for one GQA group over the first
+    n_tokens rows of kc / vc: page scores, the min(k2, pages) best pages (ties
+    to the lower page, ascending) and exact attention over their tokens.
+    hsa: Algorithm 1 (channel_select, build_aux, block_scores); quest: R24
+    over build_aux pages; sparq (page 1): R25; exact (page 1): R23."""
+    kc = np.asarray(kc)[:n_tokens]
+    vc = np.asarray(vc)[:n_tokens]
+    if method == "hsa":
+        kmax, kmin = build_aux(kc, n_tokens, page)
+        i1, qbar = channel_select(q_group, channels)
+        s = block_scores(qbar, i1, kmax, kmin)
+    elif method == "quest":
+        if channels != kc.shape[1]:
+            raise ValueError("Quest reads every channel")
+        kmax, kmin = build_aux(kc, n_tokens, page)
+        s = quest_page_scores(q_group, kmax, kmin)
+    elif method == "sparq":
+        if page != 1:
+            raise ValueError("SparQ selects tokens (page 1)")
+        s = sparq_scores(q_group, kc, channels)
+    elif method == "exact":
+        if page != 1 or channels != kc.shape[1]:
+            raise ValueError("Exact-TopK selects tokens over every channel")
+        s = exact_topk_scores(q_group, kc)
+    else:
+        raise ValueError(f"unknown method {method}")
+    sel = block_select(s, k2)
+    use = sel if sel_override is None else np.sort(np.asarray(sel_override))
+    toks = selected_tokens(use, n_tokens, page)
+    out = attention(q_group, kc[toks], vc[toks])
+    return dict(scores=s, sel=sel, tokens=toks, out=out)
