@@ -61,6 +61,11 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="issue every call eagerly instead of graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--selection-recall", action="store_true",
+                    help="only compare the selection methods (HSA, Quest, SparQ, Exact-TopK, two-stage "
+                         "RocketKV) on the Llama-8B layer and the 109K needle: recall of the exact top "
+                         "tokens, attention mass, output error, needle hits, us per decode step")
+    ap.add_argument("--recall-steps", type=int, default=8)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE of a profiler run)")
@@ -335,10 +340,124 @@ def measure(rk, WL, name, args, dev, with_cpu):
     return res
 
 
+def selection_recall(args):
+    """Selection quality of each method at its planned budget split (one layer,
+    full prompt; RocketKV adds SnapKV eviction first), against exact attention
+    over the whole prompt, on the GPU through rk_select_decode / the RocketKV
+    calls.  Per (unit, step), averaged: recall = |T & E| / |T| with E the |T|
+    tokens of largest accumulated logit q_bar . k; mass = the group's mean
+    attention probability on T; err = rel-L2 of the output against dense
+    attention; needle = the planted key is in T (the needle workload)."""
+    import torch
+
+    from sparse_decode_attention_amd import rocketkv as rk
+    from sparse_decode_attention_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows = []
+    for name in ("llama8b-layer-s32k-c16", "needle-s109k-c428"):
+        w = WL.WORKLOADS[name]
+        B, Hq, Hkv, d, G, S = w.batch, w.n_q, w.n_kv, w.d, w.group, w.seq
+        k, v, pos = WL.layer_kv(w, 0, device=dev)
+        qw = WL.window_queries(w, 0, device=dev)
+        kf = k.float()
+        qs = [WL.decode_query(w, 0, s, device=dev) for s in range(args.recall_steps)]
+        # dense reference and exact scores, float32
+        ref = []
+        for q in qs:
+            qf = q.float().view(B, Hkv, G, d)
+            logits = torch.matmul(qf, kf.transpose(2, 3).contiguous()) / math.sqrt(d)   # [B,Hkv,G,S]
+            p = torch.softmax(logits, dim=-1)
+            o = torch.matmul(p, v.float())                                                # [B,Hkv,G,d]
+            ref.append((p.mean(dim=2), o, torch.matmul(kf, qf.sum(dim=2).unsqueeze(-1)).squeeze(-1)))
+        methods = []
+        for m in ("exact", "hsa", "quest", "sparq"):
+            methods.append((m, rk.rk_select_plan(m, w.c, S, d)))
+        sp = rk.rk_split(w.c, S, w.window, w.block, d)
+        methods.append(("rocketkv", dict(page=sp["paper_page"], channels=sp["paper_k1_channels"],
+                                         k2=sp["paper_k2_blocks"], n_keep=sp["n_keep"])))
+        methods.append(("rocketkv-w", dict(page=w.block, channels=w.k1, k2=sp["k2_blocks"], n_keep=sp["n_keep"])))
+        for m, p in methods:
+            page, ch, k2 = p["page"], p["channels"], p["k2"]
+            kmax = kmin = None
+            kept = None
+            kk, vv, n = k, v, S
+            if m.startswith("rocketkv"):
+                n = p["n_keep"]
+                kept = torch.empty(B, Hkv, n, dtype=torch.int32, device=dev)
+                kk = torch.empty(B, Hkv, n, d, dtype=k.dtype, device=dev)
+                vv = torch.empty_like(kk)
+                rk.rk_snapkv_evict(qw, k, v, S, w.window, w.pool, n, kept, kk, vv, None)
+            if m != "exact":
+                kmax = torch.empty(B, Hkv, d, rk.aux_capacity(n, page), dtype=k.dtype, device=dev)
+                kmin = None if m == "sparq" else torch.empty_like(kmax)
+                rk.rk_hsa_build_aux(kk, n, 0, page, kmax, kmin, n_q_heads=Hq)
+            nblk = -(-n // page)
+            nsel = min(k2, nblk)
+            sel = torch.empty(B, Hkv, nsel, dtype=torch.int32, device=dev)
+            out = torch.empty(B, Hq, d, device=dev)
+            method = "hsa" if m.startswith("rocketkv") else m
+            ws = rk.rk_select_decode(method, qs[0], kk, vv, kmax, kmin, n, page, ch, k2, out, sel)
+            rec = mass = err = hit = 0.0
+            cnt = 0
+            tok_total = 0
+            for si, q in enumerate(qs):
+                rk.rk_select_decode(method, q, kk, vv, kmax, kmin, n, page, ch, k2, out, sel, ws=ws)
+                torch.cuda.synchronize()
+                pbar, o_ref, sc = ref[si]
+                toks = (sel.long().unsqueeze(-1) * page + torch.arange(page, device=dev)).view(B, Hkv, -1)
+                valid = toks < n
+                toks = torch.where(valid, toks, torch.zeros_like(toks))
+                if kept is not None:
+                    toks = torch.gather(kept.long(), 2, toks)
+                for b in range(B):
+                    for h in range(Hkv):
+                        T = torch.unique(toks[b, h][valid[b, h]])
+                        nt = T.numel()
+                        E = torch.topk(sc[b, h], nt).indices
+                        rec += float(torch.isin(T, E).float().mean())
+                        mass += float(pbar[b, h, T].sum())
+                        og = out.view(B, Hkv, G, d)[b, h]
+                        err += float((og - o_ref[b, h]).norm() / o_ref[b, h].norm())
+                        if w.n_plant == 1:
+                            hit += float(bool(torch.isin(pos[b, h, 0], T)))
+                        tok_total += nt
+                        cnt += 1
+            # decode time per step (eager, events)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for q in qs:
+                rk.rk_select_decode(method, q, kk, vv, kmax, kmin, n, page, ch, k2, out, sel, ws=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            est = ch * nblk / (2.0 * d)
+            rows.append(dict(workload=name, method=m, page=page, channels=ch, k2_pages=k2,
+                             tokens_attended=round(tok_total / cnt, 1), est_pairs=round(est, 1),
+                             recall=round(rec / cnt, 4), mass=round(mass / cnt, 4), out_rel_l2=round(err / cnt, 5),
+                             needle_hit=round(hit / cnt, 4) if w.n_plant == 1 else None,
+                             us_per_step=round(e0.elapsed_time(e1) * 1e3 / len(qs), 2)))
+            log(json.dumps(rows[-1]))
+            del kmax, kmin, kept, ws
+        del k, v, kf, ref
+        torch.cuda.empty_cache()
+    print("| workload | method | page | channels | pages | tokens attended | estimation (KV pairs) | "
+          "recall of exact top tokens | attention mass | output rel-L2 | needle found | us/step |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['workload']} | {r['method']} | {r['page']} | {r['channels']} | {r['k2_pages']} | "
+              f"{r['tokens_attended']} | {r['est_pairs']} | {r['recall']} | {r['mass']} | {r['out_rel_l2']} | "
+              f"{'' if r['needle_hit'] is None else r['needle_hit']} | {r['us_per_step']} |")
+    print(json.dumps({"selection_recall": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.selection_recall:
+        selection_recall(args)
         return
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only (the hot path shards over (batch, KV head) units "

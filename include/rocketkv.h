@@ -155,7 +155,11 @@ rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* 
  *                                   token n is row n
  *   kmax, kmin [B, Hkv, d, nblk_cap]  out, channel-major (page index fastest);
  *                                   nblk_cap must be a multiple of 8 so every
- *                                   channel row starts 16-byte aligned
+ *                                   channel row starts 16-byte aligned.  kmin
+ *                                   may be NULL: only Kmax is written (with
+ *                                   pages of one token Kmax = Kmin = the keys
+ *                                   themselves, channel-major: SparQ's second
+ *                                   copy of K)
  * Pages first_token/block .. ceil(n_tokens/block)-1 are (re)computed from
  * tokens [page*block, min((page+1)*block, n_tokens)); other pages are left
  * untouched, so after appending tokens n_old..n_tokens-1 a call with
@@ -215,8 +219,9 @@ size_t rk_hsa_workspace_bytes(const rk_shape* shape, int64_t n_tokens, int32_t b
  *   sel_channels_opt [B, Hkv, k1] int32             out (optional): i1 ascending
  *   block_scores_opt [B, Hkv, nblk] float32         out (optional): s1
  * nblk = ceil(n_tokens / block).  Requires 1 <= n_tokens <= kv_cap,
- * nblk <= nblk_cap (a multiple of 8), nblk <= 12288, 1 <= k1 <= d, k2 >= 1,
- * G in {1, 2, 4, 8}.
+ * nblk <= nblk_cap (a multiple of 8), nblk <= 2^22, 1 <= k1 <= d, k2 >= 1,
+ * G in {1, 2, 4, 8}.  Beyond 12288 pages per unit the page choice runs in a
+ * launch of its own before the attention.
  */
 rk_status rk_hsa_decode(const rk_shape* shape, const void* q, const void* k, const void* v,
                         int64_t kv_cap, const void* kmax, const void* kmin, int64_t nblk_cap,
@@ -300,6 +305,86 @@ rk_status rk_hsa_decode_mt(const rk_shape* shape, const void* q, const void* k, 
                            int32_t* sel_blocks_opt, int32_t* sel_channels_opt,
                            float* block_scores_opt, void* ws, size_t ws_bytes,
                            rk_stream stream);
+
+/*
+ * Dynamic-selection methods compared with HSA on the same inputs.
+ * [RKV] background (Exact-TopK, the ideal top-k attention), method details
+ * (limits of existing dynamic selection: Quest's per-page element-wise
+ * min/max along the sequence, SparQ's head-dimension sparsity; the token
+ * budget t = S / c), appendix A.3 (for Quest and SparQ the budget is shared
+ * evenly between the approximate scoring and the sparse attention; Quest
+ * chooses per attention group on accumulated scores) and B.1.1 (standalone
+ * HSA against Quest and SparQ).  Every method scores pages, keeps the
+ * top-k2 (ties to the lower page, ascending) and attends exactly over their
+ * tokens, as rk_hsa_decode does:
+ *   RK_SEL_HSA   Algorithm 1 (k1 = channels, pages of `page` tokens)
+ *   RK_SEL_QUEST page score sum over all d channels of max(q_bar_i Kmax_i,
+ *                q_bar_i Kmin_i), the bound of every token's accumulated
+ *                logit q_bar . k in the page (equals HSA with k1 = d)
+ *   RK_SEL_SPARQ token score over the `channels` channels of largest
+ *                sum_g |q_g|: sum_i q_bar_i k_n,i (pages of one token)
+ *   RK_SEL_EXACT the exact accumulated logit q_bar . k_n of every token, over
+ *                the key rows (pages of one token, every channel)
+ * with q_bar = sum_g q_g over the group's heads (float32, g ascending) and
+ * every score a float32 sum in ascending channel order, one rounded multiply
+ * and one rounded add per term.
+ */
+typedef enum {
+  RK_SEL_HSA = 0,
+  RK_SEL_QUEST = 1,
+  RK_SEL_SPARQ = 2,
+  RK_SEL_EXACT = 3
+} rk_select_method;
+
+typedef struct {
+  int32_t page;        /* tokens per page (1: token-level selection)          */
+  int32_t channels;    /* channels read per page when scoring (k1)            */
+  int32_t k2;          /* pages attended                                      */
+  int64_t attn_tokens; /* min(S, k2 * page) tokens attended                   */
+  double budget_t;     /* t = S / c                                           */
+  double est_pairs;    /* scoring traffic in KV pairs: channels values per
+                          page over ceil(S / page) pages, 2d values per pair  */
+} rk_select_plan_out;
+
+/*
+ * rk_select_plan -- page size, channels and attended pages of a method at
+ * total compression c with estimation and attention sharing t evenly
+ * ([RKV] A.3; the split inside HSA with all of c in stage 2):
+ *   HSA   page = ceil(sqrt(c)), channels = round(d * page / c) in [1, d]
+ *   QUEST page = ceil(c), channels = d (d of its 2d aux values per page)
+ *   SPARQ page = 1, channels = round(d / c) in [1, d]
+ *   EXACT page = 1, channels = d, k2 = ceil(t) (the ideal: no estimation
+ *         cost counted against the budget)
+ * and k2 = ceil((t / 2) / page) pages for the first three.  Host math only.
+ * RK_EINVAL on c < 1, seq_len < 1, head_dim < 1, an unknown method or NULL out.
+ */
+rk_status rk_select_plan(rk_select_method method, double c, int64_t seq_len, int32_t head_dim,
+                         rk_select_plan_out* out);
+
+/*
+ * rk_select_decode -- one decode step of a selection method (see above).
+ *   q, k, v, kv_cap, n_tokens, out: as for rk_hsa_decode (pages are `page`
+ *                                   consecutive tokens of the cache)
+ *   kmax, kmin [B, Hkv, d, nblk_cap]  HSA and QUEST: from rk_hsa_build_aux in
+ *                                   pages of `page` tokens.  SPARQ: kmax from
+ *                                   rk_hsa_build_aux with block 1 (the keys
+ *                                   channel-major), kmin ignored.  EXACT:
+ *                                   both ignored (may be NULL); the scores
+ *                                   come from the key rows.
+ *   channels                        HSA/SPARQ: channels scored (1..d);
+ *                                   QUEST/EXACT: must be d
+ *   sel_opt [B, Hkv, min(k2, pages)] out (optional): chosen pages ascending
+ *   scores_opt [B, Hkv, pages] float32 out (optional): the page scores
+ *   ws      workspace of rk_hsa_workspace_bytes(shape, n_tokens, page,
+ *           channels, k2) bytes
+ * SPARQ and EXACT require page = 1.  More than 12288 pages per unit take a
+ * separate page-choice launch; at most 2^22 pages.  Errors as rk_hsa_decode.
+ */
+rk_status rk_select_decode(const rk_shape* shape, rk_select_method method, const void* q,
+                           const void* k, const void* v, int64_t kv_cap, const void* kmax,
+                           const void* kmin, int64_t nblk_cap, int64_t n_tokens, int32_t page,
+                           int32_t channels, int32_t k2, float* out, int32_t* sel_opt,
+                           float* scores_opt, void* ws, size_t ws_bytes, rk_stream stream);
 
 /*
  * Kernel timing (measurement support, not part of the method).

@@ -68,14 +68,16 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
                         const void* kmax, const void* kmin, int64_t nblk_cap, int64_t n_tokens,
                         int32_t block, int32_t k1, int32_t k2, float* out, int32_t* sel_opt,
                         int32_t* chan_opt, float* s1_opt, void* ws, size_t ws_bytes,
-                        rk_stream stream, bool mt, const rk::AppendArgs* app = nullptr) {
+                        rk_stream stream, bool mt, const rk::AppendArgs* app = nullptr,
+                        bool exact_rows = false) {
   rk::Dims d;
   rk_status st = check_shape(shape, &d);
   if (st != RK_OK) return st;
-  if (!q || !k || !v || !kmax || !kmin || !out) return fail(RK_EINVAL, "null tensor argument");
+  if (!q || !k || !v || !out || (!exact_rows && (!kmax || !kmin)))
+    return fail(RK_EINVAL, "null tensor argument");
   if (mt && !cand) return fail(RK_EINVAL, "cand_idx is NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kmax) || !aligned16(kmin) ||
-      !aligned16(out))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (!exact_rows && (!aligned16(kmax) || !aligned16(kmin))))
     return fail(RK_EINVAL, "q, k, v, kmax, kmin and out must be 16-byte aligned");
   if (d.G != 1 && d.G != 2 && d.G != 4 && d.G != 8)
     return fail(RK_EUNSUPPORTED, "group size %d not built (1, 2, 4, 8)", d.G);
@@ -90,11 +92,13 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
                 (long long)kv_cap);
   }
   const int64_t nblk = (n_tokens + block - 1) / block;
-  if (nblk > nblk_cap) return fail(RK_EINVAL, "pages (%lld) exceed nblk_cap", (long long)nblk);
-  if (nblk_cap % 8) return fail(RK_EINVAL, "nblk_cap must be a multiple of 8");
-  if (nblk > rk::kMaxPages)
+  if (!exact_rows) {
+    if (nblk > nblk_cap) return fail(RK_EINVAL, "pages (%lld) exceed nblk_cap", (long long)nblk);
+    if (nblk_cap % 8) return fail(RK_EINVAL, "nblk_cap must be a multiple of 8");
+  }
+  if (nblk > rk::kMaxPagesGlobal)
     return fail(RK_EUNSUPPORTED, "pages (%lld) above %lld", (long long)nblk,
-                (long long)rk::kMaxPages);
+                (long long)rk::kMaxPagesGlobal);
   if (k1 < 1 || k1 > d.D) return fail(RK_EINVAL, "k1 (%d) outside [1, head_dim]", k1);
   if (k2 < 1) return fail(RK_EINVAL, "k2 must be >= 1");
   const rk::DecodeWs lay = rk::decode_ws_layout(d, nblk, k2);
@@ -102,7 +106,7 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
   return device_status(
       rk::launch_hsa_decode(d, q, k, v, kv_cap, mt ? cand : nullptr, cand_stride, kmax, kmin,
                             nblk_cap, n_tokens, block, k1, k2, out, sel_opt, chan_opt, s1_opt,
-                            ws, static_cast<hipStream_t>(stream), app),
+                            ws, static_cast<hipStream_t>(stream), app, exact_rows),
       mt ? "rk_hsa_decode_mt launch" : app ? "rk_hsa_append_decode launch" : "rk_hsa_decode launch");
 }
 
@@ -250,8 +254,8 @@ rk_status rk_hsa_build_aux(const rk_shape* shape, const void* k, int64_t k_cap,
   rk::Dims d;
   rk_status st = check_shape(shape, &d);
   if (st != RK_OK) return st;
-  if (!k || !kmax || !kmin) return fail(RK_EINVAL, "null tensor argument");
-  if (!aligned16(k) || !aligned16(kmax) || !aligned16(kmin))
+  if (!k || !kmax) return fail(RK_EINVAL, "null tensor argument");
+  if (!aligned16(k) || !aligned16(kmax) || (kmin && !aligned16(kmin)))
     return fail(RK_EINVAL, "k, kmax and kmin must be 16-byte aligned");
   if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
   if (n_tokens < 1 || n_tokens > (int64_t(1) << 31) - 1)
@@ -343,6 +347,88 @@ rk_status rk_hsa_decode_noalloc(const rk_shape* shape, const void* q, const void
 }
 
 size_t rk_hsa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+rk_status rk_select_plan(rk_select_method method, double c, int64_t seq_len, int32_t head_dim,
+                         rk_select_plan_out* out) {
+  if (!out) return fail(RK_EINVAL, "out is NULL");
+  if (!(c >= 1.0) || !isfinite(c)) return fail(RK_EINVAL, "compression ratio must be >= 1");
+  if (seq_len < 1 || head_dim < 1) return fail(RK_EINVAL, "seq_len and head_dim must be >= 1");
+  const double t = double(seq_len) / c;
+  const int32_t d = head_dim;
+  auto clamp_d = [d](double x) {
+    int64_t v = int64_t(floor(x + 0.5));
+    return int32_t(v < 1 ? 1 : (v > d ? d : v));
+  };
+  auto pages_for = [](double tokens, int64_t page) {
+    const int64_t k = int64_t(ceil(tokens / double(page)));
+    return int32_t(k < 1 ? 1 : (k > INT32_MAX ? INT32_MAX : k));
+  };
+  int64_t page = 1;
+  int32_t channels = d, k2 = 1;
+  switch (method) {
+    case RK_SEL_HSA:
+      page = int64_t(ceil(sqrt(c)));
+      channels = clamp_d(double(d) * double(page) / c);
+      k2 = pages_for(t / 2.0, page);
+      break;
+    case RK_SEL_QUEST:
+      page = int64_t(ceil(c));
+      channels = d;
+      k2 = pages_for(t / 2.0, page);
+      break;
+    case RK_SEL_SPARQ:
+      page = 1;
+      channels = clamp_d(double(d) / c);
+      k2 = pages_for(t / 2.0, 1);
+      break;
+    case RK_SEL_EXACT:
+      page = 1;
+      channels = d;
+      k2 = pages_for(t, 1);
+      break;
+    default:
+      return fail(RK_EINVAL, "unknown selection method %d", int(method));
+  }
+  if (page > INT32_MAX) return fail(RK_EINVAL, "page size too large");
+  const int64_t n_pages = (seq_len + page - 1) / page;
+  out->page = int32_t(page);
+  out->channels = channels;
+  out->k2 = k2;
+  out->attn_tokens = int64_t(k2) * page < seq_len ? int64_t(k2) * page : seq_len;
+  out->budget_t = t;
+  out->est_pairs = double(channels) * double(n_pages) / (2.0 * double(d));
+  return RK_OK;
+}
+
+rk_status rk_select_decode(const rk_shape* shape, rk_select_method method, const void* q,
+                           const void* k, const void* v, int64_t kv_cap, const void* kmax,
+                           const void* kmin, int64_t nblk_cap, int64_t n_tokens, int32_t page,
+                           int32_t channels, int32_t k2, float* out, int32_t* sel_opt,
+                           float* scores_opt, void* ws, size_t ws_bytes, rk_stream stream) {
+  if (!shape) return fail(RK_EINVAL, "shape is NULL");
+  switch (method) {
+    case RK_SEL_HSA:
+      break;
+    case RK_SEL_QUEST:
+      if (channels != shape->head_dim)
+        return fail(RK_EINVAL, "Quest reads every channel: channels must equal head_dim");
+      break;
+    case RK_SEL_SPARQ:
+      if (page != 1) return fail(RK_EINVAL, "SparQ selects tokens: page must be 1");
+      kmin = kmax;  // pages of one token: Kmax = Kmin = the key row, channel-major
+      break;
+    case RK_SEL_EXACT:
+      if (page != 1 || channels != shape->head_dim)
+        return fail(RK_EINVAL, "Exact-TopK selects tokens over every channel: page 1, channels = head_dim");
+      return decode_common(shape, q, k, v, kv_cap, nullptr, 0, nullptr, nullptr, 0, n_tokens, 1,
+                           channels, k2, out, sel_opt, nullptr, scores_opt, ws, ws_bytes, stream,
+                           false, nullptr, true);
+    default:
+      return fail(RK_EINVAL, "unknown selection method %d", int(method));
+  }
+  return decode_common(shape, q, k, v, kv_cap, nullptr, 0, kmax, kmin, nblk_cap, n_tokens, page,
+                       channels, k2, out, sel_opt, nullptr, scores_opt, ws, ws_bytes, stream, false);
+}
 
 rk_status rk_hsa_decode_mt(const rk_shape* shape, const void* q, const void* k, const void* v,
                            int64_t kv_cap, const int32_t* cand_idx, int64_t cand_stride,

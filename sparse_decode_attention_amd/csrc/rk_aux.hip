@@ -89,14 +89,14 @@ __global__ __launch_bounds__(kAuxThreads) void aux_build_kernel(
   }
   __syncthreads();
   T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
-  T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
+  T* nu = kmin ? kmin + size_t(u) * D * size_t(nblk_cap) : nullptr;  // NULL: only Kmax is wanted
   for (int e = t; e < D * PPW; e += kAuxThreads) {
     const int ch = e / PPW;
     const int jj = e % PPW;
     const int pp = p0 + jj;
     if (pp < nblk) {
       xu[size_t(ch) * nblk_cap + pp] = smax[ch][jj];
-      nu[size_t(ch) * nblk_cap + pp] = smin[ch][jj];
+      if (kmin) nu[size_t(ch) * nblk_cap + pp] = smin[ch][jj];
     }
   }
 }

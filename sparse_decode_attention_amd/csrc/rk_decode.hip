@@ -23,6 +23,7 @@
 // HBM-bound: bytes per unit = q + k1*nblk aux elements + 2*d*|T| K/V elements.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "rk_device.hpp"
@@ -279,6 +280,86 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
   score_staged<T, 256>(stage, np, k1, i1_q, ku, s1_opt ? s1_opt + size_t(u) * nblk + p0 : nullptr);
 }
 
+// Exact-TopK scoring: the group's accumulated logit of every token, over the
+// key rows themselves (pages of one token, all channels): s[n] = sum over
+// channels i ascending of q_bar_i * k_n,i, one rounded multiply and one
+// rounded add per term (float32), q_bar = sum_g q_g with g ascending.  One
+// thread per token reads its row with 16-byte loads; q_bar is formed once per
+// workgroup in LDS.  Writes order keys (and, when asked, the scores).
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void exact_score_kernel(const T* __restrict__ q,
+                                                          const T* __restrict__ k, int64_t kv_cap,
+                                                          int n_tokens, uint32_t* __restrict__ keys,
+                                                          int keys_pitch, float* __restrict__ s_opt) {
+#pragma clang fp contract(off)
+  constexpr int EPL = Vec16<T>::N;
+  __shared__ float qb[D];
+  const int u = blockIdx.y;
+  for (int ch = threadIdx.x; ch < D; ch += 256) {
+    float a = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) a = __fadd_rn(a, to_f32(q[(size_t(u) * G + g) * D + ch]));
+    qb[ch] = a;
+  }
+  __syncthreads();
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= n_tokens) return;
+  const T* row = k + (size_t(u) * size_t(kv_cap) + size_t(n)) * D;
+  Vec16<T> r[D / EPL];
+#pragma unroll
+  for (int c = 0; c < D / EPL; ++c) r[c] = load16(row + c * EPL);
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / EPL; ++c)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = acc + qb[c * EPL + e] * r[c].get(e);
+  keys[size_t(u) * keys_pitch + n] = order_key(acc);
+  if (s_opt) s_opt[size_t(u) * n_tokens + n] = acc;
+}
+
+// out[i] = i % period (the channel list 0..D-1 of every unit).
+__global__ __launch_bounds__(256) void fill_iota_kernel(int32_t* __restrict__ out, int period, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = i % period;
+}
+
+// Page choice in a launch of its own (more pages than the attention
+// workgroups hold in LDS, or token-level scoring): one workgroup per unit
+// takes the top-nsel of the unit's page keys (ties to the lower page) and
+// writes the chosen pages, ascending, to sel (and sel_opt).  STAGED: the keys
+// fit in LDS (with the key range taken while staging, and spare LDS for the
+// radix candidates); otherwise every pass reads them from memory (L2).
+template <bool STAGED>
+__global__ __launch_bounds__(1024) void page_select_kernel(const uint32_t* __restrict__ keys,
+                                                           int keys_pitch, int nblk, int nsel,
+                                                           int cand_cap, int32_t* __restrict__ sel,
+                                                           int32_t* __restrict__ sel_opt) {
+  extern __shared__ uint32_t pk[];
+  __shared__ TopkSmem<1024, 2048, 1> sm;
+  const int u = blockIdx.x;
+  const uint32_t* kg = keys + size_t(u) * keys_pitch;
+  int32_t* su = sel + size_t(u) * nsel;
+  int32_t* so = sel_opt ? sel_opt + size_t(u) * nsel : nullptr;
+  auto emit = [=](int r, int i) {
+    su[r] = i;
+    if (so) so[r] = i;
+  };
+  if constexpr (STAGED) {
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (int i = threadIdx.x; i < nblk; i += 1024) {
+      const uint32_t kk = kg[i];
+      pk[i] = kk;
+      lo = min(lo, kk);
+      hi = max(hi, kk);
+    }
+    __syncthreads();
+    wg_topk<1024, 2048>([&](int i) { return pk[i]; }, nblk, nsel, emit, sm, true, lo, hi, pk + nblk,
+                        cand_cap);
+  } else {
+    wg_topk<1024, 2048>([&](int i) { return kg[i]; }, nblk, nsel, emit, sm);
+  }
+}
+
 // ---- step 3 building blocks -------------------------------------------------
 // A wave streams whole pages.  Lanes split a row into LPR 16-byte chunks, so
 // SLOTS tokens are in flight per wave and each slot takes TPS tokens per chunk
@@ -445,12 +526,16 @@ __device__ __forceinline__ void merge_waves(int idx, const float* wm, const floa
 // between the choice and the K/V fetch.  Then 4 waves stream the pages and the
 // workgroup writes one partial (m, l, o[d]) per head.  TPS_: tokens per slot
 // per step (more loads in flight per wave, more registers).
-template <typename T, int D, int G, bool MT, int TPS_ = AttnShape<T, D, G>::TPS>
+//
+// PRESEL: the pages were chosen by page_select_kernel (written to presel,
+// ascending, nsel per unit); the workgroup copies its split's run of them.
+template <typename T, int D, int G, bool MT, int TPS_ = AttnShape<T, D, G>::TPS, bool PRESEL = false>
 __global__ __launch_bounds__(256) void hsa_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
     const int32_t* __restrict__ cand, int64_t cand_stride, const uint32_t* __restrict__ keys,
     int keys_pitch, int nblk, int nsel, int pages_per_split, int n_split, int units, int n_tokens,
-    int block, float scale_log2, float* __restrict__ partials, int32_t* __restrict__ sel_opt) {
+    int block, float scale_log2, float* __restrict__ partials, int32_t* __restrict__ sel_opt,
+    const int32_t* __restrict__ presel) {
   using S = AttnShape<T, D, G>;
   constexpr int EPL = S::EPL, LPR = S::LPR;
   constexpr int NW = 4;
@@ -488,12 +573,15 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   const int np = min(e0 + pages_per_split, nsel) - e0;
   int32_t* so = sel_opt && split == 0 ? sel_opt + size_t(u) * nsel : nullptr;
   const uint32_t* kg = keys + size_t(u) * keys_pitch;
-  auto emit = [=](int r, int i) {  // by value: no local needs an address
+  [[maybe_unused]] auto emit = [=](int r, int i) {  // by value: no local needs an address
     if (r >= e0 && r < e0 + np) pages[r - e0] = i;
     if (so) so[r] = i;
   };
   static_assert(kWaveTopkPages <= 16 * kWave, "one-wave top-k holds at most 16 rows");
-  if (nblk <= kWaveTopkPages) {
+  if constexpr (PRESEL) {
+    const int32_t* pg = presel + size_t(u) * nsel + e0;
+    for (int i = threadIdx.x; i < np; i += 256) pages[i] = pg[i];
+  } else if (nblk <= kWaveTopkPages) {
     // one wave selects from keys held in registers (no barrier inside) and
     // emits only the ranks this split needs (all of them for the sel output)
     if (wave == 0)
@@ -815,18 +903,21 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
                            const void* kmax, const void* kmin, int64_t nblk_cap,
                            int64_t n_tokens, int block, int k1, int k2, float* out,
                            int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                           hipStream_t s, const AppendArgs* app) {
+                           hipStream_t s, const AppendArgs* app, bool exact_rows) {
   const int nblk = int((n_tokens + block - 1) / block);
   const DecodeWs lay = decode_ws_layout(d, nblk, k2);
   char* wsb = static_cast<char*>(ws);
   float* part = reinterpret_cast<float*>(wsb + lay.partials);
   const int units = d.units();
+  // the page choice gets a launch of its own when the attention workgroups
+  // could not hold the page keys in LDS, and for token-level exact scoring
+  const bool presel = exact_rows || nblk > kMaxPages;
 
   const float scale_log2 = float(1.4426950408889634 / sqrt(double(D)));
   // one workgroup per unit when the units fill the chip, or when each of its
   // 16 waves streams at most one page (the 109K needle: 16 pages per unit),
   // where the split path's three launches cost more than one CU per unit
-  if constexpr (G <= 4) if (units >= kFusedMinUnits || lay.nsel <= kFusedThreads / kWave) {
+  if constexpr (G <= 4) if (!presel && (units >= kFusedMinUnits || lay.nsel <= kFusedThreads / kWave)) {
     // one workgroup per unit: chunk of npc pages within the LDS budget
     const int k1pf = (k1 + 15) / 16 * 16 + int(16 / sizeof(T));
     const size_t fixed = fused_lds_bytes(nblk, lay.nsel, 0, k1pf, sizeof(T), D, G);
@@ -902,6 +993,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
                    2 * D * (ppw / EPV) <= 256 * 8;
   const int n_ranges = (nblk + ppw - 1) / ppw;
   const int score_wgs = (n_ranges * units + kXcds - 1) / kXcds * kXcds;
+  uint32_t* keys = reinterpret_cast<uint32_t*>(wsb + lay.keys);
   // ALL: every channel's two rows, then the products [ppw][roundup16(k1) + 4] fp32
   const size_t lds = all ? size_t(2) * D * sizeof(T) * ppw + size_t(ppw) * ((k1 + 15) / 16 * 16 + 4) * 4
                          : size_t(k1p) * sizeof(T) * ppw;
@@ -915,8 +1007,12 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
     }
     attr_set = true;
   }
-  uint32_t* keys = reinterpret_cast<uint32_t*>(wsb + lay.keys);
-  if (all)
+  if (exact_rows)
+    RK_LAUNCH("exact_score", (exact_score_kernel<T, D, G>),
+              dim3(unsigned((n_tokens + 255) / 256), unsigned(units)), dim3(256), 0, s,
+              static_cast<const T*>(q), static_cast<const T*>(k), kv_cap, int(n_tokens), keys,
+              lay.keys_pitch, s1_opt);
+  else if (all)
     RK_LAUNCH("hsa_score", (hsa_score_kernel<T, D, G, true>), dim3(score_wgs), dim3(256), lds, s,
               static_cast<const T*>(q), static_cast<const T*>(kmax), static_cast<const T*>(kmin),
               nblk_cap, nblk, k1, ppw, units, keys, lay.keys_pitch, chan_opt, s1_opt);
@@ -926,13 +1022,43 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
               nblk_cap, nblk, k1, ppw, units, keys, lay.keys_pitch, chan_opt, s1_opt);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  // the page choice in a launch of its own (keys in LDS when they fit, with
+  // up to 4096 words of radix candidates after them)
+  int32_t* presel_pages = reinterpret_cast<int32_t*>(wsb + lay.sel);
+  if (presel) {
+    const size_t staged_words = size_t(lay.keys_pitch) + 4096;
+    const bool staged = staged_words * 4 <= kSelectKeysLds;
+    static bool sel_attr_set = false;  // once per template instantiation
+    if (!sel_attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&page_select_kernel<true>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         int(kSelectKeysLds));
+      if (e != hipSuccess) return e;
+      sel_attr_set = true;
+    }
+    if (staged)
+      RK_LAUNCH("page_select", page_select_kernel<true>, dim3(units), dim3(1024), staged_words * 4, s,
+                keys, lay.keys_pitch, nblk, lay.nsel, 4096, presel_pages, sel_opt);
+    else
+      RK_LAUNCH("page_select", page_select_kernel<false>, dim3(units), dim3(1024), 0, s, keys,
+                lay.keys_pitch, nblk, lay.nsel, 0, presel_pages, sel_opt);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (exact_rows && chan_opt) {
+      // every channel takes part, in ascending order
+      RK_LAUNCH("exact_channels", fill_iota_kernel, dim3((units * D + 255) / 256), dim3(256), 0, s,
+                chan_opt, D, units * D);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+  }
 
   // split-K sizing: aim for ~2048 workgroups over the whole launch, at least
-  // kMinPagesPerSplit pages (one per wave) and at most kMaxSplits splits per unit
+  // kMinPagesPerSplit pages (one per wave; with a separate page choice, at
+  // least 64 tokens: 16 per wave) and at most kMaxSplits splits per unit
   const int64_t total_pages = int64_t(units) * lay.nsel;
   int pps = int((total_pages + 2047) / 2048);
-  pps = pps < kMinPagesPerSplit ? kMinPagesPerSplit : pps;
+  const int pps_min = presel ? std::max(kMinPagesPerSplit, (64 + block - 1) / block) : kMinPagesPerSplit;
+  pps = pps < pps_min ? pps_min : pps;
   const int pps_cap = (lay.nsel + kMaxSplits - 1) / kMaxSplits;
   pps = pps < pps_cap ? pps_cap : pps;
   pps = (pps + 3) / 4 * 4;
@@ -940,7 +1066,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   pps = pps > nsel4 ? nsel4 : pps;
   const int n_split = (lay.nsel + pps - 1) / pps;
   const size_t attn_lds =
-      size_t(pps + (nblk > kWaveTopkPages ? lay.keys_pitch : 0)) * sizeof(uint32_t);  // <= 96 KB
+      size_t(pps + (!presel && nblk > kWaveTopkPages ? lay.keys_pitch : 0)) * sizeof(uint32_t);  // <= 96 KB
   static bool attn_attr_set = false;  // once per template instantiation
   if (!attn_attr_set) {
     for (const void* f : {reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, true>),
@@ -958,21 +1084,37 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   // at most one workgroup per CU: registers cannot limit occupancy, so each
   // wave takes 4 tokens per slot per step (fewer dependent load rounds)
   const bool one_per_cu = attn_wgs <= kComputeUnits;
-#define RK_ATTN(NAME, MTV, TPSV)                                                                  \
-  RK_LAUNCH(NAME, (hsa_attn_kernel<T, D, G, MTV, TPSV>), dim3(attn_wgs), dim3(256), attn_lds, s, \
-            static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), kv_cap, \
-            cand, cand_stride, keys, lay.keys_pitch, nblk, lay.nsel, pps, n_split, units,        \
-            int(n_tokens), block, scale_log2, part, sel_opt)
-  if (cand) {
-    if (one_per_cu)
-      RK_ATTN("hsa_attn_mt", true, 4);
+#define RK_ATTN(NAME, MTV, TPSV, PRE)                                                             \
+  RK_LAUNCH(NAME, (hsa_attn_kernel<T, D, G, MTV, TPSV, PRE>), dim3(attn_wgs), dim3(256), attn_lds, \
+            s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),      \
+            kv_cap, cand, cand_stride, keys, lay.keys_pitch, nblk, lay.nsel, pps, n_split, units, \
+            int(n_tokens), block, scale_log2, part, sel_opt, presel_pages)
+  if (presel) {
+    static bool pre_attr_set = false;  // once per template instantiation
+    if (!pre_attr_set) {
+      for (const void* f :
+           {reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, true, AttnShape<T, D, G>::TPS, true>),
+            reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, false, AttnShape<T, D, G>::TPS, true>)}) {
+        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           int(kAttnDynLds));
+        if (e != hipSuccess) return e;
+      }
+      pre_attr_set = true;
+    }
+    if (cand)
+      RK_ATTN("hsa_attn_mt", true, (AttnShape<T, D, G>::TPS), true);
     else
-      RK_ATTN("hsa_attn_mt", true, (AttnShape<T, D, G>::TPS));
+      RK_ATTN("hsa_attn", false, (AttnShape<T, D, G>::TPS), true);
+  } else if (cand) {
+    if (one_per_cu)
+      RK_ATTN("hsa_attn_mt", true, 4, false);
+    else
+      RK_ATTN("hsa_attn_mt", true, (AttnShape<T, D, G>::TPS), false);
   } else {
     if (one_per_cu)
-      RK_ATTN("hsa_attn", false, 4);
+      RK_ATTN("hsa_attn", false, 4, false);
     else
-      RK_ATTN("hsa_attn", false, (AttnShape<T, D, G>::TPS));
+      RK_ATTN("hsa_attn", false, (AttnShape<T, D, G>::TPS), false);
   }
 #undef RK_ATTN
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -987,12 +1129,12 @@ hipError_t launch_decode_d(const Dims& d, const void* q, const void* k, const vo
                            const void* kmax, const void* kmin, int64_t nblk_cap,
                            int64_t n_tokens, int block, int k1, int k2, float* out,
                            int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                           hipStream_t s, const AppendArgs* app) {
+                           hipStream_t s, const AppendArgs* app, bool exact_rows) {
 #define RK_DECODE_G(GG)                                                                        \
   case GG:                                                                                     \
     return launch_decode_t<T, D, GG>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,       \
                                      nblk_cap, n_tokens, block, k1, k2, out, sel_opt,         \
-                                     chan_opt, s1_opt, ws, s, app);
+                                     chan_opt, s1_opt, ws, s, app, exact_rows);
   switch (d.G) {
     RK_DECODE_G(1)
     RK_DECODE_G(2)
@@ -1011,23 +1153,23 @@ hipError_t launch_hsa_decode(const Dims& d, const void* q, const void* k, const 
                              const void* kmax, const void* kmin, int64_t nblk_cap,
                              int64_t n_tokens, int block, int k1, int k2, float* out,
                              int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                             hipStream_t s, const AppendArgs* app) {
+                             hipStream_t s, const AppendArgs* app, bool exact_rows) {
   if (d.bf16) {
     if (d.D == 128)
       return launch_decode_d<bf16_t, 128>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                           nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                          chan_opt, s1_opt, ws, s, app);
+                                          chan_opt, s1_opt, ws, s, app, exact_rows);
     return launch_decode_d<bf16_t, 64>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                        nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                       chan_opt, s1_opt, ws, s, app);
+                                       chan_opt, s1_opt, ws, s, app, exact_rows);
   }
   if (d.D == 128)
     return launch_decode_d<float, 128>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                        nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                       chan_opt, s1_opt, ws, s, app);
+                                       chan_opt, s1_opt, ws, s, app, exact_rows);
   return launch_decode_d<float, 64>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                     nblk_cap, n_tokens, block, k1, k2, out, sel_opt, chan_opt,
-                                    s1_opt, ws, s, app);
+                                    s1_opt, ws, s, app, exact_rows);
 }
 
 }  // namespace rk

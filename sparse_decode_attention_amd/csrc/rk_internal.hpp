@@ -9,8 +9,12 @@
 
 namespace rk {
 
-// Largest page count HSA step 2 keeps in LDS (keys of 4 bytes each).
+// Largest page count whose top-k runs inside the attention workgroups, from
+// keys held in LDS (4 bytes each).  Beyond it (and for token-level scoring
+// over key rows) a select launch of its own writes the chosen pages, which
+// the attention workgroups then read; kMaxPagesGlobal bounds that path.
 constexpr int64_t kMaxPages = 12288;
+constexpr int64_t kMaxPagesGlobal = int64_t(1) << 22;
 // Stage-1 column tile of the window-score passes (partials are sized by it).
 constexpr int kWsTile = 64;
 // Pages handled by one attention workgroup at least (split-K granularity),
@@ -70,7 +74,7 @@ inline EvictWs evict_ws_layout(const Dims& d, int64_t S, int W) {
 inline int partial_floats(int D) { return D + 4; }
 
 struct DecodeWs {
-  size_t keys, partials, total;
+  size_t keys, partials, sel, total;
   int n_split_max, nsel, keys_pitch;
 };
 inline DecodeWs decode_ws_layout(const Dims& d, int64_t nblk, int k2) {
@@ -83,6 +87,7 @@ inline DecodeWs decode_ws_layout(const Dims& d, int64_t nblk, int k2) {
   size_t off = 0;
   w.keys = off;     off += align256(u * size_t(w.keys_pitch) * sizeof(uint32_t));
   w.partials = off; off += align256(u * w.n_split_max * d.G * partial_floats(d.D) * sizeof(float));
+  w.sel = off;      off += align256(u * size_t(w.nsel) * sizeof(int32_t));  // chosen pages (select launch)
   w.total = off;
   return w;
 }
@@ -123,12 +128,16 @@ struct AppendArgs {
   void* kmin;
 };
 
+// exact_rows: page scores are the exact group logits q_bar . k_n over the
+// key rows (pages of one token, every channel; kmax/kmin unused), the
+// Exact-TopK selection; otherwise HSA step 2 over kmax/kmin.
 hipError_t launch_hsa_decode(const Dims& d, const void* q, const void* k, const void* v,
                              int64_t kv_cap, const int32_t* cand, int64_t cand_stride,
                              const void* kmax, const void* kmin, int64_t nblk_cap,
                              int64_t n_tokens, int block, int k1, int k2, float* out,
                              int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                             hipStream_t s, const AppendArgs* app = nullptr);
+                             hipStream_t s, const AppendArgs* app = nullptr,
+                             bool exact_rows = false);
 
 hipError_t launch_snapkv_evict(const Dims& d, const void* q_win, const void* k, const void* v,
                                int64_t kv_cap, int64_t S, int W, int pool_kernel,

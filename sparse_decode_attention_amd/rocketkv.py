@@ -147,8 +147,8 @@ def rk_snapkv_evict(q_win, k, v, seq_len, window, pool_kernel, n_keep, kept_idx,
 
 def rk_hsa_build_aux(k, n_tokens, first_token, block, kmax, kmin, n_q_heads=None, idx=None,
                      stream=None):
-    """HSA step 1.  k [B,Hkv,cap,d]; kmax, kmin [B,Hkv,d,nblk_cap]; idx [B,Hkv,stride] int32
-    or None (page token n is row idx[n])."""
+    """HSA step 1.  k [B,Hkv,cap,d]; kmax, kmin [B,Hkv,d,nblk_cap] (kmin None: Kmax only);
+    idx [B,Hkv,stride] int32 or None (page token n is row idx[n])."""
     _need_contig(k, kmax, kmin, idx)
     B, Hkv, cap, d = k.shape
     shape = shape_of(B, n_q_heads or Hkv, Hkv, d, _dtype_code(k))
@@ -247,6 +247,44 @@ def rk_hsa_decode_mt(q, k, v, cand_idx, n_cand, kmax, kmin, block, k1, k2, out, 
                                  kmax.shape[3], block, k1, k2, _ptr(out), _ptr(sel_blocks),
                                  _ptr(sel_channels), _ptr(block_scores), _ptr(ws), ws.numel(),
                                  _stream(stream)), "rk_hsa_decode_mt")
+    return ws
+
+
+RK_SEL = {"hsa": 0, "quest": 1, "sparq": 2, "exact": 3}
+
+
+class RkSelectPlan(ctypes.Structure):
+    _fields_ = [("page", ctypes.c_int32), ("channels", ctypes.c_int32), ("k2", ctypes.c_int32),
+                ("attn_tokens", ctypes.c_int64), ("budget_t", ctypes.c_double), ("est_pairs", ctypes.c_double)]
+
+
+_lib.rk_select_plan.argtypes = [ctypes.c_int, _f64, _i64, _i32, ctypes.POINTER(RkSelectPlan)]
+_lib.rk_select_plan.restype = ctypes.c_int
+_lib.rk_select_decode.argtypes = [_SP, ctypes.c_int, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32, _i32,
+                                  _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.rk_select_decode.restype = ctypes.c_int
+
+
+def rk_select_plan(method: str, c: float, seq_len: int, head_dim: int) -> dict:
+    """Page, channels and attended pages of a selection method ('hsa', 'quest',
+    'sparq', 'exact') at total compression c."""
+    out = RkSelectPlan()
+    _check(_lib.rk_select_plan(RK_SEL[method], c, seq_len, head_dim, ctypes.byref(out)), "rk_select_plan")
+    return {f: getattr(out, f) for f, _ in RkSelectPlan._fields_}
+
+
+def rk_select_decode(method, q, k, v, kmax, kmin, n_tokens, page, channels, k2, out, sel=None, scores=None,
+                     ws=None, stream=None):
+    """One decode step of a selection method.  kmax/kmin: aux in pages of `page`
+    tokens (hsa, quest); the block-1 Kmax (sparq, kmin may be None); None (exact)."""
+    _need_contig(q, k, v, kmax, kmin, out, sel, scores)
+    B, Hq, d = q.shape
+    shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
+    ws = _ws(rk_hsa_workspace_bytes(shape, n_tokens, page, channels, k2), k, ws, stream)
+    _check(_lib.rk_select_decode(ctypes.byref(shape), RK_SEL[method], _ptr(q), _ptr(k), _ptr(v), k.shape[2],
+                                 _ptr(kmax), _ptr(kmin), kmax.shape[3] if kmax is not None else 0, n_tokens,
+                                 page, channels, k2, _ptr(out), _ptr(sel), _ptr(scores), _ptr(ws), ws.numel(),
+                                 _stream(stream)), "rk_select_decode")
     return ws
 
 

@@ -122,7 +122,9 @@ def test_error_codes_before_any_launch(rk):
     d96 = rk.shape_of(1, 8, 2, 96, rk.RK_F32)
     assert decode(shape=byref(d96)) == rk.RK_EUNSUPPORTED
     big = rk.shape_of(1, 8, 2, 64, rk.RK_F32)
-    assert decode(shape=byref(big), n=12289 * 16, cap=12289 * 16, nblk_cap=20000) == rk.RK_EUNSUPPORTED
+    # more pages than the decode path takes (2^22)
+    assert decode(shape=byref(big), n=(1 << 22) + 1, cap=(1 << 22) + 1, block=1,
+                  nblk_cap=(1 << 22) + 8) == rk.RK_EUNSUPPORTED
 
     def evict(**kw):
         a = dict(q=_vp(FAKE), k=_vp(FAKE), v=_vp(FAKE), cap=2048, S=2048, W=16, pool=7, keep=930,
@@ -221,3 +223,33 @@ def test_noalloc_refuses_oversized_call_before_the_device(rk):
                                    256, fake, None, None, None, None)
     assert st == rk.RK_EWORKSPACE
     assert b"static scratch" in lib.rk_last_error()
+
+
+@pytest.mark.parametrize("method", ["hsa", "quest", "sparq", "exact"])
+@pytest.mark.parametrize("c,S,d", [(16, 32768, 128), (109568 / 256, 109568, 128), (4, 4096, 64),
+                                   (1, 100, 64), (1000, 5000, 128)])
+def test_select_plan_matches_oracle(rk, method, c, S, d):
+    got = rk.rk_select_plan(method, c, S, d)
+    want = O.select_plan(method, c, S, d)
+    for key in ("page", "channels", "k2", "attn_tokens"):
+        assert got[key] == want[key], key
+    for key in ("budget_t", "est_pairs"):
+        assert got[key] == pytest.approx(want[key], rel=1e-12), key
+
+
+def test_select_decode_rejects_before_any_launch(rk):
+    lib = rk.raw_library()
+    sh = rk.shape_of(1, 8, 2, 64, rk.RK_BF16)
+    f = _vp(FAKE)
+
+    def call(method, page, channels, kmax=f):
+        return lib.rk_select_decode(ctypes.byref(sh), method, f, f, f, 4096, kmax, kmax, 4096, 4000, page,
+                                    channels, 64, f, None, None, f, 16, None)   # tiny workspace
+
+    assert call(1, 16, 32) == rk.RK_EINVAL          # Quest needs every channel
+    assert call(2, 4, 8) == rk.RK_EINVAL            # SparQ needs pages of one token
+    assert call(3, 1, 32) == rk.RK_EINVAL           # Exact needs every channel
+    assert call(3, 2, 64) == rk.RK_EINVAL           # and pages of one token
+    assert call(7, 1, 64) == rk.RK_EINVAL           # unknown method
+    assert call(3, 1, 64, kmax=None) == rk.RK_EWORKSPACE   # exact ignores the aux; workspace too small
+    assert lib.rk_select_plan(0, 0.5, 100, 64, None) == rk.RK_EINVAL
