@@ -65,6 +65,21 @@ __device__ __forceinline__ Vec16<T> load16(const T* p) {
   return v;
 }
 
+// Non-temporal forms, for data read once per launch (the chosen K/V rows of
+// a decode step, streamed keys): the load is marked as streaming, so it does
+// not displace data that is reused (page keys, aux rows of other units).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ Vec16<T> load16_nt(const T* p) {
+  Vec16<T> v;
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  v.raw = __builtin_bit_cast(decltype(v.raw), x);
+  return v;
+}
+__device__ __forceinline__ uint4 load_u4_nt(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
 template <typename T>
 __device__ __forceinline__ void unpack16(const Vec16<T>& v, float* out) {
 #pragma unroll
@@ -312,17 +327,22 @@ __device__ __forceinline__ void wave_topk_emit(const KeyFn& key, int n, uint32_t
   const int lane = lane_id();
   const unsigned long long below = (1ull << lane) - 1ull;
   int base = 0, eq_seen = 0;
-#pragma unroll 2
-  for (int c0 = 0; c0 < n; c0 += kWave) {
-    const int i = c0 + lane;
-    const uint32_t kk = i < n ? key(i) : 0u;
-    const bool eq = i < n && kk == T;
-    const unsigned long long em = ballot(eq);
-    const bool sel = (i < n && kk > T) || (eq && eq_seen + int(__popcll(em & below)) < need_eq);
-    const unsigned long long sm = ballot(sel);
-    if (sel) emit(base + __popcll(sm & below), i);
-    base += __popcll(sm);
-    eq_seen += __popcll(em);
+  // two rows of 64 per iteration, unrolled by hand (a row past n selects
+  // nothing): the ballots are convergent, so the compiler cannot unroll a
+  // loop of unknown trip count itself
+  for (int c0 = 0; c0 < n; c0 += 2 * kWave) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = c0 + h * kWave + lane;
+      const uint32_t kk = i < n ? key(i) : 0u;
+      const bool eq = i < n && kk == T;
+      const unsigned long long em = ballot(eq);
+      const bool sel = (i < n && kk > T) || (eq && eq_seen + int(__popcll(em & below)) < need_eq);
+      const unsigned long long sm = ballot(sel);
+      if (sel) emit(base + __popcll(sm & below), i);
+      base += __popcll(sm);
+      eq_seen += __popcll(em);
+    }
   }
 }
 

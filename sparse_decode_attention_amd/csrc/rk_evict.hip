@@ -758,7 +758,8 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
     for (int x = 0; x < LPT; ++x) {
       const int vidx = threadIdx.x + 256 * x;
       const int key = t0 + vidx / VPR;
-      pre[x] = key < ke ? reinterpret_cast<const uint4*>(ku + size_t(key) * D)[vidx % VPR]
+      // streamed once per pass: non-temporal (measured 8-15 % faster for pass 1)
+      pre[x] = key < ke ? load_u4_nt(reinterpret_cast<const uint4*>(ku + size_t(key) * D) + vidx % VPR)
                         : make_uint4(0u, 0u, 0u, 0u);
     }
   };
