@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=0,
                     help="layers per step (0: enough that other layers' decode traffic exceeds 2x MALL)")
     ap.add_argument("--no-graph", action="store_true", help="issue every call eagerly instead of graph replay")
+    ap.add_argument("--paged", type=int, default=0, metavar="P",
+                    help="decode from a paged pool of P-token physical pages (block tables, pages in random "
+                         "order; the compact cache is copied into it after eviction); not for RocketKV-MT")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--selection-recall", action="store_true",
@@ -97,11 +100,12 @@ class Layer:
 class Path:
     """Buffers and calls of R layers of a workload."""
 
-    def __init__(self, rk, WL, w, dev, n_layers):
+    def __init__(self, rk, WL, w, dev, n_layers, paged=0):
         import torch
 
         self.rk, self.w = rk, w
         self.mt = w.mt_turns > 0
+        self.paged = paged if not self.mt else 0
         self.S = w.seq + (w.mt_turns * w.mt_append if self.mt else 0)   # MT: the last turn
         sp = rk.rk_split(w.c, self.S, w.window, w.block, w.d)
         self.n_keep, self.k2 = sp["n_keep"], WL.stage2_pages(w, sp)
@@ -186,6 +190,14 @@ class Path:
                 L.vc = torch.empty_like(L.kc)
             L.kmax = torch.empty(B, Hkv, d, rk.aux_capacity(self.cap_c, w.block), dtype=w.torch_dtype, device=dev)
             L.kmin = torch.empty_like(L.kmax)
+            if self.paged:
+                per_seq = -(-self.cap_c // self.paged)
+                n_pages = B * per_seq
+                g = torch.Generator().manual_seed(77 + r)
+                L.table = torch.randperm(n_pages, generator=g).view(B, per_seq).to(torch.int32).to(dev)
+                L.kp = torch.empty(n_pages, Hkv, self.paged, d, dtype=w.torch_dtype, device=dev)
+                L.vp = torch.empty_like(L.kp)
+                L.pages = rk.paged_kv(L.table, n_pages, self.paged)
             L.out = torch.empty(self.steps, B, Hq, d, dtype=torch.float32, device=dev)
             self.layers.append(L)
 
@@ -200,6 +212,8 @@ class Path:
                 # the compaction builds Kmax/Kmin of the compact cache on the way
                 rk.rk_snapkv_evict(L.qw, L.k, L.v, self.S, w.window, w.pool, self.n_keep, L.kept, L.kc, L.vc,
                                    None, ws=self.ws_e, kmax=L.kmax, kmin=L.kmin, block=w.block)
+                if self.paged:
+                    rk.rk_paged_write_kv(L.kc, L.vc, 0, self.n_keep, L.kp, L.vp, L.pages, n_q_heads=w.n_q)
 
     def decode_part(self):
         rk, w = self.rk, self.w
@@ -208,6 +222,13 @@ class Path:
                 if self.mt:
                     rk.rk_hsa_decode_mt(L.qs[s], L.k, L.v, L.kept, self.n_keep, L.kmax, L.kmin, w.block, w.k1,
                                         self.k2, L.out[s], ws=self.ws_d)
+                elif self.paged and L.app is not None:
+                    rk.rk_paged_hsa_append_decode(L.qs[s], L.app[s][0], L.app[s][1], L.kp, L.vp, L.pages,
+                                                  self.n_keep + s, L.kmax, L.kmin, w.block, w.k1, self.k2,
+                                                  L.out[s], ws=self.ws_d)
+                elif self.paged:
+                    rk.rk_paged_hsa_decode(L.qs[s], L.kp, L.vp, L.pages, L.kmax, L.kmin, self.n_keep, w.block,
+                                           w.k1, self.k2, L.out[s], ws=self.ws_d)
                 elif L.app is not None:   # the step appends its token, then decodes (one call)
                     rk.rk_hsa_append_decode(L.qs[s], L.app[s][0], L.app[s][1], L.kc, L.vc, self.n_keep + s,
                                             L.kmax, L.kmin, w.block, w.k1, self.k2, L.out[s], ws=self.ws_d)
@@ -222,7 +243,7 @@ def measure(rk, WL, name, args, dev, with_cpu):
     import torch
 
     w = WL.WORKLOADS[name]
-    p = Path(rk, WL, w, dev, args.layers)
+    p = Path(rk, WL, w, dev, args.layers, getattr(args, "paged", 0))
     R = p.R
     log(f"workload {w.name}: {R} layers per step, S={p.S} n_keep={p.n_keep} k1={w.k1} k2={p.k2} "
         f"decode steps={p.steps}")
@@ -330,7 +351,8 @@ def measure(rk, WL, name, args, dev, with_cpu):
         "config": {"workload": w.name, "layers_timed": R, "batch": w.batch, "seq_len": p.S, "n_q_heads": w.n_q,
                    "n_kv_heads": w.n_kv, "head_dim": w.d, "kv_dtype": w.dtype, "compression": round(w.c, 3),
                    "n_keep": p.n_keep, "k1": w.k1, "k2_pages": p.k2, "page": w.block, "decode_steps": p.steps,
-                   "appends": w.appends, "rocketkv_mt": p.mt, "graph_replay": use_graph},
+                   "appends": w.appends, "rocketkv_mt": p.mt, "graph_replay": use_graph,
+                   "paged_tokens_per_page": p.paged or None},
     }
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(w, p, args.cpu_seconds)

@@ -7,7 +7,8 @@
  *   [RKV]   papercache.org deep notes "RocketKV: Accelerating Long-Context LLM
  *           Inference via Two-Stage KV Cache Compression" (arXiv 2502.14051).
  *   [GUIDE] aifetchly blog "RocketKV Guide: Two-Stage KV Cache Compression for
- *           LLMs", section "Stage 1: Coarse-Grain Permanent Eviction via SnapKV".
+ *           LLMs", section "Stage 1: Coarse-Grain Permanent Eviction via SnapKV"
+ *           (and, for the paged pool, its serving section).
  *
  * Conventions shared by every call:
  *   - Pointers named q*, k*, v*, kmax, kmin, out, *_idx, *_opt and ws are
@@ -283,6 +284,84 @@ rk_status rk_hsa_decode_noalloc(const rk_shape* shape, const void* q, const void
 
 /* Size of rk_hsa_decode_noalloc's static scratch in bytes (16 MiB). */
 size_t rk_hsa_decode_noalloc_max_bytes(void);
+
+/*
+ * Paged K/V pools.  The aifetchly guide's serving section ("Production
+ * Deployment", Step 1: building the engine) serves RocketKV from a paged KV
+ * cache of 64 tokens per block; here K and V of the whole batch live in one
+ * pool of physical pages and a block table maps each sequence's logical
+ * pages to them, so sequences grow a page at a time without reallocating or
+ * copying.  The HSA aux data (Kmax/Kmin) stays dense per unit, as for the
+ * contiguous cache (it is 2/block of the keys).
+ *
+ *   k_pool, v_pool [n_pages, Hkv, page_tokens, d]  bf16, one physical page
+ *                  holds page_tokens consecutive tokens of one sequence for
+ *                  every KV head
+ *   block_table    [B, table_stride] int32 (device): logical page j of
+ *                  sequence b is physical page block_table[b * table_stride
+ *                  + j]; token n of sequence b, KV head h is pool row
+ *                  (block_table[b, n / page_tokens] * Hkv + h) * page_tokens
+ *                  + n % page_tokens.  Entries are clamped into [0, n_pages)
+ *                  in-kernel (a bad entry gives wrong values, never an
+ *                  out-of-bounds access).  The caller owns page allocation.
+ * page_tokens is a power of two in [1, 32768]; n_pages * Hkv * page_tokens <
+ * 2^31; every sequence of a call has the same n_tokens (at most table_stride
+ * * page_tokens).  bf16 only (RK_EUNSUPPORTED otherwise).
+ */
+typedef struct {
+  const int32_t* block_table;
+  int64_t table_stride;
+  int64_t n_pages;
+  int32_t page_tokens;
+} rk_paged_kv;
+
+/*
+ * rk_paged_write_kv -- copy rows [first_token, first_token + n_tokens) of a
+ * contiguous cache k_src, v_src [B, Hkv, src_cap, d] (e.g. the compact cache
+ * rk_snapkv_evict writes) to the same token positions of the paged pool.
+ */
+rk_status rk_paged_write_kv(const rk_shape* shape, const void* k_src, const void* v_src,
+                           int64_t src_cap, int64_t first_token, int64_t n_tokens, void* k_pool,
+                           void* v_pool, const rk_paged_kv* pages, rk_stream stream);
+
+/*
+ * rk_paged_build_aux -- rk_hsa_build_aux over the keys of a paged pool
+ * (tokens 0..n_tokens-1 of every sequence; pages from first_token/block on
+ * are (re)built).  [RKV] method details, HSA step 1.
+ */
+rk_status rk_paged_build_aux(const rk_shape* shape, const void* k_pool, const rk_paged_kv* pages,
+                             int64_t n_tokens, int64_t first_token, int32_t block, void* kmax,
+                             void* kmin, int64_t nblk_cap, rk_stream stream);
+
+/*
+ * rk_paged_append_kv -- rk_append_kv into a paged pool: token `pos` of every
+ * sequence (its page must already be in the block table).
+ */
+rk_status rk_paged_append_kv(const rk_shape* shape, const void* k_new, const void* v_new,
+                             void* k_pool, void* v_pool, const rk_paged_kv* pages, int64_t pos,
+                             void* kmax, void* kmin, int64_t nblk_cap, int32_t block,
+                             rk_stream stream);
+
+/*
+ * rk_paged_hsa_decode / rk_paged_hsa_append_decode -- rk_hsa_decode and
+ * rk_hsa_append_decode over a paged pool: same selection and arithmetic (the
+ * results equal the contiguous calls on the same tokens bit for bit), the
+ * K/V rows addressed through the block table.  Workspace from
+ * rk_hsa_workspace_bytes.
+ */
+rk_status rk_paged_hsa_decode(const rk_shape* shape, const void* q, const void* k_pool,
+                              const void* v_pool, const rk_paged_kv* pages, const void* kmax,
+                              const void* kmin, int64_t nblk_cap, int64_t n_tokens, int32_t block,
+                              int32_t k1, int32_t k2, float* out, int32_t* sel_blocks_opt,
+                              int32_t* sel_channels_opt, float* block_scores_opt, void* ws,
+                              size_t ws_bytes, rk_stream stream);
+rk_status rk_paged_hsa_append_decode(const rk_shape* shape, const void* q, const void* k_new,
+                                     const void* v_new, void* k_pool, void* v_pool,
+                                     const rk_paged_kv* pages, int64_t pos, void* kmax, void* kmin,
+                                     int64_t nblk_cap, int32_t block, int32_t k1, int32_t k2,
+                                     float* out, int32_t* sel_blocks_opt, int32_t* sel_channels_opt,
+                                     float* block_scores_opt, void* ws, size_t ws_bytes,
+                                     rk_stream stream);
 
 /*
  * rk_hsa_decode_mt -- RocketKV-MT decode: HSA over a candidate subset of a

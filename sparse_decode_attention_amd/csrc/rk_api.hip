@@ -69,7 +69,7 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
                         int32_t block, int32_t k1, int32_t k2, float* out, int32_t* sel_opt,
                         int32_t* chan_opt, float* s1_opt, void* ws, size_t ws_bytes,
                         rk_stream stream, bool mt, const rk::AppendArgs* app = nullptr,
-                        bool exact_rows = false) {
+                        bool exact_rows = false, const rk::PagedArgs* paged = nullptr) {
   rk::Dims d;
   rk_status st = check_shape(shape, &d);
   if (st != RK_OK) return st;
@@ -84,7 +84,10 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
   if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
   if (n_tokens < 1) return fail(RK_EINVAL, "n_tokens must be >= 1");
   if (n_tokens > (int64_t(1) << 31) - 1) return fail(RK_EINVAL, "n_tokens too large");
-  if (mt) {
+  if (paged) {
+    if (n_tokens > (paged->table_stride << paged->shift))
+      return fail(RK_EINVAL, "n_tokens exceeds the pages of the block table row");
+  } else if (mt) {
     if (n_tokens > cand_stride) return fail(RK_EINVAL, "n_cand exceeds cand_stride");
     if (kv_cap < 1) return fail(RK_EINVAL, "kv_cap must be >= 1");
   } else if (n_tokens > kv_cap) {
@@ -106,8 +109,26 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
   return device_status(
       rk::launch_hsa_decode(d, q, k, v, kv_cap, mt ? cand : nullptr, cand_stride, kmax, kmin,
                             nblk_cap, n_tokens, block, k1, k2, out, sel_opt, chan_opt, s1_opt,
-                            ws, static_cast<hipStream_t>(stream), app, exact_rows),
+                            ws, static_cast<hipStream_t>(stream), app, exact_rows, paged),
       mt ? "rk_hsa_decode_mt launch" : app ? "rk_hsa_append_decode launch" : "rk_hsa_decode launch");
+}
+
+// Checks a paged-pool descriptor against the shape and converts it.
+rk_status check_paged(const rk_paged_kv* pk, const rk::Dims& d, rk::PagedArgs* out) {
+  if (!pk) return fail(RK_EINVAL, "paged descriptor is NULL");
+  if (!d.bf16) return fail(RK_EUNSUPPORTED, "paged pools are built for bf16");
+  if (!pk->block_table || (reinterpret_cast<uintptr_t>(pk->block_table) & 3u))
+    return fail(RK_EINVAL, "block_table is NULL or misaligned");
+  const int32_t P = pk->page_tokens;
+  if (P < 1 || P > (1 << 15) || (P & (P - 1)))
+    return fail(RK_EINVAL, "page_tokens must be a power of two in [1, 32768]");
+  if (pk->n_pages < 1 || pk->table_stride < 1) return fail(RK_EINVAL, "n_pages and table_stride must be >= 1");
+  if (pk->n_pages * int64_t(d.Hkv) * P > (int64_t(1) << 31) - 1)
+    return fail(RK_EUNSUPPORTED, "the pool holds 2^31 or more rows");
+  int shift = 0;
+  while ((1 << shift) < P) ++shift;
+  *out = rk::PagedArgs{pk->block_table, pk->table_stride, pk->n_pages, shift, d.Hkv};
+  return RK_OK;
 }
 
 // ---- static scratch of rk_hsa_decode_noalloc -----------------------------
@@ -428,6 +449,110 @@ rk_status rk_select_decode(const rk_shape* shape, rk_select_method method, const
   }
   return decode_common(shape, q, k, v, kv_cap, nullptr, 0, kmax, kmin, nblk_cap, n_tokens, page,
                        channels, k2, out, sel_opt, nullptr, scores_opt, ws, ws_bytes, stream, false);
+}
+
+rk_status rk_paged_write_kv(const rk_shape* shape, const void* k_src, const void* v_src,
+                           int64_t src_cap, int64_t first_token, int64_t n_tokens, void* k_pool,
+                           void* v_pool, const rk_paged_kv* pages, rk_stream stream) {
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  rk::PagedArgs pg;
+  if ((st = check_paged(pages, d, &pg)) != RK_OK) return st;
+  if (!k_src || !v_src || !k_pool || !v_pool) return fail(RK_EINVAL, "null tensor argument");
+  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_pool) || !aligned16(v_pool))
+    return fail(RK_EINVAL, "tensors must be 16-byte aligned");
+  if (first_token < 0 || n_tokens < 1 || first_token + n_tokens > src_cap)
+    return fail(RK_EINVAL, "rows [first_token, first_token + n_tokens) outside the source");
+  if (first_token + n_tokens > (pg.table_stride << pg.shift) || first_token + n_tokens > (int64_t(1) << 31) - 1)
+    return fail(RK_EINVAL, "rows beyond the pages of the block table row");
+  return device_status(rk::launch_paged_write(d, k_src, v_src, src_cap, first_token, n_tokens, k_pool,
+                                              v_pool, pg, static_cast<hipStream_t>(stream)),
+                       "rk_paged_write_kv launch");
+}
+
+rk_status rk_paged_build_aux(const rk_shape* shape, const void* k_pool, const rk_paged_kv* pages,
+                             int64_t n_tokens, int64_t first_token, int32_t block, void* kmax,
+                             void* kmin, int64_t nblk_cap, rk_stream stream) {
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  rk::PagedArgs pg;
+  if ((st = check_paged(pages, d, &pg)) != RK_OK) return st;
+  if (!k_pool || !kmax) return fail(RK_EINVAL, "null tensor argument");
+  if (!aligned16(k_pool) || !aligned16(kmax) || (kmin && !aligned16(kmin)))
+    return fail(RK_EINVAL, "k_pool, kmax and kmin must be 16-byte aligned");
+  if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
+  if (n_tokens < 1 || n_tokens > (pg.table_stride << pg.shift) || n_tokens > (int64_t(1) << 31) - 1)
+    return fail(RK_EINVAL, "n_tokens outside [1, pages of the block table row]");
+  if (first_token < 0 || first_token >= n_tokens)
+    return fail(RK_EINVAL, "first_token outside [0, n_tokens)");
+  const int64_t nblk = (n_tokens + block - 1) / block;
+  if (nblk > nblk_cap) return fail(RK_EINVAL, "pages (%lld) exceed nblk_cap", (long long)nblk);
+  if (nblk_cap % 8) return fail(RK_EINVAL, "nblk_cap must be a multiple of 8");
+  return device_status(rk::launch_build_aux(d, k_pool, 0, nullptr, 0, n_tokens, first_token / block, block,
+                                            kmax, kmin, nblk_cap, static_cast<hipStream_t>(stream), &pg),
+                       "rk_paged_build_aux launch");
+}
+
+rk_status rk_paged_append_kv(const rk_shape* shape, const void* k_new, const void* v_new,
+                             void* k_pool, void* v_pool, const rk_paged_kv* pages, int64_t pos,
+                             void* kmax, void* kmin, int64_t nblk_cap, int32_t block,
+                             rk_stream stream) {
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  rk::PagedArgs pg;
+  if ((st = check_paged(pages, d, &pg)) != RK_OK) return st;
+  if (!k_new || !v_new || !k_pool || !v_pool || !kmax || !kmin)
+    return fail(RK_EINVAL, "null tensor argument");
+  if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
+  if (pos < 0 || pos >= (pg.table_stride << pg.shift) || pos > (int64_t(1) << 31) - 2)
+    return fail(RK_EINVAL, "pos outside the pages of the block table row");
+  if (pos / block >= nblk_cap) return fail(RK_EINVAL, "page of pos beyond nblk_cap");
+  if (nblk_cap % 8) return fail(RK_EINVAL, "nblk_cap must be a multiple of 8");
+  return device_status(rk::launch_append_kv(d, k_new, v_new, k_pool, v_pool, 0, pos, kmax, kmin, nblk_cap,
+                                            block, static_cast<hipStream_t>(stream), &pg),
+                       "rk_paged_append_kv launch");
+}
+
+rk_status rk_paged_hsa_decode(const rk_shape* shape, const void* q, const void* k_pool,
+                              const void* v_pool, const rk_paged_kv* pages, const void* kmax,
+                              const void* kmin, int64_t nblk_cap, int64_t n_tokens, int32_t block,
+                              int32_t k1, int32_t k2, float* out, int32_t* sel_blocks_opt,
+                              int32_t* sel_channels_opt, float* block_scores_opt, void* ws,
+                              size_t ws_bytes, rk_stream stream) {
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  rk::PagedArgs pg;
+  if ((st = check_paged(pages, d, &pg)) != RK_OK) return st;
+  return decode_common(shape, q, k_pool, v_pool, 0, nullptr, 0, kmax, kmin, nblk_cap, n_tokens, block,
+                       k1, k2, out, sel_blocks_opt, sel_channels_opt, block_scores_opt, ws, ws_bytes,
+                       stream, false, nullptr, false, &pg);
+}
+
+rk_status rk_paged_hsa_append_decode(const rk_shape* shape, const void* q, const void* k_new,
+                                     const void* v_new, void* k_pool, void* v_pool,
+                                     const rk_paged_kv* pages, int64_t pos, void* kmax, void* kmin,
+                                     int64_t nblk_cap, int32_t block, int32_t k1, int32_t k2,
+                                     float* out, int32_t* sel_blocks_opt, int32_t* sel_channels_opt,
+                                     float* block_scores_opt, void* ws, size_t ws_bytes,
+                                     rk_stream stream) {
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  rk::PagedArgs pg;
+  if ((st = check_paged(pages, d, &pg)) != RK_OK) return st;
+  if (!k_new || !v_new) return fail(RK_EINVAL, "null tensor argument");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(RK_EINVAL, "k_new and v_new must be 16-byte aligned");
+  if (pos < 0 || pos >= (pg.table_stride << pg.shift))
+    return fail(RK_EINVAL, "pos outside the pages of the block table row");
+  const rk::AppendArgs app{k_new, v_new, k_pool, v_pool, kmax, kmin};
+  return decode_common(shape, q, k_pool, v_pool, 0, nullptr, 0, kmax, kmin, nblk_cap, pos + 1, block,
+                       k1, k2, out, sel_blocks_opt, sel_channels_opt, block_scores_opt, ws, ws_bytes,
+                       stream, false, &app, false, &pg);
 }
 
 rk_status rk_hsa_decode_mt(const rk_shape* shape, const void* q, const void* k, const void* v,

@@ -379,12 +379,23 @@ struct AttnShape {
   static_assert(kWave % LPR == 0, "row chunks must tile a wave");
 };
 
-template <typename T, int D, int G, bool MT, int TPS_ = AttnShape<T, D, G>::TPS>
+// One unit's view of a paged pool (PagedArgs, resolved for the unit).
+struct UnitPages {
+  const int32_t* table;
+  int64_t n_phys;
+  int shift, hkv, h;
+};
+
+// PAGED: ku / vu are the pool base (plus the lane's channel offset) and token
+// n of the unit is pool row paged_row(n); otherwise the unit's base, with
+// row n (or, MT, its candidate row cu[n]).
+template <typename T, int D, int G, bool MT, int TPS_ = AttnShape<T, D, G>::TPS, bool PAGED = false>
 __device__ __forceinline__ void attend_pages(
     const float (&qf)[G][Vec16<T>::N], const T* ku, const T* vu, const int32_t* cu,
     int64_t kv_cap, const int* pages, int e_begin, int e_end, int e_step, int block,
     int n_tokens, float scale_log2, float (&m)[G], float (&l)[G],
-    float (&o)[G][Vec16<T>::N]) {
+    float (&o)[G][Vec16<T>::N], UnitPages up = {}) {
+  static_assert(!(MT && PAGED), "candidate lists over a paged pool are not built");
   using S = AttnShape<T, D, G, TPS_>;
   constexpr int EPL = S::EPL, LPR = S::LPR, SLOTS = S::SLOTS, TPS = S::TPS, CHUNK = S::CHUNK;
   const int slot = lane_id() / LPR;
@@ -457,7 +468,10 @@ __device__ __forceinline__ void attend_pages(
       const int pr = tau / block;
       const int tok = tau < ntok ? pages[e_begin + pr * e_step] * block + (tau - pr * block) : n_tokens;
       ok[i] = tok < n_tokens;
-      rows[i] = ok[i] ? (MT ? clamp_row(cu[tok], kv_cap) : tok) : 0;
+      if constexpr (PAGED)
+        rows[i] = ok[i] ? paged_row(up.table, tok, up.n_phys, up.shift, up.hkv, up.h) : 0;
+      else
+        rows[i] = ok[i] ? (MT ? clamp_row(cu[tok], kv_cap) : tok) : 0;
     }
     step(rows, ok);
   }
@@ -532,13 +546,14 @@ __device__ __forceinline__ void merge_waves(int idx, const float* wm, const floa
 //
 // PRESEL: the pages were chosen by page_select_kernel (written to presel,
 // ascending, nsel per unit); the workgroup copies its split's run of them.
-template <typename T, int D, int G, bool MT, int TPS_ = AttnShape<T, D, G>::TPS, bool PRESEL = false>
+template <typename T, int D, int G, bool MT, int TPS_ = AttnShape<T, D, G>::TPS, bool PRESEL = false,
+          bool PAGED = false>
 __global__ __launch_bounds__(256) void hsa_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
     const int32_t* __restrict__ cand, int64_t cand_stride, const uint32_t* __restrict__ keys,
     int keys_pitch, int nblk, int nsel, int pages_per_split, int n_split, int units, int n_tokens,
     int block, float scale_log2, float* __restrict__ partials, int32_t* __restrict__ sel_opt,
-    const int32_t* __restrict__ presel) {
+    const int32_t* __restrict__ presel, PagedArgs pga) {
   using S = AttnShape<T, D, G>;
   constexpr int EPL = S::EPL, LPR = S::LPR;
   constexpr int NW = 4;
@@ -600,11 +615,15 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   __syncthreads();
   RK_PHASE(10);
 
-  const T* ku = k + size_t(u) * size_t(kv_cap) * D + c * EPL;
-  const T* vu = v + size_t(u) * size_t(kv_cap) * D + c * EPL;
+  const size_t ubase = PAGED ? 0 : size_t(u) * size_t(kv_cap) * D;
+  const T* ku = k + ubase + c * EPL;
+  const T* vu = v + ubase + c * EPL;
   const int32_t* cu = MT ? cand + size_t(u) * size_t(cand_stride) : nullptr;
-  attend_pages<T, D, G, MT, TPS_>(qf, ku, vu, cu, kv_cap, pages, wave, np, NW, block, n_tokens,
-                            scale_log2, m, l, o);
+  const UnitPages up = PAGED ? UnitPages{pga.table + size_t(u / pga.hkv) * pga.table_stride, pga.n_phys,
+                                         pga.shift, pga.hkv, u % pga.hkv}
+                             : UnitPages{};
+  attend_pages<T, D, G, MT, TPS_, PAGED>(qf, ku, vu, cu, kv_cap, pages, wave, np, NW, block, n_tokens,
+                                         scale_log2, m, l, o, up);
   wave_state_to_lds<T, D, G>(m, l, o, wave, wm, wl, wo);
   __syncthreads();
   RK_PHASE(11);
@@ -656,14 +675,17 @@ struct AppendPtrs {
 template <typename T, bool APP>
 using CacheIn = std::conditional_t<APP, const T*, const T* __restrict__>;
 
-template <typename T, int D, int G, bool MT, bool APP = false>
+//
+// PAGED: the K/V rows live in a paged pool (PagedArgs); the append writes its
+// row there too.
+template <typename T, int D, int G, bool MT, bool APP = false, bool PAGED = false>
 __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
     const T* __restrict__ q, CacheIn<T, APP> k, CacheIn<T, APP> v, int64_t kv_cap,
     const int32_t* __restrict__ cand, int64_t cand_stride, CacheIn<T, APP> kmax,
     CacheIn<T, APP> kmin, int64_t nblk_cap, int nblk, int k1, int nsel, int npc,
     int n_tokens, int block, float scale_log2, float* __restrict__ out,
     int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt,
-    AppendPtrs<T> app) {
+    AppendPtrs<T> app, PagedArgs pga) {
   constexpr int TPS = AttnShape<T, D, G>::TPS;
   using S = AttnShape<T, D, G, TPS>;
   constexpr int EPL = S::EPL, LPR = S::LPR;
@@ -692,6 +714,15 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   for (int g = 0; g < G; ++g) unpack16(load16(q + (size_t(u) * G + g) * D + c * EPL), qf[g]);
   const int n_cached = APP ? n_tokens - 1 : n_tokens;  // tokens read from the cache
   const int app_page = (n_tokens - 1) / block;
+  const UnitPages up = PAGED ? UnitPages{pga.table + size_t(u / pga.hkv) * pga.table_stride, pga.n_phys,
+                                         pga.shift, pga.hkv, u % pga.hkv}
+                             : UnitPages{};
+  // first element of the appended token's row (APP only: row n_cached exists
+  // only when a token is appended)
+  size_t app_row = 0;
+  if constexpr (APP)
+    app_row = PAGED ? size_t(paged_row(up.table, n_cached, up.n_phys, up.shift, up.hkv, up.h)) * D
+                    : (size_t(u) * size_t(kv_cap) + size_t(n_cached)) * D;
   // APP: the new key (as T, for the patch) and the new K/V rows (as float,
   // for the attention) go to LDS; the page's old Kmax/Kmin column is fetched
   // now and folded and written back at the end, off every critical path.
@@ -711,8 +742,8 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
         app_ox = app.kmax[a];
         app_on = app.kmin[a];
       }
-      app.k[(size_t(u) * size_t(kv_cap) + size_t(n_cached)) * D + ta] = app_kn;
-      app.v[(size_t(u) * size_t(kv_cap) + size_t(n_cached)) * D + ta] = app_vn;
+      app.k[app_row + ta] = app_kn;
+      app.v[app_row + ta] = app_vn;
     }
   }
   if (wave == 0) {
@@ -779,11 +810,12 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
   }
-  const T* ku = k + size_t(u) * size_t(kv_cap) * D + c * EPL;
-  const T* vu = v + size_t(u) * size_t(kv_cap) * D + c * EPL;
+  const size_t ubase = PAGED ? 0 : size_t(u) * size_t(kv_cap) * D;
+  const T* ku = k + ubase + c * EPL;
+  const T* vu = v + ubase + c * EPL;
   const int32_t* cu = MT ? cand + size_t(u) * size_t(cand_stride) : nullptr;
-  attend_pages<T, D, G, MT, TPS>(qf, ku, vu, cu, kv_cap, pages, wave, nsel, NW, block, n_cached,
-                                 scale_log2, m, l, o);
+  attend_pages<T, D, G, MT, TPS, PAGED>(qf, ku, vu, cu, kv_cap, pages, wave, nsel, NW, block, n_cached,
+                                        scale_log2, m, l, o, up);
   if constexpr (APP) {
     // the new token, when its page was chosen (the last page, so the last
     // entry of the ascending list), goes to wave 0's token slot 0
@@ -906,9 +938,14 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
                            const void* kmax, const void* kmin, int64_t nblk_cap,
                            int64_t n_tokens, int block, int k1, int k2, float* out,
                            int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                           hipStream_t s, const AppendArgs* app, bool exact_rows) {
+                           hipStream_t s, const AppendArgs* app, bool exact_rows,
+                           const PagedArgs* paged) {
   const int nblk = int((n_tokens + block - 1) / block);
   const DecodeWs lay = decode_ws_layout(d, nblk, k2);
+  // paged pools are built for bf16 only (the API refuses the rest)
+  constexpr bool kPagedBuilt = std::is_same_v<T, bf16_t>;
+  if (paged && !kPagedBuilt) return hipErrorInvalidValue;
+  const PagedArgs pg = paged ? *paged : PagedArgs{};
   char* wsb = static_cast<char*>(ws);
   float* part = reinterpret_cast<float*>(wsb + lay.partials);
   const int units = d.units();
@@ -936,7 +973,9 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
       if (!fattr) {
         for (const void* f : {reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, true>),
                               reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false>),
-                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, true>)}) {
+                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, true>),
+                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, false, kPagedBuilt>),
+                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, true, kPagedBuilt>)}) {
           hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                              int(kFusedLdsBudget));
           if (e != hipSuccess) return e;
@@ -948,24 +987,23 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
                               static_cast<T*>(app->k), static_cast<T*>(app->v),
                               static_cast<T*>(app->kmax), static_cast<T*>(app->kmin)}
               : AppendPtrs<T>{};
+#define RK_FUSED(NAME, MTV, APPV, PGV)                                                            \
+  RK_LAUNCH(NAME, (hsa_fused_kernel<T, D, G, MTV, APPV, PGV>), dim3(units), dim3(kFusedThreads), lds, \
+            s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), kv_cap, \
+            cand, cand_stride, static_cast<const T*>(kmax), static_cast<const T*>(kmin), nblk_cap,  \
+            nblk, k1, lay.nsel, npc, int(n_tokens), block, scale_log2, out, sel_opt, chan_opt,      \
+            s1_opt, ap, pg)
       if (cand)
-        RK_LAUNCH("hsa_fused_mt", (hsa_fused_kernel<T, D, G, true>), dim3(units), dim3(kFusedThreads), lds,
-                  s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                  kv_cap, cand, cand_stride, static_cast<const T*>(kmax),
-                  static_cast<const T*>(kmin), nblk_cap, nblk, k1, lay.nsel, npc, int(n_tokens),
-                  block, scale_log2, out, sel_opt, chan_opt, s1_opt, ap);
+        RK_FUSED("hsa_fused_mt", true, false, false);
+      else if (paged && app)
+        RK_FUSED("hsa_fused_append", false, true, kPagedBuilt);
+      else if (paged)
+        RK_FUSED("hsa_fused", false, false, kPagedBuilt);
       else if (app)
-        RK_LAUNCH("hsa_fused_append", (hsa_fused_kernel<T, D, G, false, true>), dim3(units),
-                  dim3(kFusedThreads), lds, s, static_cast<const T*>(q), static_cast<const T*>(k),
-                  static_cast<const T*>(v), kv_cap, cand, cand_stride, static_cast<const T*>(kmax),
-                  static_cast<const T*>(kmin), nblk_cap, nblk, k1, lay.nsel, npc, int(n_tokens),
-                  block, scale_log2, out, sel_opt, chan_opt, s1_opt, ap);
+        RK_FUSED("hsa_fused_append", false, true, false);
       else
-        RK_LAUNCH("hsa_fused", (hsa_fused_kernel<T, D, G, false>), dim3(units), dim3(kFusedThreads), lds,
-                  s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                  kv_cap, cand, cand_stride, static_cast<const T*>(kmax),
-                  static_cast<const T*>(kmin), nblk_cap, nblk, k1, lay.nsel, npc, int(n_tokens),
-                  block, scale_log2, out, sel_opt, chan_opt, s1_opt, ap);
+        RK_FUSED("hsa_fused", false, false, false);
+#undef RK_FUSED
       return hipGetLastError();
     }
   }
@@ -973,7 +1011,8 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   // the split-K path appends with its own launch first
   if (app) {
     const hipError_t e = launch_append_kv(d, app->k_new, app->v_new, app->k, app->v, kv_cap,
-                                          n_tokens - 1, app->kmax, app->kmin, nblk_cap, block, s);
+                                          n_tokens - 1, app->kmax, app->kmin, nblk_cap, block, s,
+                                          paged);
     if (e != hipSuccess) return e;
   }
 
@@ -1084,12 +1123,33 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   // at most one workgroup per CU: registers cannot limit occupancy, so each
   // wave takes 4 tokens per slot per step (fewer dependent load rounds)
   const bool one_per_cu = attn_wgs <= kComputeUnits;
-#define RK_ATTN(NAME, MTV, TPSV, PRE)                                                             \
-  RK_LAUNCH(NAME, (hsa_attn_kernel<T, D, G, MTV, TPSV, PRE>), dim3(attn_wgs), dim3(256), attn_lds, \
-            s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),      \
-            kv_cap, cand, cand_stride, keys, lay.keys_pitch, nblk, lay.nsel, pps, n_split, units, \
-            int(n_tokens), block, scale_log2, part, sel_opt, presel_pages)
-  if (presel) {
+#define RK_ATTN_P(NAME, MTV, TPSV, PRE, PGV)                                                      \
+  RK_LAUNCH(NAME, (hsa_attn_kernel<T, D, G, MTV, TPSV, PRE, PGV>), dim3(attn_wgs), dim3(256),     \
+            attn_lds, s, static_cast<const T*>(q), static_cast<const T*>(k),                      \
+            static_cast<const T*>(v), kv_cap, cand, cand_stride, keys, lay.keys_pitch, nblk,       \
+            lay.nsel, pps, n_split, units, int(n_tokens), block, scale_log2, part, sel_opt,        \
+            presel_pages, pg)
+#define RK_ATTN(NAME, MTV, TPSV, PRE) RK_ATTN_P(NAME, MTV, TPSV, PRE, false)
+  if (paged) {
+    static bool pg_attr_set = false;  // once per template instantiation
+    if (!pg_attr_set) {
+      for (const void* f :
+           {reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, false, AttnShape<T, D, G>::TPS, false, kPagedBuilt>),
+            reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, false, 4, false, kPagedBuilt>),
+            reinterpret_cast<const void*>(&hsa_attn_kernel<T, D, G, false, AttnShape<T, D, G>::TPS, true, kPagedBuilt>)}) {
+        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           int(kAttnDynLds));
+        if (e != hipSuccess) return e;
+      }
+      pg_attr_set = true;
+    }
+    if (presel)
+      RK_ATTN_P("hsa_attn", false, (AttnShape<T, D, G>::TPS), true, kPagedBuilt);
+    else if (one_per_cu)
+      RK_ATTN_P("hsa_attn", false, 4, false, kPagedBuilt);
+    else
+      RK_ATTN_P("hsa_attn", false, (AttnShape<T, D, G>::TPS), false, kPagedBuilt);
+  } else if (presel) {
     static bool pre_attr_set = false;  // once per template instantiation
     if (!pre_attr_set) {
       for (const void* f :
@@ -1117,6 +1177,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
       RK_ATTN("hsa_attn", false, (AttnShape<T, D, G>::TPS), false);
   }
 #undef RK_ATTN
+#undef RK_ATTN_P
   if ((err = hipGetLastError()) != hipSuccess) return err;
   RK_LAUNCH("hsa_combine", (hsa_combine_kernel<D, G>), dim3((units * G + 3) / 4), dim3(256), 0, s,
             part, n_split, units, out);
@@ -1129,12 +1190,13 @@ hipError_t launch_decode_d(const Dims& d, const void* q, const void* k, const vo
                            const void* kmax, const void* kmin, int64_t nblk_cap,
                            int64_t n_tokens, int block, int k1, int k2, float* out,
                            int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                           hipStream_t s, const AppendArgs* app, bool exact_rows) {
+                           hipStream_t s, const AppendArgs* app, bool exact_rows,
+                           const PagedArgs* paged) {
 #define RK_DECODE_G(GG)                                                                        \
   case GG:                                                                                     \
     return launch_decode_t<T, D, GG>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,       \
                                      nblk_cap, n_tokens, block, k1, k2, out, sel_opt,         \
-                                     chan_opt, s1_opt, ws, s, app, exact_rows);
+                                     chan_opt, s1_opt, ws, s, app, exact_rows, paged);
   switch (d.G) {
     RK_DECODE_G(1)
     RK_DECODE_G(2)
@@ -1153,23 +1215,24 @@ hipError_t launch_hsa_decode(const Dims& d, const void* q, const void* k, const 
                              const void* kmax, const void* kmin, int64_t nblk_cap,
                              int64_t n_tokens, int block, int k1, int k2, float* out,
                              int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
-                             hipStream_t s, const AppendArgs* app, bool exact_rows) {
+                             hipStream_t s, const AppendArgs* app, bool exact_rows,
+                             const PagedArgs* paged) {
   if (d.bf16) {
     if (d.D == 128)
       return launch_decode_d<bf16_t, 128>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                           nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                          chan_opt, s1_opt, ws, s, app, exact_rows);
+                                          chan_opt, s1_opt, ws, s, app, exact_rows, paged);
     return launch_decode_d<bf16_t, 64>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                        nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                       chan_opt, s1_opt, ws, s, app, exact_rows);
+                                       chan_opt, s1_opt, ws, s, app, exact_rows, paged);
   }
   if (d.D == 128)
     return launch_decode_d<float, 128>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                        nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                       chan_opt, s1_opt, ws, s, app, exact_rows);
+                                       chan_opt, s1_opt, ws, s, app, exact_rows, paged);
   return launch_decode_d<float, 64>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                     nblk_cap, n_tokens, block, k1, k2, out, sel_opt, chan_opt,
-                                    s1_opt, ws, s, app, exact_rows);
+                                    s1_opt, ws, s, app, exact_rows, paged);
 }
 
 }  // namespace rk

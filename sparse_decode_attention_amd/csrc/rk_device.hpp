@@ -100,6 +100,14 @@ __device__ __forceinline__ int clamp_row(int32_t row, int64_t cap) {
   return uint64_t(uint32_t(row)) < uint64_t(cap) ? row : 0;
 }
 
+// Pool row of token `tok` of one unit in a paged K/V pool (see PagedArgs):
+// `table` is the unit's sequence row of the block table, `h` its head.
+__device__ __forceinline__ int paged_row(const int32_t* table, int tok, int64_t n_phys, int shift,
+                                         int hkv, int h) {
+  const int pg = clamp_row(table[tok >> shift], n_phys);
+  return ((pg * hkv + h) << shift) + (tok & ((1 << shift) - 1));
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Lanes of the wave where b holds, straight from the compare (no bool -> int

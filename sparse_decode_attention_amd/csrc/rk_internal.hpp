@@ -107,15 +107,34 @@ void prof_after(hipStream_t s);
     if (rk_prof_on_) ::rk::prof_after(stream);                      \
   } while (0)
 
+// Paged K/V: a pool of physical pages [n_phys, Hkv, P, D] (P = 1 << shift
+// tokens) shared by the batch; token n of sequence b, head h lives at pool
+// row (table[b * table_stride + n / P] * Hkv + h) * P + n % P.  Page numbers
+// are clamped into [0, n_phys) in-kernel.
+struct PagedArgs {
+  const int32_t* table;
+  int64_t table_stride;
+  int64_t n_phys;
+  int shift;
+  int hkv;
+};
+
 // ---- launchers ----
 hipError_t launch_build_aux(const Dims& d, const void* k, int64_t k_cap, const int32_t* idx,
                             int64_t idx_stride, int64_t n_tokens, int64_t first_block,
                             int block, void* kmax, void* kmin, int64_t nblk_cap,
-                            hipStream_t s);
+                            hipStream_t s, const PagedArgs* paged = nullptr);
 
 hipError_t launch_append_kv(const Dims& d, const void* k_new, const void* v_new, void* k, void* v,
                             int64_t kv_cap, int64_t pos, void* kmax, void* kmin,
-                            int64_t nblk_cap, int block, hipStream_t s);
+                            int64_t nblk_cap, int block, hipStream_t s,
+                            const PagedArgs* paged = nullptr);
+
+// Rows [first, first + n) of a dense [B, Hkv, src_cap, D] cache written to
+// the same token positions of a paged pool (bf16).
+hipError_t launch_paged_write(const Dims& d, const void* k_src, const void* v_src, int64_t src_cap,
+                              int64_t first, int64_t n, void* k_pool, void* v_pool,
+                              const PagedArgs& paged, hipStream_t s);
 
 // A decode step that first appends token n_tokens - 1 (rk_append_kv's
 // effect): the new rows and the buffers it writes.
@@ -137,7 +156,7 @@ hipError_t launch_hsa_decode(const Dims& d, const void* q, const void* k, const 
                              int64_t n_tokens, int block, int k1, int k2, float* out,
                              int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
                              hipStream_t s, const AppendArgs* app = nullptr,
-                             bool exact_rows = false);
+                             bool exact_rows = false, const PagedArgs* paged = nullptr);
 
 hipError_t launch_snapkv_evict(const Dims& d, const void* q_win, const void* k, const void* v,
                                int64_t kv_cap, int64_t S, int W, int pool_kernel,

@@ -288,6 +288,90 @@ def rk_select_decode(method, q, k, v, kmax, kmin, n_tokens, page, channels, k2, 
     return ws
 
 
+class RkPagedKv(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("table_stride", ctypes.c_int64), ("n_pages", ctypes.c_int64),
+                ("page_tokens", ctypes.c_int32)]
+
+
+_PP = ctypes.POINTER(RkPagedKv)
+_lib.rk_paged_write_kv.argtypes = [_SP, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _PP, _vp]
+_lib.rk_paged_build_aux.argtypes = [_SP, _vp, _PP, _i64, _i64, _i32, _vp, _vp, _i64, _vp]
+_lib.rk_paged_append_kv.argtypes = [_SP, _vp, _vp, _vp, _vp, _PP, _i64, _vp, _vp, _i64, _i32, _vp]
+_lib.rk_paged_hsa_decode.argtypes = [_SP, _vp, _vp, _vp, _PP, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp, _vp,
+                                     _vp, _vp, _vp, _sz, _vp]
+_lib.rk_paged_hsa_append_decode.argtypes = [_SP, _vp, _vp, _vp, _vp, _vp, _PP, _i64, _vp, _vp, _i64, _i32, _i32,
+                                            _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+for _f in ("rk_paged_write_kv", "rk_paged_build_aux", "rk_paged_append_kv", "rk_paged_hsa_decode",
+           "rk_paged_hsa_append_decode"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+def paged_kv(block_table, n_pages: int, page_tokens: int) -> RkPagedKv:
+    """Descriptor of a paged pool: block_table [B, stride] int32 on the device."""
+    _need_contig(block_table)
+    return RkPagedKv(block_table.data_ptr(), block_table.shape[1], n_pages, page_tokens)
+
+
+def rk_paged_write_kv(k_src, v_src, first_token, n_tokens, k_pool, v_pool, pages: RkPagedKv, n_q_heads=None,
+                      stream=None):
+    """Copy rows [first, first + n) of k_src, v_src [B,Hkv,cap,d] into the paged pool."""
+    _need_contig(k_src, v_src, k_pool, v_pool)
+    B, Hkv, cap, d = k_src.shape
+    shape = shape_of(B, n_q_heads or Hkv, Hkv, d, _dtype_code(k_src))
+    _check(_lib.rk_paged_write_kv(ctypes.byref(shape), _ptr(k_src), _ptr(v_src), cap, first_token, n_tokens,
+                                  _ptr(k_pool), _ptr(v_pool), ctypes.byref(pages), _stream(stream)),
+           "rk_paged_write_kv")
+
+
+def rk_paged_build_aux(k_pool, pages: RkPagedKv, batch, n_tokens, first_token, block, kmax, kmin,
+                       n_q_heads=None, stream=None):
+    """HSA step 1 over a paged pool k_pool [n_pages,Hkv,P,d]; kmax, kmin [B,Hkv,d,nblk_cap]."""
+    _need_contig(k_pool, kmax, kmin)
+    _, Hkv, _, d = k_pool.shape
+    shape = shape_of(batch, n_q_heads or Hkv, Hkv, d, _dtype_code(k_pool))
+    _check(_lib.rk_paged_build_aux(ctypes.byref(shape), _ptr(k_pool), ctypes.byref(pages), n_tokens, first_token,
+                                   block, _ptr(kmax), _ptr(kmin), kmax.shape[3], _stream(stream)),
+           "rk_paged_build_aux")
+
+
+def rk_paged_append_kv(k_new, v_new, k_pool, v_pool, pages: RkPagedKv, pos, kmax, kmin, block, n_q_heads=None,
+                       stream=None):
+    _need_contig(k_new, v_new, k_pool, v_pool, kmax, kmin)
+    B, Hkv, d = k_new.shape
+    shape = shape_of(B, n_q_heads or Hkv, Hkv, d, _dtype_code(k_new))
+    _check(_lib.rk_paged_append_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                   ctypes.byref(pages), pos, _ptr(kmax), _ptr(kmin), kmax.shape[3], block,
+                                   _stream(stream)), "rk_paged_append_kv")
+
+
+def rk_paged_hsa_decode(q, k_pool, v_pool, pages: RkPagedKv, kmax, kmin, n_tokens, block, k1, k2, out,
+                        sel_blocks=None, sel_channels=None, block_scores=None, ws=None, stream=None):
+    _need_contig(q, k_pool, v_pool, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    B, Hq, d = q.shape
+    shape = shape_of(B, Hq, k_pool.shape[1], d, _dtype_code(k_pool))
+    ws = _ws(rk_hsa_workspace_bytes(shape, n_tokens, block, k1, k2), k_pool, ws, stream)
+    _check(_lib.rk_paged_hsa_decode(ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(v_pool), ctypes.byref(pages),
+                                    _ptr(kmax), _ptr(kmin), kmax.shape[3], n_tokens, block, k1, k2, _ptr(out),
+                                    _ptr(sel_blocks), _ptr(sel_channels), _ptr(block_scores), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "rk_paged_hsa_decode")
+    return ws
+
+
+def rk_paged_hsa_append_decode(q, k_new, v_new, k_pool, v_pool, pages: RkPagedKv, pos, kmax, kmin, block, k1,
+                               k2, out, sel_blocks=None, sel_channels=None, block_scores=None, ws=None,
+                               stream=None):
+    _need_contig(q, k_new, v_new, k_pool, v_pool, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    B, Hq, d = q.shape
+    shape = shape_of(B, Hq, k_pool.shape[1], d, _dtype_code(k_pool))
+    ws = _ws(rk_hsa_workspace_bytes(shape, pos + 1, block, k1, k2), k_pool, ws, stream)
+    _check(_lib.rk_paged_hsa_append_decode(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                           _ptr(v_pool), ctypes.byref(pages), pos, _ptr(kmax), _ptr(kmin),
+                                           kmax.shape[3], block, k1, k2, _ptr(out), _ptr(sel_blocks),
+                                           _ptr(sel_channels), _ptr(block_scores), _ptr(ws), ws.numel(),
+                                           _stream(stream)), "rk_paged_hsa_append_decode")
+    return ws
+
+
 def aux_capacity(n_tokens: int, block: int) -> int:
     """Smallest valid nblk_cap for n_tokens: the page count rounded up to 8."""
     return (-(-n_tokens // block) + 7) // 8 * 8

@@ -253,3 +253,27 @@ def test_select_decode_rejects_before_any_launch(rk):
     assert call(7, 1, 64) == rk.RK_EINVAL           # unknown method
     assert call(3, 1, 64, kmax=None) == rk.RK_EWORKSPACE   # exact ignores the aux; workspace too small
     assert lib.rk_select_plan(0, 0.5, 100, 64, None) == rk.RK_EINVAL
+
+
+def test_paged_descriptor_checked_before_any_launch(rk):
+    lib = rk.raw_library()
+    sh = rk.shape_of(1, 8, 2, 128, rk.RK_BF16)
+    f = _vp(FAKE)
+
+    def dec(P=64, n_pages=16, stride=4, table=FAKE, shape=sh, n=200):
+        pk = rk.RkPagedKv(table, stride, n_pages, P)
+        return lib.rk_paged_hsa_decode(ctypes.byref(shape), f, f, f, ctypes.byref(pk), f, f, 16, n, 16, 16, 8, f,
+                                       None, None, None, f, 16, None)
+
+    assert dec() == rk.RK_EWORKSPACE                  # descriptor fine, workspace too small
+    assert dec(P=48) == rk.RK_EINVAL                  # not a power of two
+    assert dec(P=0) == rk.RK_EINVAL
+    assert dec(table=None) == rk.RK_EINVAL
+    assert dec(table=FAKE + 2) == rk.RK_EINVAL        # misaligned table
+    assert dec(n=257) == rk.RK_EINVAL                 # beyond the 4 pages of 64 of the table row
+    assert dec(n_pages=0) == rk.RK_EINVAL
+    assert dec(n_pages=1 << 26) == rk.RK_EUNSUPPORTED  # 2^31 pool rows or more
+    f32 = rk.shape_of(1, 8, 2, 128, rk.RK_F32)
+    assert dec(shape=f32) == rk.RK_EUNSUPPORTED        # bf16 only
+    assert lib.rk_paged_hsa_decode(ctypes.byref(sh), f, f, f, None, f, f, 16, 200, 16, 16, 8, f, None, None,
+                                   None, f, 1 << 20, None) == rk.RK_EINVAL
