@@ -9,4 +9,4 @@ from .rocketkv_oracle import (attention, block_scores, block_select, build_aux,
                               snapkv_select, split, table1_storage_traffic,
                               topk_lower_index, window_scores, SELECT_METHODS, select_plan,
                               exact_topk_scores, quest_page_scores, sparq_channels, sparq_scores,
-                              select_decode_unit)
+                              select_decode_unit, adakv_select, adakv_evict)

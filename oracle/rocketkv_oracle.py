@@ -45,8 +45,10 @@ Readings where the pages are silent or ambiguous:
   R15 the approximate block score is sum over i in i1 of q_bar_i * P_i[b].
   R16 no block is forced into the selection.
   R17 RocketKV-MT builds blocks over the sorted candidate list.
-  R23-R26 (the Exact-TopK, Quest and SparQ baselines and their budgets) are
-      stated with their functions at the end of this module.
+  R23-R26 (the Exact-TopK, Quest and SparQ baselines and their budgets) and
+      R27 (Ada-KV's shared budget; parity unpinned against the pages, which
+      name Ada-KV but not its rule) are stated with their functions at the
+      end of this module.
 """
 
 from __future__ import annotations
@@ -559,3 +561,59 @@ def select_decode_unit(method: str, q_group, kc, vc, n_tokens: int, page: int, c
     toks = selected_tokens(use, n_tokens, page)
     out = attention(q_group, kc[toks], vc[toks])
     return dict(scores=s, sel=sel, tokens=toks, out=out)
+
+
+# --------------------------------------------------------------------------
+# Ada-KV adaptive per-head budgets in stage 1
+# --------------------------------------------------------------------------
+# [RKV] method details ("the second stage and the framework's generality":
+# SnapKV or Ada-KV can serve as stage 1; GQA group-level selection follows
+# Ada-KV).  The notes name Ada-KV's adaptive budget allocation but not its
+# rule.  Reading R27: the budget of a sequence in a layer is shared by its
+# KV heads (groups) instead of being fixed per head: the Hkv * (n_keep - W)
+# prefix slots go to the largest pooled group scores over all of the
+# sequence's heads taken together (flattened [head, position], ties to the
+# lower head, then the lower position), so a head whose group attends to few
+# tokens keeps few and a head whose attention is spread keeps more; each head
+# also keeps its W window tokens.  The scores are comparable across heads:
+# every window row of every group is one softmax (total mass G * W per head).
+# The rule itself is parity-unpinned against the pages; the pins fix its
+# internal consistency (equal heads reduce to per-head SnapKV, the budget is
+# conserved, brute force on tiny inputs).
+def adakv_select(pooled_heads: np.ndarray, seq_len: int, window: int, n_keep: int) -> list:
+    """Kept positions of each KV head of one sequence under the shared budget
+    (reading R27).  pooled_heads [Hkv, S-W] (pooled group scores).  Returns a
+    list of Hkv int64 arrays: the head's chosen prefix positions ascending,
+    then the W window positions [S-W, S)."""
+    pooled_heads = np.asarray(pooled_heads)
+    Hkv, P = pooled_heads.shape
+    if P != seq_len - window or not (window <= n_keep <= seq_len):
+        raise ValueError("bad sizes")
+    flat = pooled_heads.reshape(-1)           # index h * P + j: (head, position) order
+    chosen = topk_lower_index(flat, Hkv * (n_keep - window))
+    out = []
+    for h in range(Hkv):
+        mine = chosen[(chosen >= h * P) & (chosen < (h + 1) * P)] - h * P
+        out.append(np.concatenate([np.sort(mine), np.arange(seq_len - window, seq_len)]).astype(np.int64))
+    return out
+
+
+def adakv_evict(q_win: np.ndarray, k: np.ndarray, window: int, pool_kernel: int, n_keep: int) -> dict:
+    """Stage 1 with Ada-KV budgets for a whole [B, H_kv] cache: window scores
+    and pooling per head as SnapKV (R5-R10), then adakv_select per sequence.
+    Returns kept (list per batch of per-head arrays), counts [B, H_kv] and
+    pooled [B, H_kv, S-W]."""
+    q_win = np.asarray(q_win, dtype=F32)
+    k = np.asarray(k, dtype=F32)
+    B, Hq, W, d = q_win.shape
+    _, Hkv, S, _ = k.shape
+    G = Hq // Hkv
+    pooled = np.zeros((B, Hkv, S - W), F32)
+    kept, counts = [], np.zeros((B, Hkv), np.int64)
+    for b in range(B):
+        for h in range(Hkv):
+            pooled[b, h] = pool_sum(window_scores(q_win[b, h * G:(h + 1) * G], k[b, h]), pool_kernel)
+        kb = adakv_select(pooled[b], S, W, n_keep)
+        kept.append(kb)
+        counts[b] = [len(x) for x in kb]
+    return dict(kept=kept, counts=counts, pooled=pooled)
