@@ -400,12 +400,22 @@ def selection_recall(args):
         methods.append(("rocketkv", dict(page=sp["paper_page"], channels=sp["paper_k1_channels"],
                                          k2=sp["paper_k2_blocks"], n_keep=sp["n_keep"])))
         methods.append(("rocketkv-w", dict(page=w.block, channels=w.k1, k2=sp["k2_blocks"], n_keep=sp["n_keep"])))
+        methods.append(("rocketkv-ada", dict(page=sp["paper_page"], channels=sp["paper_k1_channels"],
+                                             k2=sp["paper_k2_blocks"], n_keep=sp["n_keep"])))
         for m, p in methods:
             page, ch, k2 = p["page"], p["channels"], p["k2"]
             kmax = kmin = None
             kept = None
             kk, vv, n = k, v, S
-            if m.startswith("rocketkv"):
+            lens = None
+            if m == "rocketkv-ada":       # shared stage-1 budget, decode per unit length
+                n = rk.adakv_capacity(Hkv, S, w.window, p["n_keep"])
+                kept = torch.empty(B, Hkv, n, dtype=torch.int32, device=dev)
+                lens = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+                kk = torch.empty(B, Hkv, n, d, dtype=k.dtype, device=dev)
+                vv = torch.empty_like(kk)
+                rk.rk_adakv_evict(qw, k, v, S, w.window, w.pool, p["n_keep"], kept, lens, kk, vv)
+            elif m.startswith("rocketkv"):
                 n = p["n_keep"]
                 kept = torch.empty(B, Hkv, n, dtype=torch.int32, device=dev)
                 kk = torch.empty(B, Hkv, n, d, dtype=k.dtype, device=dev)
@@ -414,22 +424,29 @@ def selection_recall(args):
             if m != "exact":
                 kmax = torch.empty(B, Hkv, d, rk.aux_capacity(n, page), dtype=k.dtype, device=dev)
                 kmin = None if m == "sparq" else torch.empty_like(kmax)
-                rk.rk_hsa_build_aux(kk, n, 0, page, kmax, kmin, n_q_heads=Hq)
+                rk.rk_hsa_build_aux(kk, n, 0, page, kmax, kmin, n_q_heads=Hq)   # (ada: past a unit's rows unused)
             nblk = -(-n // page)
             nsel = min(k2, nblk)
             sel = torch.empty(B, Hkv, nsel, dtype=torch.int32, device=dev)
             out = torch.empty(B, Hq, d, device=dev)
             method = "hsa" if m.startswith("rocketkv") else m
-            ws = rk.rk_select_decode(method, qs[0], kk, vv, kmax, kmin, n, page, ch, k2, out, sel)
+
+            def call(q, ws=None):
+                if lens is not None:
+                    return rk.rk_hsa_decode_ragged(q, kk, vv, kmax, kmin, lens, n, page, ch, k2, out, sel, ws=ws)
+                return rk.rk_select_decode(method, q, kk, vv, kmax, kmin, n, page, ch, k2, out, sel, ws=ws)
+
+            ws = call(qs[0])
             rec = mass = err = hit = 0.0
             cnt = 0
             tok_total = 0
             for si, q in enumerate(qs):
-                rk.rk_select_decode(method, q, kk, vv, kmax, kmin, n, page, ch, k2, out, sel, ws=ws)
+                call(q, ws)
                 torch.cuda.synchronize()
                 pbar, o_ref, sc = ref[si]
                 toks = (sel.long().unsqueeze(-1) * page + torch.arange(page, device=dev)).view(B, Hkv, -1)
-                valid = toks < n
+                lim = lens.long().unsqueeze(-1) if lens is not None else n
+                valid = (toks < lim) & (sel.long().unsqueeze(-1) >= 0).expand(-1, -1, -1, page).reshape(B, Hkv, -1)
                 toks = torch.where(valid, toks, torch.zeros_like(toks))
                 if kept is not None:
                     toks = torch.gather(kept.long(), 2, toks)
@@ -450,10 +467,12 @@ def selection_recall(args):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for q in qs:
-                rk.rk_select_decode(method, q, kk, vv, kmax, kmin, n, page, ch, k2, out, sel, ws=ws)
+                call(q, ws)
             e1.record()
             torch.cuda.synchronize()
-            est = ch * nblk / (2.0 * d)
+            # estimation traffic over the pages each unit actually has
+            nb_eff = float(((lens.float() + page - 1) // page).mean()) if lens is not None else nblk
+            est = ch * nb_eff / (2.0 * d)
             rows.append(dict(workload=name, method=m, page=page, channels=ch, k2_pages=k2,
                              tokens_attended=round(tok_total / cnt, 1), est_pairs=round(est, 1),
                              recall=round(rec / cnt, 4), mass=round(mass / cnt, 4), out_rel_l2=round(err / cnt, 5),

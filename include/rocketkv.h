@@ -145,6 +145,36 @@ rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* 
                           void* ws, size_t ws_bytes, rk_stream stream);
 
 /*
+ * rk_adakv_evict -- stage 1 with Ada-KV's shared budget.  [RKV] method
+ * details, "the second stage and the framework's generality" (SnapKV or
+ * Ada-KV as stage 1) and the GQA paragraph (group-level selection following
+ * Ada-KV).  The notes name Ada-KV's adaptive budgets without their rule; the
+ * rule built here: window scores and pooling per unit as rk_snapkv_evict,
+ * then for each sequence the Hkv * (n_keep - W) prefix slots of its heads go
+ * to the largest pooled scores over all its KV heads together (ties to the
+ * lower head, then the lower position), so a head whose group attends to few
+ * tokens keeps few; each head also keeps its W window positions.  Head h of
+ * sequence b keeps kept_count[b, h] tokens: its chosen prefix positions
+ * ascending, then S-W .. S-1.
+ *
+ *   kept_idx   [B, Hkv, out_cap] int32  out: rows 0 .. kept_count-1 valid
+ *   kept_count [B, Hkv] int32           out
+ *   k_out, v_out [B, Hkv, out_cap, d]   out (optional, both or neither):
+ *                                       compact rows 0 .. kept_count-1
+ *   kmax_opt, kmin_opt                  out (optional, with k_out): aux of
+ *                                       each unit's kept_count tokens
+ *   others as rk_snapkv_evict (same workspace size)
+ * out_cap must be at least min(seq_len, Hkv * (n_keep - W) + W) (one head may
+ * take the whole budget); Hkv <= 64.
+ */
+rk_status rk_adakv_evict(const rk_shape* shape, const void* q_win, const void* k, const void* v,
+                         int64_t kv_cap, int64_t seq_len, int32_t window, int32_t pool_kernel,
+                         int64_t n_keep, int32_t* kept_idx, int32_t* kept_count, void* k_out,
+                         void* v_out, int64_t out_cap, float* pooled_opt, void* kmax_opt,
+                         void* kmin_opt, int64_t nblk_cap, int32_t block, void* ws, size_t ws_bytes,
+                         rk_stream stream);
+
+/*
  * rk_hsa_build_aux -- HSA step 1: per-page element-wise Kmax / Kmin.
  * [RKV] method details, HSA step 1: keys are grouped into consecutive pages
  * of `block` tokens; the element-wise max and min of each page are stored
@@ -229,6 +259,23 @@ rk_status rk_hsa_decode(const rk_shape* shape, const void* q, const void* k, con
                         int64_t n_tokens, int32_t block, int32_t k1, int32_t k2, float* out,
                         int32_t* sel_blocks_opt, int32_t* sel_channels_opt,
                         float* block_scores_opt, void* ws, size_t ws_bytes, rk_stream stream);
+
+/*
+ * rk_hsa_decode_ragged -- rk_hsa_decode where unit u has its own token count
+ * unit_tokens[u] (device int32 [B, Hkv], each in [1, max_tokens]; values
+ * outside are clamped into that range in-kernel), e.g. the kept_count of
+ * rk_adakv_evict.  Each unit chooses min(k2, its pages) pages;
+ * sel_blocks_opt [B, Hkv, min(k2, ceil(max_tokens / block))] holds -1 past a
+ * unit's choice, block_scores_opt [B, Hkv, ceil(max_tokens / block)] is
+ * valid for the unit's own pages.  max_tokens <= kv_cap and at most 12288
+ * pages; workspace rk_hsa_workspace_bytes(shape, max_tokens, ...).
+ */
+rk_status rk_hsa_decode_ragged(const rk_shape* shape, const void* q, const void* k, const void* v,
+                               int64_t kv_cap, const void* kmax, const void* kmin, int64_t nblk_cap,
+                               const int32_t* unit_tokens, int64_t max_tokens, int32_t block,
+                               int32_t k1, int32_t k2, float* out, int32_t* sel_blocks_opt,
+                               int32_t* sel_channels_opt, float* block_scores_opt, void* ws,
+                               size_t ws_bytes, rk_stream stream);
 
 /*
  * rk_hsa_append_decode -- one decode step that appends its token first:

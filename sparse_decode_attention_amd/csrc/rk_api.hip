@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -69,7 +70,8 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
                         int32_t block, int32_t k1, int32_t k2, float* out, int32_t* sel_opt,
                         int32_t* chan_opt, float* s1_opt, void* ws, size_t ws_bytes,
                         rk_stream stream, bool mt, const rk::AppendArgs* app = nullptr,
-                        bool exact_rows = false, const rk::PagedArgs* paged = nullptr) {
+                        bool exact_rows = false, const rk::PagedArgs* paged = nullptr,
+                        const int32_t* lens = nullptr) {
   rk::Dims d;
   rk_status st = check_shape(shape, &d);
   if (st != RK_OK) return st;
@@ -104,12 +106,17 @@ rk_status decode_common(const rk_shape* shape, const void* q, const void* k, con
                 (long long)rk::kMaxPagesGlobal);
   if (k1 < 1 || k1 > d.D) return fail(RK_EINVAL, "k1 (%d) outside [1, head_dim]", k1);
   if (k2 < 1) return fail(RK_EINVAL, "k2 must be >= 1");
+  if (lens) {
+    if (reinterpret_cast<uintptr_t>(lens) & 3u) return fail(RK_EINVAL, "unit_tokens misaligned");
+    if (nblk > rk::kMaxPages)
+      return fail(RK_EUNSUPPORTED, "ragged units with more than %lld pages", (long long)rk::kMaxPages);
+  }
   const rk::DecodeWs lay = rk::decode_ws_layout(d, nblk, k2);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != RK_OK) return st;
   return device_status(
       rk::launch_hsa_decode(d, q, k, v, kv_cap, mt ? cand : nullptr, cand_stride, kmax, kmin,
                             nblk_cap, n_tokens, block, k1, k2, out, sel_opt, chan_opt, s1_opt,
-                            ws, static_cast<hipStream_t>(stream), app, exact_rows, paged),
+                            ws, static_cast<hipStream_t>(stream), app, exact_rows, paged, lens),
       mt ? "rk_hsa_decode_mt launch" : app ? "rk_hsa_append_decode launch" : "rk_hsa_decode launch");
 }
 
@@ -553,6 +560,69 @@ rk_status rk_paged_hsa_append_decode(const rk_shape* shape, const void* q, const
   return decode_common(shape, q, k_pool, v_pool, 0, nullptr, 0, kmax, kmin, nblk_cap, pos + 1, block,
                        k1, k2, out, sel_blocks_opt, sel_channels_opt, block_scores_opt, ws, ws_bytes,
                        stream, false, &app, false, &pg);
+}
+
+rk_status rk_adakv_evict(const rk_shape* shape, const void* q_win, const void* k, const void* v,
+                         int64_t kv_cap, int64_t seq_len, int32_t window, int32_t pool_kernel,
+                         int64_t n_keep, int32_t* kept_idx, int32_t* kept_count, void* k_out,
+                         void* v_out, int64_t out_cap, float* pooled_opt, void* kmax_opt,
+                         void* kmin_opt, int64_t nblk_cap, int32_t block, void* ws, size_t ws_bytes,
+                         rk_stream stream) {
+  rk::Dims d;
+  rk_status st = check_shape(shape, &d);
+  if (st != RK_OK) return st;
+  if (!q_win || !k || !kept_idx || !kept_count) return fail(RK_EINVAL, "null tensor argument");
+  if ((k_out == nullptr) != (v_out == nullptr))
+    return fail(RK_EINVAL, "k_out and v_out must both be given or both be NULL");
+  if (k_out && !v) return fail(RK_EINVAL, "v is NULL but a compact cache is requested");
+  if (!aligned16(q_win) || !aligned16(k) || (v && !aligned16(v)) ||
+      (k_out && (!aligned16(k_out) || !aligned16(v_out))) ||
+      (reinterpret_cast<uintptr_t>(kept_idx) & 3u) || (reinterpret_cast<uintptr_t>(kept_count) & 3u))
+    return fail(RK_EINVAL, "tensors misaligned");
+  if (d.Hkv > 64) return fail(RK_EUNSUPPORTED, "shared budgets over more than 64 KV heads");
+  if (window < 1 || window > seq_len) return fail(RK_EINVAL, "window outside [1, seq_len]");
+  if (seq_len > kv_cap) return fail(RK_EINVAL, "seq_len exceeds kv_cap");
+  if (seq_len > (int64_t(1) << 31) - 1) return fail(RK_EINVAL, "seq_len too large");
+  if (n_keep < window || n_keep > seq_len) return fail(RK_EINVAL, "n_keep outside [W, S]");
+  if (int64_t(d.Hkv) * (seq_len - window) > (int64_t(1) << 31) - 1)
+    return fail(RK_EUNSUPPORTED, "Hkv * (seq_len - window) too large");
+  if (pool_kernel < 1 || (pool_kernel % 2) == 0 || pool_kernel > 4097)
+    return fail(RK_EINVAL, "pool_kernel must be odd, in [1, 4097]");
+  const int64_t worst = std::min<int64_t>(seq_len, int64_t(d.Hkv) * (n_keep - window) + window);
+  if (out_cap < worst)
+    return fail(RK_EINVAL, "out_cap (%lld) below min(seq_len, Hkv * (n_keep - W) + W) = %lld",
+                (long long)out_cap, (long long)worst);
+  if ((kmax_opt == nullptr) != (kmin_opt == nullptr))
+    return fail(RK_EINVAL, "kmax_opt and kmin_opt must both be given or both be NULL");
+  if (kmax_opt) {
+    if (!k_out) return fail(RK_EINVAL, "the aux outputs need the compact cache (k_out)");
+    if (!aligned16(kmax_opt) || !aligned16(kmin_opt))
+      return fail(RK_EINVAL, "kmax and kmin must be 16-byte aligned");
+    if (block < 1) return fail(RK_EINVAL, "block must be >= 1");
+    if ((worst + block - 1) / block > nblk_cap)
+      return fail(RK_EINVAL, "nblk_cap below the page count of out_cap's worst case");
+    if (nblk_cap % 8 != 0) return fail(RK_EINVAL, "nblk_cap must be a multiple of 8");
+  }
+  if (int64_t(d.G) * window > 1024) return fail(RK_EUNSUPPORTED, "group * window above 1024 rows");
+  const rk::EvictWs lay = rk::evict_ws_layout(d, seq_len, window);
+  if ((st = check_ws(ws, ws_bytes, lay.total)) != RK_OK) return st;
+  return device_status(
+      rk::launch_snapkv_evict(d, q_win, k, v, kv_cap, seq_len, window, pool_kernel, n_keep, kept_idx,
+                              k_out, v_out, out_cap, pooled_opt, kmax_opt, kmin_opt, nblk_cap, block,
+                              ws, static_cast<hipStream_t>(stream), kept_count),
+      "rk_adakv_evict launch");
+}
+
+rk_status rk_hsa_decode_ragged(const rk_shape* shape, const void* q, const void* k, const void* v,
+                               int64_t kv_cap, const void* kmax, const void* kmin, int64_t nblk_cap,
+                               const int32_t* unit_tokens, int64_t max_tokens, int32_t block,
+                               int32_t k1, int32_t k2, float* out, int32_t* sel_blocks_opt,
+                               int32_t* sel_channels_opt, float* block_scores_opt, void* ws,
+                               size_t ws_bytes, rk_stream stream) {
+  if (!unit_tokens) return fail(RK_EINVAL, "unit_tokens is NULL");
+  return decode_common(shape, q, k, v, kv_cap, nullptr, 0, kmax, kmin, nblk_cap, max_tokens, block, k1,
+                       k2, out, sel_blocks_opt, sel_channels_opt, block_scores_opt, ws, ws_bytes, stream,
+                       false, nullptr, false, nullptr, unit_tokens);
 }
 
 rk_status rk_hsa_decode_mt(const rk_shape* shape, const void* q, const void* k, const void* v,

@@ -167,7 +167,8 @@ template <typename T, int D, int G, bool ALL>
 __global__ __launch_bounds__(256) void hsa_score_kernel(
     const T* __restrict__ q, const T* __restrict__ kmax, const T* __restrict__ kmin,
     int64_t nblk_cap, int nblk, int k1, int ppw, int units, uint32_t* __restrict__ keys,
-    int keys_pitch, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt) {
+    int keys_pitch, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt,
+    const int32_t* __restrict__ lens, int n_max, int block) {
   constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   T* stage = reinterpret_cast<T*>(dyn_lds);  // [ppw][k1p]
@@ -184,7 +185,10 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
   if (item >= n_ranges * units) return;
   const int u = item / n_ranges;
   const int p0 = (item % n_ranges) * ppw;
-  const int np = min(ppw, nblk - p0);
+  // per-unit token counts (ragged units): ranges past the unit's pages idle
+  const int nblk_u = lens ? (max(1, min(lens[u], n_max)) + block - 1) / block : nblk;
+  if (p0 >= nblk_u) return;
+  const int np = min(ppw, nblk_u - p0);
   const int t = threadIdx.x;
   const int wave = t / kWave, lane = lane_id();
   RK_PHASE(16);
@@ -553,7 +557,7 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
     const int32_t* __restrict__ cand, int64_t cand_stride, const uint32_t* __restrict__ keys,
     int keys_pitch, int nblk, int nsel, int pages_per_split, int n_split, int units, int n_tokens,
     int block, float scale_log2, float* __restrict__ partials, int32_t* __restrict__ sel_opt,
-    const int32_t* __restrict__ presel, PagedArgs pga) {
+    const int32_t* __restrict__ presel, PagedArgs pga, const int32_t* __restrict__ lens) {
   using S = AttnShape<T, D, G>;
   constexpr int EPL = S::EPL, LPR = S::LPR;
   constexpr int NW = 4;
@@ -586,9 +590,13 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   }
 
   RK_PHASE(8);
+  // ragged units: this unit's tokens, pages and chosen pages
+  const int n_u = lens ? max(1, min(lens[u], n_tokens)) : n_tokens;
+  const int nblk_u = lens ? (n_u + block - 1) / block : nblk;
+  const int nsel_u = min(nsel, nblk_u);
   int* pages = reinterpret_cast<int*>(attn_lds);  // [pages_per_split]
   const int e0 = split * pages_per_split;
-  const int np = min(e0 + pages_per_split, nsel) - e0;
+  const int np = max(0, min(e0 + pages_per_split, nsel_u) - e0);
   int32_t* so = sel_opt && split == 0 ? sel_opt + size_t(u) * nsel : nullptr;
   const uint32_t* kg = keys + size_t(u) * keys_pitch;
   [[maybe_unused]] auto emit = [=](int r, int i) {  // by value: no local needs an address
@@ -603,15 +611,17 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
     // one wave selects from keys held in registers (no barrier inside) and
     // emits only the ranks this split needs (all of them for the sel output)
     if (wave == 0)
-      wave_topk_rows([=](int i) { return kg[i]; }, nblk, nsel, emit, tsm.hist[0], so ? 0 : e0,
-                     so ? nsel : e0 + np);
+      wave_topk_rows([=](int i) { return kg[i]; }, nblk_u, nsel_u, emit, tsm.hist[0], so ? 0 : e0,
+                     so ? nsel_u : e0 + np);
   } else {
     uint32_t* kl = attn_lds + pages_per_split;  // [keys_pitch]
     for (int i = threadIdx.x; i < keys_pitch / 4; i += 256)
       reinterpret_cast<uint4*>(kl)[i] = reinterpret_cast<const uint4*>(kg)[i];
     __syncthreads();
-    wg_topk<256, 1024>([&](int i) { return kl[i]; }, nblk, nsel, emit, tsm);
+    wg_topk<256, 1024>([&](int i) { return kl[i]; }, nblk_u, nsel_u, emit, tsm);
   }
+  if (so)  // ranks past a ragged unit's choice
+    for (int r = nsel_u + threadIdx.x; r < nsel; r += 256) so[r] = -1;
   __syncthreads();
   RK_PHASE(10);
 
@@ -622,7 +632,7 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   const UnitPages up = PAGED ? UnitPages{pga.table + size_t(u / pga.hkv) * pga.table_stride, pga.n_phys,
                                          pga.shift, pga.hkv, u % pga.hkv}
                              : UnitPages{};
-  attend_pages<T, D, G, MT, TPS_, PAGED>(qf, ku, vu, cu, kv_cap, pages, wave, np, NW, block, n_tokens,
+  attend_pages<T, D, G, MT, TPS_, PAGED>(qf, ku, vu, cu, kv_cap, pages, wave, np, NW, block, n_u,
                                          scale_log2, m, l, o, up);
   wave_state_to_lds<T, D, G>(m, l, o, wave, wm, wl, wo);
   __syncthreads();
@@ -685,7 +695,7 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
     CacheIn<T, APP> kmin, int64_t nblk_cap, int nblk, int k1, int nsel, int npc,
     int n_tokens, int block, float scale_log2, float* __restrict__ out,
     int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt,
-    AppendPtrs<T> app, PagedArgs pga) {
+    AppendPtrs<T> app, PagedArgs pga, const int32_t* __restrict__ lens) {
   constexpr int TPS = AttnShape<T, D, G>::TPS;
   using S = AttnShape<T, D, G, TPS>;
   constexpr int EPL = S::EPL, LPR = S::LPR;
@@ -712,7 +722,12 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   float qf[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) unpack16(load16(q + (size_t(u) * G + g) * D + c * EPL), qf[g]);
-  const int n_cached = APP ? n_tokens - 1 : n_tokens;  // tokens read from the cache
+  // ragged units (not with APP): this unit's tokens, pages and chosen pages;
+  // the LDS layout keeps the launch-wide nblk and nsel
+  const int n_unit = lens ? max(1, min(lens[u], n_tokens)) : n_tokens;
+  const int nblk_u = lens ? (n_unit + block - 1) / block : nblk;
+  const int nsel_u = min(nsel, nblk_u);
+  const int n_cached = APP ? n_tokens - 1 : n_unit;  // tokens read from the cache
   const int app_page = (n_tokens - 1) / block;
   const UnitPages up = PAGED ? UnitPages{pga.table + size_t(u / pga.hkv) * pga.table_stride, pga.n_phys,
                                          pga.shift, pga.hkv, u % pga.hkv}
@@ -760,8 +775,8 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
 
   const T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
   const T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
-  for (int p0 = 0; p0 < nblk; p0 += npc) {
-    const int np = min(npc, nblk - p0);
+  for (int p0 = 0; p0 < nblk_u; p0 += npc) {
+    const int np = min(npc, nblk_u - p0);
     stage_rows<T, NT>(xu + p0, nu + p0, nblk_cap, np, k1, i1_off, stage);
     if (APP && p0 == 0 && ta >= 0) {
       app_knt[ta] = app_kn;
@@ -795,10 +810,12 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   };
   if (nblk <= kWaveTopkPages) {
     if (wave == 0)
-      wave_topk_rows([=](int i) { return pkeys[i]; }, nblk, nsel, emit, tsm.hist[0], 0, nsel);
+      wave_topk_rows([=](int i) { return pkeys[i]; }, nblk_u, nsel_u, emit, tsm.hist[0], 0, nsel_u);
   } else {
-    wg_topk<NT, 1024>([&](int i) { return pkeys[i]; }, nblk, nsel, emit, tsm);
+    wg_topk<NT, 1024>([&](int i) { return pkeys[i]; }, nblk_u, nsel_u, emit, tsm);
   }
+  if (so)  // ranks past a ragged unit's choice
+    for (int r = nsel_u + t; r < nsel; r += NT) so[r] = -1;
   __syncthreads();
   RK_PHASE(3);
 
@@ -814,7 +831,7 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   const T* ku = k + ubase + c * EPL;
   const T* vu = v + ubase + c * EPL;
   const int32_t* cu = MT ? cand + size_t(u) * size_t(cand_stride) : nullptr;
-  attend_pages<T, D, G, MT, TPS, PAGED>(qf, ku, vu, cu, kv_cap, pages, wave, nsel, NW, block, n_cached,
+  attend_pages<T, D, G, MT, TPS, PAGED>(qf, ku, vu, cu, kv_cap, pages, wave, nsel_u, NW, block, n_cached,
                                         scale_log2, m, l, o, up);
   if constexpr (APP) {
     // the new token, when its page was chosen (the last page, so the last
@@ -939,7 +956,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
                            int64_t n_tokens, int block, int k1, int k2, float* out,
                            int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
                            hipStream_t s, const AppendArgs* app, bool exact_rows,
-                           const PagedArgs* paged) {
+                           const PagedArgs* paged, const int32_t* lens) {
   const int nblk = int((n_tokens + block - 1) / block);
   const DecodeWs lay = decode_ws_layout(d, nblk, k2);
   // paged pools are built for bf16 only (the API refuses the rest)
@@ -992,7 +1009,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
             s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), kv_cap, \
             cand, cand_stride, static_cast<const T*>(kmax), static_cast<const T*>(kmin), nblk_cap,  \
             nblk, k1, lay.nsel, npc, int(n_tokens), block, scale_log2, out, sel_opt, chan_opt,      \
-            s1_opt, ap, pg)
+            s1_opt, ap, pg, lens)
       if (cand)
         RK_FUSED("hsa_fused_mt", true, false, false);
       else if (paged && app)
@@ -1057,11 +1074,13 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   else if (all)
     RK_LAUNCH("hsa_score", (hsa_score_kernel<T, D, G, true>), dim3(score_wgs), dim3(256), lds, s,
               static_cast<const T*>(q), static_cast<const T*>(kmax), static_cast<const T*>(kmin),
-              nblk_cap, nblk, k1, ppw, units, keys, lay.keys_pitch, chan_opt, s1_opt);
+              nblk_cap, nblk, k1, ppw, units, keys, lay.keys_pitch, chan_opt, s1_opt, lens,
+              int(n_tokens), block);
   else
     RK_LAUNCH("hsa_score", (hsa_score_kernel<T, D, G, false>), dim3(score_wgs), dim3(256), lds, s,
               static_cast<const T*>(q), static_cast<const T*>(kmax), static_cast<const T*>(kmin),
-              nblk_cap, nblk, k1, ppw, units, keys, lay.keys_pitch, chan_opt, s1_opt);
+              nblk_cap, nblk, k1, ppw, units, keys, lay.keys_pitch, chan_opt, s1_opt, lens,
+              int(n_tokens), block);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -1128,7 +1147,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
             attn_lds, s, static_cast<const T*>(q), static_cast<const T*>(k),                      \
             static_cast<const T*>(v), kv_cap, cand, cand_stride, keys, lay.keys_pitch, nblk,       \
             lay.nsel, pps, n_split, units, int(n_tokens), block, scale_log2, part, sel_opt,        \
-            presel_pages, pg)
+            presel_pages, pg, lens)
 #define RK_ATTN(NAME, MTV, TPSV, PRE) RK_ATTN_P(NAME, MTV, TPSV, PRE, false)
   if (paged) {
     static bool pg_attr_set = false;  // once per template instantiation
@@ -1191,12 +1210,12 @@ hipError_t launch_decode_d(const Dims& d, const void* q, const void* k, const vo
                            int64_t n_tokens, int block, int k1, int k2, float* out,
                            int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
                            hipStream_t s, const AppendArgs* app, bool exact_rows,
-                           const PagedArgs* paged) {
+                           const PagedArgs* paged, const int32_t* lens) {
 #define RK_DECODE_G(GG)                                                                        \
   case GG:                                                                                     \
     return launch_decode_t<T, D, GG>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,       \
                                      nblk_cap, n_tokens, block, k1, k2, out, sel_opt,         \
-                                     chan_opt, s1_opt, ws, s, app, exact_rows, paged);
+                                     chan_opt, s1_opt, ws, s, app, exact_rows, paged, lens);
   switch (d.G) {
     RK_DECODE_G(1)
     RK_DECODE_G(2)
@@ -1216,23 +1235,23 @@ hipError_t launch_hsa_decode(const Dims& d, const void* q, const void* k, const 
                              int64_t n_tokens, int block, int k1, int k2, float* out,
                              int32_t* sel_opt, int32_t* chan_opt, float* s1_opt, void* ws,
                              hipStream_t s, const AppendArgs* app, bool exact_rows,
-                             const PagedArgs* paged) {
+                             const PagedArgs* paged, const int32_t* lens) {
   if (d.bf16) {
     if (d.D == 128)
       return launch_decode_d<bf16_t, 128>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                           nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                          chan_opt, s1_opt, ws, s, app, exact_rows, paged);
+                                          chan_opt, s1_opt, ws, s, app, exact_rows, paged, lens);
     return launch_decode_d<bf16_t, 64>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                        nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                       chan_opt, s1_opt, ws, s, app, exact_rows, paged);
+                                       chan_opt, s1_opt, ws, s, app, exact_rows, paged, lens);
   }
   if (d.D == 128)
     return launch_decode_d<float, 128>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                        nblk_cap, n_tokens, block, k1, k2, out, sel_opt,
-                                       chan_opt, s1_opt, ws, s, app, exact_rows, paged);
+                                       chan_opt, s1_opt, ws, s, app, exact_rows, paged, lens);
   return launch_decode_d<float, 64>(d, q, k, v, kv_cap, cand, cand_stride, kmax, kmin,
                                     nblk_cap, n_tokens, block, k1, k2, out, sel_opt, chan_opt,
-                                    s1_opt, ws, s, app, exact_rows, paged);
+                                    s1_opt, ws, s, app, exact_rows, paged, lens);
 }
 
 }  // namespace rk

@@ -529,12 +529,77 @@ __global__ __launch_bounds__(1024) void select_final_kernel(const float* __restr
 }
 
 // Compact cache rows: out[n] = in[kept[n]] for K and V.
+// Ada-KV shared budget: one workgroup per sequence takes the K = Hkv * kper
+// largest pooled scores over all of its heads together (flattened [head,
+// position], ties to the lower head, then position), staged in LDS when they
+// fit (`staged`, with spare LDS for radix candidates) or read from memory each
+// pass.  The chosen flattened indices come out ascending into tmp, so each
+// head's run is contiguous: its bounds are found by binary search, its
+// positions written to kept[unit][0 ..) and followed by the W window
+// positions, and counts[unit] = its prefix count + W.
+constexpr int kAdaMaxHeads = 64;
+__global__ __launch_bounds__(1024) void adakv_select_kernel(const float* __restrict__ pooled, int Hkv,
+                                                            int P, int W, int kper, int staged,
+                                                            int cand_cap, int32_t* __restrict__ tmp,
+                                                            int32_t* __restrict__ kept, int kept_stride,
+                                                            int32_t* __restrict__ counts) {
+  extern __shared__ uint32_t skeys[];
+  __shared__ TopkSmem<1024, 2048, 1> sm;
+  __shared__ int start[kAdaMaxHeads + 1];
+  const int b = blockIdx.x;
+  const int n = Hkv * P;
+  const int K = Hkv * kper;
+  const float* pb = pooled + size_t(b) * n;
+  int32_t* tb = tmp + size_t(b) * n;
+  auto emit = [=](int r, int i) { tb[r] = i; };
+  if (staged) {
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (int i = threadIdx.x; i < n; i += 1024) {
+      const uint32_t kk = order_key(pb[i]);
+      skeys[i] = kk;
+      lo = min(lo, kk);
+      hi = max(hi, kk);
+    }
+    __syncthreads();
+    wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, n, K, emit, sm, true, lo, hi, skeys + n, cand_cap);
+  } else {
+    wg_topk<1024, 2048>([&](int i) { return order_key(pb[i]); }, n, K, emit, sm);
+  }
+  __syncthreads();
+  // start[h] = number of chosen indices below h * P (tb is ascending)
+  if (threadIdx.x <= Hkv) {
+    const int target = threadIdx.x * P;
+    int lo = 0, hi = K;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (tb[mid] < target) lo = mid + 1; else hi = mid;
+    }
+    start[threadIdx.x] = lo;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < K; r += 1024) {
+    const int i = tb[r];
+    const int h = i / P;
+    kept[(size_t(b) * Hkv + h) * kept_stride + (r - start[h])] = i - h * P;
+  }
+  for (int e = threadIdx.x; e < Hkv * W; e += 1024) {
+    const int h = e / W, w = e % W;
+    const int cnt = start[h + 1] - start[h];
+    kept[(size_t(b) * Hkv + h) * kept_stride + cnt + w] = P + w;
+    if (w == 0) counts[size_t(b) * Hkv + h] = cnt + W;
+  }
+}
+
+// kept rows are kept_stride apart; with lens, unit u keeps lens[u] rows
+// (Ada-KV budgets), else n_keep.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k,
                                                      const T* __restrict__ v, int64_t kv_cap,
                                                      const int32_t* __restrict__ kept,
-                                                     int n_keep, T* __restrict__ k_out,
-                                                     T* __restrict__ v_out, int64_t out_cap) {
+                                                     int n_keep_max, T* __restrict__ k_out,
+                                                     T* __restrict__ v_out, int64_t out_cap,
+                                                     int kept_stride,
+                                                     const int32_t* __restrict__ lens) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int CPR = D / EPL;
   constexpr int RPP = 256 / CPR;  // rows per pass
@@ -542,7 +607,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ k,
   const int u = blockIdx.y;
   const int n0 = blockIdx.x * 64;
   const int ch = threadIdx.x % CPR;
-  const int* ku = kept + size_t(u) * n_keep;
+  const int* ku = kept + size_t(u) * kept_stride;
+  const int n_keep = lens ? min(lens[u], n_keep_max) : n_keep_max;
   // the workgroup's 64 rows: every index, then every K and V load, in flight
   // before any is used
   constexpr int NI = 64 / RPP;
@@ -583,8 +649,9 @@ constexpr int kGatherWideThreads = 512;
 template <typename T, int D>
 __global__ __launch_bounds__(kGatherWideThreads, 4) void gather_aux_wide_kernel(
     const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
-    const int32_t* __restrict__ kept, int n_keep, T* __restrict__ k_out, T* __restrict__ v_out,
-    int64_t out_cap, int block, T* __restrict__ kmax, T* __restrict__ kmin, int64_t nblk_cap) {
+    const int32_t* __restrict__ kept, int n_keep_max, T* __restrict__ k_out, T* __restrict__ v_out,
+    int64_t out_cap, int block, T* __restrict__ kmax, T* __restrict__ kmin, int64_t nblk_cap,
+    int kept_stride, const int32_t* __restrict__ lens) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int CPR = D / EPL;
   constexpr int PPW = kGatherWideThreads / CPR;
@@ -597,13 +664,14 @@ __global__ __launch_bounds__(kGatherWideThreads, 4) void gather_aux_wide_kernel(
   const int c = t % CPR;
   const int j = t / CPR;
   const int u = blockIdx.y;
+  const int n_keep = lens ? min(lens[u], n_keep_max) : n_keep_max;
   const int nblk = (n_keep + block - 1) / block;
   const int p0 = blockIdx.x * PPW;
   const int p = p0 + j;
   if (p < nblk) {
     const int n0 = p * block;
     const int n1 = min(n0 + block, n_keep);
-    const int* ku = kept + size_t(u) * n_keep;
+    const int* ku = kept + size_t(u) * kept_stride;
     float mx[EPL], mn[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
@@ -887,8 +955,9 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gather_aux_kernel(
     const T* __restrict__ k, const T* __restrict__ v, int64_t kv_cap,
-    const int32_t* __restrict__ kept, int n_keep, T* __restrict__ k_out, T* __restrict__ v_out,
-    int64_t out_cap, int block, T* __restrict__ kmax, T* __restrict__ kmin, int64_t nblk_cap) {
+    const int32_t* __restrict__ kept, int n_keep_max, T* __restrict__ k_out, T* __restrict__ v_out,
+    int64_t out_cap, int block, T* __restrict__ kmax, T* __restrict__ kmin, int64_t nblk_cap,
+    int kept_stride, const int32_t* __restrict__ lens) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int CPR = D / EPL;
   constexpr int RG = 4;
@@ -901,6 +970,7 @@ __global__ __launch_bounds__(256) void gather_aux_kernel(
   const int g = (t / CPR) % RG;
   const int j = t / (CPR * RG);
   const int u = blockIdx.y;
+  const int n_keep = lens ? min(lens[u], n_keep_max) : n_keep_max;
   const int nblk = (n_keep + block - 1) / block;
   const int p0 = blockIdx.x * PPW;
   const int p = p0 + j;
@@ -912,7 +982,7 @@ __global__ __launch_bounds__(256) void gather_aux_kernel(
   }
   if (p < nblk) {
     const int n1 = min((p + 1) * block, n_keep);
-    const int* ku = kept + size_t(u) * n_keep;
+    const int* ku = kept + size_t(u) * kept_stride;
     using Rw = decltype(Vec16<T>::raw);
     // NI rows per round: all their indices, then all their K and V loads,
     // are in flight before any is used (the index -> row chain is the latency)
@@ -983,9 +1053,14 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
                           int64_t kv_cap, int64_t S64, int W, int pool_kernel, int64_t n_keep,
                           int32_t* kept, void* k_out, void* v_out, int64_t out_cap,
                           float* pooled_opt, void* kmax, void* kmin, int64_t nblk_cap, int block,
-                          void* ws, hipStream_t s) {
+                          void* ws, hipStream_t s, int32_t* ada_counts) {
   const int S = int(S64);
   const int P = S - W;
+  // Ada-KV budgets: kept rows are out_cap apart and unit u keeps
+  // ada_counts[u] of them (at most n_rows), else every unit keeps n_keep
+  const bool ada = ada_counts != nullptr;
+  const int kept_stride = ada ? int(out_cap) : int(n_keep);
+  const int n_rows = ada ? int(std::min<int64_t>(S64, int64_t(d.Hkv) * (n_keep - W) + W)) : int(n_keep);
   const EvictWs lay = evict_ws_layout(d, S64, W);
   char* wsb = static_cast<char*>(ws);
   float2* partials = reinterpret_cast<float2*>(wsb + lay.partials);
@@ -1053,7 +1128,8 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
     for (const void* f : {reinterpret_cast<const void*>(&select_kernel),
                           reinterpret_cast<const void*>(&select_pool_kernel<31>),
                           reinterpret_cast<const void*>(&select_chunk_kernel),
-                          reinterpret_cast<const void*>(&select_final_kernel)}) {
+                          reinterpret_cast<const void*>(&select_final_kernel),
+                          reinterpret_cast<const void*>(&adakv_select_kernel)}) {
       hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          int(kSelectKeysLds));
       if (e != hipSuccess) return e;
@@ -1061,6 +1137,25 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
     attr_set = true;
   }
   const int h = (pool_kernel - 1) / 2;
+  if (ada) {
+    // pooling of every unit first (the shared choice reads all heads of a
+    // sequence), then one workgroup per sequence; the spent window scores
+    // hold its chosen flattened indices
+    if (P > 0) {
+      if (h == 31)
+        RK_LAUNCH("pool_sum", pool_sum_reg_kernel<31>, dim3((P + 2047) / 2048, units), dim3(256), 0, s,
+                  scores, P, pooled);
+      else
+        RK_LAUNCH("pool_sum", pool_sum_kernel, dim3((P + 255) / 256, units), dim3(256),
+                  size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    const size_t nkeys = size_t(d.Hkv) * P;
+    const int staged = (nkeys + 4096) * 4 <= kSelectKeysLds ? 1 : 0;
+    RK_LAUNCH("select_tokens", adakv_select_kernel, dim3(d.B), dim3(1024),
+              staged ? (nkeys + 4096) * 4 : size_t(0), s, pooled, d.Hkv, P, W, int(n_keep) - W, staged,
+              staged ? 4096 : 0, reinterpret_cast<int32_t*>(scores), kept, kept_stride, ada_counts);
+  } else {
   // kernel 63 with the haloed scores in LDS and enough units to spread the
   // pooling over the CUs: pooling inside the select launch (at batch 32,
   // 49 -> 41 us for both; at batch 1 the 8 workgroups' LDS reads of the
@@ -1107,7 +1202,9 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
                 cand_cap, kept);
     }
   }
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int32_t* lens = ada ? ada_counts : nullptr;
   if (k_out && kmax) {
     // wide workgroups (whole-line aux runs) unless they would leave most CUs
     // idle: at batch 1 with 32K keys (152 of them) they measured as fast as
@@ -1115,24 +1212,24 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
     // (8 of them) keeps 4-page workgroups, which spread its copy over more CUs
     constexpr int PPW = 256 / ((D / Vec16<T>::N) * 4);
     constexpr int PPW_WIDE = kGatherWideThreads / (D / Vec16<T>::N);
-    const int64_t nblk = (n_keep + block - 1) / block;
+    const int64_t nblk = (n_rows + block - 1) / block;
     const int64_t wide_wgs = (nblk + PPW_WIDE - 1) / PPW_WIDE * units;
     if (wide_wgs >= kComputeUnits / 4)
       RK_LAUNCH("gather_kv", (gather_aux_wide_kernel<T, D>),
                 dim3(unsigned((nblk + PPW_WIDE - 1) / PPW_WIDE), units), dim3(kGatherWideThreads),
-                0, s, kk, static_cast<const T*>(v), kv_cap, kept, int(n_keep),
+                0, s, kk, static_cast<const T*>(v), kv_cap, kept, n_rows,
                 static_cast<T*>(k_out), static_cast<T*>(v_out), out_cap, block,
-                static_cast<T*>(kmax), static_cast<T*>(kmin), nblk_cap);
+                static_cast<T*>(kmax), static_cast<T*>(kmin), nblk_cap, kept_stride, lens);
     else
       RK_LAUNCH("gather_kv", (gather_aux_kernel<T, D>), dim3(unsigned((nblk + PPW - 1) / PPW), units),
-                dim3(256), 0, s, kk, static_cast<const T*>(v), kv_cap, kept, int(n_keep),
+                dim3(256), 0, s, kk, static_cast<const T*>(v), kv_cap, kept, n_rows,
                 static_cast<T*>(k_out), static_cast<T*>(v_out), out_cap, block,
-                static_cast<T*>(kmax), static_cast<T*>(kmin), nblk_cap);
+                static_cast<T*>(kmax), static_cast<T*>(kmin), nblk_cap, kept_stride, lens);
     err = hipGetLastError();
   } else if (k_out) {
-    RK_LAUNCH("gather_kv", (gather_kernel<T, D>), dim3(unsigned((n_keep + 63) / 64), units),
-                       dim3(256), 0, s, kk, static_cast<const T*>(v), kv_cap, kept, int(n_keep),
-                       static_cast<T*>(k_out), static_cast<T*>(v_out), out_cap);
+    RK_LAUNCH("gather_kv", (gather_kernel<T, D>), dim3(unsigned((n_rows + 63) / 64), units),
+                       dim3(256), 0, s, kk, static_cast<const T*>(v), kv_cap, kept, n_rows,
+                       static_cast<T*>(k_out), static_cast<T*>(v_out), out_cap, kept_stride, lens);
     err = hipGetLastError();
   }
   return err;
@@ -1144,10 +1241,12 @@ hipError_t launch_snapkv_evict(const Dims& d, const void* q_win, const void* k, 
                                int64_t kv_cap, int64_t S, int W, int pool_kernel,
                                int64_t n_keep, int32_t* kept, void* k_out, void* v_out,
                                int64_t out_cap, float* pooled_opt, void* kmax, void* kmin,
-                               int64_t nblk_cap, int block, void* ws, hipStream_t s) {
+                               int64_t nblk_cap, int block, void* ws, hipStream_t s,
+                               int32_t* ada_counts) {
 #define RK_EVICT(TT, DD)                                                                      \
   return launch_evict_t<TT, DD>(d, q_win, k, v, kv_cap, S, W, pool_kernel, n_keep, kept, k_out, \
-                                v_out, out_cap, pooled_opt, kmax, kmin, nblk_cap, block, ws, s)
+                                v_out, out_cap, pooled_opt, kmax, kmin, nblk_cap, block, ws, s, \
+                                ada_counts)
   if (d.bf16) {
     if (d.D == 128) RK_EVICT(bf16_t, 128);
     RK_EVICT(bf16_t, 64);

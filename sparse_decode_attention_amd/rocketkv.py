@@ -372,6 +372,50 @@ def rk_paged_hsa_append_decode(q, k_new, v_new, k_pool, v_pool, pages: RkPagedKv
     return ws
 
 
+_lib.rk_adakv_evict.argtypes = [_SP, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _i64, _vp,
+                                _vp, _vp, _i64, _i32, _vp, _sz, _vp]
+_lib.rk_adakv_evict.restype = ctypes.c_int
+_lib.rk_hsa_decode_ragged.argtypes = [_SP, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp,
+                                      _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.rk_hsa_decode_ragged.restype = ctypes.c_int
+
+
+def adakv_capacity(n_kv_heads: int, seq_len: int, window: int, n_keep: int) -> int:
+    """Rows a unit may keep under the shared budget: min(S, Hkv * (n_keep - W) + W)."""
+    return min(seq_len, n_kv_heads * (n_keep - window) + window)
+
+
+def rk_adakv_evict(q_win, k, v, seq_len, window, pool_kernel, n_keep, kept_idx, kept_count, k_out=None,
+                   v_out=None, pooled=None, ws=None, stream=None, kmax=None, kmin=None, block=16):
+    """Stage 1 with the shared (Ada-KV) budget.  kept_idx [B,Hkv,out_cap], kept_count [B,Hkv] int32;
+    k_out, v_out [B,Hkv,out_cap,d] or None; kmax/kmin as rk_snapkv_evict."""
+    _need_contig(q_win, k, v, kept_idx, kept_count, k_out, v_out, pooled, kmax, kmin)
+    B, Hq, W, d = q_win.shape
+    shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
+    ws = _ws(rk_snapkv_workspace_bytes(shape, seq_len, window), k, ws, stream)
+    out_cap = kept_idx.shape[2]
+    nblk_cap = kmax.shape[3] if kmax is not None else 0
+    _check(_lib.rk_adakv_evict(ctypes.byref(shape), _ptr(q_win), _ptr(k), _ptr(v), k.shape[2], seq_len, window,
+                               pool_kernel, n_keep, _ptr(kept_idx), _ptr(kept_count), _ptr(k_out), _ptr(v_out),
+                               out_cap, _ptr(pooled), _ptr(kmax), _ptr(kmin), nblk_cap, block, _ptr(ws), ws.numel(),
+                               _stream(stream)), "rk_adakv_evict")
+    return ws
+
+
+def rk_hsa_decode_ragged(q, k, v, kmax, kmin, unit_tokens, max_tokens, block, k1, k2, out, sel_blocks=None,
+                         sel_channels=None, block_scores=None, ws=None, stream=None):
+    """rk_hsa_decode with a token count per unit (unit_tokens [B,Hkv] int32 on the device)."""
+    _need_contig(q, k, v, kmax, kmin, unit_tokens, out, sel_blocks, sel_channels, block_scores)
+    B, Hq, d = q.shape
+    shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
+    ws = _ws(rk_hsa_workspace_bytes(shape, max_tokens, block, k1, k2), k, ws, stream)
+    _check(_lib.rk_hsa_decode_ragged(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), k.shape[2], _ptr(kmax),
+                                     _ptr(kmin), kmax.shape[3], _ptr(unit_tokens), max_tokens, block, k1, k2,
+                                     _ptr(out), _ptr(sel_blocks), _ptr(sel_channels), _ptr(block_scores),
+                                     _ptr(ws), ws.numel(), _stream(stream)), "rk_hsa_decode_ragged")
+    return ws
+
+
 def aux_capacity(n_tokens: int, block: int) -> int:
     """Smallest valid nblk_cap for n_tokens: the page count rounded up to 8."""
     return (-(-n_tokens // block) + 7) // 8 * 8

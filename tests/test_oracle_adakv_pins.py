@@ -22,9 +22,10 @@ def test_worked_example_concentrated_head_keeps_fewer():
 
 @pytest.mark.parametrize("seed", range(6))
 def test_equal_heads_reduce_to_per_head_snapkv(seed):
-    """When every head has the same pooled scores the shared budget splits
-    evenly (the cut's ties span all heads), so each head keeps exactly its
-    SnapKV selection."""
+    """When every head has the same pooled scores, and no value at the cut is
+    repeated within a head, the shared budget splits evenly (the cut value's
+    copies span the heads), so each head keeps exactly its SnapKV selection.
+    (A value repeated within a head at the cut goes to the lower heads first.)"""
     rng = np.random.default_rng(seed)
     S, W, n_keep, H = 200, 8, 57, 4
     row = rng.standard_normal(S - W).astype(np.float32)
@@ -64,3 +65,14 @@ def test_adakv_evict_on_a_small_prompt_conserves_the_budget():
     res = O.adakv_evict(q, k, W, 7, 60)
     assert (res["counts"].sum(axis=1) == Hkv * 60).all()
     assert 17 in res["kept"][0][1].tolist()
+
+
+def test_equal_heads_with_a_tied_cut_favour_the_lower_heads():
+    """Equal heads whose cut value repeats within a head: the tied copies are
+    taken head by head, lowest head first (the flattened order)."""
+    S, W, n_keep = 10, 2, 5                     # 3 prefix slots per head, 6 shared
+    row = np.array([5, 3, 3, 3, 3, 0, 0, 0], np.float32)
+    kept = O.adakv_select(np.tile(row, (2, 1)), S, W, n_keep)
+    # 5 in both heads (2 slots), then four 3s of head 0 (4 slots)
+    assert kept[0].tolist() == [0, 1, 2, 3, 4, 8, 9]
+    assert kept[1].tolist() == [0, 8, 9]
