@@ -535,7 +535,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        # storage type of q, K and V; products accumulate in float32 either way
+        "dtype": main_res["config"]["kv_dtype"],
         "data": "synthetic",
         "config": main_res["config"],
     }
