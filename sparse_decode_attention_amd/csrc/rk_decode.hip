@@ -695,8 +695,10 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
     CacheIn<T, APP> kmin, int64_t nblk_cap, int nblk, int k1, int nsel, int npc,
     int n_tokens, int block, float scale_log2, float* __restrict__ out,
     int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt,
-    AppendPtrs<T> app, PagedArgs pga, const int32_t* __restrict__ lens) {
-  constexpr int TPS = AttnShape<T, D, G>::TPS;
+    AppendPtrs<T> app, PagedArgs pga, const int32_t* __restrict__ lens, int cand_in_lds) {
+  // tokens per slot per step: MT 2 (with its candidate indices in LDS, 1, 3,
+  // 4, 8 and 10 measured 0.6-3.5 us per step slower at batch 8 x 32 heads)
+  constexpr int TPS = MT ? 2 : AttnShape<T, D, G>::TPS;
   using S = AttnShape<T, D, G, TPS>;
   constexpr int EPL = S::EPL, LPR = S::LPR;
   constexpr int NT = kFusedThreads, NW = NT / kWave;
@@ -704,7 +706,10 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   uint32_t* pkeys = reinterpret_cast<uint32_t*>(dyn_lds);
   int* pages = reinterpret_cast<int*>(pkeys + ((nblk + 3) & ~3));
-  unsigned char* region = reinterpret_cast<unsigned char*>(pages + ((nsel + 3) & ~3));
+  // MT with cand_in_lds: the unit's candidate indices [roundup4(n_tokens)]
+  int32_t* cand_l = reinterpret_cast<int32_t*>(pages + ((nsel + 3) & ~3));
+  unsigned char* region = reinterpret_cast<unsigned char*>(
+      cand_l + (MT && cand_in_lds ? (n_tokens + 3) & ~3 : 0));
   T* stage = reinterpret_cast<T*>(region);
   float* wm = reinterpret_cast<float*>(region);
   float* wl = wm + NW * G;
@@ -769,6 +774,21 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
       for (int g = 0; g < G; ++g) qx[r][g] = to_f32(q[(size_t(u) * G + g) * D + r * kWave + lane]);
     wave_choose_channels<T, D, G>(qx, k1, i1_q, i1_off, chan_opt ? chan_opt + size_t(u) * k1 : nullptr,
                                   tsm.hist[0]);
+  } else if (MT && cand_in_lds) {
+    // RocketKV-MT: the unit's candidate indices do not depend on the page
+    // choice, so waves 1.. fetch all of them into LDS while wave 0 chooses
+    // the channels (8 loads per thread in flight per round); the streaming
+    // then finds each chosen token's row without a memory round trip
+    const int32_t* cg = cand + size_t(u) * size_t(cand_stride);
+    constexpr int NC = 8, NTC = NT - kWave;
+    for (int i0 = t - kWave; i0 < n_unit; i0 += NTC * NC) {
+      int32_t cb[NC];
+#pragma unroll
+      for (int x = 0; x < NC; ++x) cb[x] = i0 + x * NTC < n_unit ? cg[i0 + x * NTC] : 0;
+#pragma unroll
+      for (int x = 0; x < NC; ++x)
+        if (i0 + x * NTC < n_unit) cand_l[i0 + x * NTC] = cb[x];
+    }
   }
   __syncthreads();
   RK_PHASE(1);
@@ -830,7 +850,7 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   const size_t ubase = PAGED ? 0 : size_t(u) * size_t(kv_cap) * D;
   const T* ku = k + ubase + c * EPL;
   const T* vu = v + ubase + c * EPL;
-  const int32_t* cu = MT ? cand + size_t(u) * size_t(cand_stride) : nullptr;
+  const int32_t* cu = MT ? (cand_in_lds ? cand_l : cand + size_t(u) * size_t(cand_stride)) : nullptr;
   attend_pages<T, D, G, MT, TPS, PAGED>(qf, ku, vu, cu, kv_cap, pages, wave, nsel_u, NW, block, n_cached,
                                         scale_log2, m, l, o, up);
   if constexpr (APP) {
@@ -877,11 +897,13 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
 }
 
 // Dynamic LDS of the fused kernel for a chunk of npc pages.
-inline size_t fused_lds_bytes(int nblk, int nsel, int npc, int k1p, size_t esize, int D, int G) {
+inline size_t fused_lds_bytes(int nblk, int nsel, int npc, int k1p, size_t esize, int D, int G,
+                              int64_t n_cand) {
   const size_t stage = size_t(npc) * k1p * esize;
   constexpr int NW = kFusedThreads / kWave;
   const size_t merge = (size_t(2) * NW * G + size_t(NW) * G * D) * sizeof(float);
-  return size_t((nblk + 3) & ~3) * 4 + size_t((nsel + 3) & ~3) * 4 + (stage > merge ? stage : merge);
+  return size_t((nblk + 3) & ~3) * 4 + size_t((nsel + 3) & ~3) * 4 + size_t((n_cand + 3) & ~3) * 4 +
+         (stage > merge ? stage : merge);
 }
 
 // One wave per (unit, head) merges the split partials.  Lane s (< n_split)
@@ -977,15 +999,23 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   if constexpr (G <= 4) if (!presel && (units >= kFusedMinUnits || lay.nsel <= kFusedThreads / kWave)) {
     // one workgroup per unit: chunk of npc pages within the LDS budget
     const int k1pf = (k1 + 15) / 16 * 16 + int(16 / sizeof(T));
-    const size_t fixed = fused_lds_bytes(nblk, lay.nsel, 0, k1pf, sizeof(T), D, G);
-    const size_t keys_sel = size_t((nblk + 3) & ~3) * 4 + size_t((lay.nsel + 3) & ~3) * 4;
+    // MT: the candidate indices go to LDS when they leave room for a staged
+    // chunk of at least 64 pages
+    const int64_t cand_words = (n_tokens + 3) & ~int64_t(3);
+    const bool cand_lds = cand && size_t((nblk + 3) & ~3) * 4 + size_t((lay.nsel + 3) & ~3) * 4 +
+                                         size_t(cand_words) * 4 + size_t(64) * k1pf * sizeof(T) <=
+                                     kFusedLdsBudget;
+    const int64_t n_cand = cand_lds ? n_tokens : 0;
+    const size_t fixed = fused_lds_bytes(nblk, lay.nsel, 0, k1pf, sizeof(T), D, G, n_cand);
+    const size_t keys_sel = size_t((nblk + 3) & ~3) * 4 + size_t((lay.nsel + 3) & ~3) * 4 +
+                            size_t((n_cand + 3) & ~3) * 4;
     int npc = kFusedLdsBudget > keys_sel
                   ? int((kFusedLdsBudget - keys_sel) / (size_t(k1pf) * sizeof(T))) / 8 * 8
                   : 0;
     const int nblk8 = (nblk + 7) / 8 * 8;
     npc = npc > nblk8 ? nblk8 : npc;
     if (npc >= 8 && fixed <= kFusedLdsBudget) {
-      const size_t lds = fused_lds_bytes(nblk, lay.nsel, npc, k1pf, sizeof(T), D, G);
+      const size_t lds = fused_lds_bytes(nblk, lay.nsel, npc, k1pf, sizeof(T), D, G, n_cand);
       static bool fattr = false;  // once per template instantiation
       if (!fattr) {
         for (const void* f : {reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, true>),
@@ -1009,7 +1039,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
             s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), kv_cap, \
             cand, cand_stride, static_cast<const T*>(kmax), static_cast<const T*>(kmin), nblk_cap,  \
             nblk, k1, lay.nsel, npc, int(n_tokens), block, scale_log2, out, sel_opt, chan_opt,      \
-            s1_opt, ap, pg, lens)
+            s1_opt, ap, pg, lens, cand_lds ? 1 : 0)
       if (cand)
         RK_FUSED("hsa_fused_mt", true, false, false);
       else if (paged && app)

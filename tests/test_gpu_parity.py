@@ -479,6 +479,15 @@ def test_fused_mt_decode(rk):
     _decode_only(rk, w, 700, 32, 12, cand_total=2900, units_to_check=[(0, 0), (2, 17), (4, 31)])
 
 
+def test_fused_mt_decode_long_candidate_list(rk):
+    """A candidate list too long for the fused workgroup's LDS (40 000 indices,
+    160 KB): the streaming reads the indices from memory instead."""
+    say("fused MT decode, 160 units, 40000 candidates")
+    base = WL.WORKLOADS["mt-mha-b8-s32k-c32"]
+    w = WL.scaled(base, batch=5, n_q=32, n_kv=32, seq=41000, n_plant=4)
+    _decode_only(rk, w, 40000, 32, 12, cand_total=41000, units_to_check=[(0, 0), (4, 31)], steps=1)
+
+
 def test_split_decode_many_workgroups(rk):
     """96 units on the split-K path with 768 attention workgroups (more than one
     per CU: the two-tokens-per-slot variant), next to the batch-1 tests that run
