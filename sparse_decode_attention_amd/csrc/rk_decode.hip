@@ -464,18 +464,30 @@ __device__ __forceinline__ void attend_pages(
   const int npw = e_end > e_begin ? (e_end - e_begin + e_step - 1) / e_step : 0;
   const int ntok = npw * block;
   for (int tc = 0; tc < ntok; tc += CHUNK) {
-    int rows[TPS];
+    int rows[TPS], tok[TPS];
     bool ok[TPS];
+    // every token's page entry, then every token's row lookup (MT candidate
+    // index, paged table entry), with no branch between them, so the reads
+    // of a step are in flight together; masked tokens read token 0's entry
 #pragma unroll
     for (int i = 0; i < TPS; ++i) {
       const int tau = tc + slot + SLOTS * i;
       const int pr = tau / block;
-      const int tok = tau < ntok ? pages[e_begin + pr * e_step] * block + (tau - pr * block) : n_tokens;
-      ok[i] = tok < n_tokens;
+      const int prc = pr < npw ? pr : npw - 1;  // past the wave's pages: its last one
+      const int t0 = pages[e_begin + prc * e_step] * block + (tau - pr * block);
+      ok[i] = pr < npw && t0 < n_tokens;
+      tok[i] = ok[i] ? t0 : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < TPS; ++i) {
+      int r;
       if constexpr (PAGED)
-        rows[i] = ok[i] ? paged_row(up.table, tok, up.n_phys, up.shift, up.hkv, up.h) : 0;
+        r = paged_row(up.table, tok[i], up.n_phys, up.shift, up.hkv, up.h);
+      else if constexpr (MT)
+        r = clamp_row(cu[tok[i]], kv_cap);
       else
-        rows[i] = ok[i] ? (MT ? clamp_row(cu[tok], kv_cap) : tok) : 0;
+        r = tok[i];
+      rows[i] = ok[i] ? r : 0;
     }
     step(rows, ok);
   }
@@ -695,7 +707,7 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
     CacheIn<T, APP> kmin, int64_t nblk_cap, int nblk, int k1, int nsel, int npc,
     int n_tokens, int block, float scale_log2, float* __restrict__ out,
     int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt,
-    AppendPtrs<T> app, PagedArgs pga, const int32_t* __restrict__ lens, int cand_in_lds) {
+    AppendPtrs<T> app, PagedArgs pga, const int32_t* __restrict__ lens) {
   // tokens per slot per step: MT 2 (with its candidate indices in LDS, 1, 3,
   // 4, 8 and 10 measured 0.6-3.5 us per step slower at batch 8 x 32 heads)
   constexpr int TPS = MT ? 2 : AttnShape<T, D, G>::TPS;
@@ -706,10 +718,9 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   uint32_t* pkeys = reinterpret_cast<uint32_t*>(dyn_lds);
   int* pages = reinterpret_cast<int*>(pkeys + ((nblk + 3) & ~3));
-  // MT with cand_in_lds: the unit's candidate indices [roundup4(n_tokens)]
+  // MT: the unit's candidate indices [roundup4(n_tokens)]
   int32_t* cand_l = reinterpret_cast<int32_t*>(pages + ((nsel + 3) & ~3));
-  unsigned char* region = reinterpret_cast<unsigned char*>(
-      cand_l + (MT && cand_in_lds ? (n_tokens + 3) & ~3 : 0));
+  unsigned char* region = reinterpret_cast<unsigned char*>(cand_l + (MT ? (n_tokens + 3) & ~3 : 0));
   T* stage = reinterpret_cast<T*>(region);
   float* wm = reinterpret_cast<float*>(region);
   float* wl = wm + NW * G;
@@ -774,7 +785,7 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
       for (int g = 0; g < G; ++g) qx[r][g] = to_f32(q[(size_t(u) * G + g) * D + r * kWave + lane]);
     wave_choose_channels<T, D, G>(qx, k1, i1_q, i1_off, chan_opt ? chan_opt + size_t(u) * k1 : nullptr,
                                   tsm.hist[0]);
-  } else if (MT && cand_in_lds) {
+  } else if (MT) {
     // RocketKV-MT: the unit's candidate indices do not depend on the page
     // choice, so waves 1.. fetch all of them into LDS while wave 0 chooses
     // the channels (8 loads per thread in flight per round); the streaming
@@ -850,7 +861,7 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   const size_t ubase = PAGED ? 0 : size_t(u) * size_t(kv_cap) * D;
   const T* ku = k + ubase + c * EPL;
   const T* vu = v + ubase + c * EPL;
-  const int32_t* cu = MT ? (cand_in_lds ? cand_l : cand + size_t(u) * size_t(cand_stride)) : nullptr;
+  const int32_t* cu = MT ? cand_l : nullptr;
   attend_pages<T, D, G, MT, TPS, PAGED>(qf, ku, vu, cu, kv_cap, pages, wave, nsel_u, NW, block, n_cached,
                                         scale_log2, m, l, o, up);
   if constexpr (APP) {
@@ -999,13 +1010,12 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   if constexpr (G <= 4) if (!presel && (units >= kFusedMinUnits || lay.nsel <= kFusedThreads / kWave)) {
     // one workgroup per unit: chunk of npc pages within the LDS budget
     const int k1pf = (k1 + 15) / 16 * 16 + int(16 / sizeof(T));
-    // MT: the candidate indices go to LDS when they leave room for a staged
-    // chunk of at least 64 pages
-    const int64_t cand_words = (n_tokens + 3) & ~int64_t(3);
-    const bool cand_lds = cand && size_t((nblk + 3) & ~3) * 4 + size_t((lay.nsel + 3) & ~3) * 4 +
-                                         size_t(cand_words) * 4 + size_t(64) * k1pf * sizeof(T) <=
-                                     kFusedLdsBudget;
-    const int64_t n_cand = cand_lds ? n_tokens : 0;
+    // MT: the candidate indices go to LDS; a list that leaves no room for a
+    // staged chunk of 64 pages takes the split path
+    const int64_t n_cand = cand ? n_tokens : 0;
+    const bool cand_fits = size_t((nblk + 3) & ~3) * 4 + size_t((lay.nsel + 3) & ~3) * 4 +
+                               size_t((n_cand + 3) & ~3) * 4 + size_t(64) * k1pf * sizeof(T) <=
+                           kFusedLdsBudget;
     const size_t fixed = fused_lds_bytes(nblk, lay.nsel, 0, k1pf, sizeof(T), D, G, n_cand);
     const size_t keys_sel = size_t((nblk + 3) & ~3) * 4 + size_t((lay.nsel + 3) & ~3) * 4 +
                             size_t((n_cand + 3) & ~3) * 4;
@@ -1014,7 +1024,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
                   : 0;
     const int nblk8 = (nblk + 7) / 8 * 8;
     npc = npc > nblk8 ? nblk8 : npc;
-    if (npc >= 8 && fixed <= kFusedLdsBudget) {
+    if (npc >= 8 && fixed <= kFusedLdsBudget && cand_fits) {
       const size_t lds = fused_lds_bytes(nblk, lay.nsel, npc, k1pf, sizeof(T), D, G, n_cand);
       static bool fattr = false;  // once per template instantiation
       if (!fattr) {
@@ -1039,7 +1049,7 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
             s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), kv_cap, \
             cand, cand_stride, static_cast<const T*>(kmax), static_cast<const T*>(kmin), nblk_cap,  \
             nblk, k1, lay.nsel, npc, int(n_tokens), block, scale_log2, out, sel_opt, chan_opt,      \
-            s1_opt, ap, pg, lens, cand_lds ? 1 : 0)
+            s1_opt, ap, pg, lens)
       if (cand)
         RK_FUSED("hsa_fused_mt", true, false, false);
       else if (paged && app)

@@ -479,13 +479,22 @@ def test_fused_mt_decode(rk):
     _decode_only(rk, w, 700, 32, 12, cand_total=2900, units_to_check=[(0, 0), (2, 17), (4, 31)])
 
 
-def test_fused_mt_decode_long_candidate_list(rk):
-    """A candidate list too long for the fused workgroup's LDS (40 000 indices,
-    160 KB): the streaming reads the indices from memory instead."""
-    say("fused MT decode, 160 units, 40000 candidates")
+def test_mt_decode_long_candidate_list_many_units(rk):
+    """160 units whose candidate lists (40 000 indices, 160 KB) do not fit the
+    fused workgroup's LDS: the split path, which reads them from memory."""
+    say("MT decode, 160 units, 40000 candidates")
     base = WL.WORKLOADS["mt-mha-b8-s32k-c32"]
     w = WL.scaled(base, batch=5, n_q=32, n_kv=32, seq=41000, n_plant=4)
     _decode_only(rk, w, 40000, 32, 12, cand_total=41000, units_to_check=[(0, 0), (4, 31)], steps=1)
+    kc, vc, _ = WL.layer_kv(w, 0, device=DEV)
+    cand = torch.arange(40000, device=DEV, dtype=torch.int32).repeat(5, 32, 1).contiguous()
+    kmax = torch.empty(5, 32, 128, rk.aux_capacity(40000, 16), dtype=kc.dtype, device=DEV)
+    kmin = torch.empty_like(kmax)
+    rk.rk_hsa_build_aux(kc, 40000, 0, 16, kmax, kmin, idx=cand)
+    rk.rk_profile_begin()
+    rk.rk_hsa_decode_mt(WL.decode_query(w, 0, 0, device=DEV), kc, vc, cand, 40000, kmax, kmin, 16, 32, 12,
+                        torch.empty(5, 32, 128, device=DEV))
+    assert set(rk.rk_profile_end()) == {"hsa_score", "hsa_attn_mt", "hsa_combine"}
 
 
 def test_split_decode_many_workgroups(rk):
