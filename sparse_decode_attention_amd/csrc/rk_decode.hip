@@ -368,9 +368,11 @@ __global__ __launch_bounds__(1024) void page_select_kernel(const uint32_t* __res
 
 // ---- step 3 building blocks -------------------------------------------------
 // A wave streams whole pages.  Lanes split a row into LPR 16-byte chunks, so
-// SLOTS tokens are in flight per wave and each slot takes TPS tokens per chunk
-// before one softmax rescale.  Per lane: running max m, sum l and o over its
-// channel chunk, per head of the group, in the exp2 domain.
+// SLOTS tokens are in flight per wave and each slot takes TPS tokens per chunk.
+// Per lane: a reference m (at most kLazyRescale below the running maximum),
+// the sum l and o over its channel chunk of exp2(score - m) weights, per
+// head of the group, in the exp2 domain.
+constexpr float kLazyRescale = 8.0f;
 template <typename T, int D, int G, int TPS_ = (G >= 4 ? 2 : 4)>
 struct AttnShape {
   static constexpr int EPL = Vec16<T>::N;
@@ -403,6 +405,15 @@ __device__ __forceinline__ void attend_pages(
   using S = AttnShape<T, D, G, TPS_>;
   constexpr int EPL = S::EPL, LPR = S::LPR, SLOTS = S::SLOTS, TPS = S::TPS, CHUNK = S::CHUNK;
   const int slot = lane_id() / LPR;
+  // bf16: q's values (bf16 to begin with, so exact) as packed pairs
+  uint32_t qp[G][4];
+  if constexpr (std::is_same_v<T, bf16_t>) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        qp[g][e2] = (__float_as_uint(qf[g][2 * e2]) >> 16) | (__float_as_uint(qf[g][2 * e2 + 1]) & 0xffff0000u);
+  }
   // One step: TPS tokens per slot (rows[i], valid when ok[i]): K and V rows
   // with 16-byte loads, scores, one online-softmax rescale, V accumulation.
   auto step = [&](const int (&rows)[TPS], const bool (&ok)[TPS]) {
@@ -422,16 +433,32 @@ __device__ __forceinline__ void attend_pages(
         vr[i].raw = {};
       }
     float x[G][TPS];
+    if constexpr (std::is_same_v<T, bf16_t>) {
+      // bf16: the key's packed pairs straight into two-term dot products
+      // with q's pairs (no unpacking of the key)
 #pragma unroll
-    for (int i = 0; i < TPS; ++i) {
-      float kf[EPL];
-      unpack16(kr[i], kf);
+      for (int i = 0; i < TPS; ++i) {
+        const uint32_t kw[4] = {kr[i].raw.x, kr[i].raw.y, kr[i].raw.z, kr[i].raw.w};
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float s = 0.f;
+        for (int g = 0; g < G; ++g) {
+          float s = 0.f;
 #pragma unroll
-        for (int ee = 0; ee < EPL; ++ee) s += qf[g][ee] * kf[ee];
-        x[g][i] = group_sum<LPR>(s) * scale_log2;
+          for (int e2 = 0; e2 < 4; ++e2) s = dot2_bf16(qp[g][e2], kw[e2], s);
+          x[g][i] = group_sum<LPR>(s) * scale_log2;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPS; ++i) {
+        float kf[EPL];
+        unpack16(kr[i], kf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float s = 0.f;
+#pragma unroll
+          for (int ee = 0; ee < EPL; ++ee) s += qf[g][ee] * kf[ee];
+          x[g][i] = group_sum<LPR>(s) * scale_log2;
+        }
       }
     }
 #pragma unroll
@@ -440,20 +467,29 @@ __device__ __forceinline__ void attend_pages(
 #pragma unroll
       for (int i = 0; i < TPS; ++i)
         if (ok[i]) cm = fmaxf(cm, x[g][i]);
-      const float mn = fmaxf(m[g], cm);
-      const float corr = fast_exp2(m[g] - mn);
+      // the reference m moves (and l, o are rescaled) only when a score
+      // passes it by more than kLazyRescale, which after the first step is
+      // rare; the weights exp2(x - m) then stay below 2^kLazyRescale
+      const bool up = cm > m[g] + kLazyRescale;
+      if (ballot(up)) {
+        const float mn = up ? cm : m[g];
+        const float corr = fast_exp2(m[g] - mn);
+        l[g] = l[g] * corr;
+#pragma unroll
+        for (int ee = 0; ee < EPL; ++ee) o[g][ee] = o[g][ee] * corr;
+        m[g] = mn;
+      }
       float p[TPS];
       float ps = 0.f;
 #pragma unroll
       for (int i = 0; i < TPS; ++i) {
-        p[i] = ok[i] ? fast_exp2(x[g][i] - mn) : 0.f;
+        p[i] = ok[i] ? fast_exp2(x[g][i] - m[g]) : 0.f;
         ps += p[i];
       }
-      l[g] = l[g] * corr + ps;
-      m[g] = mn;
+      l[g] = l[g] + ps;
 #pragma unroll
       for (int ee = 0; ee < EPL; ++ee) {
-        float acc = o[g][ee] * corr;
+        float acc = o[g][ee];
 #pragma unroll
         for (int i = 0; i < TPS; ++i) acc += p[i] * vr[i].get(ee);
         o[g][ee] = acc;

@@ -114,6 +114,13 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 // round trip, which costs two extra instructions per call).
 __device__ __forceinline__ unsigned long long ballot(bool b) { return __builtin_amdgcn_ballot_w64(b); }
 
+// a.lo * b.lo + a.hi * b.hi + c over packed bf16 pairs (v_dot2c_f32_bf16)
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a), __builtin_bit_cast(bf16x2_v, b), c,
+                                         false);
+}
+
 // XCD-aware work mapping.  MI355X deals the workgroups of a launch out to its
 // 8 XCDs round robin (workgroup L to XCD L mod 8), and each XCD has its own
 // L2.  With a 1-D grid of 8 * ceil(n/8) workgroups, XCD x here takes the
