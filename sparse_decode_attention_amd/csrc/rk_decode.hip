@@ -191,7 +191,6 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
   const int np = min(ppw, nblk_u - p0);
   const int t = threadIdx.x;
   const int wave = t / kWave, lane = lane_id();
-  RK_PHASE(16);
   const T* xu = kmax + size_t(u) * D * size_t(nblk_cap) + p0;
   const T* nu = kmin + size_t(u) * D * size_t(nblk_cap) + p0;
   const int nv = (np + EPV - 1) / EPV;  // 16-byte vectors per row slice
@@ -219,7 +218,6 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
     wave_choose_channels<T, D, G>(qx, k1, i1_q, i1_off,
                                   chan_opt && p0 == 0 ? chan_opt + size_t(u) * k1 : nullptr,
                                   hist);
-  RK_PHASE(17);
   if (ALL) {
 #pragma unroll
     for (int x = 0; x < NBA; ++x) {
@@ -231,7 +229,6 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
     }
   }
   __syncthreads();
-  RK_PHASE(18);
   uint32_t* ku = keys + size_t(u) * keys_pitch + p0;
   if (ALL) {
     // s1[b] = sum over i1 (ascending) of q_bar_i * P_i[b], P_i read from the
@@ -249,7 +246,6 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
       prod[b * pp + j] = i1_q[j] * to_f32(stage[size_t(r) * ppw + b]);
     }
     __syncthreads();
-    RK_PHASE(19);
     for (int b = t; b < np; b += 256) {
       const float* pb = prod + b * pp;
       float acc = 0.f;
@@ -275,7 +271,6 @@ __global__ __launch_bounds__(256) void hsa_score_kernel(
       ku[b] = order_key(acc);
       if (s1_opt) s1_opt[size_t(u) * nblk + p0 + b] = acc;
     }
-    RK_PHASE(20);
     return;
   }
 
@@ -654,7 +649,6 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
     for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
   }
 
-  RK_PHASE(8);
   // ragged units: this unit's tokens, pages and chosen pages
   const int n_u = lens ? max(1, min(lens[u], n_tokens)) : n_tokens;
   const int nblk_u = lens ? (n_u + block - 1) / block : nblk;
@@ -688,7 +682,6 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
   if (so)  // ranks past a ragged unit's choice
     for (int r = nsel_u + threadIdx.x; r < nsel; r += 256) so[r] = -1;
   __syncthreads();
-  RK_PHASE(10);
 
   const size_t ubase = PAGED ? 0 : size_t(u) * size_t(kv_cap) * D;
   const T* ku = k + ubase + c * EPL;
@@ -701,7 +694,6 @@ __global__ __launch_bounds__(256) void hsa_attn_kernel(
                                          scale_log2, m, l, o, up);
   wave_state_to_lds<T, D, G>(m, l, o, wave, wm, wl, wo);
   __syncthreads();
-  RK_PHASE(11);
   // merge the 4 waves in order and write this split's partial per head
   float* pw = partials + (size_t(u) * n_split + split) * G * PF;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
@@ -787,7 +779,6 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   const int wave = t / kWave, lane = lane_id();
   const int c = lane % LPR;
 
-  RK_PHASE(0);
   float qf[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) unpack16(load16(q + (size_t(u) * G + g) * D + c * EPL), qf[g]);
@@ -855,7 +846,6 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
     }
   }
   __syncthreads();
-  RK_PHASE(1);
 
   const T* xu = kmax + size_t(u) * D * size_t(nblk_cap);
   const T* nu = kmin + size_t(u) * D * size_t(nblk_cap);
@@ -886,7 +876,6 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
     __syncthreads();
   }
 
-  RK_PHASE(2);
   int32_t* so = sel_opt ? sel_opt + size_t(u) * nsel : nullptr;
   auto emit = [=](int r, int i) {
     pages[r] = i;
@@ -901,7 +890,6 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   if (so)  // ranks past a ragged unit's choice
     for (int r = nsel_u + t; r < nsel; r += NT) so[r] = -1;
   __syncthreads();
-  RK_PHASE(3);
 
   float m[G], l[G], o[G][EPL];
 #pragma unroll
@@ -938,10 +926,8 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
       }
     }
   }
-  RK_PHASE(4);
   wave_state_to_lds<T, D, G>(m, l, o, wave, wm, wl, wo);  // the staged chunk is no longer read
   __syncthreads();
-  RK_PHASE(5);
   for (int idx = t; idx < G * D; idx += NT) {
     float mm, ll, oo;
     merge_waves<D, G, NW>(idx, wm, wl, wo, &mm, &ll, &oo);

@@ -7,11 +7,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// Phase marker for external timing probes; compiles to nothing in the library.
-#ifndef RK_PHASE
-#define RK_PHASE(slot)
-#endif
-
 namespace rk {
 
 constexpr int kWave = 64;
@@ -237,12 +232,10 @@ __device__ __forceinline__ void wg_topk_emit(const KeyFn& key, int n, uint32_t T
   if (all_eq) {
     int n_ge = 0;
     for (int i = lo; i < hi; ++i) n_ge += key(i) >= T ? 1 : 0;
-    RK_PHASE(6);
     int total;
     int pos = wg_excl_scan<NT>(n_ge, tmp, &total);
     for (int i = lo; i < hi; ++i)
       if (key(i) >= T) emit(pos++, i);
-    RK_PHASE(7);
     return;
   }
   int n_gt = 0, n_eq = 0;
@@ -251,7 +244,6 @@ __device__ __forceinline__ void wg_topk_emit(const KeyFn& key, int n, uint32_t T
     n_gt += kk > T;
     n_eq += kk == T;
   }
-  RK_PHASE(6);
   const int2 before = wg_excl_scan2<NT>(n_gt, n_eq, tmp);
   int eq_seen = before.y;
   int pos = before.x + min(before.y, need_eq);
@@ -264,7 +256,6 @@ __device__ __forceinline__ void wg_topk_emit(const KeyFn& key, int n, uint32_t T
     }
     if (sel) emit(pos++, i);
   }
-  RK_PHASE(7);
 }
 
 // Workgroup top-k: calls emit(rank, position) for the k largest keys among
@@ -392,7 +383,6 @@ __device__ __forceinline__ uint3 wave_rank_range(const uint32_t (&kz)[R], int /*
     }
   }
   __builtin_amdgcn_wave_barrier();
-  RK_PHASE(25);
   const uint32_t mine = lane < cnt ? slots[lane] : 0u;
   int gt = 0, ge = 0;
 #pragma unroll
@@ -405,7 +395,6 @@ __device__ __forceinline__ uint3 wave_rank_range(const uint32_t (&kz)[R], int /*
       ge += sv[e] >= mine ? 1 : 0;
     }
   }
-  RK_PHASE(26);
   const unsigned long long hit = ballot(lane < cnt && gt < need && ge >= need);
   const int L = __ffsll(static_cast<long long>(hit)) - 1;
   const int gtL = __builtin_amdgcn_readlane(gt, L), geL = __builtin_amdgcn_readlane(ge, L);
@@ -474,9 +463,7 @@ __device__ __forceinline__ TopkCut wave_topk_cut(const uint32_t (&kz)[R], int n,
       return cut;
     }
     if (in_range <= kWaveRankMax) {
-      RK_PHASE(24);
       const uint3 c = wave_rank_range(kz, n, lo, hi, need, hist);
-      RK_PHASE(27);
       cut.T = cut.thr = c.x;
       cut.need_eq = int(c.y);
       cut.fast = c.y == c.z;
@@ -566,9 +553,7 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&kr)[R], int n, int k,
   }
   uint32_t kz[R], lo, hi;
   topk_prepare(kr, n, kz, lo, hi);
-  RK_PHASE(9);
   const TopkCut cut = wave_topk_cut<R, 256>(kz, n, k, lo, hi, hist);
-  RK_PHASE(23);
   wave_emit_cut(kz, n, cut, emit, rank_lo, rank_hi);
 }
 
@@ -643,7 +628,6 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
     lo = min(lo, sm.red[w]);
     hi = max(hi, sm.red[NW + w]);
   }
-  RK_PHASE(13);
   int need = k;      // keys still to take among the candidates [lo, hi]
   int in_range = n;  // candidates in [lo, hi]
   uint32_t T;        // threshold: keys above are taken, need_eq of the keys equal to it
@@ -703,9 +687,6 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
     }
     from_cand = from_cand || gather;
     __syncthreads();
-    RK_PHASE(12);
-    if (pass == 0) RK_PHASE(14);
-    if (pass == 1) RK_PHASE(17);
     int3 f;
     if constexpr (NW > 4) {
       // one wave walks the histogram and shares the result: with several
@@ -720,7 +701,6 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
       }
       __syncthreads();
       f = make_int3(sm.tmp[0], sm.tmp[1], sm.tmp[2]);
-      if (pass == 0) RK_PHASE(18);
     } else {
       f = wave_find_bin<BINS>(h, need);
     }
@@ -745,7 +725,6 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
     need = f.y;
     in_range = f.z;
   }
-  RK_PHASE(15);
   if (n <= kWaveEmitMax) {
     if (wave == 0) {
       if (all_eq)  // keys >= T: keys above T - 1 (T >= 1 here, else all n keys would be taken)
@@ -756,7 +735,6 @@ __device__ __forceinline__ void wg_topk(const KeyFn& key, int n, int k, const Em
   } else {
     wg_topk_emit<NT>(key, n, T, need_eq, all_eq, emit, sm.tmp);
   }
-  RK_PHASE(16);
 }
 
 // Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32), result in every

@@ -321,7 +321,6 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
   const float* pu = pooled + size_t(u) * P;
   int32_t* ku = kept + size_t(u) * n_keep;
   auto emit = [&](int r, int i) { ku[r] = i; };
-  RK_PHASE(0);
   if (staged) {
     // 16-byte loads where the row allows it, all of a thread's loads in flight
     // (the key range comes along: no separate pass for it)
@@ -354,7 +353,6 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
     }
     for (int i = 4 * P4 + threadIdx.x; i < P; i += 1024) put(i, pu[i]);
     __syncthreads();
-    RK_PHASE(1);
     // the LDS after the keys (cand_cap words) takes the later passes' candidates
     wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, P, n_keep - W, emit, sm, true, lo, hi,
                         skeys + P, cand_cap);
@@ -796,7 +794,6 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
   // guarantees at most 4 items.  Its Q fragments stay in registers.
   const bool active = wave < items;
   const int rg = wave / CS, cs = wave % CS;
-  RK_PHASE(PASS == 1 ? 18 : 21);
   bf16x8_t a[KS];
   {
     const int arow = rg * 32 + (lane & 31);
@@ -843,7 +840,6 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
     stash();
   }
   __syncthreads();
-  RK_PHASE(PASS == 1 ? 19 : 22);
   for (int t0 = kb; t0 < ke; t0 += TK) {
     const bool next = t0 + TK < ke;
     if (next) fetch(t0 + TK);             // in flight while this tile is multiplied
@@ -918,7 +914,6 @@ __global__ __launch_bounds__(256, 4) void ws_mfma_kernel(
     }
     __syncthreads();
   }
-  RK_PHASE(PASS == 1 ? 20 : 23);
   if (PASS == 1) {
     if (wave < items) {
       // the two half-waves hold disjoint keys of the same 32 rows
