@@ -479,6 +479,39 @@ def test_fused_mt_decode(rk):
     _decode_only(rk, w, 700, 32, 12, cand_total=2900, units_to_check=[(0, 0), (2, 17), (4, 31)])
 
 
+@pytest.mark.parametrize("dtype,B,k2,mt", [
+    ("bf16", 1, 32, False),    # split path
+    ("bf16", 20, 16, False),   # one fused workgroup per unit
+    ("f32", 1, 32, False),
+    ("bf16", 40, 16, True),    # MT, fused (160 units of 4 query heads... here 320)
+])
+def test_decode_wide_score_range(rk, dtype, B, k2, mt):
+    """Scores spread over hundreds of log2 units, with the largest keys planted
+    late in the pages a wave walks: the online softmax's reference must move
+    (and l, o be rescaled) in the middle of the stream, not just at its start;
+    every unit checked against the oracle."""
+    say("wide score range", dtype, B, k2, mt)
+    Hkv, G, d, n, block, k1 = 8, 4, 128, 997, 16, 32
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = torch.randn(B, Hkv, n + 40, d, generator=gen).to(tdt)
+    vc = torch.randn(B, Hkv, n + 40, d, generator=gen).to(tdt)
+    q = (torch.randn(B, Hkv * G, d, generator=gen) * 6).to(tdt)
+    qbar = q.float().view(B, Hkv, G, d).sum(2)
+    # keys aligned with the group's mean query, ever stronger towards the end
+    # of the cache: token j of the planted set scores about 40 * (j + 1) above
+    # the rest (scaled by 1/sqrt(d) and log2 e, hundreds of log2 units)
+    plant = torch.tensor([100, 300, 520, 700, 900, 990])
+    for j, t in enumerate(plant.tolist()):
+        kc[:, :, t] = (qbar / qbar.norm(dim=-1, keepdim=True) * (3.0 * (j + 1))).to(tdt)
+    kc, vc, q = kc.to(DEV), vc.to(DEV), q.to(DEV)
+    cand = None
+    if mt:
+        cand = torch.arange(n, dtype=torch.int32, device=DEV).repeat(B, Hkv, 1).contiguous()
+    kmax, kmin = U.aux_and_check(rk, kc, n, block, Hkv * G, idx=cand)
+    U.decode_and_check(rk, q, kc, vc, kmax, kmin, n, block, k1, k2, cand=cand)
+
+
 def test_mt_decode_long_candidate_list_many_units(rk):
     """160 units whose candidate lists (40 000 indices, 160 KB) do not fit the
     fused workgroup's LDS: the split path, which reads them from memory."""
