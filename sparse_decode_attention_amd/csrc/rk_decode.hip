@@ -817,8 +817,6 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
         app_ox = app.kmax[a];
         app_on = app.kmin[a];
       }
-      app.k[app_row + ta] = app_kn;
-      app.v[app_row + ta] = app_vn;
     }
   }
   if (wave == 0) {
@@ -943,6 +941,8 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
     const size_t a = (size_t(u) * D + ta) * size_t(nblk_cap) + app_page;
     app.kmax[a] = mx;
     app.kmin[a] = mn;
+    app.k[app_row + ta] = app_kn;
+    app.v[app_row + ta] = app_vn;
   }
 }
 
