@@ -385,6 +385,9 @@ struct UnitPages {
   const int32_t* table;
   int64_t n_phys;
   int shift, hkv, h;
+  // when set: the first pool row of each of the sequence's pages for this
+  // unit's head, already clamped (the fused kernel keeps them in LDS)
+  const int32_t* base = nullptr;
 };
 
 // PAGED: ku / vu are the pool base (plus the lane's channel offset) and token
@@ -530,7 +533,8 @@ __device__ __forceinline__ void attend_pages(
     for (int i = 0; i < TPS; ++i) {
       int r;
       if constexpr (PAGED)
-        r = paged_row(up.table, tok[i], up.n_phys, up.shift, up.hkv, up.h);
+        r = up.base ? up.base[tok[i] >> up.shift] + (tok[i] & ((1 << up.shift) - 1))
+                    : paged_row(up.table, tok[i], up.n_phys, up.shift, up.hkv, up.h);
       else if constexpr (MT)
         r = clamp_row(cu[tok[i]], kv_cap);
       else
@@ -763,9 +767,11 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   uint32_t* pkeys = reinterpret_cast<uint32_t*>(dyn_lds);
   int* pages = reinterpret_cast<int*>(pkeys + ((nblk + 3) & ~3));
-  // MT: the unit's candidate indices [roundup4(n_tokens)]
+  // MT: the unit's candidate indices [roundup4(n_tokens)]; PAGED: the first
+  // pool row of each of its pages [roundup4(n_tokens / P)]
   int32_t* cand_l = reinterpret_cast<int32_t*>(pages + ((nsel + 3) & ~3));
-  unsigned char* region = reinterpret_cast<unsigned char*>(cand_l + (MT ? (n_tokens + 3) & ~3 : 0));
+  const int n_rows_l = MT ? n_tokens : PAGED ? ((n_tokens - 1) >> pga.shift) + 1 : 0;
+  unsigned char* region = reinterpret_cast<unsigned char*>(cand_l + ((n_rows_l + 3) & ~3));
   T* stage = reinterpret_cast<T*>(region);
   float* wm = reinterpret_cast<float*>(region);
   float* wl = wm + NW * G;
@@ -842,6 +848,11 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
       for (int x = 0; x < NC; ++x)
         if (i0 + x * NTC < n_unit) cand_l[i0 + x * NTC] = cb[x];
     }
+  } else if (PAGED) {
+    // paged pool: the same for the unit's block-table row, as pool row bases
+    const int n_pg = ((n_unit - 1) >> pga.shift) + 1;
+    for (int i = t - kWave; i < n_pg; i += NT - kWave)
+      cand_l[i] = (clamp_row(up.table[i], up.n_phys) * up.hkv + up.h) << up.shift;
   }
   __syncthreads();
 
@@ -901,8 +912,10 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
   const T* ku = k + ubase + c * EPL;
   const T* vu = v + ubase + c * EPL;
   const int32_t* cu = MT ? cand_l : nullptr;
+  UnitPages upl = up;
+  if constexpr (PAGED) upl.base = cand_l;
   attend_pages<T, D, G, MT, TPS, PAGED>(qf, ku, vu, cu, kv_cap, pages, wave, nsel_u, NW, block, n_cached,
-                                        scale_log2, m, l, o, up);
+                                        scale_log2, m, l, o, upl);
   if constexpr (APP) {
     // the new token, when its page was chosen (the last page, so the last
     // entry of the ascending list), goes to wave 0's token slot 0
@@ -1049,9 +1062,10 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
   if constexpr (G <= 4) if (!presel && (units >= kFusedMinUnits || lay.nsel <= kFusedThreads / kWave)) {
     // one workgroup per unit: chunk of npc pages within the LDS budget
     const int k1pf = (k1 + 15) / 16 * 16 + int(16 / sizeof(T));
-    // MT: the candidate indices go to LDS; a list that leaves no room for a
-    // staged chunk of 64 pages takes the split path
-    const int64_t n_cand = cand ? n_tokens : 0;
+    // MT: the candidate indices go to LDS, paged pools the page table's row
+    // bases; a list that leaves no room for a staged chunk of 64 pages takes
+    // the split path
+    const int64_t n_cand = cand ? n_tokens : paged ? ((n_tokens - 1) >> pg.shift) + 1 : 0;
     const bool cand_fits = size_t((nblk + 3) & ~3) * 4 + size_t((lay.nsel + 3) & ~3) * 4 +
                                size_t((n_cand + 3) & ~3) * 4 + size_t(64) * k1pf * sizeof(T) <=
                            kFusedLdsBudget;
