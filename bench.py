@@ -51,8 +51,8 @@ MODEL_LAYERS = 32            # the stacks the large workloads stand for
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mt-mha-b8-s32k-c32")
     ap.add_argument("--also", default="llama8b-stack-b32-s32k-c64",
                     help="a second workload measured in the same run ('' for none)")
