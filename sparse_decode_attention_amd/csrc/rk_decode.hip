@@ -733,10 +733,11 @@ struct AppendPtrs {
 // in flight per wave, hence the full 1024-thread workgroup (4 waves per SIMD).
 //
 // APP (a decode step that first appends token n_tokens - 1, as rk_append_kv
-// would): the workgroup writes the unit's new K/V row and the refreshed
-// Kmax/Kmin column of the last page up front, patches that column into its
-// own staged scores, and lets the new token into the attention from
-// registers rather than reading back what it wrote.
+// would): the workgroup reads the last page's Kmax/Kmin column up front,
+// patches the new key into its own staged copy of that column, lets the new
+// token into the attention from LDS, and writes the new K/V row and the
+// refreshed column at the very end (stores issued while the pages stream
+// slow the stream), never reading back what it wrote.
 //
 // Dynamic LDS: page keys [roundup4(nblk)] | chosen pages [roundup4(nsel)] |
 // a region holding first the staged chunk [npc][k1p], then the waves' merge
@@ -806,7 +807,7 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
                     : (size_t(u) * size_t(kv_cap) + size_t(n_cached)) * D;
   // APP: the new key (as T, for the patch) and the new K/V rows (as float,
   // for the attention) go to LDS; the page's old Kmax/Kmin column is fetched
-  // now and folded and written back at the end, off every critical path.
+  // now and folded and written back at the end, after the stream.
   // The last waves do this work: wave 0's loads for the channel choice must
   // not queue behind the scattered column reads.
   __shared__ T app_knt[APP ? D : 1];
