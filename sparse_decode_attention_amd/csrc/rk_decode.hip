@@ -750,8 +750,8 @@ using CacheIn = std::conditional_t<APP, const T*, const T* __restrict__>;
 //
 // PAGED: the K/V rows live in a paged pool (PagedArgs); the append writes its
 // row there too.
-template <typename T, int D, int G, bool MT, bool APP = false, bool PAGED = false>
-__global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
+template <typename T, int D, int G, bool MT, bool APP = false, bool PAGED = false, int NT_ = kFusedThreads>
+__global__ __launch_bounds__(NT_) void hsa_fused_kernel(
     const T* __restrict__ q, CacheIn<T, APP> k, CacheIn<T, APP> v, int64_t kv_cap,
     const int32_t* __restrict__ cand, int64_t cand_stride, CacheIn<T, APP> kmax,
     CacheIn<T, APP> kmin, int64_t nblk_cap, int nblk, int k1, int nsel, int npc,
@@ -759,11 +759,13 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
     int32_t* __restrict__ sel_opt, int32_t* __restrict__ chan_opt, float* __restrict__ s1_opt,
     AppendPtrs<T> app, PagedArgs pga, const int32_t* __restrict__ lens) {
   // tokens per slot per step: MT 2 (with its candidate indices in LDS, 1, 3,
-  // 4, 8 and 10 measured 0.6-3.5 us per step slower at batch 8 x 32 heads)
-  constexpr int TPS = MT ? 2 : AttnShape<T, D, G>::TPS;
+  // 4, 8 and 10 measured 0.6-3.5 us per step slower at batch 8 x 32 heads);
+  // the 512-thread form for groups of four holds 4 (registers are twice as
+  // plentiful per wave, so each wave keeps twice the rows in flight)
+  constexpr int TPS = MT ? 2 : NT_ == kFusedThreadsWide ? 4 : AttnShape<T, D, G>::TPS;
   using S = AttnShape<T, D, G, TPS>;
   constexpr int EPL = S::EPL, LPR = S::LPR;
-  constexpr int NT = kFusedThreads, NW = NT / kWave;
+  constexpr int NT = NT_, NW = NT / kWave;
   constexpr int R = D / kWave;
   extern __shared__ __align__(16) unsigned char dyn_lds[];
   uint32_t* pkeys = reinterpret_cast<uint32_t*>(dyn_lds);
@@ -962,9 +964,8 @@ __global__ __launch_bounds__(kFusedThreads) void hsa_fused_kernel(
 
 // Dynamic LDS of the fused kernel for a chunk of npc pages.
 inline size_t fused_lds_bytes(int nblk, int nsel, int npc, int k1p, size_t esize, int D, int G,
-                              int64_t n_cand) {
+                              int64_t n_cand, int NW) {
   const size_t stage = size_t(npc) * k1p * esize;
-  constexpr int NW = kFusedThreads / kWave;
   const size_t merge = (size_t(2) * NW * G + size_t(NW) * G * D) * sizeof(float);
   return size_t((nblk + 3) & ~3) * 4 + size_t((nsel + 3) & ~3) * 4 + size_t((n_cand + 3) & ~3) * 4 +
          (stage > merge ? stage : merge);
@@ -1070,7 +1071,13 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
     const bool cand_fits = size_t((nblk + 3) & ~3) * 4 + size_t((lay.nsel + 3) & ~3) * 4 +
                                size_t((n_cand + 3) & ~3) * 4 + size_t(64) * k1pf * sizeof(T) <=
                            kFusedLdsBudget;
-    const size_t fixed = fused_lds_bytes(nblk, lay.nsel, 0, k1pf, sizeof(T), D, G, n_cand);
+    // groups of four at large batch: 512-thread workgroups (8 waves with up
+    // to 256 registers each, 4 tokens per slot per step) measured 1.1 us per
+    // step faster than 1024 threads at batch 32; MT and the few-pages batch-1
+    // case keep 1024 (16 waves)
+    const bool wide = G == 4 && !cand && units >= kFusedMinUnits;
+    const int nw = (wide ? kFusedThreadsWide : kFusedThreads) / kWave;
+    const size_t fixed = fused_lds_bytes(nblk, lay.nsel, 0, k1pf, sizeof(T), D, G, n_cand, nw);
     const size_t keys_sel = size_t((nblk + 3) & ~3) * 4 + size_t((lay.nsel + 3) & ~3) * 4 +
                             size_t((n_cand + 3) & ~3) * 4;
     int npc = kFusedLdsBudget > keys_sel
@@ -1079,14 +1086,21 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
     const int nblk8 = (nblk + 7) / 8 * 8;
     npc = npc > nblk8 ? nblk8 : npc;
     if (npc >= 8 && fixed <= kFusedLdsBudget && cand_fits) {
-      const size_t lds = fused_lds_bytes(nblk, lay.nsel, npc, k1pf, sizeof(T), D, G, n_cand);
+      const size_t lds = fused_lds_bytes(nblk, lay.nsel, npc, k1pf, sizeof(T), D, G, n_cand, nw);
+      // the wide form is built for groups of four only
+      constexpr int kWideNT = G == 4 ? kFusedThreadsWide : kFusedThreads;
       static bool fattr = false;  // once per template instantiation
       if (!fattr) {
-        for (const void* f : {reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, true>),
-                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false>),
-                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, true>),
-                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, false, kPagedBuilt>),
-                              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, true, kPagedBuilt>)}) {
+        for (const void* f :
+             {reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, true>),
+              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false>),
+              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, true>),
+              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, false, kPagedBuilt>),
+              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, true, kPagedBuilt>),
+              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, false, false, kWideNT>),
+              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, true, false, kWideNT>),
+              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, false, kPagedBuilt, kWideNT>),
+              reinterpret_cast<const void*>(&hsa_fused_kernel<T, D, G, false, true, kPagedBuilt, kWideNT>)}) {
           hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                              int(kFusedLdsBudget));
           if (e != hipSuccess) return e;
@@ -1098,22 +1112,30 @@ hipError_t launch_decode_t(const Dims& d, const void* q, const void* k, const vo
                               static_cast<T*>(app->k), static_cast<T*>(app->v),
                               static_cast<T*>(app->kmax), static_cast<T*>(app->kmin)}
               : AppendPtrs<T>{};
-#define RK_FUSED(NAME, MTV, APPV, PGV)                                                            \
-  RK_LAUNCH(NAME, (hsa_fused_kernel<T, D, G, MTV, APPV, PGV>), dim3(units), dim3(kFusedThreads), lds, \
+#define RK_FUSED(NAME, MTV, APPV, PGV, NTV)                                                       \
+  RK_LAUNCH(NAME, (hsa_fused_kernel<T, D, G, MTV, APPV, PGV, NTV>), dim3(units), dim3(NTV), lds,    \
             s, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), kv_cap, \
             cand, cand_stride, static_cast<const T*>(kmax), static_cast<const T*>(kmin), nblk_cap,  \
             nblk, k1, lay.nsel, npc, int(n_tokens), block, scale_log2, out, sel_opt, chan_opt,      \
             s1_opt, ap, pg, lens)
+#define RK_FUSED_NT(NAME, APPV, PGV)                  \
+  do {                                                \
+    if (wide)                                         \
+      RK_FUSED(NAME, false, APPV, PGV, kWideNT);      \
+    else                                              \
+      RK_FUSED(NAME, false, APPV, PGV, kFusedThreads); \
+  } while (0)
       if (cand)
-        RK_FUSED("hsa_fused_mt", true, false, false);
+        RK_FUSED("hsa_fused_mt", true, false, false, kFusedThreads);
       else if (paged && app)
-        RK_FUSED("hsa_fused_append", false, true, kPagedBuilt);
+        RK_FUSED_NT("hsa_fused_append", true, kPagedBuilt);
       else if (paged)
-        RK_FUSED("hsa_fused", false, false, kPagedBuilt);
+        RK_FUSED_NT("hsa_fused", false, kPagedBuilt);
       else if (app)
-        RK_FUSED("hsa_fused_append", false, true, false);
+        RK_FUSED_NT("hsa_fused_append", true, false);
       else
-        RK_FUSED("hsa_fused", false, false, false);
+        RK_FUSED_NT("hsa_fused", false, false);
+#undef RK_FUSED_NT
 #undef RK_FUSED
       return hipGetLastError();
     }

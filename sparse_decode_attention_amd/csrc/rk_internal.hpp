@@ -38,6 +38,8 @@ constexpr int kWaveTopkPages = 1024;
 // workgroup per unit, with at most this much dynamic LDS per workgroup.
 constexpr int kFusedMinUnits = 160;
 constexpr int kFusedThreads = 1024;
+// Workgroup size of the large-batch fused decode for groups of four heads.
+constexpr int kFusedThreadsWide = 512;
 constexpr size_t kFusedLdsBudget = 144 * 1024;
 // Dynamic LDS of an attention workgroup at most: the unit's page keys and the
 // pages of its split, kMaxPages 4-byte entries each.
