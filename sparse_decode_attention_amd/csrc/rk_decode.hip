@@ -724,13 +724,15 @@ struct AppendPtrs {
 };
 
 // Steps 2 and 3 in one workgroup per unit, for large batches (the units alone
-// fill the chip, so no split-K, no partials and no combine).  1024 threads:
+// fill the chip, so no split-K, no partials and no combine).  NT_ threads:
 // wave 0 makes the channel choice; all threads stage and score the unit's
 // pages chunk by chunk (npc pages per chunk); one wave (or, for many pages,
-// the workgroup) takes the top-k2 pages; 16 waves stream them and the
-// workgroup writes the normalised output.  Gathers of scattered pages on
-// this chip gain bandwidth with resident waves per CU rather than with loads
-// in flight per wave, hence the full 1024-thread workgroup (4 waves per SIMD).
+// the workgroup) takes the top-k2 pages; all waves stream them and the
+// workgroup writes the normalised output.  Gathers of scattered rows on this
+// chip gain bandwidth with resident waves per CU more than with loads in
+// flight per wave, hence 1024 threads (4 waves per SIMD) by default; groups
+// of four heads, whose per-token state leaves 1024-thread waves room for
+// only 8 rows in flight, measured faster at 512 threads with 16 rows per wave.
 //
 // APP (a decode step that first appends token n_tokens - 1, as rk_append_kv
 // would): the workgroup reads the last page's Kmax/Kmin column up front,
