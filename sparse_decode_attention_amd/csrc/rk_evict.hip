@@ -536,6 +536,253 @@ __global__ __launch_bounds__(1024) void select_final_kernel(const float* __restr
 // positions written to kept[unit][0 ..) and followed by the W window
 // positions, and counts[unit] = its prefix count + W.
 constexpr int kAdaMaxHeads = 64;
+
+// ---- Ada-KV shared budget over many workgroups ------------------------------
+// For a sequence whose Hkv * P pooled keys do not fit one workgroup's LDS,
+// the cut is found by a most-significant-digit radix select in three passes
+// (key bits 31-21, 20-10, 9-0), one launch each: every workgroup adds the
+// LDS histogram of kAdaChunk keys into the sequence's global 2048-bin
+// histogram of that pass.  A pass needs the prefix fixed by the earlier
+// ones: each of its workgroups finds it again from the earlier passes'
+// histograms (8 KB each, read from L2), so no launch does only that and no
+// workgroup waits for another.  The count launch finds the cut T the same
+// way and counts, per unit and kAdaEmitChunk chunk, the keys above and equal
+// to T; the emit launch writes each unit's kept positions: keys above T, and
+// keys equal to it in flattened (head-major, then position) order, so a lower
+// head takes its equal keys first.
+constexpr int kAdaChunk = 8192;      // keys per histogram workgroup (1024 threads x 8)
+constexpr int kAdaBins = 2048;
+constexpr int kAdaEmitChunk = 4096;  // positions per emit workgroup (256 threads x 16)
+constexpr int kAdaCountChunks = 4;   // emit chunks per count workgroup (1024 threads)
+struct AdaCut {
+  uint32_t T;  // the cut: the K-th largest key of the sequence
+  int need;    // keys equal to T that are taken
+};
+
+// zeroes the three passes' histograms (a fill kernel, so the sequence of
+// launches stays capturable)
+__global__ __launch_bounds__(256) void ada_clear_kernel(uint32_t* __restrict__ hist, int words) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < words) hist[i] = 0u;
+}
+
+// hist: [3][B][kAdaBins]
+__global__ __launch_bounds__(1024) void ada_hist_kernel(const float* __restrict__ pooled, int B, int n, int pass,
+                                                       int K, uint32_t* __restrict__ hist) {
+  __shared__ __align__(16) uint32_t h[kAdaBins];
+  __shared__ __align__(16) uint32_t hp[2 * kAdaBins];
+  __shared__ int res[2];
+  const int b = blockIdx.y;
+  for (int i = threadIdx.x; i < kAdaBins; i += 1024) h[i] = 0u;
+  uint32_t prefix = 0u;
+  if (pass > 0) {
+    // the earlier passes' histograms of this sequence, one after another
+    const uint32_t* hb0 = hist + size_t(b) * kAdaBins;
+    for (int i = threadIdx.x; i < pass * kAdaBins / 4; i += 1024) {
+      const int p = i / (kAdaBins / 4), j = i % (kAdaBins / 4);
+      reinterpret_cast<uint4*>(hp)[i] =
+          reinterpret_cast<const uint4*>(hb0 + size_t(p) * B * kAdaBins)[j];
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      uint32_t pre = 0u;
+      int need = K;
+      for (int p = 0; p < pass; ++p) {
+        const int3 f = wave_find_bin<kAdaBins>(hp + p * kAdaBins, need);
+        pre = (pre << 11) | uint32_t(f.x);
+        need = f.y;
+      }
+      if (threadIdx.x == 0) res[0] = int(pre);
+    }
+    __syncthreads();
+    prefix = uint32_t(res[0]);
+  } else {
+    __syncthreads();
+  }
+  const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+  const uint32_t mask = pass == 2 ? 1023u : 2047u;
+  const int fixed = pass == 0 ? 32 : pass == 1 ? 21 : 10;  // key bits [fixed, 32) equal the prefix
+  const float* pb = pooled + size_t(b) * n;
+  const int i0 = blockIdx.x * kAdaChunk;
+  const int i1 = min(i0 + kAdaChunk, n);
+  for (int i = i0 + int(threadIdx.x); i < i1; i += 1024) {
+    const uint32_t kk = order_key(pb[i]);
+    if (fixed == 32 || (kk >> fixed) == prefix) atomicAdd(&h[(kk >> shift) & mask], 1u);
+  }
+  __syncthreads();
+  uint32_t* hb = hist + (size_t(pass) * B + b) * kAdaBins;
+  for (int i = threadIdx.x; i < kAdaBins; i += 1024)
+    if (h[i]) atomicAdd(&hb[i], h[i]);
+}
+
+// The cut from the three histograms, then the keys above and equal to it in
+// each kAdaEmitChunk chunk of each unit: cnt[u * nchunk + c].  Workgroup
+// (0, unit 0 of b) stores the cut of sequence b.
+__global__ __launch_bounds__(1024) void ada_count_kernel(const float* __restrict__ pooled, int B, int Hkv, int P,
+                                                        int nchunk, int K, const uint32_t* __restrict__ hist,
+                                                        AdaCut* __restrict__ cut, int2* __restrict__ cnt) {
+  __shared__ __align__(16) uint32_t hp[3 * kAdaBins];
+  __shared__ int res[2];
+  __shared__ int red[2][1024 / kWave];
+  const int cc = blockIdx.x, u = blockIdx.y;
+  const int b = u / Hkv;
+  const uint32_t* hb0 = hist + size_t(b) * kAdaBins;
+  for (int i = threadIdx.x; i < 3 * kAdaBins / 4; i += 1024) {
+    const int p = i / (kAdaBins / 4), j = i % (kAdaBins / 4);
+    reinterpret_cast<uint4*>(hp)[i] = reinterpret_cast<const uint4*>(hb0 + size_t(p) * B * kAdaBins)[j];
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    uint32_t pre = 0u;
+    int need = K;
+    for (int p = 0; p < 3; ++p) {
+      const int3 f = wave_find_bin<kAdaBins>(hp + p * kAdaBins, need);
+      pre = (pre << (p == 2 ? 10 : 11)) | uint32_t(f.x);
+      need = f.y;
+    }
+    if (threadIdx.x == 0) {
+      res[0] = int(pre);
+      res[1] = need;
+      if (cc == 0 && u % Hkv == 0) cut[b] = AdaCut{pre, need};
+    }
+  }
+  __syncthreads();
+  const uint32_t T = uint32_t(res[0]);
+  // thread t counts sub-chunk t / 256 of this workgroup's kAdaCountChunks
+  const int sc = threadIdx.x / 256;
+  const int c = cc * kAdaCountChunks + sc;
+  const float* pu = pooled + size_t(u) * P;
+  const int i1 = min((c + 1) * kAdaEmitChunk, P);
+  int gt = 0, eq = 0;
+  for (int i = c * kAdaEmitChunk + int(threadIdx.x % 256); i < i1; i += 256) {
+    const uint32_t kk = order_key(pu[i]);
+    gt += kk > T ? 1 : 0;
+    eq += kk == T ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    gt += __shfl_xor(gt, off);
+    eq += __shfl_xor(eq, off);
+  }
+  const int wave = threadIdx.x / kWave;
+  if (lane_id() == 0) {
+    red[0][wave] = gt;
+    red[1][wave] = eq;
+  }
+  __syncthreads();
+  if (threadIdx.x < kAdaCountChunks && cc * kAdaCountChunks + int(threadIdx.x) < nchunk) {
+    constexpr int WPS = 256 / kWave;  // waves per sub-chunk
+    int g = 0, e = 0;
+    for (int w = 0; w < WPS; ++w) {
+      g += red[0][threadIdx.x * WPS + w];
+      e += red[1][threadIdx.x * WPS + w];
+    }
+    cnt[size_t(u) * nchunk + cc * kAdaCountChunks + threadIdx.x] = make_int2(g, e);
+  }
+}
+
+// Each unit's kept positions (ascending) then the window's, and its count;
+// workgroup c writes the positions chunk c selects.  mode 0: the cut;
+// 1: every key (the budget covers them all); -1: none.
+__global__ __launch_bounds__(256) void ada_emit_kernel(const float* __restrict__ pooled, int Hkv, int P, int W,
+                                                      int nchunk, int mode, const AdaCut* __restrict__ cut,
+                                                      const int2* __restrict__ cnt,
+                                                      int32_t* __restrict__ kept, int kept_stride,
+                                                      int32_t* __restrict__ counts) {
+  constexpr int NWV = 256 / kWave;
+  constexpr int RPW = kAdaEmitChunk / 256;  // rows of 64 positions per wave
+  __shared__ int wsum[2][NWV];
+  const int c = blockIdx.x, u = blockIdx.y;
+  const int b = u / Hkv, h = u % Hkv;
+  const int t = threadIdx.x, lane = lane_id(), wv = t / kWave;
+  int32_t* ku = kept + size_t(u) * kept_stride;
+  const int i0 = c * kAdaEmitChunk;
+  const int i1 = min(i0 + kAdaEmitChunk, P);
+  int n_sel;
+  if (mode != 0) {
+    if (mode == 1)
+      for (int i = i0 + t; i < i1; i += 256) ku[i] = i;
+    n_sel = mode == 1 ? P : 0;
+  } else {
+    const uint32_t T = cut[b].T;
+    // sums over the sequence's chunk counts (every wave the same): keys
+    // equal to T in lower heads, and this unit's counts before chunk c and
+    // in total
+    const int2* cb = cnt + size_t(b) * Hkv * nchunk;
+    int eq_lower = 0, eq_u = 0, gt_u = 0, gt_pre = 0, eq_pre = 0, eq_c = 0;
+    for (int j = lane; j < (h + 1) * nchunk; j += kWave) {
+      const int2 v = cb[j];
+      if (j < h * nchunk) {
+        eq_lower += v.y;
+      } else {
+        const int cj = j - h * nchunk;
+        eq_u += v.y;
+        gt_u += v.x;
+        gt_pre += cj < c ? v.x : 0;
+        eq_pre += cj < c ? v.y : 0;
+        eq_c += cj == c ? v.y : 0;
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      eq_lower += __shfl_xor(eq_lower, off);
+      eq_u += __shfl_xor(eq_u, off);
+      gt_u += __shfl_xor(gt_u, off);
+      gt_pre += __shfl_xor(gt_pre, off);
+      eq_pre += __shfl_xor(eq_pre, off);
+      eq_c += __shfl_xor(eq_c, off);
+    }
+    const int eq_take = max(0, min(cut[b].need - eq_lower, eq_u));  // this unit's keys equal to T
+    const int eq_chunk = max(0, min(eq_take - eq_pre, eq_c));       // ... of them in chunk c
+    // at most the room before the window (never exceeded by a consistent
+    // cut; the bound keeps every store inside the unit's row regardless)
+    const int room = kept_stride - W;
+    n_sel = min(gt_u + eq_take, room);
+    // wave wv holds positions [i0 + wv * 64 * RPW, +64 * RPW) of the chunk
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int r0 = i0 + wv * kWave * RPW;
+    uint32_t kk[RPW];
+    int g = 0, e = 0;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int i = r0 + r * kWave + lane;
+      kk[r] = i < i1 ? order_key(pooled[size_t(u) * P + i]) : 0u;
+      const bool in = i < i1;
+      g += __popcll(ballot(in && kk[r] > T));
+      e += __popcll(ballot(in && kk[r] == T));
+    }
+    if (lane == 0) {
+      wsum[0][wv] = g;
+      wsum[1][wv] = e;
+    }
+    __syncthreads();
+    int g_w = 0, e_w = 0;
+    for (int w = 0; w < wv; ++w) {
+      g_w += wsum[0][w];
+      e_w += wsum[1][w];
+    }
+    int base = gt_pre + min(eq_pre, eq_take) + g_w + min(e_w, eq_chunk);
+    int eq_seen = e_w;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int i = r0 + r * kWave + lane;
+      const bool in = i < i1;
+      const bool eq = in && kk[r] == T;
+      const unsigned long long em = ballot(eq);
+      const bool sel = (in && kk[r] > T) || (eq && eq_seen + int(__popcll(em & below)) < eq_chunk);
+      const unsigned long long sm = ballot(sel);
+      const int pos = base + int(__popcll(sm & below));
+      if (sel && pos < room) ku[pos] = i;
+      base += __popcll(sm);
+      eq_seen += __popcll(em);
+    }
+  }
+  if (c == 0) {
+    for (int w = t; w < W; w += 256) ku[n_sel + w] = P + w;
+    if (t == 0) counts[u] = n_sel + W;
+  }
+}
+
 __global__ __launch_bounds__(1024) void adakv_select_kernel(const float* __restrict__ pooled, int Hkv,
                                                             int P, int W, int kper, int staged,
                                                             int cand_cap, int32_t* __restrict__ tmp,
@@ -1147,9 +1394,36 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
     }
     const size_t nkeys = size_t(d.Hkv) * P;
     const int staged = (nkeys + 4096) * 4 <= kSelectKeysLds ? 1 : 0;
-    RK_LAUNCH("select_tokens", adakv_select_kernel, dim3(d.B), dim3(1024),
-              staged ? (nkeys + 4096) * 4 : size_t(0), s, pooled, d.Hkv, P, W, int(n_keep) - W, staged,
-              staged ? 4096 : 0, reinterpret_cast<int32_t*>(scores), kept, kept_stride, ada_counts);
+    if (staged) {
+      RK_LAUNCH("select_tokens", adakv_select_kernel, dim3(d.B), dim3(1024), (nkeys + 4096) * 4, s,
+                pooled, d.Hkv, P, W, int(n_keep) - W, staged, 4096, reinterpret_cast<int32_t*>(scores), kept,
+                kept_stride, ada_counts);
+    } else {
+      // more keys than one workgroup's LDS: the radix select spread over
+      // many workgroups (one workgroup per sequence took 645 us at batch 1 x
+      // 8 heads x 32K keys).  Its histograms, cuts and chunk counts live in
+      // the spent window-score region: B * 24 KB + units * P / 512 bytes,
+      // well below its units * P * 4 bytes (over 137 KB per sequence here).
+      const int n = int(nkeys);
+      const int K = d.Hkv * (int(n_keep) - W);
+      const int nchunk = (P + kAdaEmitChunk - 1) / kAdaEmitChunk;
+      uint32_t* hist = reinterpret_cast<uint32_t*>(scores);  // [3][B][kAdaBins]
+      AdaCut* cutp = reinterpret_cast<AdaCut*>(hist + size_t(3) * d.B * kAdaBins);
+      int2* cntp = reinterpret_cast<int2*>(cutp + d.B);
+      const int mode = K <= 0 ? -1 : K >= n ? 1 : 0;
+      if (mode == 0) {
+        const int words = 3 * d.B * kAdaBins;
+        RK_LAUNCH("select_tokens", ada_clear_kernel, dim3((words + 255) / 256), dim3(256), 0, s, hist, words);
+        for (int pass = 0; pass < 3; ++pass)
+          RK_LAUNCH("select_tokens", ada_hist_kernel, dim3((n + kAdaChunk - 1) / kAdaChunk, d.B), dim3(1024),
+                    0, s, pooled, d.B, n, pass, K, hist);
+        RK_LAUNCH("select_tokens", ada_count_kernel,
+                  dim3((nchunk + kAdaCountChunks - 1) / kAdaCountChunks, units), dim3(1024), 0, s, pooled,
+                  d.B, d.Hkv, P, nchunk, K, hist, cutp, cntp);
+      }
+      RK_LAUNCH("select_tokens", ada_emit_kernel, dim3(nchunk, units), dim3(256), 0, s, pooled, d.Hkv, P, W,
+                nchunk, mode, cutp, cntp, kept, kept_stride, ada_counts);
+    }
   } else {
   // kernel 63 with the haloed scores in LDS and enough units to spread the
   // pooling over the CUs: pooling inside the select launch (at batch 32,

@@ -29,11 +29,15 @@ def say(*a):
     print("[case]", *a, file=sys.stderr, flush=True)
 
 
-def ada_evict_and_check(rk, w, n_keep, block=16, aux=True):
-    """rk_adakv_evict on layer 0 of w, checked against the oracle; returns the
-    GPU's kept counts, compact cache and aux."""
-    k, v, _ = WL.layer_kv(w, 0, device=DEV)
-    qw = WL.window_queries(w, 0, device=DEV)
+def ada_evict_and_check(rk, w, n_keep, block=16, aux=True, kvq=None):
+    """rk_adakv_evict on layer 0 of w (or on the given K, V and window
+    queries), checked against the oracle; returns the GPU's kept counts,
+    compact cache and aux."""
+    if kvq is None:
+        k, v, _ = WL.layer_kv(w, 0, device=DEV)
+        qw = WL.window_queries(w, 0, device=DEV)
+    else:
+        k, v, qw = kvq
     B, Hkv, S, d = k.shape
     W = w.window
     G = w.group
@@ -87,6 +91,38 @@ def ada_evict_and_check(rk, w, n_keep, block=16, aux=True):
 def test_adakv_evict(rk, w, n_keep):
     say("adakv evict", w.name, w.batch, w.n_kv, w.seq, n_keep)
     ada_evict_and_check(rk, w, n_keep, block=w.block)
+
+
+@pytest.mark.parametrize("B,seq,n_keep", [
+    (2, 5000, 1200),     # 40K keys per sequence, two sequences: the many-workgroup cut
+    (1, 9000, 9000),     # budget covers every key
+    (1, 9000, 32),       # budget is the window alone
+])
+def test_adakv_evict_many_workgroup_select(rk, B, seq, n_keep):
+    """Sequences with more pooled keys than one workgroup's LDS holds: the
+    shared cut comes from the radix select spread over many workgroups."""
+    w = WL.scaled(LLAMA, batch=B, seq=seq, n_plant=32)
+    assert n_keep in (w.window, seq) or w.n_kv * (seq - w.window) * 4 > 140 * 1024
+    say("adakv evict, many-workgroup select", B, seq, n_keep)
+    ada_evict_and_check(rk, w, n_keep, block=w.block)
+
+
+def test_adakv_tied_heads_many_workgroup_select(rk):
+    """The even heads hold one head's keys and queries and the odd heads
+    another's, so every pooled value appears four times and the cut falls
+    inside a run of equal keys spread over heads: the lower heads take
+    theirs first."""
+    w = WL.scaled(LLAMA, batch=2, seq=6000, n_plant=16)
+    say("adakv evict, tied heads", w.batch, w.seq)
+    k, v, _ = WL.layer_kv(w, 0, device=DEV)
+    qw = WL.window_queries(w, 0, device=DEV)
+    G = w.group
+    k = k[:, :2].repeat(1, 4, 1, 1).contiguous()
+    v = v[:, :2].repeat(1, 4, 1, 1).contiguous()
+    qw = qw[:, :2 * G].repeat(1, 4, 1, 1).contiguous()
+    cnt = ada_evict_and_check(rk, w, 1500, block=w.block, kvq=(k, v, qw))[0].cpu().numpy()
+    # heads with the same data: the lower one never keeps fewer
+    assert (cnt[:, :2] >= cnt[:, 6:]).all()
 
 
 def test_adakv_equal_heads_is_snapkv(rk):
