@@ -783,9 +783,12 @@ __global__ __launch_bounds__(256) void ada_emit_kernel(const float* __restrict__
   }
 }
 
+// A sequence whose Hkv * P pooled keys (and a 4096-key candidate buffer) fit
+// in LDS: one workgroup stages their order keys, takes the workgroup top-k of
+// the flattened keys into tmp (ascending), then splits it by head.
 __global__ __launch_bounds__(1024) void adakv_select_kernel(const float* __restrict__ pooled, int Hkv,
-                                                            int P, int W, int kper, int staged,
-                                                            int cand_cap, int32_t* __restrict__ tmp,
+                                                            int P, int W, int kper, int cand_cap,
+                                                            int32_t* __restrict__ tmp,
                                                             int32_t* __restrict__ kept, int kept_stride,
                                                             int32_t* __restrict__ counts) {
   extern __shared__ uint32_t skeys[];
@@ -797,19 +800,15 @@ __global__ __launch_bounds__(1024) void adakv_select_kernel(const float* __restr
   const float* pb = pooled + size_t(b) * n;
   int32_t* tb = tmp + size_t(b) * n;
   auto emit = [=](int r, int i) { tb[r] = i; };
-  if (staged) {
-    uint32_t lo = 0xffffffffu, hi = 0u;
-    for (int i = threadIdx.x; i < n; i += 1024) {
-      const uint32_t kk = order_key(pb[i]);
-      skeys[i] = kk;
-      lo = min(lo, kk);
-      hi = max(hi, kk);
-    }
-    __syncthreads();
-    wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, n, K, emit, sm, true, lo, hi, skeys + n, cand_cap);
-  } else {
-    wg_topk<1024, 2048>([&](int i) { return order_key(pb[i]); }, n, K, emit, sm);
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = threadIdx.x; i < n; i += 1024) {
+    const uint32_t kk = order_key(pb[i]);
+    skeys[i] = kk;
+    lo = min(lo, kk);
+    hi = max(hi, kk);
   }
+  __syncthreads();
+  wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, n, K, emit, sm, true, lo, hi, skeys + n, cand_cap);
   __syncthreads();
   // start[h] = number of chosen indices below h * P (tb is ascending)
   if (threadIdx.x <= Hkv) {
@@ -1381,8 +1380,9 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   const int h = (pool_kernel - 1) / 2;
   if (ada) {
     // pooling of every unit first (the shared choice reads all heads of a
-    // sequence), then one workgroup per sequence; the spent window scores
-    // hold its chosen flattened indices
+    // sequence), then the shared choice: one workgroup per sequence when
+    // its keys fit in LDS (the spent window scores hold its chosen flattened
+    // indices), else the radix select over many workgroups
     if (P > 0) {
       if (h == 31)
         RK_LAUNCH("pool_sum", pool_sum_reg_kernel<31>, dim3((P + 2047) / 2048, units), dim3(256), 0, s,
@@ -1393,10 +1393,9 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     const size_t nkeys = size_t(d.Hkv) * P;
-    const int staged = (nkeys + 4096) * 4 <= kSelectKeysLds ? 1 : 0;
-    if (staged) {
+    if ((nkeys + 4096) * 4 <= kSelectKeysLds) {
       RK_LAUNCH("select_tokens", adakv_select_kernel, dim3(d.B), dim3(1024), (nkeys + 4096) * 4, s,
-                pooled, d.Hkv, P, W, int(n_keep) - W, staged, 4096, reinterpret_cast<int32_t*>(scores), kept,
+                pooled, d.Hkv, P, W, int(n_keep) - W, 4096, reinterpret_cast<int32_t*>(scores), kept,
                 kept_stride, ada_counts);
     } else {
       // more keys than one workgroup's LDS: the radix select spread over
