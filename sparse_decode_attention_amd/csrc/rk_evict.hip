@@ -1409,6 +1409,9 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
       uint32_t* hist = reinterpret_cast<uint32_t*>(scores);  // [3][B][kAdaBins]
       AdaCut* cutp = reinterpret_cast<AdaCut*>(hist + size_t(3) * d.B * kAdaBins);
       int2* cntp = reinterpret_cast<int2*>(cutp + d.B);
+      const size_t ws_need = size_t(3) * d.B * kAdaBins * 4 + size_t(d.B) * sizeof(AdaCut) +
+                             size_t(units) * nchunk * sizeof(int2);
+      if (ws_need > size_t(units) * P * sizeof(float)) return hipErrorInvalidValue;
       const int mode = K <= 0 ? -1 : K >= n ? 1 : 0;
       if (mode == 0) {
         const int words = 3 * d.B * kAdaBins;
