@@ -1322,17 +1322,18 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   const int CS = RG >= 4 ? 1 : 4 / RG;
   // keys per workgroup: about 8192 workgroups per pass (8 per CU slot; at
   // batch 32, 2048 measured 8 % slower and 16384 slower again), in whole
-  // 128-key tiles, but at least 2 tiles, so each workgroup's window-row fetch
-  // is spread over a streamed run of K (at batch 1 one-tile workgroups
-  // measured 4 % slower for the whole eviction, two-tile ones 6 % faster
-  // than four-tile ones on the 109K prompt).  Splitting the passes over
-  // unit chunks small enough for the second pass to re-read K from the MALL
-  // measured slower: the smaller launches lose more than the re-read gains.
+  // 128-key tiles, but at least 4 tiles, so each workgroup's window-row fetch
+  // is spread over a streamed run of K (at batch 1, with non-temporal tile
+  // loads, four-tile workgroups measured 1 % (32K prompt) and 3-5 % (109K
+  // prompt) faster for the whole eviction than two-tile ones, eight-tile
+  // ones 1-5 % slower).  Splitting the passes over unit chunks small enough
+  // for the second pass to re-read K from the MALL measured slower: the
+  // smaller launches lose more than the re-read gains.
   auto range = [&](int keys) {
     const int wpu = (8192 + units - 1) / units;
     int kpw = (keys + wpu - 1) / wpu;
     kpw = (kpw + TK - 1) / TK * TK;
-    return kpw < 2 * TK ? 2 * TK : kpw;
+    return kpw < 4 * TK ? 4 * TK : kpw;
   };
   const int kpw1 = range(S);
   const int n_wg1 = mfma ? (S + kpw1 - 1) / kpw1 : lay.n_tiles;
