@@ -75,6 +75,12 @@ __device__ __forceinline__ uint4 load_u4_nt(const uint4* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
 }
 
+// 16-byte non-temporal store (a vector store with the streaming hint).
+template <typename T>
+__device__ __forceinline__ void store16_nt(T* p, const Vec16<T>& v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v.raw), reinterpret_cast<u32x4_t*>(p));
+}
+
 template <typename T>
 __device__ __forceinline__ void unpack16(const Vec16<T>& v, float* out) {
 #pragma unroll

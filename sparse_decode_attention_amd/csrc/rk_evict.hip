@@ -903,7 +903,6 @@ __global__ __launch_bounds__(kGatherWideThreads, 4) void gather_aux_wide_kernel(
   static_assert(kGatherWideThreads % CPR == 0, "workgroup shape");
   __shared__ T smax[D][PPW + 1];
   __shared__ T smin[D][PPW + 1];
-  using Rw = decltype(Vec16<T>::raw);
   const int t = threadIdx.x;
   const int c = t % CPR;
   const int j = t / CPR;
@@ -930,15 +929,17 @@ __global__ __launch_bounds__(kGatherWideThreads, 4) void gather_aux_wide_kernel(
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         const size_t a = (size_t(u) * size_t(kv_cap) + size_t(src[i])) * D + c * EPL;
-        kr[i] = load16(k + a);
-        vr[i] = load16(v + a);
+        // rows moved once: non-temporal loads and stores (at batch 32,
+        // 201 -> 175 us for the copy with its aux; stores alone 184 us)
+        kr[i] = load16_nt(k + a);
+        vr[i] = load16_nt(v + a);
       }
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         if (b0 + i < n1) {
           const size_t dst = (size_t(u) * size_t(out_cap) + size_t(b0 + i)) * D + c * EPL;
-          *reinterpret_cast<Rw*>(k_out + dst) = kr[i].raw;
-          *reinterpret_cast<Rw*>(v_out + dst) = vr[i].raw;
+          store16_nt(k_out + dst, kr[i]);
+          store16_nt(v_out + dst, vr[i]);
         }
         float x[EPL];
         unpack16(kr[i], x);
