@@ -54,6 +54,12 @@ typedef enum {
 
 typedef enum { RK_F32 = 0, RK_BF16 = 1 } rk_dtype;
 
+/* Sequence pooling of the stage-1 window scores: the windowed sum (the
+ * reading built by default; it ranks as average pooling does) or the
+ * windowed maximum (the notes say only "pooling"; max pooling is the other
+ * plain reading). */
+typedef enum { RK_POOL_SUM = 0, RK_POOL_MAX = 1 } rk_pool_op;
+
 /* A hipStream_t, passed as an opaque pointer. */
 typedef void* rk_stream;
 
@@ -145,6 +151,22 @@ rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* 
                           void* ws, size_t ws_bytes, rk_stream stream);
 
 /*
+ * rk_snapkv_evict_pool -- rk_snapkv_evict with the pooling operation given:
+ * RK_POOL_SUM is rk_snapkv_evict; RK_POOL_MAX makes pooled[j] the largest
+ * score over [j-h, j+h] within the prefix ([RKV] quick read and method
+ * details, pooling paragraph: the kind of pooling is not stated).  A maximum
+ * involves no rounding, so pooled is then exact for any grouping.  Other
+ * arguments, requirements and errors as rk_snapkv_evict; RK_EINVAL for any
+ * other pool_op.
+ */
+rk_status rk_snapkv_evict_pool(const rk_shape* shape, const void* q_win, const void* k,
+                               const void* v, int64_t kv_cap, int64_t seq_len, int32_t window,
+                               int32_t pool_kernel, int32_t pool_op, int64_t n_keep,
+                               int32_t* kept_idx, void* k_out, void* v_out, int64_t out_cap,
+                               float* pooled_opt, void* kmax_opt, void* kmin_opt, int64_t nblk_cap,
+                               int32_t block, void* ws, size_t ws_bytes, rk_stream stream);
+
+/*
  * rk_adakv_evict -- stage 1 with Ada-KV's shared budget.  [RKV] method
  * details, "the second stage and the framework's generality" (SnapKV or
  * Ada-KV as stage 1) and the GQA paragraph (group-level selection following
@@ -173,6 +195,17 @@ rk_status rk_adakv_evict(const rk_shape* shape, const void* q_win, const void* k
                          void* v_out, int64_t out_cap, float* pooled_opt, void* kmax_opt,
                          void* kmin_opt, int64_t nblk_cap, int32_t block, void* ws, size_t ws_bytes,
                          rk_stream stream);
+
+/*
+ * rk_adakv_evict_pool -- rk_adakv_evict with the pooling operation given
+ * (RK_POOL_SUM or RK_POOL_MAX, as rk_snapkv_evict_pool); otherwise the same.
+ */
+rk_status rk_adakv_evict_pool(const rk_shape* shape, const void* q_win, const void* k, const void* v,
+                              int64_t kv_cap, int64_t seq_len, int32_t window, int32_t pool_kernel,
+                              int32_t pool_op, int64_t n_keep, int32_t* kept_idx,
+                              int32_t* kept_count, void* k_out, void* v_out, int64_t out_cap,
+                              float* pooled_opt, void* kmax_opt, void* kmin_opt, int64_t nblk_cap,
+                              int32_t block, void* ws, size_t ws_bytes, rk_stream stream);
 
 /*
  * rk_hsa_build_aux -- HSA step 1: per-page element-wise Kmax / Kmin.

@@ -38,7 +38,8 @@ Readings where the pages are silent or ambiguous:
   R8  group aggregation is a sum over the G heads and the W window rows.
   R9  pooling is an average pool evaluated as a zero-padded windowed SUM of
       width k (same ranking as the average); parity of this choice with the
-      pages is unpinned.
+      pages is unpinned.  Max pooling, the other plain reading, is kept as
+      the option pool_op="max" (pool_max).
   R11 ties in every top-k go to the lower index.
   R12 kept tokens are stored in ascending original position.
   R14 sign 0 selects Kmax (q_bar >= 0).
@@ -200,6 +201,34 @@ def pool_sum(scores: np.ndarray, kernel: int) -> np.ndarray:
     return out
 
 
+def pool_max(scores: np.ndarray, kernel: int) -> np.ndarray:
+    """The other reading of the sequence pooling (R9): max pooling.
+
+    [RKV] quick read and method details, pooling paragraph: the notes name
+    the pooling and its kernel size but not its kind.  out[j] = the largest
+    of scores[i] for i in [j-h, j+h] within [0, n), h = (kernel-1)/2.  A
+    maximum involves no rounding.  kernel must be odd.
+    """
+    s = np.asarray(scores, dtype=F32)
+    if kernel < 1 or kernel % 2 == 0:
+        raise ValueError("pool kernel must be odd and positive")
+    n = s.shape[0]
+    h = (kernel - 1) // 2
+    out = np.empty(n, dtype=F32)
+    for j in range(n):
+        out[j] = s[max(0, j - h):min(n, j + h + 1)].max()
+    return out
+
+
+def pool(scores: np.ndarray, kernel: int, op: str = "sum") -> np.ndarray:
+    """Sequence pooling by reading: "sum" (R9, built by default) or "max"."""
+    if op == "sum":
+        return pool_sum(scores, kernel)
+    if op == "max":
+        return pool_max(scores, kernel)
+    raise ValueError("pool op must be 'sum' or 'max'")
+
+
 def snapkv_select(pooled: np.ndarray, seq_len: int, window: int, n_keep: int) -> np.ndarray:
     """Kept token positions of one KV head (readings R7, R11, R12).
 
@@ -215,7 +244,7 @@ def snapkv_select(pooled: np.ndarray, seq_len: int, window: int, n_keep: int) ->
 
 
 def snapkv_evict(q_win: np.ndarray, k: np.ndarray, v: np.ndarray | None,
-                 window: int, pool_kernel: int, n_keep: int) -> dict:
+                 window: int, pool_kernel: int, n_keep: int, pool_op: str = "sum") -> dict:
     """Stage 1 for a whole [B, H_kv] cache.
 
     q_win: [B, H_q, W, d]; k, v: [B, H_kv, S, d] (v may be None for the
@@ -236,7 +265,7 @@ def snapkv_evict(q_win: np.ndarray, k: np.ndarray, v: np.ndarray | None,
     for b in range(B):
         for h in range(Hkv):
             sc = window_scores(q_win[b, h * G:(h + 1) * G], k[b, h])
-            pooled[b, h] = pool_sum(sc, pool_kernel)
+            pooled[b, h] = pool(sc, pool_kernel, pool_op)
             kept[b, h] = snapkv_select(pooled[b, h], S, W, n_keep)
     out = dict(kept=kept, pooled=pooled)
     out["k"] = np.take_along_axis(k, kept[..., None], axis=2)
@@ -598,7 +627,8 @@ def adakv_select(pooled_heads: np.ndarray, seq_len: int, window: int, n_keep: in
     return out
 
 
-def adakv_evict(q_win: np.ndarray, k: np.ndarray, window: int, pool_kernel: int, n_keep: int) -> dict:
+def adakv_evict(q_win: np.ndarray, k: np.ndarray, window: int, pool_kernel: int, n_keep: int,
+                pool_op: str = "sum") -> dict:
     """Stage 1 with Ada-KV budgets for a whole [B, H_kv] cache: window scores
     and pooling per head as SnapKV (R5-R10), then adakv_select per sequence.
     Returns kept (list per batch of per-head arrays), counts [B, H_kv] and
@@ -612,7 +642,7 @@ def adakv_evict(q_win: np.ndarray, k: np.ndarray, window: int, pool_kernel: int,
     kept, counts = [], np.zeros((B, Hkv), np.int64)
     for b in range(B):
         for h in range(Hkv):
-            pooled[b, h] = pool_sum(window_scores(q_win[b, h * G:(h + 1) * G], k[b, h]), pool_kernel)
+            pooled[b, h] = pool(window_scores(q_win[b, h * G:(h + 1) * G], k[b, h]), pool_kernel, pool_op)
         kb = adakv_select(pooled[b], S, W, n_keep)
         kept.append(kb)
         counts[b] = [len(x) for x in kb]

@@ -236,6 +236,17 @@ rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* 
                           void* v_out, int64_t out_cap, float* pooled_opt, void* kmax_opt,
                           void* kmin_opt, int64_t nblk_cap, int32_t block, void* ws,
                           size_t ws_bytes, rk_stream stream) {
+  return rk_snapkv_evict_pool(shape, q_win, k, v, kv_cap, seq_len, window, pool_kernel, RK_POOL_SUM,
+                              n_keep, kept_idx, k_out, v_out, out_cap, pooled_opt, kmax_opt,
+                              kmin_opt, nblk_cap, block, ws, ws_bytes, stream);
+}
+
+rk_status rk_snapkv_evict_pool(const rk_shape* shape, const void* q_win, const void* k,
+                               const void* v, int64_t kv_cap, int64_t seq_len, int32_t window,
+                               int32_t pool_kernel, int32_t pool_op, int64_t n_keep,
+                               int32_t* kept_idx, void* k_out, void* v_out, int64_t out_cap,
+                               float* pooled_opt, void* kmax_opt, void* kmin_opt, int64_t nblk_cap,
+                               int32_t block, void* ws, size_t ws_bytes, rk_stream stream) {
   rk::Dims d;
   rk_status st = check_shape(shape, &d);
   if (st != RK_OK) return st;
@@ -252,6 +263,8 @@ rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* 
   if (n_keep < window || n_keep > seq_len) return fail(RK_EINVAL, "n_keep outside [W, S]");
   if (pool_kernel < 1 || (pool_kernel % 2) == 0 || pool_kernel > 4097)
     return fail(RK_EINVAL, "pool_kernel must be odd, in [1, 4097]");
+  if (pool_op != RK_POOL_SUM && pool_op != RK_POOL_MAX)
+    return fail(RK_EINVAL, "pool_op must be RK_POOL_SUM or RK_POOL_MAX");
   if (k_out && out_cap < n_keep) return fail(RK_EINVAL, "out_cap below n_keep");
   if ((kmax_opt == nullptr) != (kmin_opt == nullptr))
     return fail(RK_EINVAL, "kmax_opt and kmin_opt must both be given or both be NULL");
@@ -269,9 +282,9 @@ rk_status rk_snapkv_evict(const rk_shape* shape, const void* q_win, const void* 
   const rk::EvictWs lay = rk::evict_ws_layout(d, seq_len, window);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != RK_OK) return st;
   return device_status(
-      rk::launch_snapkv_evict(d, q_win, k, v, kv_cap, seq_len, window, pool_kernel, n_keep,
-                              kept_idx, k_out, v_out, out_cap, pooled_opt, kmax_opt, kmin_opt,
-                              nblk_cap, block, ws, static_cast<hipStream_t>(stream)),
+      rk::launch_snapkv_evict(d, q_win, k, v, kv_cap, seq_len, window, pool_kernel, pool_op,
+                              n_keep, kept_idx, k_out, v_out, out_cap, pooled_opt, kmax_opt,
+                              kmin_opt, nblk_cap, block, ws, static_cast<hipStream_t>(stream)),
       "rk_snapkv_evict launch");
 }
 
@@ -568,6 +581,17 @@ rk_status rk_adakv_evict(const rk_shape* shape, const void* q_win, const void* k
                          void* v_out, int64_t out_cap, float* pooled_opt, void* kmax_opt,
                          void* kmin_opt, int64_t nblk_cap, int32_t block, void* ws, size_t ws_bytes,
                          rk_stream stream) {
+  return rk_adakv_evict_pool(shape, q_win, k, v, kv_cap, seq_len, window, pool_kernel, RK_POOL_SUM,
+                             n_keep, kept_idx, kept_count, k_out, v_out, out_cap, pooled_opt,
+                             kmax_opt, kmin_opt, nblk_cap, block, ws, ws_bytes, stream);
+}
+
+rk_status rk_adakv_evict_pool(const rk_shape* shape, const void* q_win, const void* k, const void* v,
+                              int64_t kv_cap, int64_t seq_len, int32_t window, int32_t pool_kernel,
+                              int32_t pool_op, int64_t n_keep, int32_t* kept_idx,
+                              int32_t* kept_count, void* k_out, void* v_out, int64_t out_cap,
+                              float* pooled_opt, void* kmax_opt, void* kmin_opt, int64_t nblk_cap,
+                              int32_t block, void* ws, size_t ws_bytes, rk_stream stream) {
   rk::Dims d;
   rk_status st = check_shape(shape, &d);
   if (st != RK_OK) return st;
@@ -588,6 +612,8 @@ rk_status rk_adakv_evict(const rk_shape* shape, const void* q_win, const void* k
     return fail(RK_EUNSUPPORTED, "Hkv * (seq_len - window) too large");
   if (pool_kernel < 1 || (pool_kernel % 2) == 0 || pool_kernel > 4097)
     return fail(RK_EINVAL, "pool_kernel must be odd, in [1, 4097]");
+  if (pool_op != RK_POOL_SUM && pool_op != RK_POOL_MAX)
+    return fail(RK_EINVAL, "pool_op must be RK_POOL_SUM or RK_POOL_MAX");
   const int64_t worst = std::min<int64_t>(seq_len, int64_t(d.Hkv) * (n_keep - window) + window);
   if (out_cap < worst)
     return fail(RK_EINVAL, "out_cap (%lld) below min(seq_len, Hkv * (n_keep - W) + W) = %lld",
@@ -607,9 +633,10 @@ rk_status rk_adakv_evict(const rk_shape* shape, const void* q_win, const void* k
   const rk::EvictWs lay = rk::evict_ws_layout(d, seq_len, window);
   if ((st = check_ws(ws, ws_bytes, lay.total)) != RK_OK) return st;
   return device_status(
-      rk::launch_snapkv_evict(d, q_win, k, v, kv_cap, seq_len, window, pool_kernel, n_keep, kept_idx,
-                              k_out, v_out, out_cap, pooled_opt, kmax_opt, kmin_opt, nblk_cap, block,
-                              ws, static_cast<hipStream_t>(stream), kept_count),
+      rk::launch_snapkv_evict(d, q_win, k, v, kv_cap, seq_len, window, pool_kernel, pool_op,
+                              n_keep, kept_idx, k_out, v_out, out_cap, pooled_opt, kmax_opt,
+                              kmin_opt, nblk_cap, block, ws, static_cast<hipStream_t>(stream),
+                              kept_count),
       "rk_adakv_evict launch");
 }
 

@@ -232,7 +232,16 @@ __global__ __launch_bounds__(256) void ws_pass2_kernel(const T* __restrict__ q_w
 // non-negative, so the regrouping changes a sum by a few ulp at most; zeros
 // past either end add nothing.  Results go through LDS so the stores are
 // coalesced whatever the row alignment.
-template <int H>
+// The pooling's combining operation: a rounded add, or (the max reading of
+// the pooling) a maximum, which is exact, so any grouping gives the same
+// value.  Window scores are never negative, so the zeros past either end of
+// the prefix leave a maximum unchanged as they leave a sum.
+template <bool MX>
+__device__ __forceinline__ float pool_comb(float a, float b) {
+  return MX ? fmaxf(a, b) : __fadd_rn(a, b);
+}
+
+template <int H, bool MX = false>
 __global__ __launch_bounds__(256) void pool_sum_reg_kernel(const float* __restrict__ scores,
                                                            int P, float* __restrict__ pooled) {
   constexpr int PT = 8;
@@ -264,17 +273,17 @@ __global__ __launch_bounds__(256) void pool_sum_reg_kernel(const float* __restri
   // output e (0 <= e < PT) sums v[e .. e + 2H]
   float mid = v[PT - 1];
 #pragma unroll
-  for (int i = PT; i <= 2 * H; ++i) mid = __fadd_rn(mid, v[i]);
+  for (int i = PT; i <= 2 * H; ++i) mid = pool_comb<MX>(mid, v[i]);
   float left[PT];  // left[e] = v[e] + ... + v[PT - 2]
   left[PT - 1] = 0.f;
 #pragma unroll
-  for (int e = PT - 2; e >= 0; --e) left[e] = e == PT - 2 ? v[e] : __fadd_rn(v[e], left[e + 1]);
+  for (int e = PT - 2; e >= 0; --e) left[e] = e == PT - 2 ? v[e] : pool_comb<MX>(v[e], left[e + 1]);
   float right = 0.f;  // v[2H + 1] + ... + v[2H + e]
 #pragma unroll
   for (int e = 0; e < PT; ++e) {
-    if (e > 0) right = e == 1 ? v[2 * H + 1] : __fadd_rn(right, v[2 * H + e]);
-    float acc = e < PT - 1 ? __fadd_rn(left[e], mid) : mid;
-    if (e > 0) acc = __fadd_rn(acc, right);
+    if (e > 0) right = e == 1 ? v[2 * H + 1] : pool_comb<MX>(right, v[2 * H + e]);
+    float acc = e < PT - 1 ? pool_comb<MX>(left[e], mid) : mid;
+    if (e > 0) acc = pool_comb<MX>(acc, right);
     res[PT * t + e] = acc;
   }
   __syncthreads();
@@ -286,7 +295,9 @@ __global__ __launch_bounds__(256) void pool_sum_reg_kernel(const float* __restri
   }
 }
 
-// pooled[j] = sum_{i=j-h}^{j+h} score[i] (zero outside [0, P)), left to right.
+// pooled[j] = sum_{i=j-h}^{j+h} score[i] (zero outside [0, P)), left to right;
+// MX: the maximum of the same terms.
+template <bool MX = false>
 __global__ __launch_bounds__(256) void pool_sum_kernel(const float* __restrict__ scores, int P, int h,
                                                    float* __restrict__ pooled) {
   extern __shared__ float tile[];  // 256 + 2h
@@ -303,7 +314,7 @@ __global__ __launch_bounds__(256) void pool_sum_kernel(const float* __restrict__
   float acc = 0.f;
   for (int i = 0; i <= 2 * h; ++i) {
     const int src = j - h + i;
-    if (src >= 0 && src < P) acc = __fadd_rn(acc, tile[threadIdx.x + i]);
+    if (src >= 0 && src < P) acc = pool_comb<MX>(acc, tile[threadIdx.x + i]);
   }
   pooled[size_t(u) * P + j] = acc;
 }
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
 // into order keys in place once every thread has read its window, and selects
 // as select_kernel does.  Saves the pooled scores' round trip through memory
 // and a launch; the pooled scores are still written when asked for.
-template <int H>
+template <int H, bool MX = false>
 __global__ __launch_bounds__(1024) void select_pool_kernel(const float* __restrict__ scores,
                                                            int S, int W, int n_keep, int cand_cap,
                                                            float* __restrict__ pooled_opt,
@@ -433,17 +444,17 @@ __global__ __launch_bounds__(1024) void select_pool_kernel(const float* __restri
       }
       float mid = v[PT - 1];
 #pragma unroll
-      for (int i = PT; i <= 2 * H; ++i) mid = __fadd_rn(mid, v[i]);
+      for (int i = PT; i <= 2 * H; ++i) mid = pool_comb<MX>(mid, v[i]);
       float left[PT];
       left[PT - 1] = 0.f;
 #pragma unroll
-      for (int e = PT - 2; e >= 0; --e) left[e] = e == PT - 2 ? v[e] : __fadd_rn(v[e], left[e + 1]);
+      for (int e = PT - 2; e >= 0; --e) left[e] = e == PT - 2 ? v[e] : pool_comb<MX>(v[e], left[e + 1]);
       float right = 0.f;
 #pragma unroll
       for (int e = 0; e < PT; ++e) {
-        if (e > 0) right = e == 1 ? v[2 * H + 1] : __fadd_rn(right, v[2 * H + e]);
-        float acc = e < PT - 1 ? __fadd_rn(left[e], mid) : mid;
-        if (e > 0) acc = __fadd_rn(acc, right);
+        if (e > 0) right = e == 1 ? v[2 * H + 1] : pool_comb<MX>(right, v[2 * H + e]);
+        float acc = e < PT - 1 ? pool_comb<MX>(left[e], mid) : mid;
+        if (e > 0) acc = pool_comb<MX>(acc, right);
         out[c][e] = acc;
       }
     }
@@ -1292,8 +1303,8 @@ __global__ __launch_bounds__(256) void gather_aux_kernel(
 
 template <typename T, int D>
 hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const void* v,
-                          int64_t kv_cap, int64_t S64, int W, int pool_kernel, int64_t n_keep,
-                          int32_t* kept, void* k_out, void* v_out, int64_t out_cap,
+                          int64_t kv_cap, int64_t S64, int W, int pool_kernel, int pool_op,
+                          int64_t n_keep, int32_t* kept, void* k_out, void* v_out, int64_t out_cap,
                           float* pooled_opt, void* kmax, void* kmin, int64_t nblk_cap, int block,
                           void* ws, hipStream_t s, int32_t* ada_counts) {
   const int S = int(S64);
@@ -1370,6 +1381,7 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   if (!attr_set) {
     for (const void* f : {reinterpret_cast<const void*>(&select_kernel),
                           reinterpret_cast<const void*>(&select_pool_kernel<31>),
+                          reinterpret_cast<const void*>(&select_pool_kernel<31, true>),
                           reinterpret_cast<const void*>(&select_chunk_kernel),
                           reinterpret_cast<const void*>(&select_final_kernel),
                           reinterpret_cast<const void*>(&adakv_select_kernel)}) {
@@ -1380,18 +1392,32 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
     attr_set = true;
   }
   const int h = (pool_kernel - 1) / 2;
+  const bool mx = pool_op == 1;  // max pooling (else sums)
+  // the pooling launch of the paths that pool separately
+  auto pool = [&]() {
+    if (h == 31) {
+      if (mx)
+        RK_LAUNCH("pool_sum", (pool_sum_reg_kernel<31, true>), dim3((P + 2047) / 2048, units), dim3(256), 0,
+                  s, scores, P, pooled);
+      else
+        RK_LAUNCH("pool_sum", pool_sum_reg_kernel<31>, dim3((P + 2047) / 2048, units), dim3(256), 0, s,
+                  scores, P, pooled);
+    } else {
+      if (mx)
+        RK_LAUNCH("pool_sum", pool_sum_kernel<true>, dim3((P + 255) / 256, units), dim3(256),
+                  size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
+      else
+        RK_LAUNCH("pool_sum", pool_sum_kernel<false>, dim3((P + 255) / 256, units), dim3(256),
+                  size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
+    }
+  };
   if (ada) {
     // pooling of every unit first (the shared choice reads all heads of a
     // sequence), then the shared choice: one workgroup per sequence when
     // its keys fit in LDS (the spent window scores hold its chosen flattened
     // indices), else the radix select over many workgroups
     if (P > 0) {
-      if (h == 31)
-        RK_LAUNCH("pool_sum", pool_sum_reg_kernel<31>, dim3((P + 2047) / 2048, units), dim3(256), 0, s,
-                  scores, P, pooled);
-      else
-        RK_LAUNCH("pool_sum", pool_sum_kernel, dim3((P + 255) / 256, units), dim3(256),
-                  size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
+      pool();
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     const size_t nkeys = size_t(d.Hkv) * P;
@@ -1438,17 +1464,17 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
   if (P > 0 && h == kPoolH && pool_words * 4 <= kSelectKeysLds && units >= kComputeUnits / 4) {
     const size_t words = std::max(pool_words, size_t(P) + 4096);
     const int cand_cap = int(std::min<size_t>(4096, kSelectKeysLds / 4 - size_t(P)));
-    RK_LAUNCH("select_tokens", select_pool_kernel<kPoolH>, dim3(units), dim3(1024),
-              std::min(words, kSelectKeysLds / 4) * 4, s, scores, S, W, int(n_keep), cand_cap,
-              pooled_opt, kept);
+    if (mx)
+      RK_LAUNCH("select_tokens", (select_pool_kernel<kPoolH, true>), dim3(units), dim3(1024),
+                std::min(words, kSelectKeysLds / 4) * 4, s, scores, S, W, int(n_keep), cand_cap,
+                pooled_opt, kept);
+    else
+      RK_LAUNCH("select_tokens", select_pool_kernel<kPoolH>, dim3(units), dim3(1024),
+                std::min(words, kSelectKeysLds / 4) * 4, s, scores, S, W, int(n_keep), cand_cap,
+                pooled_opt, kept);
   } else {
     if (P > 0) {
-      if (h == 31)
-        RK_LAUNCH("pool_sum", pool_sum_reg_kernel<31>, dim3((P + 2047) / 2048, units), dim3(256),
-                  0, s, scores, P, pooled);
-      else
-        RK_LAUNCH("pool_sum", pool_sum_kernel, dim3((P + 255) / 256, units), dim3(256),
-                  size_t(256 + 2 * h) * sizeof(float), s, scores, P, h, pooled);
+      pool();
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     const int staged = size_t(P) * 4 <= kSelectKeysLds ? 1 : 0;
@@ -1511,15 +1537,15 @@ hipError_t launch_evict_t(const Dims& d, const void* q_win, const void* k, const
 }  // namespace
 
 hipError_t launch_snapkv_evict(const Dims& d, const void* q_win, const void* k, const void* v,
-                               int64_t kv_cap, int64_t S, int W, int pool_kernel,
+                               int64_t kv_cap, int64_t S, int W, int pool_kernel, int pool_op,
                                int64_t n_keep, int32_t* kept, void* k_out, void* v_out,
                                int64_t out_cap, float* pooled_opt, void* kmax, void* kmin,
                                int64_t nblk_cap, int block, void* ws, hipStream_t s,
                                int32_t* ada_counts) {
-#define RK_EVICT(TT, DD)                                                                      \
-  return launch_evict_t<TT, DD>(d, q_win, k, v, kv_cap, S, W, pool_kernel, n_keep, kept, k_out, \
-                                v_out, out_cap, pooled_opt, kmax, kmin, nblk_cap, block, ws, s, \
-                                ada_counts)
+#define RK_EVICT(TT, DD)                                                                  \
+  return launch_evict_t<TT, DD>(d, q_win, k, v, kv_cap, S, W, pool_kernel, pool_op, n_keep, \
+                                kept, k_out, v_out, out_cap, pooled_opt, kmax, kmin,        \
+                                nblk_cap, block, ws, s, ada_counts)
   if (d.bf16) {
     if (d.D == 128) RK_EVICT(bf16_t, 128);
     RK_EVICT(bf16_t, 64);

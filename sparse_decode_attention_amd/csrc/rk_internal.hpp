@@ -162,7 +162,7 @@ hipError_t launch_hsa_decode(const Dims& d, const void* q, const void* k, const 
                              const int32_t* lens = nullptr);
 
 hipError_t launch_snapkv_evict(const Dims& d, const void* q_win, const void* k, const void* v,
-                               int64_t kv_cap, int64_t S, int W, int pool_kernel,
+                               int64_t kv_cap, int64_t S, int W, int pool_kernel, int pool_op,
                                int64_t n_keep, int32_t* kept, void* k_out, void* v_out,
                                int64_t out_cap, float* pooled_opt, void* kmax, void* kmin,
                                int64_t nblk_cap, int block, void* ws, hipStream_t s,

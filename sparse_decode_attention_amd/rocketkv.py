@@ -45,6 +45,11 @@ _lib.rk_snapkv_workspace_bytes.argtypes = [_SP, _i64, _i32]
 _lib.rk_snapkv_workspace_bytes.restype = _sz
 _lib.rk_snapkv_evict.argtypes = [_SP, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i64, _vp, _vp, _vp,
                                  _i64, _vp, _vp, _vp, _i64, _i32, _vp, _sz, _vp]
+_lib.rk_snapkv_evict_pool.argtypes = [_SP, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i64, _vp, _vp,
+                                      _vp, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _sz, _vp]
+_lib.rk_snapkv_evict_pool.restype = ctypes.c_int
+# pooling operations (rk_pool_op)
+POOL_OPS = {"sum": 0, "max": 1}
 _lib.rk_hsa_build_aux.argtypes = [_SP, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _i64, _vp]
 _lib.rk_hsa_workspace_bytes.argtypes = [_SP, _i64, _i32, _i32, _i32]
 _lib.rk_hsa_workspace_bytes.restype = _sz
@@ -126,11 +131,12 @@ def rk_snapkv_workspace_bytes(shape: RkShape, seq_len: int, window: int) -> int:
 
 def rk_snapkv_evict(q_win, k, v, seq_len, window, pool_kernel, n_keep, kept_idx,
                     k_out=None, v_out=None, pooled=None, ws=None, stream=None,
-                    kmax=None, kmin=None, block=16):
+                    kmax=None, kmin=None, block=16, pool_op="sum"):
     """Stage 1.  q_win [B,Hq,W,d]; k, v [B,Hkv,cap,d]; kept_idx [B,Hkv,n_keep] int32;
     k_out, v_out [B,Hkv,out_cap,d] or None (RocketKV-MT); pooled [B,Hkv,S-W] fp32 or None;
     kmax, kmin [B,Hkv,d,nblk_cap] or None: also build the compact cache's Kmax/Kmin in
-    pages of `block` tokens."""
+    pages of `block` tokens; pool_op "sum" (rk_snapkv_evict) or "max"
+    (rk_snapkv_evict_pool with RK_POOL_MAX)."""
     _need_contig(q_win, k, v, kept_idx, k_out, v_out, pooled, kmax, kmin)
     B, Hq, W, d = q_win.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
@@ -138,10 +144,17 @@ def rk_snapkv_evict(q_win, k, v, seq_len, window, pool_kernel, n_keep, kept_idx,
     ws = _ws(nbytes, k, ws, stream)
     out_cap = k_out.shape[2] if k_out is not None else 0
     nblk_cap = kmax.shape[3] if kmax is not None else 0
-    _check(_lib.rk_snapkv_evict(ctypes.byref(shape), _ptr(q_win), _ptr(k), _ptr(v), k.shape[2],
-                                seq_len, window, pool_kernel, n_keep, _ptr(kept_idx), _ptr(k_out),
-                                _ptr(v_out), out_cap, _ptr(pooled), _ptr(kmax), _ptr(kmin), nblk_cap,
-                                block, _ptr(ws), ws.numel(), _stream(stream)), "rk_snapkv_evict")
+    if pool_op == "sum":
+        _check(_lib.rk_snapkv_evict(ctypes.byref(shape), _ptr(q_win), _ptr(k), _ptr(v), k.shape[2],
+                                    seq_len, window, pool_kernel, n_keep, _ptr(kept_idx), _ptr(k_out),
+                                    _ptr(v_out), out_cap, _ptr(pooled), _ptr(kmax), _ptr(kmin), nblk_cap,
+                                    block, _ptr(ws), ws.numel(), _stream(stream)), "rk_snapkv_evict")
+    else:
+        _check(_lib.rk_snapkv_evict_pool(ctypes.byref(shape), _ptr(q_win), _ptr(k), _ptr(v), k.shape[2],
+                                         seq_len, window, pool_kernel, POOL_OPS.get(pool_op, -1), n_keep,
+                                         _ptr(kept_idx), _ptr(k_out), _ptr(v_out), out_cap, _ptr(pooled),
+                                         _ptr(kmax), _ptr(kmin), nblk_cap, block, _ptr(ws), ws.numel(),
+                                         _stream(stream)), "rk_snapkv_evict_pool")
     return ws
 
 
@@ -375,6 +388,9 @@ def rk_paged_hsa_append_decode(q, k_new, v_new, k_pool, v_pool, pages: RkPagedKv
 _lib.rk_adakv_evict.argtypes = [_SP, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _i64, _vp,
                                 _vp, _vp, _i64, _i32, _vp, _sz, _vp]
 _lib.rk_adakv_evict.restype = ctypes.c_int
+_lib.rk_adakv_evict_pool.argtypes = [_SP, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
+                                     _i64, _vp, _vp, _vp, _i64, _i32, _vp, _sz, _vp]
+_lib.rk_adakv_evict_pool.restype = ctypes.c_int
 _lib.rk_hsa_decode_ragged.argtypes = [_SP, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp,
                                       _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.rk_hsa_decode_ragged.restype = ctypes.c_int
@@ -386,19 +402,21 @@ def adakv_capacity(n_kv_heads: int, seq_len: int, window: int, n_keep: int) -> i
 
 
 def rk_adakv_evict(q_win, k, v, seq_len, window, pool_kernel, n_keep, kept_idx, kept_count, k_out=None,
-                   v_out=None, pooled=None, ws=None, stream=None, kmax=None, kmin=None, block=16):
+                   v_out=None, pooled=None, ws=None, stream=None, kmax=None, kmin=None, block=16,
+                   pool_op="sum"):
     """Stage 1 with the shared (Ada-KV) budget.  kept_idx [B,Hkv,out_cap], kept_count [B,Hkv] int32;
-    k_out, v_out [B,Hkv,out_cap,d] or None; kmax/kmin as rk_snapkv_evict."""
+    k_out, v_out [B,Hkv,out_cap,d] or None; kmax/kmin and pool_op as rk_snapkv_evict."""
     _need_contig(q_win, k, v, kept_idx, kept_count, k_out, v_out, pooled, kmax, kmin)
     B, Hq, W, d = q_win.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     ws = _ws(rk_snapkv_workspace_bytes(shape, seq_len, window), k, ws, stream)
     out_cap = kept_idx.shape[2]
     nblk_cap = kmax.shape[3] if kmax is not None else 0
-    _check(_lib.rk_adakv_evict(ctypes.byref(shape), _ptr(q_win), _ptr(k), _ptr(v), k.shape[2], seq_len, window,
-                               pool_kernel, n_keep, _ptr(kept_idx), _ptr(kept_count), _ptr(k_out), _ptr(v_out),
-                               out_cap, _ptr(pooled), _ptr(kmax), _ptr(kmin), nblk_cap, block, _ptr(ws), ws.numel(),
-                               _stream(stream)), "rk_adakv_evict")
+    _check(_lib.rk_adakv_evict_pool(ctypes.byref(shape), _ptr(q_win), _ptr(k), _ptr(v), k.shape[2], seq_len,
+                                    window, pool_kernel, POOL_OPS.get(pool_op, -1), n_keep, _ptr(kept_idx),
+                                    _ptr(kept_count), _ptr(k_out), _ptr(v_out), out_cap, _ptr(pooled), _ptr(kmax),
+                                    _ptr(kmin), nblk_cap, block, _ptr(ws), ws.numel(), _stream(stream)),
+           "rk_adakv_evict_pool")
     return ws
 
 

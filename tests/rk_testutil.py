@@ -62,7 +62,7 @@ def ascending(x) -> bool:
 
 # --------------------------------------------------------------------------
 def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compact=True, out_cap=None,
-                    aux_block=None):
+                    aux_block=None, pool_op="sum"):
     """Run rk_snapkv_evict and check every (or the given) unit against the oracle;
     with aux_block, the call also builds Kmax/Kmin of the compact cache, checked
     bit-exactly.  Returns (kept, k_out, v_out, pooled, swaps), plus (kmax, kmin)
@@ -83,7 +83,7 @@ def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compa
                               dtype=k.dtype, device=dev)
             kmin = torch.full_like(kmax, 7.0)
     rk.rk_snapkv_evict(qw, k, v, S, W, pool, n_keep, kept, ko, vo, pooled, kmax=kmax, kmin=kmin,
-                       block=aux_block or 16)
+                       block=aux_block or 16, pool_op=pool_op)
     torch.cuda.synchronize()
     swaps = 0
     units = units_to_check or [(b, h) for b in range(B) for h in range(Hkv)]
@@ -91,7 +91,7 @@ def evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=None, compa
         q_np = np32(qw[b, h * G:(h + 1) * G])
         k_np = np32(k[b, h, :S])
         sc = O.window_scores(q_np, k_np)
-        pl = O.pool_sum(sc, pool)
+        pl = O.pool(sc, pool, pool_op)
         if S > W:
             g_pl = np32(pooled[b, h])
             scale = float(np.abs(pl).max())

@@ -152,6 +152,22 @@ def test_error_codes_before_any_launch(rk):
     need = lib.rk_snapkv_workspace_bytes(byref(sh), 2048, 16)
     assert need > 0 and evict(wsb=need - 1) == rk.RK_EWORKSPACE
 
+    def evict_pool(op, **kw):
+        a = dict(pool=7, keep=930, wsb=1 << 30)
+        a.update(kw)
+        return lib.rk_snapkv_evict_pool(byref(sh), _vp(FAKE), _vp(FAKE), _vp(FAKE), 2048, 2048, 16,
+                                        a["pool"], op, a["keep"], _vp(FAKE), _vp(FAKE), _vp(FAKE), 930,
+                                        None, None, None, 0, 16, _vp(FAKE), a["wsb"], None)
+
+    assert evict_pool(2) == rk.RK_EINVAL and evict_pool(-1) == rk.RK_EINVAL   # no such pooling
+    assert b"pool_op" in lib.rk_last_error()
+    assert evict_pool(1, pool=8) == rk.RK_EINVAL
+    assert evict_pool(1, wsb=100) == rk.RK_EWORKSPACE                         # max pooling passes the checks
+    ada = lib.rk_adakv_evict_pool(byref(sh), _vp(FAKE), _vp(FAKE), _vp(FAKE), 2048, 2048, 16, 7, 5, 930,
+                                  _vp(FAKE), _vp(FAKE), _vp(FAKE), _vp(FAKE), 2048, None, None, None, 0, 16,
+                                  _vp(FAKE), 1 << 30, None)
+    assert ada == rk.RK_EINVAL and b"pool_op" in lib.rk_last_error()
+
     def aux(**kw):
         a = dict(k=_vp(FAKE), cap=1024, idx=None, stride=0, n=1000, first=0, block=16, nblk_cap=64)
         a.update(kw)

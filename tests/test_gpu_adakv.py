@@ -29,7 +29,7 @@ def say(*a):
     print("[case]", *a, file=sys.stderr, flush=True)
 
 
-def ada_evict_and_check(rk, w, n_keep, block=16, aux=True, kvq=None):
+def ada_evict_and_check(rk, w, n_keep, block=16, aux=True, kvq=None, pool_op="sum"):
     """rk_adakv_evict on layer 0 of w (or on the given K, V and window
     queries), checked against the oracle; returns the GPU's kept counts,
     compact cache and aux."""
@@ -51,15 +51,16 @@ def ada_evict_and_check(rk, w, n_keep, block=16, aux=True, kvq=None):
     if aux:
         kmax = torch.full((B, Hkv, d, rk.aux_capacity(cap, block)), 7.0, dtype=k.dtype, device=DEV)
         kmin = torch.full_like(kmax, 7.0)
-    rk.rk_adakv_evict(qw, k, v, S, W, w.pool, n_keep, kept, cnt, ko, vo, pooled, kmax=kmax, kmin=kmin, block=block)
+    rk.rk_adakv_evict(qw, k, v, S, W, w.pool, n_keep, kept, cnt, ko, vo, pooled, kmax=kmax, kmin=kmin, block=block,
+                      pool_op=pool_op)
     torch.cuda.synchronize()
     counts = cnt.cpu().numpy()
     assert (counts.sum(axis=1) == Hkv * n_keep).all()
     swaps = 0
     for b in range(B):
         g_pl = U.np32(pooled[b])
-        o_pl = np.stack([O.pool_sum(O.window_scores(U.np32(qw[b, h * G:(h + 1) * G]), U.np32(k[b, h])), w.pool)
-                         for h in range(Hkv)])
+        o_pl = np.stack([O.pool(O.window_scores(U.np32(qw[b, h * G:(h + 1) * G]), U.np32(k[b, h])), w.pool,
+                                pool_op) for h in range(Hkv)])
         np.testing.assert_allclose(g_pl, o_pl, rtol=1e-4, atol=1e-6 * float(np.abs(o_pl).max()))
         mine = O.adakv_select(g_pl, S, W, n_keep)       # exact on the GPU's own pooled scores
         want = O.adakv_select(o_pl, S, W, n_keep)       # the oracle's: near-tie swaps only
@@ -123,6 +124,15 @@ def test_adakv_tied_heads_many_workgroup_select(rk):
     cnt = ada_evict_and_check(rk, w, 1500, block=w.block, kvq=(k, v, qw))[0].cpu().numpy()
     # heads with the same data: the lower one never keeps fewer
     assert (cnt[:, :2] >= cnt[:, 6:]).all()
+
+
+@pytest.mark.parametrize("B,seq,n_keep", [(2, 3000, 900), (1, 9000, 2000)])
+def test_adakv_evict_max_pooling(rk, B, seq, n_keep):
+    """The max reading of the pooling under the shared budget: one workgroup
+    per sequence (16K keys) and the many-workgroup select (72K keys)."""
+    w = WL.scaled(LLAMA, batch=B, seq=seq, n_plant=32)
+    say("adakv evict, max pooling", B, seq, n_keep)
+    ada_evict_and_check(rk, w, n_keep, block=w.block, pool_op="max")
 
 
 def test_adakv_equal_heads_is_snapkv(rk):

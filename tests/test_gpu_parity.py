@@ -114,6 +114,27 @@ def test_shapes_and_ragged_tails(rk, dtype, d, G, S, W, pool):
     say("swaps", res["swaps_evict"], res["swaps_decode"])
 
 
+@pytest.mark.parametrize("B,n_kv,d,dtype,S,W,pool,n_keep", [
+    (1, 8, 128, "bf16", 3000, 32, 63, 900),     # kernel 63, pooled in its own launch
+    (20, 8, 128, "bf16", 1500, 32, 63, 400),    # 160 units: pooled inside the select launch
+    (2, 2, 64, "f32", 777, 16, 7, 300),         # other kernel widths
+    (1, 2, 64, "bf16", 300, 4, 1, 100),         # kernel 1: the scores themselves
+])
+def test_evict_max_pooling(rk, B, n_kv, d, dtype, S, W, pool, n_keep):
+    """The max reading of the pooling (rk_snapkv_evict_pool, RK_POOL_MAX)
+    against the oracle's pool_max on every pooling path."""
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=B, n_kv=n_kv, n_q=4 * n_kv, d=d, dtype=dtype, seq=S, window=W, pool=pool,
+                  n_plant=8)
+    say("evict, max pooling", B, n_kv, d, dtype, S, W, pool, n_keep)
+    k, v, _ = WL.layer_kv(w, 0, device=DEV)
+    qw = WL.window_queries(w, 0, device=DEV)
+    units = [(0, 0), (B - 1, n_kv - 1), (B // 2, n_kv // 2)]
+    swaps = U.evict_and_check(rk, qw, k, v, S, W, pool, n_keep, units_to_check=units, aux_block=16,
+                              pool_op="max")[4]
+    say("  swaps", swaps)
+
+
 @pytest.mark.parametrize("n_keep,out_cap", [(700, 700), (705, 760)])
 def test_compaction_aux_many_pages(rk, n_keep, out_cap):
     """Batch 32 x 8 KV heads: the compaction with Kmax/Kmin takes its wide

@@ -149,6 +149,50 @@ def test_pool_left_to_right_order():
     assert O.pool_sum(s, 3)[1] == np.float32(1.0)
 
 
+def test_pool_max_hand_worked():
+    """Max pooling (the other reading of the pooling paragraph), worked by hand:
+    windows are cut at the ends, never padded into the result."""
+    s = np.array([1, 5, 2, 0, 3], np.float32)
+    assert O.pool_max(s, 1).tolist() == [1, 5, 2, 0, 3]
+    assert O.pool_max(s, 3).tolist() == [5, 5, 5, 3, 3]
+    assert O.pool_max(s, 5).tolist() == [5, 5, 5, 5, 3]
+    assert O.pool_max(s, 63).tolist() == [5] * 5
+    with pytest.raises(ValueError):
+        O.pool_max(s, 2)
+    with pytest.raises(ValueError):
+        O.pool(s, 3, "mean")
+
+
+@pytest.mark.parametrize("k", [1, 7, 63])
+def test_pool_max_is_a_maximum_filter(k):
+    """Equal to scipy's one-dimensional maximum filter with out-of-range
+    samples ignored, and a spike spreads to exactly k positions."""
+    from scipy.ndimage import maximum_filter1d
+    rng = np.random.default_rng(k)
+    s = rng.random(300).astype(np.float32)
+    want = maximum_filter1d(s, size=k, mode="constant", cval=-np.inf)
+    np.testing.assert_array_equal(O.pool_max(s, k), want)
+    delta = np.zeros(101, np.float32)
+    delta[50] = 2.0
+    out = O.pool_max(delta, k)
+    assert (out == 2.0).sum() == k and np.all(out[50 - k // 2:51 + k // 2] == 2.0)
+
+
+def test_pool_max_kernel_one_is_sum_kernel_one():
+    """With kernel 1 both readings leave the scores as they are, so stage 1
+    keeps the same tokens under either."""
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 4, 8, 16)).astype(np.float32)
+    k = rng.standard_normal((1, 2, 120, 16)).astype(np.float32)
+    a = O.snapkv_evict(q, k, None, 8, 1, 40)
+    b = O.snapkv_evict(q, k, None, 8, 1, 40, pool_op="max")
+    assert np.array_equal(a["kept"], b["kept"]) and np.array_equal(a["pooled"], b["pooled"])
+    c = O.snapkv_evict(q, k, None, 8, 7, 40, pool_op="max")
+    for h in range(2):
+        sc = O.window_scores(q[0, 2 * h:2 * h + 2], k[0, h])
+        np.testing.assert_array_equal(c["pooled"][0, h], O.pool_max(sc, 7))
+
+
 # ---------------------------------------------------------------- window scores
 def _window_scores_loop(q, k):
     """Pure-Python per-row softmax on a tiny case (brute force)."""
