@@ -822,8 +822,8 @@ __global__ __launch_bounds__(1024) void adakv_select_kernel(const float* __restr
   wg_topk<1024, 2048>([&](int i) { return skeys[i]; }, n, K, emit, sm, true, lo, hi, skeys + n, cand_cap);
   __syncthreads();
   // start[h] = number of chosen indices below h * P (tb is ascending)
-  if (threadIdx.x <= Hkv) {
-    const int target = threadIdx.x * P;
+  if (int(threadIdx.x) <= Hkv) {
+    const int target = int(threadIdx.x) * P;
     int lo = 0, hi = K;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
