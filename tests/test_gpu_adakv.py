@@ -135,6 +135,28 @@ def test_adakv_evict_max_pooling(rk, B, seq, n_keep):
     ada_evict_and_check(rk, w, n_keep, block=w.block, pool_op="max")
 
 
+def test_adakv_all_keys_equal_many_workgroup_select(rk):
+    """Every key row the same vector and every head the same queries: each
+    window row spreads its probability evenly, and every head computes the
+    same values, so with pool kernel 1 every pooled score of the sequence is
+    one value and the whole budget goes in flattened order: head 0 takes its
+    whole prefix, head 1 the rest of the budget, later heads nothing.  (With
+    different queries per head the heads' even scores differ in the last
+    bits, through the rounding of their logits, and the cut follows those.)"""
+    w = WL.scaled(LLAMA, batch=1, seq=9000, n_plant=0, pool=1)
+    say("adakv evict, all keys equal", w.batch, w.seq)
+    k, v, _ = WL.layer_kv(w, 0, device=DEV)
+    qw = WL.window_queries(w, 0, device=DEV)
+    k = k[:, :1, :1].expand(-1, w.n_kv, k.shape[2], -1).contiguous()
+    qw = qw[:, :w.group].repeat(1, w.n_kv, 1, 1).contiguous()
+    P = w.seq - w.window
+    n_keep = w.window + (3 * P) // (2 * w.n_kv)         # budget: 1.5 heads' prefixes
+    cnt = ada_evict_and_check(rk, w, n_keep, block=w.block, kvq=(k, v, qw))[0].cpu().numpy()
+    budget = w.n_kv * (n_keep - w.window)
+    want = [min(P, max(0, budget - h * P)) + w.window for h in range(w.n_kv)]
+    assert cnt[0].tolist() == want, (cnt[0].tolist(), want)
+
+
 def test_adakv_equal_heads_is_snapkv(rk):
     """Every head with the same keys and queries: the shared budget splits
     evenly and the result is rk_snapkv_evict's.  Pool kernel 1, so the cut
