@@ -135,6 +135,30 @@ def test_evict_max_pooling(rk, B, n_kv, d, dtype, S, W, pool, n_keep):
     say("  swaps", swaps)
 
 
+@pytest.mark.parametrize("B,S,pool,op,n_keep", [
+    (1, 3000, 1, "sum", 900),      # keys staged in LDS, pooling in its own launch
+    (20, 1500, 63, "max", 400),    # 160 units: pooling inside the select launch
+    (1, 45000, 1, "sum", 5000),    # more keys than LDS holds: chunked select
+])
+def test_stage1_select_all_ties(rk, B, S, pool, op, n_keep):
+    """Every key row of a unit the same vector: each window row spreads its
+    probability evenly over the prefix, so every pooled score of a unit is
+    one value (with kernel 1, or the maximum over any kernel) and the lower
+    positions win every tie: the unit keeps its first n_keep - W positions."""
+    base = WL.WORKLOADS["llama8b-layer-s32k-c16"]
+    w = WL.scaled(base, batch=B, seq=S, pool=pool, n_plant=0)
+    say("stage 1, all ties", B, S, pool, op, n_keep)
+    k, v, _ = WL.layer_kv(w, 0, device=DEV)
+    qw = WL.window_queries(w, 0, device=DEV)
+    k = k[:, :, :1].expand(-1, -1, S, -1).contiguous()
+    units = [(0, 0), (B - 1, w.n_kv - 1)]
+    kept = U.evict_and_check(rk, qw, k, v, S, w.window, pool, n_keep, units_to_check=units, pool_op=op)[0]
+    want = torch.cat([torch.arange(n_keep - w.window), torch.arange(S - w.window, S)]).to(torch.int32)
+    for b in range(B):
+        for h in range(w.n_kv):
+            assert torch.equal(kept[b, h].cpu(), want), (b, h)
+
+
 @pytest.mark.parametrize("n_keep,out_cap", [(700, 700), (705, 760)])
 def test_compaction_aux_many_pages(rk, n_keep, out_cap):
     """Batch 32 x 8 KV heads: the compaction with Kmax/Kmin takes its wide
