@@ -78,7 +78,21 @@ def _check(status: int, what: str):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor argument (None passes NULL).  Every tensor the
+    library reads or writes lives in GPU memory: a host tensor is refused here,
+    before a kernel could dereference its address."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must be on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need_dtype(dtype, *ts):
+    """Index, count and float32 output arguments have one fixed element type."""
+    for t in ts:
+        if t is not None and t.dtype != dtype:
+            raise TypeError(f"expected {dtype} tensor, got {t.dtype}")
 
 
 def _stream(stream):
@@ -138,6 +152,9 @@ def rk_snapkv_evict(q_win, k, v, seq_len, window, pool_kernel, n_keep, kept_idx,
     pages of `block` tokens; pool_op "sum" (rk_snapkv_evict) or "max"
     (rk_snapkv_evict_pool with RK_POOL_MAX)."""
     _need_contig(q_win, k, v, kept_idx, k_out, v_out, pooled, kmax, kmin)
+    _need_dtype(k.dtype, q_win, v, k_out, v_out, kmax, kmin)
+    _need_dtype(torch.int32, kept_idx)
+    _need_dtype(torch.float32, pooled)
     B, Hq, W, d = q_win.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     nbytes = rk_snapkv_workspace_bytes(shape, seq_len, window)
@@ -163,6 +180,8 @@ def rk_hsa_build_aux(k, n_tokens, first_token, block, kmax, kmin, n_q_heads=None
     """HSA step 1.  k [B,Hkv,cap,d]; kmax, kmin [B,Hkv,d,nblk_cap] (kmin None: Kmax only);
     idx [B,Hkv,stride] int32 or None (page token n is row idx[n])."""
     _need_contig(k, kmax, kmin, idx)
+    _need_dtype(k.dtype, kmax, kmin)
+    _need_dtype(torch.int32, idx)
     B, Hkv, cap, d = k.shape
     shape = shape_of(B, n_q_heads or Hkv, Hkv, d, _dtype_code(k))
     _check(_lib.rk_hsa_build_aux(ctypes.byref(shape), _ptr(k), cap, _ptr(idx),
@@ -182,6 +201,7 @@ def rk_append_kv(k_new, v_new, k, v, pos, kmax, kmin, block, n_q_heads=None, str
     """Append row `pos` (k_new, v_new [B,Hkv,d]) to k, v [B,Hkv,cap,d] and fold it
     into page pos // block of kmax, kmin [B,Hkv,d,nblk_cap]."""
     _need_contig(k_new, v_new, k, v, kmax, kmin)
+    _need_dtype(k.dtype, k_new, v_new, v, kmax, kmin)
     B, Hkv, cap, d = k.shape
     shape = shape_of(B, n_q_heads or Hkv, Hkv, d, _dtype_code(k))
     _check(_lib.rk_append_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k), _ptr(v), cap, pos,
@@ -198,6 +218,9 @@ def rk_hsa_decode(q, k, v, kmax, kmin, n_tokens, block, k1, k2, out, sel_blocks=
     out [B,Hq,d] fp32; optional sel_blocks [B,Hkv,min(k2,nblk)], sel_channels [B,Hkv,k1],
     block_scores [B,Hkv,nblk]."""
     _need_contig(q, k, v, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    _need_dtype(k.dtype, q, v, kmax, kmin)
+    _need_dtype(torch.int32, sel_blocks, sel_channels)
+    _need_dtype(torch.float32, out, block_scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     ws = _ws(rk_hsa_workspace_bytes(shape, n_tokens, block, k1, k2), k, ws, stream)
@@ -213,6 +236,9 @@ def rk_hsa_append_decode(q, k_new, v_new, k, v, pos, kmax, kmin, block, k1, k2, 
                          stream=None):
     """rk_append_kv at pos followed by rk_hsa_decode over pos + 1 tokens, in one call."""
     _need_contig(q, k_new, v_new, k, v, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    _need_dtype(k.dtype, q, k_new, v_new, v, kmax, kmin)
+    _need_dtype(torch.int32, sel_blocks, sel_channels)
+    _need_dtype(torch.float32, out, block_scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     ws = _ws(rk_hsa_workspace_bytes(shape, pos + 1, block, k1, k2), k, ws, stream)
@@ -236,6 +262,9 @@ def rk_hsa_decode_noalloc(q, k, v, kmax, kmin, n_tokens, block, k1, k2, out, sel
     """rk_hsa_decode with the library's static scratch instead of a workspace:
     allocates nothing (every tensor, out included, comes from the caller)."""
     _need_contig(q, k, v, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    _need_dtype(k.dtype, q, v, kmax, kmin)
+    _need_dtype(torch.int32, sel_blocks, sel_channels)
+    _need_dtype(torch.float32, out, block_scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     _check(_lib.rk_hsa_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), k.shape[2],
@@ -252,6 +281,9 @@ def rk_hsa_decode_mt(q, k, v, cand_idx, n_cand, kmax, kmin, block, k1, k2, out, 
                      sel_channels=None, block_scores=None, ws=None, stream=None):
     """RocketKV-MT decode over the candidate rows cand_idx [B,Hkv,stride] of the full k, v."""
     _need_contig(q, k, v, cand_idx, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    _need_dtype(k.dtype, q, v, kmax, kmin)
+    _need_dtype(torch.int32, cand_idx, sel_blocks, sel_channels)
+    _need_dtype(torch.float32, out, block_scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     ws = _ws(rk_hsa_workspace_bytes(shape, n_cand, block, k1, k2), k, ws, stream)
@@ -322,7 +354,8 @@ for _f in ("rk_paged_write_kv", "rk_paged_build_aux", "rk_paged_append_kv", "rk_
 def paged_kv(block_table, n_pages: int, page_tokens: int) -> RkPagedKv:
     """Descriptor of a paged pool: block_table [B, stride] int32 on the device."""
     _need_contig(block_table)
-    return RkPagedKv(block_table.data_ptr(), block_table.shape[1], n_pages, page_tokens)
+    _need_dtype(torch.int32, block_table)
+    return RkPagedKv(_ptr(block_table).value, block_table.shape[1], n_pages, page_tokens)
 
 
 def rk_paged_write_kv(k_src, v_src, first_token, n_tokens, k_pool, v_pool, pages: RkPagedKv, n_q_heads=None,
@@ -407,6 +440,9 @@ def rk_adakv_evict(q_win, k, v, seq_len, window, pool_kernel, n_keep, kept_idx, 
     """Stage 1 with the shared (Ada-KV) budget.  kept_idx [B,Hkv,out_cap], kept_count [B,Hkv] int32;
     k_out, v_out [B,Hkv,out_cap,d] or None; kmax/kmin and pool_op as rk_snapkv_evict."""
     _need_contig(q_win, k, v, kept_idx, kept_count, k_out, v_out, pooled, kmax, kmin)
+    _need_dtype(k.dtype, q_win, v, k_out, v_out, kmax, kmin)
+    _need_dtype(torch.int32, kept_idx, kept_count)
+    _need_dtype(torch.float32, pooled)
     B, Hq, W, d = q_win.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     ws = _ws(rk_snapkv_workspace_bytes(shape, seq_len, window), k, ws, stream)
@@ -424,6 +460,9 @@ def rk_hsa_decode_ragged(q, k, v, kmax, kmin, unit_tokens, max_tokens, block, k1
                          sel_channels=None, block_scores=None, ws=None, stream=None):
     """rk_hsa_decode with a token count per unit (unit_tokens [B,Hkv] int32 on the device)."""
     _need_contig(q, k, v, kmax, kmin, unit_tokens, out, sel_blocks, sel_channels, block_scores)
+    _need_dtype(k.dtype, q, v, kmax, kmin)
+    _need_dtype(torch.int32, unit_tokens, sel_blocks, sel_channels)
+    _need_dtype(torch.float32, out, block_scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     ws = _ws(rk_hsa_workspace_bytes(shape, max_tokens, block, k1, k2), k, ws, stream)

@@ -293,3 +293,26 @@ def test_paged_descriptor_checked_before_any_launch(rk):
     assert dec(shape=f32) == rk.RK_EUNSUPPORTED        # bf16 only
     assert lib.rk_paged_hsa_decode(ctypes.byref(sh), f, f, f, None, f, f, 16, 200, 16, 16, 8, f, None, None,
                                    None, f, 1 << 20, None) == rk.RK_EINVAL
+
+
+def test_binding_refuses_host_tensors_and_wrong_types(rk):
+    """The binding stops a host tensor (whose address a kernel would fault on)
+    and index / output tensors of the wrong element type before the library
+    is called."""
+    import torch
+    k = torch.zeros(1, 2, 64, 64)
+    kmax = torch.zeros(1, 2, 64, 8)
+    with pytest.raises(ValueError, match="on the GPU"):
+        rk.rk_hsa_build_aux(k, 64, 0, 16, kmax, kmax.clone())
+    with pytest.raises(TypeError):
+        rk.rk_hsa_build_aux(k, 64, 0, 16, kmax.to(torch.bfloat16), kmax.clone())
+    with pytest.raises(TypeError):
+        rk.rk_hsa_build_aux(k, 64, 0, 16, kmax, kmax.clone(), idx=torch.zeros(1, 2, 64, dtype=torch.int64))
+    q = torch.zeros(1, 4, 64)
+    with pytest.raises(TypeError):   # the output is float32
+        rk.rk_hsa_decode(q, k, k, kmax, kmax, 64, 16, 16, 4, torch.zeros(1, 4, 64, dtype=torch.float64))
+    with pytest.raises(TypeError):   # indices are int32
+        rk.rk_hsa_decode(q, k, k, kmax, kmax, 64, 16, 16, 4, torch.zeros(1, 4, 64),
+                         sel_blocks=torch.zeros(1, 2, 4, dtype=torch.int64))
+    with pytest.raises(TypeError):   # the paged block table is int32
+        rk.paged_kv(torch.zeros(1, 4, dtype=torch.int64), 4, 16)
