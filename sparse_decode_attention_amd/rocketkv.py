@@ -323,6 +323,9 @@ def rk_select_decode(method, q, k, v, kmax, kmin, n_tokens, page, channels, k2, 
     """One decode step of a selection method.  kmax/kmin: aux in pages of `page`
     tokens (hsa, quest); the block-1 Kmax (sparq, kmin may be None); None (exact)."""
     _need_contig(q, k, v, kmax, kmin, out, sel, scores)
+    _need_dtype(k.dtype, q, v, kmax, kmin)
+    _need_dtype(torch.int32, sel)
+    _need_dtype(torch.float32, out, scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k.shape[1], d, _dtype_code(k))
     ws = _ws(rk_hsa_workspace_bytes(shape, n_tokens, page, channels, k2), k, ws, stream)
@@ -362,6 +365,7 @@ def rk_paged_write_kv(k_src, v_src, first_token, n_tokens, k_pool, v_pool, pages
                       stream=None):
     """Copy rows [first, first + n) of k_src, v_src [B,Hkv,cap,d] into the paged pool."""
     _need_contig(k_src, v_src, k_pool, v_pool)
+    _need_dtype(k_pool.dtype, k_src, v_src, v_pool)
     B, Hkv, cap, d = k_src.shape
     shape = shape_of(B, n_q_heads or Hkv, Hkv, d, _dtype_code(k_src))
     _check(_lib.rk_paged_write_kv(ctypes.byref(shape), _ptr(k_src), _ptr(v_src), cap, first_token, n_tokens,
@@ -373,6 +377,7 @@ def rk_paged_build_aux(k_pool, pages: RkPagedKv, batch, n_tokens, first_token, b
                        n_q_heads=None, stream=None):
     """HSA step 1 over a paged pool k_pool [n_pages,Hkv,P,d]; kmax, kmin [B,Hkv,d,nblk_cap]."""
     _need_contig(k_pool, kmax, kmin)
+    _need_dtype(k_pool.dtype, kmax, kmin)
     _, Hkv, _, d = k_pool.shape
     shape = shape_of(batch, n_q_heads or Hkv, Hkv, d, _dtype_code(k_pool))
     _check(_lib.rk_paged_build_aux(ctypes.byref(shape), _ptr(k_pool), ctypes.byref(pages), n_tokens, first_token,
@@ -383,6 +388,7 @@ def rk_paged_build_aux(k_pool, pages: RkPagedKv, batch, n_tokens, first_token, b
 def rk_paged_append_kv(k_new, v_new, k_pool, v_pool, pages: RkPagedKv, pos, kmax, kmin, block, n_q_heads=None,
                        stream=None):
     _need_contig(k_new, v_new, k_pool, v_pool, kmax, kmin)
+    _need_dtype(k_pool.dtype, k_new, v_new, v_pool, kmax, kmin)
     B, Hkv, d = k_new.shape
     shape = shape_of(B, n_q_heads or Hkv, Hkv, d, _dtype_code(k_new))
     _check(_lib.rk_paged_append_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
@@ -393,6 +399,9 @@ def rk_paged_append_kv(k_new, v_new, k_pool, v_pool, pages: RkPagedKv, pos, kmax
 def rk_paged_hsa_decode(q, k_pool, v_pool, pages: RkPagedKv, kmax, kmin, n_tokens, block, k1, k2, out,
                         sel_blocks=None, sel_channels=None, block_scores=None, ws=None, stream=None):
     _need_contig(q, k_pool, v_pool, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    _need_dtype(k_pool.dtype, q, v_pool, kmax, kmin)
+    _need_dtype(torch.int32, sel_blocks, sel_channels)
+    _need_dtype(torch.float32, out, block_scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k_pool.shape[1], d, _dtype_code(k_pool))
     ws = _ws(rk_hsa_workspace_bytes(shape, n_tokens, block, k1, k2), k_pool, ws, stream)
@@ -407,6 +416,9 @@ def rk_paged_hsa_append_decode(q, k_new, v_new, k_pool, v_pool, pages: RkPagedKv
                                k2, out, sel_blocks=None, sel_channels=None, block_scores=None, ws=None,
                                stream=None):
     _need_contig(q, k_new, v_new, k_pool, v_pool, kmax, kmin, out, sel_blocks, sel_channels, block_scores)
+    _need_dtype(k_pool.dtype, q, k_new, v_new, v_pool, kmax, kmin)
+    _need_dtype(torch.int32, sel_blocks, sel_channels)
+    _need_dtype(torch.float32, out, block_scores)
     B, Hq, d = q.shape
     shape = shape_of(B, Hq, k_pool.shape[1], d, _dtype_code(k_pool))
     ws = _ws(rk_hsa_workspace_bytes(shape, pos + 1, block, k1, k2), k_pool, ws, stream)
