@@ -69,6 +69,10 @@ def parse():
                          "RocketKV) on the Llama-8B layer and the 109K needle: recall of the exact top "
                          "tokens, attention mass, output error, needle hits, us per decode step")
     ap.add_argument("--recall-steps", type=int, default=8)
+    ap.add_argument("--evict-compare", default="", metavar="WORKLOADS",
+                    help="only time stage 1 on the given comma-separated workloads, per-head SnapKV "
+                         "against Ada-KV's shared budget (both with compaction and Kmax/Kmin): ms per "
+                         "layer and per-kernel us, one JSON line per workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (scales the HBM byte "
                          "counters FETCH_SIZE / WRITE_SIZE of a profiler run)")
@@ -362,6 +366,70 @@ def measure(rk, WL, name, args, dev, with_cpu):
     return res
 
 
+def evict_compare(args):
+    """Stage 1 alone: rk_snapkv_evict against rk_adakv_evict on one layer of
+    each workload, both compacting and building Kmax/Kmin, the same workspace;
+    medians over args.steps calls after args.warmup, plus the library's
+    per-kernel times of one call."""
+    import statistics
+
+    import torch
+
+    from sparse_decode_attention_amd import rocketkv as rk
+    from sparse_decode_attention_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for wname in args.evict_compare.split(","):
+        w = WL.WORKLOADS[wname]
+        S, W = w.seq, w.window
+        n_keep = rk.rk_split(w.c, S, W, w.block, w.d)["n_keep"]
+        k, v, _ = WL.layer_kv(w, 0, device=dev)
+        qw = WL.window_queries(w, 0, device=dev)
+        B, Hkv, d = w.batch, w.n_kv, w.d
+        cap = rk.adakv_capacity(Hkv, S, W, n_keep)
+        ws = torch.empty(rk.rk_snapkv_workspace_bytes(rk.shape_of(B, w.n_q, Hkv, d, k.dtype), S, W),
+                         dtype=torch.uint8, device=dev)
+        res = {"evict_compare": wname, "n_keep": n_keep, "ada_out_cap": cap}
+        for mode in ("snapkv", "adakv"):
+            oc = cap if mode == "adakv" else n_keep
+            kept = torch.empty(B, Hkv, oc, dtype=torch.int32, device=dev)
+            cnt = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+            kk = torch.empty(B, Hkv, oc, d, dtype=k.dtype, device=dev)
+            vv = torch.empty_like(kk)
+            kmax = torch.empty(B, Hkv, d, rk.aux_capacity(oc, w.block), dtype=k.dtype, device=dev)
+            kmin = torch.empty_like(kmax)
+
+            def run():
+                if mode == "adakv":
+                    rk.rk_adakv_evict(qw, k, v, S, W, w.pool, n_keep, kept, cnt, kk, vv, ws=ws, kmax=kmax,
+                                      kmin=kmin, block=w.block)
+                else:
+                    rk.rk_snapkv_evict(qw, k, v, S, W, w.pool, n_keep, kept, kk, vv, None, ws=ws, kmax=kmax,
+                                       kmin=kmin, block=w.block)
+
+            for _ in range(args.warmup):
+                run()
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(args.steps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                run()
+                b.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b))
+            rk.rk_profile_begin()
+            run()
+            prof = rk.rk_profile_end()
+            res[mode + "_ms_per_layer"] = round(statistics.median(times), 4)
+            res[mode + "_kernels_us"] = {n: round(t[1] * 1e3, 1) for n, t in prof.items()}
+            del kept, cnt, kk, vv, kmax, kmin
+        print(json.dumps(res), flush=True)
+        del k, v, qw, ws
+        torch.cuda.empty_cache()
+
+
 def selection_recall(args):
     """Selection quality of each method at its planned budget split (one layer,
     full prompt; RocketKV adds SnapKV eviction first), against exact attention
@@ -499,6 +567,9 @@ def main():
         return
     if args.selection_recall:
         selection_recall(args)
+        return
+    if args.evict_compare:
+        evict_compare(args)
         return
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only (the hot path shards over (batch, KV head) units "
