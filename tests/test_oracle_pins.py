@@ -453,3 +453,17 @@ def test_attention_single_key_returns_its_value():
     v = np.array([[0.5, -2.0, 3.25]])
     out = O.attention(np.array([[900.0, 0.0, 0.0]]), np.array([[1.0, 0.0, 0.0]]), v)
     np.testing.assert_allclose(out[0], v[0], rtol=0, atol=0)
+
+
+def test_block_select_and_selected_tokens_hand_worked():
+    """Page choice and the tokens it covers, worked by hand: ties go to the
+    lower page, the choice is ascending, k2 past the page count takes every
+    page, and a ragged last page covers only its valid tokens."""
+    s1 = np.array([0.5, 2.0, 2.0, -1.0, 3.0], np.float32)
+    assert O.block_select(s1, 1).tolist() == [4]
+    assert O.block_select(s1, 2).tolist() == [1, 4]          # 2.0 at pages 1 and 2: the lower wins
+    assert O.block_select(s1, 3).tolist() == [1, 2, 4]
+    assert O.block_select(s1, 99).tolist() == [0, 1, 2, 3, 4]
+    assert O.selected_tokens(np.array([0, 2]), 8, 3).tolist() == [0, 1, 2, 6, 7]
+    assert O.selected_tokens(np.array([1]), 8, 3).tolist() == [3, 4, 5]
+    assert O.selected_tokens(np.array([], np.int64), 8, 3).tolist() == []
